@@ -1,0 +1,121 @@
+/*
+ * wtconv.h -- C ABI of libwtconv, the WTConv layer (wavelet convolution) for
+ * AMD Instinct MI355X (gfx950), forward and backward.
+ *
+ * The layer, per channel c of an NCHW activation x (source: "Fast and
+ * Memory-Efficient Wavelet Convolutions via I/O-Aware Reformulation", arXiv
+ * 2608.10805; its English abstract describes WTConv as a drop-in replacement
+ * for a depthwise convolution, and the technical summary's Methodology section
+ * describes the analysis, the per-level convolutions with learned per-channel
+ * scales, and the synthesis cascade):
+ *
+ *   y = s0[c] * (W0[c] (*) x + b0[c])
+ *     + sum over levels l = 1..L of the Haar synthesis, from level l back to full
+ *       resolution, of Z_l^b = s_l[4c+b] * (W_l[4c+b] (*) A_l^b),  b = 0..3,
+ *
+ * where A_l^0..3 are the four subbands of the orthonormal 2D Haar analysis
+ * (2x2 taps of +-1/2) of the level-(l-1) low-pass band (level 0 is x itself),
+ * (*) is a k x k cross-correlation with zero 'same' padding at the level's own
+ * resolution, and the synthesis of level l adds the reconstruction of level l+1
+ * into the low-pass band before its inverse Haar step.  Band order: 0 low-pass,
+ * 1 top-row-minus-bottom-row, 2 left-column-minus-right-column, 3 diagonal.
+ *
+ * Layout
+ *   activations  x, y, dy, dx: NCHW contiguous, fp32 (WTCONV_F32) or fp16
+ *                (WTCONV_F16) per the descriptor; device memory, 16-byte aligned.
+ *   parameters   always fp32, device memory:
+ *                w_base [C][k][k], bias [C] (may be NULL: zero bias), s_base [C],
+ *                w_lvl [L][4C][k][k] and s_lvl [L][4C] with band b of channel c
+ *                at index 4c+b (both may be NULL when L == 0).
+ *   gradients    fp32, same shapes as their parameters; OVERWRITTEN, never
+ *                accumulated.  dw/ds are gradients of the raw (unfolded)
+ *                weights and scales.
+ * Shape rules  n, c, h, w >= 1; k in {1, 3, 5, 7}; 0 <= L <= WTCONV_MAX_LEVELS;
+ *              h and w divisible by 2^L and h, w <= WTCONV_MAX_SIDE.
+ * fp16 mode    fp16 storage of activations only: every product and sum is fp32,
+ *              each output element is rounded once to fp16 (round to nearest
+ *              even).
+ * Ownership    The caller allocates every buffer, including the workspace
+ *              (size from wtconv_workspace_size).  The library allocates no
+ *              device memory and holds no state between calls; calls are
+ *              reentrant.
+ * Execution    All work is enqueued on `stream` (0 = the null stream) with no
+ *              host synchronisation; outputs are ready when the stream reaches
+ *              that point.  Inputs and outputs must not overlap (y != x,
+ *              dx != dy).  Results are bitwise reproducible run to run (no
+ *              floating-point atomics).
+ * Errors       Arguments are validated before any HIP call; a bad argument
+ *              returns its status code and enqueues nothing.  A failed kernel
+ *              launch returns WTCONV_ERR_HIP.  Asynchronous faults are reported
+ *              by the HIP runtime at the caller's next synchronisation.
+ */
+#ifndef WTCONV_H
+#define WTCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WTCONV_MAX_LEVELS 6
+#define WTCONV_MAX_SIDE 4096
+
+typedef enum {
+    WTCONV_OK = 0,
+    WTCONV_ERR_NULL = 1,        /* a required pointer is NULL */
+    WTCONV_ERR_SHAPE = 2,       /* sizes, levels or divisibility rule violated */
+    WTCONV_ERR_UNSUPPORTED = 3, /* kernel size or dtype not built */
+    WTCONV_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    WTCONV_ERR_HIP = 5,         /* the HIP runtime rejected a launch */
+    WTCONV_ERR_ALIAS = 6        /* an output overlaps an input */
+} wtconv_status_t;
+
+typedef enum { WTCONV_F32 = 0, WTCONV_F16 = 1 } wtconv_dtype_t;
+
+typedef enum { WTCONV_OP_FWD = 0, WTCONV_OP_BWD_DATA = 1, WTCONV_OP_BWD_WEIGHT = 2 } wtconv_op_t;
+
+typedef struct {
+    int64_t n, c, h, w;   /* activation shape, NCHW */
+    int32_t k;            /* odd kernel size of the base and every per-level conv */
+    int32_t levels;       /* number of Haar levels L */
+    int32_t dtype;        /* wtconv_dtype_t of the activations */
+} wtconv_desc_t;
+
+/* hipStream_t without pulling in the HIP headers. */
+typedef struct ihipStream_t *wtconv_stream_t;
+
+/* Bytes of device workspace `op` needs for `desc` (0 for the forward and the
+ * data backward).  Errors as for the op itself. */
+wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op, size_t *bytes);
+
+/* y = WTConv(x).  The per-channel scales are folded into the weights (and the
+ * base scale into the bias) on chip, the Haar analysis is recomputed on chip
+ * from the staged input, and the synthesis of all levels is one closed-form
+ * pass indexed by the bits of each output coordinate (technical summary,
+ * Methodology, reformulations 1-3).  x is read once and y written once. */
+wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,
+                               const float *s_base, const float *w_lvl, const float *s_lvl, void *y,
+                               void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
+
+/* dx = d<dy, WTConv(x)>/dx.  The layer is linear in x and the orthonormal Haar
+ * synthesis is the transpose of the analysis, so this is the same fused pass
+ * on dy with every kernel turned by 180 degrees and no bias.  Forward outputs
+ * and all gradients are part of the method (technical summary, Key
+ * Contributions). */
+wtconv_status_t wtconv_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
+                                     const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
+                                     void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char *wtconv_status_string(wtconv_status_t status);
+
+/* Library version, "major.minor.patch". */
+const char *wtconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WTCONV_H */

@@ -1,0 +1,146 @@
+// wtconv_api.hip -- the C ABI of libwtconv (include/wtconv.h): argument
+// validation, launch planning and dispatch.  Validation happens before any HIP
+// call; nothing is allocated; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/wtconv.h"
+#include "wtconv_launch.h"
+
+int wtc_dwconv_max_width(int k);
+hipError_t wtc_launch_dwconv(int dtype, int k, const void *in, void *out, const float *w_base, const float *bias,
+                             const float *s_base, int N, int C, int H, int W, int rotate, hipStream_t stream);
+
+namespace {
+
+constexpr int kFusedThreads = 256;
+constexpr int kMaxLdsFloats = 160 * 1024 / 4;
+
+// LDS budget of one fused workgroup.  The default keeps two workgroups per
+// compute unit; WTCONV_LDS_KB (16..160) overrides it for tuning.
+int lds_budget_floats()
+{
+    int kb = 64;
+    if (const char *e = std::getenv("WTCONV_LDS_KB")) {
+        int v = std::atoi(e);
+        if (v >= 16 && v <= 160) kb = v;
+    }
+    return kb * 1024 / 4;
+}
+
+wtconv_status_t check_desc(const wtconv_desc_t *d)
+{
+    if (!d) return WTCONV_ERR_NULL;
+    if (d->n < 1 || d->c < 1 || d->h < 1 || d->w < 1) return WTCONV_ERR_SHAPE;
+    if (d->h > WTCONV_MAX_SIDE || d->w > WTCONV_MAX_SIDE) return WTCONV_ERR_SHAPE;
+    if (d->levels < 0 || d->levels > WTCONV_MAX_LEVELS) return WTCONV_ERR_SHAPE;
+    const int64_t g = (int64_t)1 << d->levels;
+    if (d->h % g || d->w % g) return WTCONV_ERR_SHAPE;
+    if (d->k != 1 && d->k != 3 && d->k != 5 && d->k != 7) return WTCONV_ERR_UNSUPPORTED;
+    if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_F16) return WTCONV_ERR_UNSUPPORTED;
+    if (d->n * d->c > (int64_t)1 << 24) return WTCONV_ERR_SHAPE;  // grid size
+    if (d->levels == 0 && d->w > wtc_dwconv_max_width(d->k)) return WTCONV_ERR_UNSUPPORTED;
+    return WTCONV_OK;
+}
+
+size_t act_bytes(const wtconv_desc_t *d)
+{
+    return (size_t)(d->n * d->c * d->h * d->w) * (d->dtype == WTCONV_F32 ? 4 : 2);
+}
+
+bool overlaps(const void *a, const void *b, size_t bytes)
+{
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + bytes && pb < pa + bytes;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+wtconv_status_t check_params(const wtconv_desc_t *d, const float *w_base, const float *s_base, const float *w_lvl,
+                             const float *s_lvl)
+{
+    if (!w_base || !s_base) return WTCONV_ERR_NULL;
+    if (d->levels > 0 && (!w_lvl || !s_lvl)) return WTCONV_ERR_NULL;
+    return WTCONV_OK;
+}
+
+wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *w_base, const float *bias,
+                           const float *s_base, const float *w_lvl, const float *s_lvl, void *out, int rotate,
+                           wtconv_stream_t stream)
+{
+    wtconv_status_t st = check_desc(d);
+    if (st != WTCONV_OK) return st;
+    if (!in || !out) return WTCONV_ERR_NULL;
+    if ((st = check_params(d, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
+    if (!aligned16(in) || !aligned16(out)) return WTCONV_ERR_UNSUPPORTED;
+    if (overlaps(in, out, act_bytes(d))) return WTCONV_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (d->levels == 0) {
+        e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
+                              (int)d->w, rotate, s);
+    } else {
+        WtcFusedPlan p;
+        if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                kFusedThreads, lds_budget_floats()) &&
+            wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                kFusedThreads, kMaxLdsFloats))
+            return WTCONV_ERR_UNSUPPORTED;
+        e = wtc_launch_fused(d->dtype, p, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
+    }
+    return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op, size_t *bytes)
+{
+    wtconv_status_t st = check_desc(desc);
+    if (st != WTCONV_OK) return st;
+    if (!bytes) return WTCONV_ERR_NULL;
+    switch (op) {
+    case WTCONV_OP_FWD:
+    case WTCONV_OP_BWD_DATA: *bytes = 0; return WTCONV_OK;
+    default: return WTCONV_ERR_UNSUPPORTED;
+    }
+}
+
+wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,
+                               const float *s_base, const float *w_lvl, const float *s_lvl, void *y,
+                               void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return fused_pass(desc, x, w_base, bias, s_base, w_lvl, s_lvl, y, 0, stream);
+}
+
+wtconv_status_t wtconv_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
+                                     const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
+                                     void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    return fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, stream);
+}
+
+const char *wtconv_status_string(wtconv_status_t status)
+{
+    switch (status) {
+    case WTCONV_OK: return "ok";
+    case WTCONV_ERR_NULL: return "a required pointer is NULL";
+    case WTCONV_ERR_SHAPE: return "invalid shape, level count or divisibility";
+    case WTCONV_ERR_UNSUPPORTED: return "unsupported kernel size, dtype, alignment or size";
+    case WTCONV_ERR_WORKSPACE: return "workspace missing or too small";
+    case WTCONV_ERR_HIP: return "HIP launch error";
+    case WTCONV_ERR_ALIAS: return "an output overlaps an input";
+    default: return "unknown status";
+    }
+}
+
+const char *wtconv_version(void) { return "0.1.0"; }
+
+}  // extern "C"

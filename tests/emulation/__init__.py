@@ -1,0 +1,80 @@
+"""Loader of the CPU emulation of the fused kernels (test tool, see wtconv_emu.cpp)."""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(os.path.dirname(_HERE))
+_SRC = os.path.join(_HERE, "wtconv_emu.cpp")
+_DEPS = [_SRC] + [os.path.join(_ROOT, "level_haar_wavelet_amd", "csrc", f)
+                  for f in ("wtconv_fused_body.h", "wtconv_plan.h")]
+_LIB = os.path.join(_ROOT, "_build", "libwtconv_emu.so")
+_lib = None
+
+
+def _compiler():
+    for cand in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def available():
+    return _compiler() is not None
+
+
+def build():
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(d) > os.path.getmtime(_LIB) for d in _DEPS)
+    if stale:
+        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run([_compiler(), "-std=c++17", "-O2", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        vp = ctypes.c_void_p
+        ci = ctypes.c_int
+        lib.emu_fused.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci]
+        lib.emu_fused.restype = ci
+        lib.emu_fused_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
+        lib.emu_fused_plan.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def fused_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, budget_floats=16384):
+    out = (ctypes.c_int * 8)()
+    rc = _load().emu_fused_plan(n, c, h, w, k, levels, rotate, nthreads, budget_floats, out)
+    if rc != 0:
+        raise ValueError("no plan")
+    keys = ("tile_h", "tile_w", "strip_h", "out_bw", "tiles_y", "tiles_x", "lds_floats", "nthreads")
+    return dict(zip(keys, list(out)))
+
+
+def fused(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32", nthreads=256,
+          budget_floats=16384):
+    """Run the fused pass on the CPU emulation.  x: (N, C, H, W) float array."""
+    lib = _load()
+    n, c, h, w = x.shape
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    out = np.full_like(xin, np.nan)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.emu_fused(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, k, levels,
+                       rotate, *[ptr(a) for a in keep], nthreads, budget_floats)
+    if rc != 0:
+        raise ValueError("emu_fused failed: %d" % rc)
+    return out.astype(np.float64)

@@ -1,0 +1,108 @@
+// wtconv_emu.cpp -- CPU emulation of the fused WTConv kernels (test tool).
+//
+// Runs the very phase functions the GPU kernels run (wtconv_fused_body.h),
+// one workgroup after another and, inside a phase, one thread after another,
+// with every LDS, input and output access bounds-checked (an out-of-range
+// index aborts the process with its line number).  Barriers fall between
+// phases, so this ordering is one legal interleaving of the workgroup.  Used
+// by the CPU test suite to check the tiling, strip and LDS-layout logic against
+// the oracle before any GPU run; it is never part of the product library.
+#define WTC_EMULATE 1
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../level_haar_wavelet_amd/csrc/wtconv_fused_body.h"
+
+template <typename T, int K, int BW>
+static void run_fused(const WtcFusedArgs<T> &a)
+{
+    const WtcFusedPlan &p = a.p;
+    const int nblocks = p.n * p.c * p.tiles_y * p.tiles_x;
+    std::vector<float> lds((size_t)p.lds_floats);
+    const int nth = p.nthreads;
+    for (int bid = 0; bid < nblocks; ++bid) {
+        // poison LDS so that a read of a value no phase wrote shows up as NaN
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcCtx<T>> ctx((size_t)nth);
+        for (int t = 0; t < nth; ++t) {
+            ctx[t].lds = lds.data();
+            ctx[t].tid = t;
+            ctx[t].nth = nth;
+            ctx[t].lds_n = p.lds_floats;
+            ctx[t].plane_n = (int64_t)p.h * p.w;
+            wtc_fused_setup<T>(a, ctx[t], bid, nblocks);
+        }
+        for (int t = 0; t < nth; ++t) wtc_phase_fold<T, K>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_phase_coarse<T, K>(a, ctx[t]);
+        for (int m = 2; m <= p.levels; ++m)
+            for (int t = 0; t < nth; ++t) wtc_phase_deep_level<T, K>(a, ctx[t], m);
+        for (int t = 0; t < nth; ++t) wtc_phase_deep_conv<T, K>(a, ctx[t]);
+        const int ty0 = ctx[0].ty0;
+        for (int s0 = ty0; s0 < ty0 + p.tile_h; s0 += p.strip_h) {
+            for (int t = 0; t < nth; ++t) wtc_phase_stage<T, K>(a, ctx[t], s0);
+            for (int t = 0; t < nth; ++t) wtc_phase_strip_bands<T, K>(a, ctx[t], s0);
+            for (int t = 0; t < nth; ++t) wtc_phase_strip_conv1<T, K>(a, ctx[t], s0);
+            for (int t = 0; t < nth; ++t) wtc_phase_strip_out<T, K, BW>(a, ctx[t], s0);
+        }
+    }
+}
+
+template <typename T, int K>
+static void run_k(const WtcFusedArgs<T> &a)
+{
+    switch (a.p.out_bw) {
+    case 8: run_fused<T, K, 8>(a); break;
+    case 4: run_fused<T, K, 4>(a); break;
+    default: run_fused<T, K, 2>(a); break;
+    }
+}
+
+template <typename T>
+static int run_t(const WtcFusedArgs<T> &a)
+{
+    switch (a.p.k) {
+    case 1: run_k<T, 1>(a); return 0;
+    case 3: run_k<T, 3>(a); return 0;
+    case 5: run_k<T, 5>(a); return 0;
+    case 7: run_k<T, 7>(a); return 0;
+    default: return -1;
+    }
+}
+
+extern "C" {
+
+// Plan of a fused launch, for inspection by the tests: fills out[0..7] with
+// tile_h, tile_w, strip_h, out_bw, tiles_y, tiles_x, lds_floats, nthreads.
+int emu_fused_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int budget_floats,
+                   int *out)
+{
+    WtcFusedPlan p;
+    if (wtc_make_fused_plan(&p, n, c, h, w, k, levels, rotate, nthreads, budget_floats)) return -1;
+    out[0] = p.tile_h;
+    out[1] = p.tile_w;
+    out[2] = p.strip_h;
+    out[3] = p.out_bw;
+    out[4] = p.tiles_y;
+    out[5] = p.tiles_x;
+    out[6] = p.lds_floats;
+    out[7] = p.nthreads;
+    return 0;
+}
+
+// The fused pass on host arrays.  dtype 0: float in/out, 1: _Float16 in/out.
+int emu_fused(int dtype, const void *in, void *out, int n, int c, int h, int w, int k, int levels, int rotate,
+              const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+              int nthreads, int budget_floats)
+{
+    WtcFusedPlan p;
+    if (wtc_make_fused_plan(&p, n, c, h, w, k, levels, rotate, nthreads, budget_floats)) return -1;
+    if (dtype == 0) {
+        WtcFusedArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        return run_t<float>(a);
+    }
+    WtcFusedArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return run_t<_Float16>(a);
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+"""The fused kernels' phase code run on the CPU (bounds-checked emulation)
+against the oracle.  Small LDS budgets force tiling and short strips so that
+the halo, clipping and strip logic is exercised on shapes the oracle finishes
+instantly."""
+import numpy as np
+import pytest
+
+from level_haar_wavelet_amd.synthetic import make_inputs
+from tests import emulation as emu
+
+pytestmark = pytest.mark.skipif(not emu.available(), reason="no clang++ for the emulation")
+
+
+def _check(y, ref, tol=1e-4):
+    assert not np.isnan(y).any()
+    err = np.abs(y - ref) / (1.0 + np.abs(ref))
+    assert err.max() <= tol, err.max()
+
+
+CASES = [
+    # n, c, h, w, k, L, budget floats (None: whole plane)
+    (2, 3, 16, 16, 5, 2, None),
+    (1, 2, 16, 24, 3, 3, None),
+    (1, 2, 8, 8, 7, 1, None),
+    (1, 2, 12, 20, 1, 2, None),
+    (1, 1, 56, 56, 5, 3, None),
+    (1, 2, 28, 28, 5, 2, None),
+    (1, 1, 32, 32, 5, 5, None),
+    (1, 1, 64, 64, 5, 4, 9000),    # strips
+    (1, 1, 64, 96, 3, 3, 4000),    # tiles and strips
+    (1, 1, 64, 64, 5, 2, 3500),    # small tiles, short strips
+    (1, 2, 48, 80, 5, 4, 5000),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_fused_matches_oracle(orc, case, rotate):
+    n, c, h, w, k, L, budget = case
+    inp = make_inputs(n, c, h, w, k, L, seed=h + w + k + L)
+    budget = budget or 1 << 22
+    y = emu.fused(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate,
+                  budget_floats=budget)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.x, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    _check(y, ref)
+
+
+def test_emulated_fp16(orc):
+    n, c, h, w, k, L = 1, 2, 32, 32, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, dtype="f16", seed=9)
+    y = emu.fused(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, dtype="f16")
+    ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel <= 5e-3, rel
+    # one rounding to fp16 of an fp32 result: within half an fp16 ulp plus fp32 noise
+    assert np.abs(y - ref).max() <= np.abs(ref).max() * 2.0 ** -10
+
+
+def test_plans_fit_and_tile():
+    p = emu.fused_plan(64, 96, 56, 56, 5, 3, budget_floats=1 << 22)
+    assert (p["tile_h"], p["tile_w"], p["strip_h"]) == (56, 56, 56)
+    p = emu.fused_plan(1, 1, 64, 64, 5, 4, budget_floats=9000)
+    assert p["lds_floats"] <= 9000 and p["strip_h"] < p["tile_h"]
+    p = emu.fused_plan(1, 1, 64, 96, 3, 3, budget_floats=4000)
+    assert p["lds_floats"] <= 4000 and p["tiles_y"] * p["tiles_x"] > 1

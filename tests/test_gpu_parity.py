@@ -1,0 +1,124 @@
+"""GPU parity: libwtconv against the CPU oracle, element by element, on the
+same seeded inputs, through the C ABI.  Small shapes span several tiles, strips
+and ragged edges; the workload shapes are compared in full where the oracle is
+fast enough and on sampled planes otherwise."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from level_haar_wavelet_amd.synthetic import WORKLOADS, make_inputs, sweep_workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests.gpu_util import DevInputs, assert_close, backward_data, forward
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # n, c, h, w, k, L, dtype
+    (2, 8, 16, 16, 5, 2, "f32"),
+    (1, 3, 16, 24, 3, 3, "f32"),
+    (2, 2, 8, 8, 7, 1, "f32"),
+    (1, 4, 12, 20, 1, 2, "f32"),
+    (2, 3, 10, 14, 5, 1, "f32"),
+    (1, 2, 64, 48, 5, 4, "f32"),
+    (1, 2, 32, 32, 5, 5, "f32"),
+    (1, 1, 64, 64, 3, 6, "f32"),
+    (2, 3, 9, 13, 5, 0, "f32"),
+    (2, 3, 16, 16, 7, 0, "f16"),
+    (2, 8, 16, 16, 5, 2, "f16"),
+    (1, 3, 24, 40, 3, 3, "f16"),
+    (1, 2, 28, 28, 5, 2, "f16"),
+    (1, 2, 96, 160, 5, 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c)))
+def test_small_shapes(orc, case):
+    n, c, h, w, k, L, dt = case
+    _log("case %s" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=n * 1000 + h + w + k + L)
+    d = DevInputs(inp, dt)
+    y = forward(d)
+    dx = backward_data(d)
+    torch.cuda.synchronize()
+    ref_y = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    ref_dx = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(y, ref_y, dt, "y")
+    assert_close(dx, ref_dx, dt, "dx")
+
+
+def test_no_bias_and_forced_tiling(orc, monkeypatch):
+    """Small LDS budget: several tiles per plane, strips, XCD remap of tiles."""
+    monkeypatch.setenv("WTCONV_LDS_KB", "16")
+    n, c, h, w, k, L = 1, 8, 128, 96, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, seed=77)
+    inp.bias = None
+    d = DevInputs(inp, "f32")
+    y = forward(d)
+    torch.cuda.synchronize()
+    ref = orc.forward(inp.x, inp.w_base, None, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(y, ref, "f32", "y tiled")
+
+
+def test_deterministic_and_guarded(orc):
+    """Two runs are bitwise equal and nothing is written outside the output."""
+    n, c, h, w, k, L = 2, 4, 56, 56, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, seed=3)
+    d = DevInputs(inp, "f32")
+    numel = n * c * h * w
+    guard = 4096
+    buf = torch.full((numel + 2 * guard,), 12345.0, device="cuda")
+    out = buf[guard:guard + numel].view(n, c, h, w)
+    forward(d, y=out)
+    first = out.clone()
+    forward(d, y=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert bool((buf[:guard] == 12345.0).all()) and bool((buf[guard + numel:] == 12345.0).all())
+
+
+def _workload_case(orc, wl, planes=None):
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    d = DevInputs(inp, wl.dtype)
+    y = forward(d)
+    dx = backward_data(d)
+    torch.cuda.synchronize()
+    sel = slice(None) if planes is None else planes
+    xs, dys = inp.x[sel], inp.dy[sel]
+    ref_y = orc.forward(xs, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+    ref_dx = orc.backward_data(dys, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+    assert_close(y[sel], ref_y, wl.dtype, "%s y" % wl.name)
+    assert_close(dx[sel], ref_dx, wl.dtype, "%s dx" % wl.name)
+
+
+def test_workload_tiny(orc):
+    _workload_case(orc, WORKLOADS["tiny"])
+
+
+def test_workload_stage1_full(orc):
+    _log("stage1 64x96x56x56 L=3 fp32, full comparison")
+    _workload_case(orc, WORKLOADS["stage1"])
+
+
+def test_workload_stage2_full(orc):
+    _log("stage2 64x192x28x28 L=2 fp16, full comparison")
+    _workload_case(orc, WORKLOADS["stage2"])
+
+
+@pytest.mark.parametrize("wl", sweep_workloads(), ids=lambda w: "L%d_%s" % (w.levels, w.dtype))
+def test_workload_sweep_sampled(orc, wl):
+    _log("sweep 32x128x128x128 L=%d %s, samples n=0 and n=31" % (wl.levels, wl.dtype))
+    _workload_case(orc, wl, planes=np.array([0, 31]))
+
+
+def test_workload_large_sampled(orc):
+    _log("large 16x256x256x256 L=4 fp16, sample n=5")
+    _workload_case(orc, WORKLOADS["large"], planes=np.array([5]))
