@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libwtconv.so")
 ARCH = os.environ.get("WTCONV_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fno-strict-aliasing", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 

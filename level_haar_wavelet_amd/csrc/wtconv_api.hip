@@ -20,14 +20,29 @@ constexpr int kMaxLdsFloats = 160 * 1024 / 4;
 
 // LDS budget of one fused workgroup.  The default keeps two workgroups per
 // compute unit; WTCONV_LDS_KB (16..160) overrides it for tuning.
-int lds_budget_floats()
+int env_int(const char *name, int dflt, int lo, int hi)
 {
-    int kb = 64;
-    if (const char *e = std::getenv("WTCONV_LDS_KB")) {
+    if (const char *e = std::getenv(name)) {
         int v = std::atoi(e);
-        if (v >= 16 && v <= 160) kb = v;
+        if (v >= lo && v <= hi) return v;
     }
-    return kb * 1024 / 4;
+    return dflt;
+}
+
+int lds_budget_floats() { return env_int("WTCONV_LDS_KB", 64, 16, 160) * 1024 / 4; }
+
+// LDS budget of the whole-plane kernel: two workgroups per compute unit.
+int whole_budget_floats() { return env_int("WTCONV_WHOLE_LDS_KB", 80, 8, 160) * 1024 / 4; }
+
+// Images per workgroup of the whole-plane kernel: as many as keep at least
+// four workgroups per compute unit (WTCONV_PLANES overrides).
+int whole_planes(const wtconv_desc_t *d)
+{
+    int forced = env_int("WTCONV_PLANES", 0, 1, 64);
+    if (forced) return forced;
+    for (int p = 8; p > 1; p /= 2)
+        if (d->c * ((d->n + p - 1) / p) >= 1024) return p;
+    return 1;
 }
 
 wtconv_status_t check_desc(const wtconv_desc_t *d)
@@ -82,6 +97,14 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
         e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
                               (int)d->w, rotate, s);
     } else {
+        WtcWholePlan wp;
+        if (!env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
+            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                kFusedThreads, whole_planes(d), d->dtype == WTCONV_F32 ? 4 : 2,
+                                whole_budget_floats()) == 0) {
+            e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
+            return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+        }
         WtcFusedPlan p;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                 kFusedThreads, lds_budget_floats()) &&

@@ -1,0 +1,94 @@
+// wtconv_whole.hip -- the whole-plane fused WTConv forward / data-backward
+// kernel for gfx950 (phases in wtconv_whole_body.h).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "wtconv_launch.h"
+#include "wtconv_whole_body.h"
+
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads issued before it (the next image's input) stay in flight.  The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int K, int BW>
+__global__ __launch_bounds__(256) void wtconv_whole_kernel(WtcWholeArgs<T> a)
+{
+    extern __shared__ float wtc_lds[];
+    WtcWholeCtx<T> ctx;
+    ctx.lds = wtc_lds;
+    ctx.tid = threadIdx.x;
+    ctx.nth = blockDim.x;
+    wtc_whole_setup<T>(a, ctx, blockIdx.x);
+    wtc_whole_load<T, K, BW>(a, ctx, 0);
+    wtc_whole_init<T, K>(a, ctx);
+    wtc_lds_barrier();
+    wtc_whole_fold<T, K>(a, ctx);
+    wtc_whole_table<T, K, BW>(a, ctx);
+    for (int img = 0; img < ctx.nimg; ++img) {
+        wtc_whole_select<T>(a, ctx, img);
+        wtc_whole_store_input<T, K, BW>(a, ctx);
+        wtc_lds_barrier();
+        if (img + 1 < ctx.nimg) wtc_whole_load<T, K, BW>(a, ctx, img + 1);
+        wtc_whole_analysis1<T, K>(a, ctx);
+        wtc_lds_barrier();
+        for (int m = 2; m <= a.p.levels; ++m) {
+            wtc_whole_analysis<T, K>(a, ctx, m);
+            wtc_lds_barrier();
+        }
+        wtc_whole_conv<T, K, BW>(a, ctx);
+        wtc_lds_barrier();
+        // the next image's input store touches only the input map, which the
+        // convolution phase above has finished reading
+        wtc_whole_out<T, K, BW>(a, ctx);
+    }
+}
+
+template <typename T, int K, int BW>
+static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
+    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const unsigned groups = (unsigned)((a.p.n + a.p.planes - 1) / a.p.planes);
+    const unsigned blocks = groups * (unsigned)a.p.c;
+    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t launch_k(const WtcWholeArgs<T> &a, hipStream_t stream)
+{
+    switch (a.p.out_bw) {
+    case 8: return launch_bw<T, K, 8>(a, stream);
+    case 4: return launch_bw<T, K, 4>(a, stream);
+    default: return launch_bw<T, K, 2>(a, stream);
+    }
+}
+
+template <typename T>
+static hipError_t launch_t(const WtcWholeArgs<T> &a, hipStream_t stream)
+{
+    switch (a.p.k) {
+    case 1: return launch_k<T, 1>(a, stream);
+    case 3: return launch_k<T, 3>(a, stream);
+    case 5: return launch_k<T, 5>(a, stream);
+    case 7: return launch_k<T, 7>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, void *out, const float *w_base,
+                            const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+                            hipStream_t stream)
+{
+    if (dtype == 0) {
+        WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        return launch_t<float>(a, stream);
+    }
+    WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return launch_t<_Float16>(a, stream);
+}

@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(os.path.dirname(_HERE))
 _SRC = os.path.join(_HERE, "wtconv_emu.cpp")
 _DEPS = [_SRC] + [os.path.join(_ROOT, "level_haar_wavelet_amd", "csrc", f)
-                  for f in ("wtconv_fused_body.h", "wtconv_plan.h")]
+                  for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h")]
 _LIB = os.path.join(_ROOT, "_build", "libwtconv_emu.so")
 _lib = None
 
@@ -31,7 +31,7 @@ def build():
     if stale:
         os.makedirs(os.path.dirname(_LIB), exist_ok=True)
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run([_compiler(), "-std=c++17", "-O2", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC], check=True)
+        subprocess.run([_compiler(), "-std=c++17", "-O2", "-fno-strict-aliasing", "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -46,6 +46,10 @@ def _load():
         lib.emu_fused.restype = ci
         lib.emu_fused_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
         lib.emu_fused_plan.restype = ci
+        lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci]
+        lib.emu_whole.restype = ci
+        lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
+        lib.emu_whole_plan.restype = ci
         _lib = lib
     return _lib
 
@@ -77,4 +81,29 @@ def fused(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
                        rotate, *[ptr(a) for a in keep], nthreads, budget_floats)
     if rc != 0:
         raise ValueError("emu_fused failed: %d" % rc)
+    return out.astype(np.float64)
+
+
+def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f32", budget_floats=40960):
+    out = (ctypes.c_int * 7)()
+    rc = _load().emu_whole_plan(n, c, h, w, k, levels, rotate, nthreads, planes, 4 if dtype == "f32" else 2,
+                                budget_floats, out)
+    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok")
+    return dict(zip(keys, list(out)))
+
+
+def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32", nthreads=256, planes=1,
+          budget_floats=40960):
+    """Run the whole-plane kernel on the CPU emulation."""
+    lib = _load()
+    n, c, h, w = x.shape
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    out = np.full_like(xin, np.nan)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.emu_whole(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, k, levels,
+                       rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats)
+    if rc != 0:
+        raise ValueError("emu_whole failed: %d" % rc)
     return out.astype(np.float64)

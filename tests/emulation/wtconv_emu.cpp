@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "../../level_haar_wavelet_amd/csrc/wtconv_fused_body.h"
+#include "../../level_haar_wavelet_amd/csrc/wtconv_whole_body.h"
 
 template <typename T, int K, int BW>
 static void run_fused(const WtcFusedArgs<T> &a)
@@ -70,7 +71,102 @@ static int run_t(const WtcFusedArgs<T> &a)
     }
 }
 
+template <typename T, int K, int BW>
+static void run_whole(const WtcWholeArgs<T> &a)
+{
+    const WtcWholePlan &p = a.p;
+    const int groups = (p.n + p.planes - 1) / p.planes;
+    const int nblocks = groups * p.c;
+    std::vector<float> lds((size_t)p.lds_floats);
+    const int nth = p.nthreads;
+    for (int bid = 0; bid < nblocks; ++bid) {
+        // poison LDS: the kernel must zero it before use
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcWholeCtx<T>> ctx((size_t)nth);
+        for (int t = 0; t < nth; ++t) {
+            ctx[t].lds = lds.data();
+            ctx[t].tid = t;
+            ctx[t].nth = nth;
+            ctx[t].lds_n = p.lds_floats;
+            ctx[t].img_n = (int64_t)p.h * p.w;
+            wtc_whole_setup<T>(a, ctx[t], bid);
+        }
+        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_whole_init<T, K>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_whole_fold<T, K>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_whole_table<T, K, BW>(a, ctx[t]);
+        for (int img = 0; img < ctx[0].nimg; ++img) {
+            for (int t = 0; t < nth; ++t) {
+                wtc_whole_select<T>(a, ctx[t], img);
+                wtc_whole_store_input<T, K, BW>(a, ctx[t]);
+            }
+            for (int t = 0; t < nth; ++t) {
+                if (img + 1 < ctx[t].nimg) wtc_whole_load<T, K, BW>(a, ctx[t], img + 1);
+                wtc_whole_analysis1<T, K>(a, ctx[t]);
+            }
+            for (int m = 2; m <= p.levels; ++m)
+                for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
+            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW>(a, ctx[t]);
+        }
+    }
+}
+
+template <typename T, int K>
+static void run_whole_k(const WtcWholeArgs<T> &a)
+{
+    switch (a.p.out_bw) {
+    case 8: run_whole<T, K, 8>(a); break;
+    case 4: run_whole<T, K, 4>(a); break;
+    default: run_whole<T, K, 2>(a); break;
+    }
+}
+
+template <typename T>
+static int run_whole_t(const WtcWholeArgs<T> &a)
+{
+    switch (a.p.k) {
+    case 1: run_whole_k<T, 1>(a); return 0;
+    case 3: run_whole_k<T, 3>(a); return 0;
+    case 5: run_whole_k<T, 5>(a); return 0;
+    case 7: run_whole_k<T, 7>(a); return 0;
+    default: return -1;
+    }
+}
+
 extern "C" {
+
+// Whole-plane plan: out[0..6] = planes, vec, out_bw, lds_floats, blocks, nthreads, ok.
+int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int planes, int ebytes,
+                   int budget_floats, int *out)
+{
+    WtcWholePlan p;
+    int rc = wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, ebytes, budget_floats);
+    out[0] = p.planes;
+    out[1] = p.vec;
+    out[2] = p.out_bw;
+    out[3] = p.lds_floats;
+    out[4] = p.items;
+    out[5] = p.nthreads;
+    out[6] = rc == 0;
+    return rc;
+}
+
+int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, int k, int levels, int rotate,
+              const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+              int nthreads, int planes, int budget_floats)
+{
+    WtcWholePlan p;
+    if (wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
+                            budget_floats))
+        return -1;
+    if (dtype == 0) {
+        WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        return run_whole_t<float>(a);
+    }
+    WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return run_whole_t<_Float16>(a);
+}
 
 // Plan of a fused launch, for inspection by the tests: fills out[0..7] with
 // tile_h, tile_w, strip_h, out_bw, tiles_y, tiles_x, lds_floats, nthreads.
