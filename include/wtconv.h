@@ -36,7 +36,8 @@
  *              each output element is rounded once to fp16 (round to nearest
  *              even).
  * Ownership    The caller allocates every buffer, including the workspace
- *              (size from wtconv_workspace_size).  The library allocates no
+ *              (size from wtconv_workspace_size, 256-byte aligned; its contents
+ *              need no initialisation and are scratch after the call).  The library allocates no
  *              device memory and holds no state between calls; calls are
  *              reentrant.
  * Execution    All work is enqueued on `stream` (0 = the null stream) with no
@@ -107,6 +108,20 @@ wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const f
 wtconv_status_t wtconv_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
                                      const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
                                      void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
+
+/* Parameter gradients of <dy, WTConv(x)>, with the chain rule through the
+ * folded scales (technical summary, Methodology, reformulation 3):
+ *   dw_base = s0 * G0,  dbias = s0 * Gb,  ds_base = <W0, G0> + b0 * Gb,
+ *   dw_lvl  = s_l * G_l, ds_lvl = <W_l, G_l>   (per channel and band),
+ * where G0 / G_l are the correlations, summed over N, H and W, of dy (or its
+ * Haar analysis) with x (or its Haar analysis) and Gb = sum dy.  Needs the
+ * workspace from wtconv_workspace_size(desc, WTCONV_OP_BWD_WEIGHT).  dw_lvl and
+ * ds_lvl may be NULL when L == 0. */
+wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                       const float *w_base, const float *bias, const float *s_base,
+                                       const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                       float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
+                                       size_t workspace_bytes, wtconv_stream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char *wtconv_status_string(wtconv_status_t status);

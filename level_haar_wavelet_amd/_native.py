@@ -39,6 +39,7 @@ SIGNATURES = {
     "wtconv_workspace_size": [_dp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)],
     "wtconv_forward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_data": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "wtconv_backward_weight": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
 }
 
 

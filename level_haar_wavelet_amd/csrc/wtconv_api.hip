@@ -116,6 +116,60 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
 }
 
+// Weight-gradient plan: the whole-plane kernel when the plane fits in LDS,
+// otherwise the level-by-level tiled steps.  Both write partial rows
+// [groups][C][plen] that the finalize pass reduces.
+struct WgradChoice {
+    bool whole;
+    WtcWgradPlan wp;
+    int groups;
+    int plen;
+    WtcWtileCarve cv;
+    size_t total_bytes;
+};
+
+int wgrad_groups(const wtconv_desc_t *d)
+{
+    int forced = env_int("WTCONV_WGRAD_GROUPS", 0, 1, 4096);
+    if (forced) return forced;
+    // enough workgroups to fill the chip a few times over
+    int g = (int)((2048 + d->c - 1) / d->c);
+    return g < 1 ? 1 : g;
+}
+
+wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
+{
+    const int kk = d->k * d->k;
+    ch->plen = kk + 1 + 4 * d->levels * kk;
+    int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 64);
+    if (!planes) {
+        planes = 1;
+        for (int p = 8; p > 1; p /= 2)
+            if (d->c * ((d->n + p - 1) / p) >= 1024) {
+                planes = p;
+                break;
+            }
+    }
+    ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
+                wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels,
+                                    kFusedThreads, planes, d->dtype == WTCONV_F32 ? 4 : 2,
+                                    whole_budget_floats()) == 0;
+    if (ch->whole) {
+        ch->groups = ch->wp.groups;
+    } else {
+        ch->groups = (int)wgrad_groups(d);
+        for (int j = 0; j <= d->levels; ++j) {
+            WtcWtilePlan tp;
+            if (wtc_make_wtile_plan(&tp, (int)d->n, (int)d->c, d->k, d->levels, j, (int)(d->h >> j),
+                                    (int)(d->w >> j), kFusedThreads, ch->groups, kMaxLdsFloats))
+                return WTCONV_ERR_UNSUPPORTED;
+        }
+    }
+    wtc_wtile_carve(&ch->cv, d->n, d->c, d->h, d->w, ch->whole ? 0 : d->levels, ch->groups, ch->plen);
+    ch->total_bytes = ch->cv.total;
+    return WTCONV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,8 +182,59 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     switch (op) {
     case WTCONV_OP_FWD:
     case WTCONV_OP_BWD_DATA: *bytes = 0; return WTCONV_OK;
+    case WTCONV_OP_BWD_WEIGHT: {
+        WgradChoice ch;
+        if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
+        *bytes = ch.total_bytes;
+        return WTCONV_OK;
+    }
     default: return WTCONV_ERR_UNSUPPORTED;
     }
+}
+
+wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                       const float *w_base, const float *bias, const float *s_base,
+                                       const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                       float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
+                                       size_t workspace_bytes, wtconv_stream_t stream)
+{
+    wtconv_status_t st = check_desc(desc);
+    if (st != WTCONV_OK) return st;
+    if (!x || !dy || !dw_base || !dbias || !ds_base) return WTCONV_ERR_NULL;
+    if ((st = check_params(desc, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
+    if (desc->levels > 0 && (!dw_lvl || !ds_lvl)) return WTCONV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dy)) return WTCONV_ERR_UNSUPPORTED;
+    WgradChoice ch;
+    if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
+    if (!workspace || workspace_bytes < ch.total_bytes) return WTCONV_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    float *partial = (float *)ws;
+    hipError_t e = hipSuccess;
+    if (ch.whole) {
+        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
+    } else {
+        float *bx[2] = {(float *)(ws + ch.cv.off_ux[0]), (float *)(ws + ch.cv.off_ux[1])};
+        float *bd[2] = {(float *)(ws + ch.cv.off_ud[0]), (float *)(ws + ch.cv.off_ud[1])};
+        const void *cx = x, *cd = dy;
+        int dt = desc->dtype;
+        for (int j = 0; j <= desc->levels && e == hipSuccess; ++j) {
+            WtcWtilePlan tp;
+            wtc_make_wtile_plan(&tp, (int)desc->n, (int)desc->c, desc->k, desc->levels, j, (int)(desc->h >> j),
+                                (int)(desc->w >> j), kFusedThreads, ch.groups, kMaxLdsFloats);
+            float *ux = j < desc->levels ? bx[j % 2] : nullptr;
+            float *ud = j < desc->levels ? bd[j % 2] : nullptr;
+            e = wtc_launch_wgrad_tile(dt, tp, cx, cd, ux, ud, partial, s);
+            cx = ux;
+            cd = ud;
+            dt = WTCONV_F32;
+        }
+    }
+    if (e == hipSuccess)
+        e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels, ch.groups, ch.plen, partial, w_base,
+                                      bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
+    return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
 }
 
 wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,

@@ -7,6 +7,8 @@
 
 #include "wtconv_plan.h"
 #include "wtconv_whole_body.h"
+#include "wtconv_wgrad_body.h"
+#include "wtconv_wgrad_tile_body.h"
 
 // Fused forward (rotate = 0) or data backward (rotate = 1), per plan p.
 hipError_t wtc_launch_fused(int dtype, const WtcFusedPlan &p, const void *in, void *out, const float *w_base,
@@ -17,5 +19,19 @@ hipError_t wtc_launch_fused(int dtype, const WtcFusedPlan &p, const void *in, vo
 hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, void *out, const float *w_base,
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                             hipStream_t stream);
+
+// Fused parameter-gradient correlations (partials per workgroup) and the
+// fixed-order reduction with the chain rule.
+hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,
+                            hipStream_t stream);
+hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int plen, const float *partial,
+                                     const float *w_base, const float *bias, const float *s_base,
+                                     const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                     float *ds_base, float *dw_lvl, float *ds_lvl, hipStream_t stream);
+
+// Step `p.step` of the level-by-level tiled parameter gradient (input dtype:
+// 0 fp32, 1 fp16; steps after the first read the fp32 maps of the previous).
+hipError_t wtc_launch_wgrad_tile(int in_dtype, const WtcWtilePlan &p, const void *x, const void *dy, float *ux,
+                                 float *ud, float *partial, hipStream_t stream);
 
 #endif  // WTCONV_LAUNCH_H

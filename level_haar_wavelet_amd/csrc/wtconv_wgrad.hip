@@ -1,0 +1,128 @@
+// wtconv_wgrad.hip -- parameter-gradient kernels of the WTConv layer for
+// gfx950: the fused per-channel correlation kernel (phases in
+// wtconv_wgrad_body.h) and the second pass that sums the workgroup partials in
+// a fixed order and applies the chain rule through the scales.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "wtconv_launch.h"
+#include "wtconv_wgrad_body.h"
+
+static __device__ __forceinline__ void wtc_lds_barrier_wg() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int K, int VEC>
+__global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
+{
+    extern __shared__ float wtc_lds[];
+    WtcWgradCtx<T, VEC> ctx;
+    ctx.lds = wtc_lds;
+    ctx.tid = threadIdx.x;
+    ctx.nth = blockDim.x;
+    wtc_wgrad_setup<T, VEC>(a, ctx, blockIdx.x);
+    wtc_wgrad_load<T, VEC>(a, ctx, 0);
+    wtc_wgrad_zero<T, VEC>(a, ctx);
+    wtc_lds_barrier_wg();
+    wtc_wgrad_table<T, K, VEC>(a, ctx);
+    float acc[WTC_WG_QMAX][K * K + 1];
+#pragma unroll
+    for (int s = 0; s < WTC_WG_QMAX; ++s)
+#pragma unroll
+        for (int e = 0; e < K * K + 1; ++e) acc[s][e] = 0.0f;
+    for (int img = 0; img < ctx.nimg; ++img) {
+        wtc_wgrad_store_input<T, K, VEC>(a, ctx);
+        wtc_lds_barrier_wg();
+        if (img + 1 < ctx.nimg) wtc_wgrad_load<T, VEC>(a, ctx, img + 1);
+        for (int m = 1; m <= a.p.levels; ++m) {
+            wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
+            wtc_lds_barrier_wg();
+        }
+        wtc_wgrad_correlate<T, K, VEC>(a, ctx, acc);
+        wtc_lds_barrier_wg();
+    }
+#pragma unroll
+    for (int s = 0; s < WTC_WG_QMAX; ++s) {
+        if (s < a.p.q) {
+            wtc_wgrad_park<T, K, VEC>(a, ctx, acc[s]);
+            wtc_lds_barrier_wg();
+            wtc_wgrad_gather<T, K, VEC>(a, ctx, s);
+            wtc_lds_barrier_wg();
+        }
+    }
+    wtc_wgrad_write<T, K, VEC>(a, ctx);
+}
+
+__global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k, int levels, int groups, int plen,
+                                                                    const float *partial, const float *w_base,
+                                                                    const float *bias, const float *s_base,
+                                                                    const float *w_lvl, const float *s_lvl,
+                                                                    float *dw_base, float *dbias, float *ds_base,
+                                                                    float *dw_lvl, float *ds_lvl)
+{
+    const int nmaps = 1 + 4 * levels;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= C * nmaps) return;
+    const int c = idx / nmaps, g = idx - c * nmaps;
+    wtc_wgrad_finalize_one(c, g, C, k, levels, groups, plen, partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base,
+                           dbias, ds_base, dw_lvl, ds_lvl);
+}
+
+template <typename T, int K, int VEC>
+static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
+    const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const unsigned blocks = (unsigned)(a.p.groups * a.p.c);
+    hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t launch_wgrad_k(const WtcWgradArgs<T> &a, hipStream_t stream)
+{
+    constexpr int VMAX = 16 / sizeof(T);
+    switch (a.p.vec) {
+    case VMAX: return launch_wgrad<T, K, VMAX>(a, stream);
+    case VMAX / 2: return launch_wgrad<T, K, VMAX / 2>(a, stream);
+    case VMAX / 4: return launch_wgrad<T, K, VMAX / 4>(a, stream);
+    default: return launch_wgrad<T, K, 1>(a, stream);
+    }
+}
+
+template <typename T>
+static hipError_t launch_wgrad_t(const WtcWgradArgs<T> &a, hipStream_t stream)
+{
+    switch (a.p.k) {
+    case 1: return launch_wgrad_k<T, 1>(a, stream);
+    case 3: return launch_wgrad_k<T, 3>(a, stream);
+    case 5: return launch_wgrad_k<T, 5>(a, stream);
+    case 7: return launch_wgrad_k<T, 7>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,
+                            hipStream_t stream)
+{
+    if (dtype == 0) {
+        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial, p};
+        return launch_wgrad_t<float>(a, stream);
+    }
+    WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial, p};
+    return launch_wgrad_t<_Float16>(a, stream);
+}
+
+hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int plen, const float *partial,
+                                     const float *w_base, const float *bias, const float *s_base,
+                                     const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                     float *ds_base, float *dw_lvl, float *ds_lvl, hipStream_t stream)
+{
+    const int n = C * (1 + 4 * levels);
+    hipLaunchKernelGGL(wtconv_wgrad_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, C, k, levels,
+                       groups, plen, partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl,
+                       ds_lvl);
+    return hipGetLastError();
+}

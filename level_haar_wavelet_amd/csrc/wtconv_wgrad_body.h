@@ -1,0 +1,475 @@
+// wtconv_wgrad_body.h -- fused parameter gradients of the WTConv layer for
+// planes that fit in LDS whole, written as phases separated by workgroup
+// barriers (the kernel in wtconv_wgrad.hip and a CPU emulation run the same
+// code).
+//
+// Source: "Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
+// Reformulation" (arXiv 2608.10805), technical summary: Key Contributions
+// (all parameter gradients of the layer) and Methodology, reformulations 1 and
+// 3 (Haar analysis recomputed on chip; scales folded into the weights, so the
+// chain rule brings the scale back into the weight and scale gradients).
+//
+// With U_m / B_m^b the plain (unnormalised) Haar sums of the forward pass, the
+// orthonormal subbands are A = 2^-m B(x) and the gradient at a level's band
+// outputs is dZ = 2^-m B(dy) (the synthesis is the transposed analysis), so
+//   G_m^b[u][v] = sum_{n,i,j} dZ[i][j] A[i+u-r][j+v-r]
+//               = 4^-m sum B(dy)[i][j] B(x)[i+u-r][j+v-r],
+//   G_0[u][v]   = sum dy[h][w] x[h+u-r][w+v-r],   G_b = sum dy,
+// and then (in the second kernel)
+//   dW_m^b = s_m^b G_m^b,  ds_m^b = <W_m^b, G_m^b>,
+//   dW_0 = s_0 G_0,  db_0 = s_0 G_b,  ds_0 = <W_0, G_0> + b_0 G_b.
+//
+// One workgroup owns one channel and P images.  The correlation work is cut
+// into 4x4 pieces of the dy-side maps ("A" maps: dy itself, then the four
+// bands of every level); thread t owns pieces [Q t, Q t + Q) for the whole
+// life of the workgroup and keeps one k x k (+1) accumulator set per piece, so
+// the cross-thread reduction happens once per workgroup, in a fixed order.
+#ifndef WTCONV_WGRAD_BODY_H
+#define WTCONV_WGRAD_BODY_H
+
+#include "wtconv_whole_body.h"
+
+#define WTC_WG_QMAX 3  // pieces per thread
+#define WTC_WG_P 4     // piece side
+#define WTC_WG_NCH 4   // input chunks per thread and image (each of x and dy)
+
+struct WtcWgradPlan {
+    int32_t n, c, h, w, k, levels;
+    int32_t nthreads;
+    int32_t planes;     // images per workgroup
+    int32_t groups;     // workgroups per channel
+    int32_t q;          // pieces per thread
+    int32_t npieces;
+    int32_t nmaps;      // 1 + 4L
+    int32_t plen;       // floats of one partial result: k*k + 1 + 4L k*k
+    int32_t vec;        // activation elements per global chunk
+    WtcMap x;           // x with an r-wide zero border (origin (r, r))
+    WtcMap dy;          // dy (origin (0, 0)), zero beyond the image
+    WtcMap u[WTC_MAXL + 1];  // B_m(x): 4 bands with an r border
+    WtcMap d[WTC_MAXL + 1];  // B_m(dy): 4 bands, origin (0, 0)
+    int32_t first[1 + 4 * WTC_MAXL + 1];  // first piece of every map, then the total
+    int32_t tab_off;    // piece descriptors, 2 ints each
+    int32_t res_off;    // per-map results, nmaps x (k*k + 1)
+    int32_t red_off;    // reduction scratch, nthreads x (k*k + 1), aliases the maps
+    int32_t lds_floats;
+};
+
+static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
+{
+    const int32_t L = p->levels, r = p->k / 2, kk = p->k * p->k, P = WTC_WG_P;
+    int32_t off = 0;
+    p->x.off = off;
+    p->x.rows = wtc_roundup(p->h, P) + 2 * r;
+    p->x.pitch = wtc_roundup(wtc_roundup(p->w, P) + 2 * r, 4) | 1;
+    off += p->x.rows * p->x.pitch;
+    p->dy.off = off;
+    p->dy.rows = wtc_roundup(p->h, P);
+    p->dy.pitch = wtc_roundup(p->w, P) | 1;
+    off += p->dy.rows * p->dy.pitch;
+    for (int32_t m = 0; m <= WTC_MAXL; ++m) {
+        p->u[m].off = p->u[m].pitch = p->u[m].rows = 0;
+        p->d[m] = p->u[m];
+    }
+    for (int32_t m = 1; m <= L; ++m) {
+        const int32_t Hm = p->h >> m, Wm = p->w >> m;
+        p->u[m].off = off;
+        p->u[m].rows = wtc_roundup(Hm, P) + 2 * r;
+        p->u[m].pitch = (wtc_roundup(Wm, P) + 2 * r) | 1;
+        off += 4 * p->u[m].rows * p->u[m].pitch;
+        p->d[m].off = off;
+        p->d[m].rows = wtc_roundup(Hm, P);
+        p->d[m].pitch = wtc_roundup(Wm, P) | 1;
+        off += 4 * p->d[m].rows * p->d[m].pitch;
+    }
+    const int32_t maps_end = off;
+    // pieces: map 0 is the base (full resolution), map 1 + 4(m-1) + b is band b of level m
+    p->nmaps = 1 + 4 * L;
+    int32_t np = 0;
+    for (int32_t g = 0; g < p->nmaps; ++g) {
+        const int32_t m = g == 0 ? 0 : (g - 1) / 4 + 1;
+        p->first[g] = np;
+        np += ((p->h >> m) + P - 1) / P * (((p->w >> m) + P - 1) / P);
+    }
+    p->first[p->nmaps] = np;
+    p->npieces = np;
+    p->q = (np + p->nthreads - 1) / p->nthreads;
+    p->plen = kk + 1 + 4 * L * kk;
+    off = wtc_roundup(off, 4);
+    p->tab_off = off;
+    off += 2 * np;
+    // the reduction runs after the last image: its scratch reuses the maps and
+    // the table; the per-map results come after both
+    p->red_off = 0;
+    off = wtc_max(off, p->nthreads * (kk + 1));
+    p->res_off = wtc_roundup(off, 4);
+    off = p->res_off + p->nmaps * (kk + 1);
+    (void)maps_end;
+    p->lds_floats = wtc_roundup(off, 4);
+    return p->lds_floats;
+}
+
+static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
+                                      int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
+                                      int32_t budget_floats)
+{
+    p->n = n;
+    p->c = c;
+    p->h = h;
+    p->w = w;
+    p->k = k;
+    p->levels = levels;
+    p->nthreads = nthreads;
+    p->planes = planes < 1 ? 1 : (planes > n ? n : planes);
+    p->groups = (n + p->planes - 1) / p->planes;
+    if (levels < 0 || levels > WTC_MAXL) return -1;
+    if (h % (1 << levels) || w % (1 << levels)) return -1;
+    int32_t vec = 16 / elem_bytes;
+    while (vec > 1 && w % vec) vec /= 2;
+    p->vec = vec;
+    const int64_t chunks = (int64_t)h * (w / vec);
+    if (chunks > (int64_t)WTC_WG_NCH * nthreads) return -1;
+    wtc_wgrad_layout(p);
+    if (p->q > WTC_WG_QMAX) return -1;
+    // descriptor fields: pitches below 256, LDS indexes below 65536
+    if (p->x.pitch > 255 || p->dy.pitch > 255 || p->lds_floats > 65535) return -1;
+    return p->lds_floats <= budget_floats ? 0 : -1;
+}
+
+template <typename T>
+struct WtcWgradArgs {
+    const T *x;
+    const T *dy;
+    float *partial;  // [groups][C][plen]
+    WtcWgradPlan p;
+};
+
+template <typename T, int VEC>
+struct WtcWgradCtx {
+    float *lds;
+    int tid, nth;
+    int c, n0, nimg, group;
+    T prex[WTC_WG_NCH][VEC];
+    T prey[WTC_WG_NCH][VEC];
+#ifdef WTC_EMULATE
+    int64_t lds_n;
+#endif
+};
+
+template <typename T, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_setup(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int bid)
+{
+    const WtcWgradPlan &p = a.p;
+    ctx.c = bid % p.c;
+    ctx.group = bid / p.c;
+    ctx.n0 = ctx.group * p.planes;
+    ctx.nimg = wtc_min(p.planes, p.n - ctx.n0);
+}
+
+template <typename T, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_zero(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
+{
+    for (int i = ctx.tid; i < a.p.lds_floats; i += ctx.nth) WTC_LDS(ctx, i) = 0.0f;
+}
+
+// Loads of one image of x and dy into registers (every lane loads a valid chunk).
+template <typename T, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int img)
+{
+    const WtcWgradPlan &p = a.p;
+    const int64_t plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
+    const int cpr = p.w / VEC, total = p.h * cpr;
+#pragma unroll
+    for (int q = 0; q < WTC_WG_NCH; ++q) {
+        const int idx = wtc_min(ctx.tid + q * ctx.nth, total - 1);
+        const int64_t e = plane + (int64_t)idx * VEC;
+#ifdef WTC_EMULATE
+        const int64_t all = (int64_t)p.n * p.c * p.h * p.w;
+        for (int t = 0; t < VEC; ++t) {
+            ctx.prex[q][t] = wtc_chk(a.x, e + t, all, __LINE__);
+            ctx.prey[q][t] = wtc_chk(a.dy, e + t, all, __LINE__);
+        }
+#else
+        if constexpr (VEC * sizeof(T) == 16) {
+            typedef float v4 __attribute__((ext_vector_type(4)));
+            v4 d0 = __builtin_nontemporal_load((const v4 *)(a.x + e));
+            v4 d1 = __builtin_nontemporal_load((const v4 *)(a.dy + e));
+            __builtin_memcpy(&ctx.prex[q][0], &d0, 16);
+            __builtin_memcpy(&ctx.prey[q][0], &d1, 16);
+        } else if constexpr (VEC * sizeof(T) == 8) {
+            typedef float v2 __attribute__((ext_vector_type(2)));
+            v2 d0 = __builtin_nontemporal_load((const v2 *)(a.x + e));
+            v2 d1 = __builtin_nontemporal_load((const v2 *)(a.dy + e));
+            __builtin_memcpy(&ctx.prex[q][0], &d0, 8);
+            __builtin_memcpy(&ctx.prey[q][0], &d1, 8);
+        } else {
+#pragma unroll
+            for (int t = 0; t < VEC; ++t) {
+                ctx.prex[q][t] = a.x[e + t];
+                ctx.prey[q][t] = a.dy[e + t];
+            }
+        }
+#endif
+    }
+}
+
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_store_input(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
+{
+    constexpr int R = K / 2;
+    const WtcWgradPlan &p = a.p;
+    const int cpr = p.w / VEC, total = p.h * cpr;
+#pragma unroll
+    for (int q = 0; q < WTC_WG_NCH; ++q) {
+        const int idx = ctx.tid + q * ctx.nth;
+        if (idx < total) {
+            const int row = idx / cpr, col = (idx - row * cpr) * VEC;
+            const int ox = p.x.off + (row + R) * p.x.pitch + col + R;
+            const int od = p.dy.off + row * p.dy.pitch + col;
+#pragma unroll
+            for (int t = 0; t < VEC; ++t) {
+                WTC_LDS(ctx, ox + t) = wtc_to_float(ctx.prex[q][t]);
+                WTC_LDS(ctx, od + t) = wtc_to_float(ctx.prey[q][t]);
+            }
+        }
+    }
+}
+
+// Haar level m of both pyramids: x side from x (m = 1) or U_{m-1}(x) into the
+// bordered maps, dy side into the interior maps.
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_analysis(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int m)
+{
+    constexpr int R = K / 2;
+    const WtcWgradPlan &p = a.p;
+    const int Hm = p.h >> m, Wm = p.w >> m;
+    const WtcMap ux = p.u[m], ud = p.d[m];
+    int sx, sxp, sd, sdp;  // source origins (index of element (0, 0)) and pitches
+    if (m == 1) {
+        sx = p.x.off + R * p.x.pitch + R;
+        sxp = p.x.pitch;
+        sd = p.dy.off;
+        sdp = p.dy.pitch;
+    } else {
+        sx = p.u[m - 1].off + R * p.u[m - 1].pitch + R;
+        sxp = p.u[m - 1].pitch;
+        sd = p.d[m - 1].off;
+        sdp = p.d[m - 1].pitch;
+    }
+    const int stx = ux.rows * ux.pitch, std_ = ud.rows * ud.pitch;
+    const int total = Hm * Wm;
+    int i = ctx.tid / Wm, j = ctx.tid - (ctx.tid / Wm) * Wm;
+    const int di = ctx.nth / Wm, dj = ctx.nth - di * Wm;
+    for (int idx = ctx.tid; idx < total; idx += ctx.nth) {
+        {
+            const int s = sx + (2 * i) * sxp + 2 * j;
+            const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
+            const float x10 = WTC_LDS(ctx, s + sxp), x11 = WTC_LDS(ctx, s + sxp + 1);
+            const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+            const int o = ux.off + (i + R) * ux.pitch + j + R;
+            WTC_LDS(ctx, o) = sa + sc;
+            WTC_LDS(ctx, o + stx) = sa - sc;
+            WTC_LDS(ctx, o + 2 * stx) = da + dc;
+            WTC_LDS(ctx, o + 3 * stx) = da - dc;
+        }
+        {
+            const int s = sd + (2 * i) * sdp + 2 * j;
+            const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
+            const float x10 = WTC_LDS(ctx, s + sdp), x11 = WTC_LDS(ctx, s + sdp + 1);
+            const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+            const int o = ud.off + i * ud.pitch + j;
+            WTC_LDS(ctx, o) = sa + sc;
+            WTC_LDS(ctx, o + std_) = sa - sc;
+            WTC_LDS(ctx, o + 2 * std_) = da + dc;
+            WTC_LDS(ctx, o + 3 * std_) = da - dc;
+        }
+        i += di;
+        j += dj;
+        if (j >= Wm) {
+            j -= Wm;
+            ++i;
+        }
+    }
+}
+
+// Piece descriptors, two ints: (LDS index of the x-side window at row i0 - r,
+// column j0 - r) | (LDS index of the dy-side piece) << 16, and x-side pitch |
+// dy-side pitch << 8 | map index << 16.
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_table(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
+{
+    constexpr int P = WTC_WG_P;
+    const WtcWgradPlan &p = a.p;
+    for (int it = ctx.tid; it < p.npieces; it += ctx.nth) {
+        int g = 0;
+        while (g + 1 < p.nmaps && it >= p.first[g + 1]) ++g;
+        const int m = g == 0 ? 0 : (g - 1) / 4 + 1, b = g == 0 ? 0 : (g - 1) % 4;
+        const int Wm = p.w >> m, npc = (Wm + P - 1) / P;
+        const int rem = it - p.first[g];
+        const int pr = rem / npc, pc = rem - pr * npc;
+        int d0, d1, d2;
+        if (m == 0) {
+            // x map origin (r, r): element (i0 - r, j0 - r) sits at (i0, j0)
+            d0 = p.x.off + (P * pr) * p.x.pitch + P * pc;
+            d1 = p.dy.off + (P * pr) * p.dy.pitch + P * pc;
+            d2 = p.x.pitch | (p.dy.pitch << 16);
+        } else {
+            const WtcMap ux = p.u[m], ud = p.d[m];
+            d0 = ux.off + b * ux.rows * ux.pitch + (P * pr) * ux.pitch + P * pc;
+            d1 = ud.off + b * ud.rows * ud.pitch + (P * pr) * ud.pitch + P * pc;
+            d2 = ux.pitch | (ud.pitch << 16);
+        }
+        int *tab = (int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
+        tab[0] = (int)((unsigned)d0 | ((unsigned)d1 << 16));
+        tab[1] = (d2 & 0xff) | (((d2 >> 16) & 0xff) << 8) | (g << 16);
+    }
+}
+
+// Correlation of one 4x4 dy-side piece with its x-side window, added to acc
+// (k*k taps, then the sum of the dy-side values).
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1, int xp, int dp,
+                                      float (&acc)[K * K + 1])
+{
+    constexpr int P = WTC_WG_P;
+    float av[P][P];
+#pragma unroll
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+        for (int c = 0; c < P; ++c) av[r][c] = WTC_LDS(ctx, d1 + r * dp + c);
+#pragma unroll
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+        for (int c = 0; c < P; ++c) acc[K * K] += av[r][c];
+#pragma unroll
+    for (int t = 0; t < P + K - 1; ++t) {
+        float row[P + K - 1];
+#pragma unroll
+        for (int e = 0; e < P + K - 1; ++e) row[e] = WTC_LDS(ctx, d0 + t * xp + e);
+#pragma unroll
+        for (int r = 0; r < P; ++r) {
+            const int u = t - r;
+            if (u < 0 || u >= K) continue;
+#pragma unroll
+            for (int v = 0; v < K; ++v)
+#pragma unroll
+                for (int c = 0; c < P; ++c) acc[u * K + v] = wtc_fma(av[r][c], row[c + v], acc[u * K + v]);
+        }
+    }
+}
+
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx,
+                                          float (&acc)[WTC_WG_QMAX][K * K + 1])
+{
+    const WtcWgradPlan &p = a.p;
+#pragma unroll
+    for (int s = 0; s < WTC_WG_QMAX; ++s) {
+        const int it = p.q * ctx.tid + s;
+        if (s < p.q && it < p.npieces) {
+            const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
+            const unsigned t0 = (unsigned)tab[0], t1 = (unsigned)tab[1];
+            wtc_wgrad_piece<T, K, VEC>(ctx, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
+                                      (int)((t1 >> 8) & 0xffu), acc[s]);
+        }
+    }
+}
+
+// After the last image: per set s, every thread parks its accumulators in
+// LDS, then one thread per (map, tap) sums the threads that own pieces of
+// that map, in thread order, into the per-map result.
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_park(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx,
+                                     const float (&acc)[K * K + 1])
+{
+    constexpr int n1 = K * K + 1;
+    const WtcWgradPlan &p = a.p;
+#pragma unroll
+    for (int e = 0; e < n1; ++e) WTC_LDS(ctx, p.red_off + ctx.tid * n1 + e) = acc[e];
+}
+
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_gather(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int s)
+{
+    constexpr int n1 = K * K + 1;
+    const WtcWgradPlan &p = a.p;
+    for (int idx = ctx.tid; idx < p.nmaps * n1; idx += ctx.nth) {
+        const int g = idx / n1, e = idx - g * n1;
+        // threads whose piece q t + s lies in [first[g], first[g+1])
+        const int lo = wtc_max(0, (p.first[g] - s + p.q - 1) / p.q);
+        const int hi = wtc_min(p.nthreads, (p.first[g + 1] - s + p.q - 1) / p.q);
+        float sum = WTC_LDS(ctx, p.res_off + idx);
+        for (int t = lo; t < hi; ++t) sum += WTC_LDS(ctx, p.red_off + t * n1 + e);
+        WTC_LDS(ctx, p.res_off + idx) = sum;
+    }
+}
+
+// Write the workgroup's per-map results: partial[group][c][plen] with
+// G_0 (k*k), G_b, then G of every band of every level (k*k each).
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_write(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
+{
+    constexpr int kk = K * K, n1 = kk + 1;
+    const WtcWgradPlan &p = a.p;
+#ifndef WTC_EMULATE
+    float *dst = a.partial + ((int64_t)ctx.group * p.c + ctx.c) * p.plen;
+#endif
+    for (int e = ctx.tid; e < p.plen; e += ctx.nth) {
+        float v;
+        if (e < kk) v = WTC_LDS(ctx, p.res_off + e);
+        else if (e == kk) v = WTC_LDS(ctx, p.res_off + kk);
+        else {
+            const int g = 1 + (e - kk - 1) / kk, t = (e - kk - 1) % kk;
+            v = WTC_LDS(ctx, p.res_off + g * n1 + t);
+        }
+#ifdef WTC_EMULATE
+        wtc_chk(a.partial, ((int64_t)ctx.group * p.c + ctx.c) * p.plen + e, (int64_t)p.groups * p.c * p.plen,
+                __LINE__) = v;
+#else
+        dst[e] = v;
+#endif
+    }
+}
+
+// Second pass: one thread per (channel, map) sums the workgroup partials in
+// group order and applies the chain rule through the scales.
+WTC_HD WTC_INLINE void wtc_wgrad_finalize_one(int c, int g, int C, int k, int levels, int groups, int plen,
+                                             const float *partial, const float *w_base, const float *bias,
+                                             const float *s_base, const float *w_lvl, const float *s_lvl,
+                                             float *dw_base, float *dbias, float *ds_base, float *dw_lvl,
+                                             float *ds_lvl)
+{
+    const int kk = k * k;
+    const int off = g == 0 ? 0 : kk + 1 + (g - 1) * kk;
+    float gsum[49];
+    float gb = 0.0f;
+    for (int t = 0; t < kk; ++t) gsum[t] = 0.0f;
+    for (int q = 0; q < groups; ++q) {
+        const float *src = partial + ((int64_t)q * C + c) * plen + off;
+        for (int t = 0; t < kk; ++t) gsum[t] += src[t];
+        if (g == 0) gb += src[kk];
+    }
+    if (g == 0) {
+        const float s0 = s_base[c];
+        const float b0 = bias ? bias[c] : 0.0f;
+        float ds = 0.0f;
+        for (int t = 0; t < kk; ++t) {
+            dw_base[c * kk + t] = s0 * gsum[t];
+            ds = wtc_fma(w_base[c * kk + t], gsum[t], ds);
+        }
+        dbias[c] = s0 * gb;
+        ds_base[c] = wtc_fma(b0, gb, ds);
+    } else {
+        const int m = (g - 1) / 4 + 1, b = (g - 1) % 4;
+        const int64_t ch = (int64_t)(m - 1) * 4 * C + 4 * c + b;
+        const float s = s_lvl[ch];
+        float ds = 0.0f;
+        for (int t = 0; t < kk; ++t) {
+            const float gt = ldexpf(gsum[t], -2 * m);
+            dw_lvl[ch * kk + t] = s * gt;
+            ds = wtc_fma(w_lvl[ch * kk + t], gt, ds);
+        }
+        ds_lvl[ch] = ds;
+    }
+}
+
+#endif  // WTCONV_WGRAD_BODY_H

@@ -414,7 +414,7 @@ WTC_HD WTC_INLINE void wtc_whole_desc(WtcWholeCtx<T> &ctx, int off, int &d0, int
 template <typename T, int K, int BW>
 WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
-    constexpr int R = K / 2, kk = K * K;
+    constexpr int kk = K * K;
     const WtcWholePlan &p = a.p;
     const int nblk = (p.h / 2) * (p.w / BW);
     const WtcMap xm = p.x;

@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(os.path.dirname(_HERE))
 _SRC = os.path.join(_HERE, "wtconv_emu.cpp")
 _DEPS = [_SRC] + [os.path.join(_ROOT, "level_haar_wavelet_amd", "csrc", f)
-                  for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h")]
+                  for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h", "wtconv_wgrad_body.h", "wtconv_wgrad_tile_body.h")]
 _LIB = os.path.join(_ROOT, "_build", "libwtconv_emu.so")
 _lib = None
 
@@ -50,6 +50,12 @@ def _load():
         lib.emu_whole.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
         lib.emu_whole_plan.restype = ci
+        lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad.restype = ci
+        lib.emu_wgrad_plan.argtypes = [ci] * 10 + [ctypes.POINTER(ci)]
+        lib.emu_wgrad_plan.restype = ci
+        lib.emu_wgrad_tiled.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad_tiled.restype = ci
         _lib = lib
     return _lib
 
@@ -107,3 +113,37 @@ def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
     if rc != 0:
         raise ValueError("emu_whole failed: %d" % rc)
     return out.astype(np.float64)
+
+
+def wgrad_plan(n, c, h, w, k, levels, nthreads=256, planes=1, dtype="f32", budget_floats=40960):
+    out = (ctypes.c_int * 6)()
+    rc = _load().emu_wgrad_plan(n, c, h, w, k, levels, nthreads, planes, 4 if dtype == "f32" else 2,
+                                budget_floats, out)
+    keys = ("lds_floats", "npieces", "q", "groups", "plen", "vec")
+    d = dict(zip(keys, list(out)))
+    d["ok"] = rc == 0
+    return d
+
+
+def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nthreads=256, planes=1,
+          budget_floats=40960, tiled=False):
+    """Parameter gradients through the emulated fused weight-gradient kernel."""
+    lib = _load()
+    n, c, h, w = x.shape
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    dyin = np.ascontiguousarray(dy, dtype=npdt)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl if levels else np.zeros(1)),
+            _f32(s_lvl if levels else np.zeros(1))]
+    outs = [np.full((c, k, k), np.nan, np.float32), np.full((c,), np.nan, np.float32),
+            np.full((c,), np.nan, np.float32), np.full((max(levels, 1), 4 * c, k, k), np.nan, np.float32),
+            np.full((max(levels, 1), 4 * c), np.nan, np.float32)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    fn = lib.emu_wgrad_tiled if tiled else lib.emu_wgrad
+    rc = fn(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, h, w, k, levels,
+            *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes, budget_floats)
+    if rc != 0:
+        raise ValueError("emu_wgrad failed: %d" % rc)
+    outs[3] = outs[3][:levels]
+    outs[4] = outs[4][:levels]
+    return [o.astype(np.float64) for o in outs]

@@ -10,10 +10,13 @@
 #define WTC_EMULATE 1
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <vector>
 
 #include "../../level_haar_wavelet_amd/csrc/wtconv_fused_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_whole_body.h"
+#include "../../level_haar_wavelet_amd/csrc/wtconv_wgrad_body.h"
+#include "../../level_haar_wavelet_amd/csrc/wtconv_wgrad_tile_body.h"
 
 template <typename T, int K, int BW>
 static void run_fused(const WtcFusedArgs<T> &a)
@@ -134,7 +137,208 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
     }
 }
 
+template <typename T, int K, int VEC>
+static void run_wgrad(const WtcWgradArgs<T> &a)
+{
+    const WtcWgradPlan &p = a.p;
+    const int nblocks = p.groups * p.c;
+    std::vector<float> lds((size_t)p.lds_floats);
+    const int nth = p.nthreads;
+    for (int bid = 0; bid < nblocks; ++bid) {
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcWgradCtx<T, VEC>> ctx((size_t)nth);
+        std::vector<float> acc((size_t)nth * WTC_WG_QMAX * (K * K + 1), 0.0f);
+        auto A = [&](int t) -> float(&)[WTC_WG_QMAX][K * K + 1] {
+            return *reinterpret_cast<float(*)[WTC_WG_QMAX][K * K + 1]>(&acc[(size_t)t * WTC_WG_QMAX * (K * K + 1)]);
+        };
+        for (int t = 0; t < nth; ++t) {
+            ctx[t].lds = lds.data();
+            ctx[t].tid = t;
+            ctx[t].nth = nth;
+            ctx[t].lds_n = p.lds_floats;
+            wtc_wgrad_setup<T, VEC>(a, ctx[t], bid);
+        }
+        for (int t = 0; t < nth; ++t) wtc_wgrad_load<T, VEC>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_wgrad_zero<T, VEC>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_wgrad_table<T, K, VEC>(a, ctx[t]);
+        for (int img = 0; img < ctx[0].nimg; ++img) {
+            for (int t = 0; t < nth; ++t) wtc_wgrad_store_input<T, K, VEC>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t)
+                if (img + 1 < ctx[t].nimg) wtc_wgrad_load<T, VEC>(a, ctx[t], img + 1);
+            for (int m = 1; m <= p.levels; ++m)
+                for (int t = 0; t < nth; ++t) wtc_wgrad_analysis<T, K, VEC>(a, ctx[t], m);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_correlate<T, K, VEC>(a, ctx[t], A(t));
+        }
+        for (int s = 0; s < p.q; ++s) {
+            for (int t = 0; t < nth; ++t) wtc_wgrad_park<T, K, VEC>(a, ctx[t], A(t)[s]);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_gather<T, K, VEC>(a, ctx[t], s);
+        }
+        for (int t = 0; t < nth; ++t) wtc_wgrad_write<T, K, VEC>(a, ctx[t]);
+    }
+}
+
+template <typename T, int K>
+static void run_wgrad_k(const WtcWgradArgs<T> &a)
+{
+    constexpr int VMAX = 16 / sizeof(T);
+    switch (a.p.vec) {
+    case VMAX: run_wgrad<T, K, VMAX>(a); break;
+    case VMAX / 2: run_wgrad<T, K, VMAX / 2>(a); break;
+    case VMAX / 4: run_wgrad<T, K, VMAX / 4>(a); break;
+    default: run_wgrad<T, K, 1>(a); break;
+    }
+}
+
+template <typename T>
+static int run_wgrad_t(const WtcWgradArgs<T> &a)
+{
+    switch (a.p.k) {
+    case 1: run_wgrad_k<T, 1>(a); return 0;
+    case 3: run_wgrad_k<T, 3>(a); return 0;
+    case 5: run_wgrad_k<T, 5>(a); return 0;
+    case 7: run_wgrad_k<T, 7>(a); return 0;
+    default: return -1;
+    }
+}
+
+template <typename TI, int K>
+static void run_wtile(const WtcWtileArgs<TI> &a)
+{
+    const WtcWtilePlan &p = a.p;
+    const int nblocks = p.groups * p.c;
+    std::vector<float> lds((size_t)p.lds_floats);
+    const int nth = p.nthreads;
+    const int units = p.n * p.tiles_y * p.tiles_x;
+    for (int bid = 0; bid < nblocks; ++bid) {
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcWtileCtx> ctx((size_t)nth);
+        std::vector<float> acc((size_t)nth * WTC_WT_QMAX * (K * K + 1), 0.0f);
+        auto A = [&](int t) -> float(&)[WTC_WT_QMAX][K * K + 1] {
+            return *reinterpret_cast<float(*)[WTC_WT_QMAX][K * K + 1]>(&acc[(size_t)t * WTC_WT_QMAX * (K * K + 1)]);
+        };
+        for (int t = 0; t < nth; ++t) {
+            ctx[t].lds = lds.data();
+            ctx[t].tid = t;
+            ctx[t].nth = nth;
+            ctx[t].lds_n = p.lds_floats;
+            ctx[t].c = bid % p.c;
+            ctx[t].group = bid / p.c;
+        }
+        const int u0 = ctx[0].group * p.units_per_wg, u1 = std::min(units, u0 + p.units_per_wg);
+        for (int t = 0; t < nth; ++t) wtc_wtile_zero<TI>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_wtile_table<TI, K>(a, ctx[t]);
+        for (int u = u0; u < u1; ++u) {
+            for (int t = 0; t < nth; ++t) wtc_wtile_stage<TI, K>(a, ctx[t], u);
+            if (p.step < p.levels)
+                for (int t = 0; t < nth; ++t) wtc_wtile_analysis<TI, K>(a, ctx[t], u);
+            for (int t = 0; t < nth; ++t) wtc_wtile_correlate<TI, K>(a, ctx[t], A(t));
+        }
+        for (int s = 0; s < p.q; ++s) {
+            for (int t = 0; t < nth; ++t) wtc_wtile_park<TI, K>(a, ctx[t], A(t)[s]);
+            for (int t = 0; t < nth; ++t) wtc_wtile_gather<TI, K>(a, ctx[t], s);
+        }
+        for (int t = 0; t < nth; ++t) wtc_wtile_write<TI, K>(a, ctx[t]);
+    }
+}
+
+template <typename TI>
+static int run_wtile_t(const WtcWtileArgs<TI> &a)
+{
+    switch (a.p.k) {
+    case 1: run_wtile<TI, 1>(a); return 0;
+    case 3: run_wtile<TI, 3>(a); return 0;
+    case 5: run_wtile<TI, 5>(a); return 0;
+    case 7: run_wtile<TI, 7>(a); return 0;
+    default: return -1;
+    }
+}
+
 extern "C" {
+
+// Parameter gradients through the level-by-level tiled steps and the finalize.
+int emu_wgrad_tiled(int dtype, const void *x, const void *dy, int n, int c, int h, int w, int k, int levels,
+                    const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
+                    const float *s_lvl, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                    int nthreads, int groups, int budget_floats)
+{
+    const int kk = k * k, plen = kk + 1 + 4 * levels * kk;
+    // one workspace carved exactly as the library carves it; NaN-filled so a
+    // read of something no step wrote shows up
+    WtcWtileCarve cv;
+    wtc_wtile_carve(&cv, n, c, h, w, levels, groups, plen);
+    std::vector<float> wsbuf(cv.total / sizeof(float) + 64, __builtin_nanf(""));
+    char *ws = (char *)wsbuf.data();
+    float *partialp = (float *)ws;
+    const void *curx = x, *curd = dy;
+    int curdt = dtype;
+    for (int j = 0; j <= levels; ++j) {
+        WtcWtilePlan p;
+        if (wtc_make_wtile_plan(&p, n, c, k, levels, j, h >> j, w >> j, nthreads, groups, budget_floats)) return -1;
+        float *ux = nullptr, *ud = nullptr;
+        if (j < levels) {
+            ux = (float *)(ws + cv.off_ux[j % 2]);
+            ud = (float *)(ws + cv.off_ud[j % 2]);
+        }
+        int rc;
+        if (curdt == 0) {
+            WtcWtileArgs<float> a{(const float *)curx, (const float *)curd, ux, ud, partialp, p};
+            rc = run_wtile_t<float>(a);
+        } else {
+            WtcWtileArgs<_Float16> a{(const _Float16 *)curx, (const _Float16 *)curd, ux, ud, partialp, p};
+            rc = run_wtile_t<_Float16>(a);
+        }
+        if (rc) return rc;
+        curx = ux;
+        curd = ud;
+        curdt = 0;
+    }
+    for (int cc = 0; cc < c; ++cc)
+        for (int g = 0; g < 1 + 4 * levels; ++g)
+            wtc_wgrad_finalize_one(cc, g, c, k, levels, groups, plen, partialp, w_base, bias, s_base, w_lvl,
+                                   s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
+    return 0;
+}
+
+// Parameter gradients through the fused weight-gradient phases and the
+// fixed-order finalize.  Outputs overwritten, fp32.
+int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int w, int k, int levels,
+              const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+              float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl, int nthreads, int planes,
+              int budget_floats)
+{
+    WtcWgradPlan p;
+    if (wtc_make_wgrad_plan(&p, n, c, h, w, k, levels, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats))
+        return -1;
+    std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
+    int rc;
+    if (dtype == 0) {
+        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial.data(), p};
+        rc = run_wgrad_t<float>(a);
+    } else {
+        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p};
+        rc = run_wgrad_t<_Float16>(a);
+    }
+    if (rc) return rc;
+    for (int cc = 0; cc < c; ++cc)
+        for (int g = 0; g < 1 + 4 * levels; ++g)
+            wtc_wgrad_finalize_one(cc, g, c, k, levels, p.groups, p.plen, partial.data(), w_base, bias, s_base,
+                                   w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
+    return 0;
+}
+
+int emu_wgrad_plan(int n, int c, int h, int w, int k, int levels, int nthreads, int planes, int ebytes,
+                   int budget_floats, int *out)
+{
+    WtcWgradPlan p;
+    int rc = wtc_make_wgrad_plan(&p, n, c, h, w, k, levels, nthreads, planes, ebytes, budget_floats);
+    out[0] = p.lds_floats;
+    out[1] = p.npieces;
+    out[2] = p.q;
+    out[3] = p.groups;
+    out[4] = p.plen;
+    out[5] = p.vec;
+    return rc;
+}
 
 // Whole-plane plan: out[0..6] = planes, vec, out_bw, lds_floats, blocks, nthreads, ok.
 int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int planes, int ebytes,

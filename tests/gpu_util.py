@@ -58,3 +58,17 @@ def assert_grad_close(got, ref, act_dtype, what=""):
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     tol = TOL_F32_GRAD_L2 if act_dtype == "f32" else TOL_F16_L2
     assert rel <= tol, "%s: rel L2 %.3e > %.1e" % (what, rel, tol)
+
+
+def backward_weight(d, **kw):
+    return wt.wtconv_backward_weight(d.x, d.dy, d.w_base, d.bias, d.s_base, d.w_lvl, d.s_lvl, **kw)
+
+
+GRAD_NAMES = ("dw_base", "dbias", "ds_base", "dw_lvl", "ds_lvl")
+
+
+def assert_grads_close(got, ref, act_dtype, what=""):
+    for name, g, r in zip(GRAD_NAMES, got, ref):
+        if r is None or np.asarray(r).size == 0:
+            continue
+        assert_grad_close(g, np.asarray(r), act_dtype, "%s %s" % (what, name))

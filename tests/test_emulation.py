@@ -66,3 +66,31 @@ def test_plans_fit_and_tile():
     assert p["lds_floats"] <= 9000 and p["strip_h"] < p["tile_h"]
     p = emu.fused_plan(1, 1, 64, 96, 3, 3, budget_floats=4000)
     assert p["lds_floats"] <= 4000 and p["tiles_y"] * p["tiles_x"] > 1
+
+
+WGRAD_CASES = [
+    # n, c, h, w, k, L, dtype, planes or groups
+    (2, 3, 16, 16, 5, 2, "f32", 2),
+    (3, 2, 16, 24, 3, 3, "f32", 3),
+    (2, 3, 9, 13, 5, 0, "f32", 2),
+    (3, 2, 28, 28, 5, 2, "f16", 2),
+    (2, 2, 56, 56, 5, 3, "f32", 2),
+    (1, 2, 64, 96, 5, 4, "f16", 3),
+]
+
+
+@pytest.mark.parametrize("case", WGRAD_CASES)
+@pytest.mark.parametrize("tiled", [False, True])
+def test_emulated_weight_gradients_match_oracle(orc, case, tiled):
+    n, c, h, w, k, L, dt, g = case
+    if not tiled and not emu.wgrad_plan(n, c, h, w, k, L, planes=g, dtype=dt)["ok"]:
+        pytest.skip("plane too large for the whole-plane weight-gradient kernel")
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + L)
+    got = emu.wgrad(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, dtype=dt,
+                    planes=g, tiled=tiled)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    for gg, rr in zip(got, ref):
+        if rr.size == 0:
+            continue
+        assert not np.isnan(gg).any()
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6

@@ -1,0 +1,127 @@
+"""GPU parity of the parameter gradients (wtconv_backward_weight) against the
+CPU oracle, through the C ABI: relative L2 per gradient tensor <= 1e-4 for
+fp32 activations, <= 5e-3 for fp16 storage.  Shapes cover the whole-plane
+kernel and the level-by-level tiled path; at the large workloads the
+full-batch launch is checked as the sum of batch chunks, each chunk against
+the oracle where it is cheap enough."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from level_haar_wavelet_amd.synthetic import WORKLOADS, make_inputs, sweep_workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests.gpu_util import DevInputs, assert_grads_close, backward_weight
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle(orc, inp, k, L, sel=slice(None)):
+    return orc.backward_weight(inp.x[sel], inp.dy[sel], inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+
+
+SMALL = [
+    (2, 8, 16, 16, 5, 2, "f32"),
+    (3, 3, 16, 24, 3, 3, "f32"),
+    (2, 2, 8, 8, 7, 1, "f32"),
+    (1, 4, 12, 20, 1, 2, "f32"),
+    (2, 3, 10, 14, 5, 1, "f32"),
+    (1, 2, 32, 32, 5, 5, "f32"),
+    (2, 3, 9, 13, 5, 0, "f32"),
+    (2, 8, 16, 16, 5, 2, "f16"),
+    (3, 2, 28, 28, 5, 2, "f16"),
+    (1, 2, 96, 160, 5, 4, "f32"),   # tiled path
+    (2, 2, 128, 128, 3, 5, "f16"),  # tiled path
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c)))
+def test_small_shapes(orc, case):
+    n, c, h, w, k, L, dt = case
+    _log("wgrad case %s" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=n * 100 + h + w + k + L)
+    d = DevInputs(inp, dt)
+    got = backward_weight(d)
+    torch.cuda.synchronize()
+    assert_grads_close(got, _oracle(orc, inp, k, L), dt, str(case))
+
+
+def test_tiled_path_forced(orc, monkeypatch):
+    monkeypatch.setenv("WTCONV_NO_WHOLE", "1")
+    n, c, h, w, k, L = 3, 4, 56, 56, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, seed=11)
+    d = DevInputs(inp, "f32")
+    got = backward_weight(d)
+    torch.cuda.synchronize()
+    assert_grads_close(got, _oracle(orc, inp, k, L), "f32", "forced tiled")
+
+
+def test_deterministic(orc):
+    inp = make_inputs(4, 8, 56, 56, 5, 3, seed=12)
+    d = DevInputs(inp, "f32")
+    a = [t.clone() for t in backward_weight(d)]
+    b = backward_weight(d)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_workload_tiny(orc):
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    got = backward_weight(DevInputs(inp, wl.dtype))
+    torch.cuda.synchronize()
+    assert_grads_close(got, _oracle(orc, inp, wl.k, wl.levels), wl.dtype, "tiny")
+
+
+@pytest.mark.parametrize("name", ["stage1", "stage2"])
+def test_workload_full(orc, name):
+    wl = WORKLOADS[name]
+    _log("wgrad %s full" % name)
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    got = backward_weight(DevInputs(inp, wl.dtype))
+    torch.cuda.synchronize()
+    assert_grads_close(got, _oracle(orc, inp, wl.k, wl.levels), wl.dtype, name)
+
+
+def _chunked(orc, wl, chunk, check_chunks):
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    d = DevInputs(inp, wl.dtype)
+    full = [None if t is None else t.double().cpu().numpy() for t in backward_weight(d)]
+    torch.cuda.synchronize()
+    total = None
+    for i, n0 in enumerate(range(0, wl.n, chunk)):
+        sub = make_inputs(1, 1, 2, 2, wl.k, wl.levels, seed=0)  # shape holder only
+        sub.x, sub.dy = inp.x[n0:n0 + chunk], inp.dy[n0:n0 + chunk]
+        sub.w_base, sub.bias, sub.s_base, sub.w_lvl, sub.s_lvl = inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl
+        part = [None if t is None else t.double().cpu().numpy() for t in backward_weight(DevInputs(sub, wl.dtype))]
+        torch.cuda.synchronize()
+        if i in check_chunks:
+            assert_grads_close(part, _oracle(orc, inp, wl.k, wl.levels, slice(n0, n0 + chunk)), wl.dtype,
+                               "%s chunk %d" % (wl.name, i))
+        if total is None:
+            total = part
+        else:
+            # ds and dw are linear in the (x, dy) pairs, so chunks add up
+            total = [t + p for t, p in zip(total, part)]
+    for name, f, t in zip(("dw_base", "dbias", "ds_base", "dw_lvl", "ds_lvl"), full, total):
+        rel = np.linalg.norm(f - t) / max(np.linalg.norm(t), 1e-30)
+        assert rel <= 1e-5, (wl.name, name, rel)
+
+
+@pytest.mark.parametrize("wl", sweep_workloads(), ids=lambda w: "L%d_%s" % (w.levels, w.dtype))
+def test_workload_sweep_chunked(orc, wl):
+    _log("wgrad sweep L=%d %s" % (wl.levels, wl.dtype))
+    _chunked(orc, wl, chunk=8, check_chunks=(0,))
+
+
+def test_workload_large_chunked(orc):
+    _log("wgrad large")
+    _chunked(orc, WORKLOADS["large"], chunk=4, check_chunks=(1,))
