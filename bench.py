@@ -1,0 +1,280 @@
+"""Benchmark of the WTConv layer on one MI355X: forward + backward (data and
+parameter gradients) per step, on synthetic WTConvNeXt-shaped tensors.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
+
+Prints ONE JSON line.  A step is one pass of the whole layer: wtconv_forward,
+wtconv_backward_data and wtconv_backward_weight on one batch already resident
+in device memory.  `value` is the achieved rate on the modeled minimum bytes
+of a step (forward reads x and writes y, the data backward reads dy and
+writes dx, the weight backward reads x and dy: 6 E e bytes for E elements of
+e bytes).  Kernel durations are measured with HIP events on the stream the
+library launches on.  The `roofline` object is for the dominant kernel of the
+step; the `cpu_baseline` object times the CPU oracle on a bounded sample of
+the same workload.  Other options:
+    --cpu-sample N   images of the CPU-oracle sample (default: the whole batch; 0 disables it)
+    --mall-flush     write a 512 MiB buffer between timed steps
+    --all            also print one line per workload (stderr)
+    --copy-calibration BYTES   only run a plain device copy (for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "WTConv fwd+bwd µs/layer and achieved HBM GB/s (% of peak), fp32/fp16, L=1–5"
+HBM_PEAK_GBS = 8000.0
+# fp32 FMA on the vector ALUs without packed instructions (the library is built
+# with packed fp32 switched off): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+PACKED_FP32_PUBLISHED_TFLOPS = 157.3
+
+KERNEL_SOURCES = ("wtconv_whole_body.h", "wtconv_whole.hip", "wtconv_wgrad_body.h", "wtconv_wgrad.hip",
+                  "wtconv_fused_body.h", "wtconv_fused.hip", "wtconv_plan.h", "wtconv_wgrad_tile_body.h",
+                  "wtconv_wgrad_tile.hip", "wtconv_api.hip")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "level_haar_wavelet_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def conv_flops(wl) -> float:
+    """Algorithmic FLOPs of one op: 2 k^2 (1 + S(L)) per element, S(L) = sum 4^(1-l)."""
+    s = sum(4.0 ** (1 - l) for l in range(1, wl.levels + 1))
+    return 2.0 * wl.k * wl.k * (1.0 + s) * wl.elems
+
+
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    it was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != digest:
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def run_gpu(args, wl):
+    import torch
+
+    import level_haar_wavelet_amd as wt
+    from level_haar_wavelet_amd import _native
+    from level_haar_wavelet_amd.synthetic import make_inputs
+
+    _native.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
+    T = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev, dtype=dt)
+    x, dy = T(inp.x, tdt), T(inp.dy, tdt)
+    w0, b0, s0, wl_, sl_ = T(inp.w_base), T(inp.bias), T(inp.s_base), T(inp.w_lvl), T(inp.s_lvl)
+    y, dx = torch.empty_like(x), torch.empty_like(dy)
+    ws_bytes = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, 0 if wl.dtype == "f32" else 1,
+                                        _native.OP_BWD_WEIGHT)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(w0), torch.empty_like(b0), torch.empty_like(s0), torch.empty_like(wl_),
+             torch.empty_like(sl_))
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.mall_flush else None
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        wt.wtconv_backward_weight(x, dy, w0, b0, s0, wl_, sl_, workspace=ws, grads=grads, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    if flush is None:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            step(evs[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_total = start.elapsed_time(end)
+    else:
+        ms_total = 0.0
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush.fill_(i & 255)
+            torch.cuda.synchronize()
+            step(evs[i])
+            torch.cuda.synchronize()
+            ms_total += evs[i][0].elapsed_time(evs[i][3])
+        wall = time.perf_counter() - t0
+    per = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]
+    avg = [sum(p[j] for p in per) / len(per) * 1000.0 for j in range(3)]  # us per op
+    return {"ms_per_step": ms_total / args.steps, "us_ops": avg, "wall_s": wall}
+
+
+def cpu_baseline(wl, images, min_seconds=2.0):
+    """The CPU oracle (as it stands) on `images` images of the workload: one
+    forward, data backward and weight backward, repeated until at least
+    `min_seconds` have passed; the rate is the sample's own modeled bytes
+    (6 E e per pass) over the mean time of a pass."""
+    import oracle
+    from level_haar_wavelet_amd.synthetic import make_inputs
+
+    images = max(1, min(images, wl.n))
+    inp = make_inputs(images, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    threads = oracle.default_threads()
+    try:
+        threads = min(threads, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        pass
+    args = (inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+    oracle.forward(inp.x[:1], *args, nthreads=1)  # load the library outside the timing
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp.x, *args, nthreads=threads)
+        oracle.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels,
+                             nthreads=threads)
+        oracle.backward_weight(inp.x, inp.dy, *args, nthreads=threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 50:
+            break
+    per = dt / passes
+    e = images * wl.c * wl.h * wl.w
+    return {"value": round(6.0 * e * wl.ebytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d images (%dx%dx%dx%d), fwd + bwd_data + bwd_weight in fp64, %d passes, %.3f s/pass"
+                      % (images, wl.n, images, wl.c, wl.h, wl.w, passes, per),
+            "seconds_per_pass": round(per, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stage1")
+    ap.add_argument("--levels", type=int, default=None)
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--mall-flush", action="store_true")
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU layer; more than one GPU is not supported in this build "
+              "(the layer needs no collective for forward or data backward; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration:
+        import torch
+
+        a = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration}))
+        return
+
+    from level_haar_wavelet_amd.synthetic import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    if args.levels is not None or args.dtype is not None:
+        wl = wl.with_levels(args.levels if args.levels is not None else wl.levels, args.dtype)
+
+    res = run_gpu(args, wl)
+    E, e = wl.elems, wl.ebytes
+    step_bytes = 6.0 * E * e
+    ms = res["ms_per_step"]
+    value = step_bytes / (ms * 1e-3) / 1e9
+    us_f, us_b, us_w = res["us_ops"]
+    flops = conv_flops(wl)
+    ops = {"wtconv_forward": us_f, "wtconv_backward_data": us_b, "wtconv_backward_weight": us_w}
+    dominant = max(ops, key=ops.get)
+    achieved = flops / (ops[dominant] * 1e-6) / 1e12
+    digest = source_digest()
+    traffic = measured_traffic(dominant, digest)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s %dx%dx%dx%d k=%d L=%d %s" % (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels,
+                                                                 "fp32" if wl.dtype == "f32" else "fp16 storage"),
+                   "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w, "k": wl.k, "levels": wl.levels,
+                   "parallelism": "single GPU"},
+        "us_fwd": round(us_f, 2),
+        "us_bwd_data": round(us_b, 2),
+        "us_bwd_weight": round(us_w, 2),
+        "us_fwd_bwd": round(us_f + us_b + us_w, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "modeled_bytes_per_step": step_bytes,
+        "mall_flush": bool(args.mall_flush),
+        "roofline": {
+            "bound": "alu",
+            "kernel": dominant,
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_FP32_PEAK_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "flops_per_launch": flops,
+            "peak_published_packed_fp32": PACKED_FP32_PUBLISHED_TFLOPS,
+            "source_digest": digest,
+        },
+    }
+    if args.cpu_sample > 0:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+
+    if args.all:
+        from level_haar_wavelet_amd.synthetic import sweep_workloads
+
+        for w2 in [WORKLOADS["stage2"]] + sweep_workloads() + [WORKLOADS["large"]]:
+            r2 = run_gpu(args, w2)
+            v2 = 6.0 * w2.elems * w2.ebytes / (r2["ms_per_step"] * 1e-3) / 1e9
+            print(json.dumps({"workload": w2.name, "levels": w2.levels, "dtype": w2.dtype,
+                              "us_fwd": round(r2["us_ops"][0], 2), "us_bwd_data": round(r2["us_ops"][1], 2),
+                              "us_bwd_weight": round(r2["us_ops"][2], 2), "ms_per_step": round(r2["ms_per_step"], 4),
+                              "GB/s": round(v2, 1), "hbm_frac": round(v2 / HBM_PEAK_GBS, 4)}), file=sys.stderr,
+                  flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,19 +51,31 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
     wtc_wgrad_write<T, K, VEC>(a, ctx);
 }
 
+// One wave per (channel, map): lane t < k*k sums tap t over the workgroup
+// partials in group order (consecutive lanes read consecutive floats), lane
+// k*k does the same for the sum of dy; the scale gradient <W, G> (+ b0 Gb) is
+// a fixed butterfly reduction across the wave, so the result is bitwise
+// reproducible.
 __global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k, int levels, int groups, int plen,
-                                                                    const float *partial, const float *w_base,
-                                                                    const float *bias, const float *s_base,
-                                                                    const float *w_lvl, const float *s_lvl,
-                                                                    float *dw_base, float *dbias, float *ds_base,
-                                                                    float *dw_lvl, float *ds_lvl)
+                                                                    const float *__restrict__ partial,
+                                                                    const float *__restrict__ w_base,
+                                                                    const float *__restrict__ bias,
+                                                                    const float *__restrict__ s_base,
+                                                                    const float *__restrict__ w_lvl,
+                                                                    const float *__restrict__ s_lvl, float *dw_base,
+                                                                    float *dbias, float *ds_base, float *dw_lvl,
+                                                                    float *ds_lvl)
 {
     const int nmaps = 1 + 4 * levels;
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= C * nmaps) return;
-    const int c = idx / nmaps, g = idx - c * nmaps;
-    wtc_wgrad_finalize_one(c, g, C, k, levels, groups, plen, partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base,
-                           dbias, ds_base, dw_lvl, ds_lvl);
+    const int lane = threadIdx.x & 63;
+    const int pair = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (pair >= C * nmaps) return;  // whole waves leave together
+    const int c = pair / nmaps, g = pair - c * nmaps;
+    float term = wtc_wgrad_finalize_lane(lane, c, g, C, k, groups, plen, partial, w_base, bias, s_base, w_lvl,
+                                         s_lvl, dw_base, dbias, dw_lvl);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) term += __shfl_xor(term, d, 64);
+    if (lane == 0) wtc_wgrad_finalize_store(c, g, C, term, ds_base, ds_lvl);
 }
 
 template <typename T, int K, int VEC>
@@ -120,8 +132,8 @@ hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int p
                                      const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
                                      float *ds_base, float *dw_lvl, float *ds_lvl, hipStream_t stream)
 {
-    const int n = C * (1 + 4 * levels);
-    hipLaunchKernelGGL(wtconv_wgrad_finalize_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, C, k, levels,
+    const int pairs = C * (1 + 4 * levels);  // one wave each, four per workgroup
+    hipLaunchKernelGGL(wtconv_wgrad_finalize_kernel, dim3((pairs + 3) / 4), dim3(256), 0, stream, C, k, levels,
                        groups, plen, partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl,
                        ds_lvl);
     return hipGetLastError();

@@ -430,46 +430,74 @@ WTC_HD WTC_INLINE void wtc_wgrad_write(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
     }
 }
 
-// Second pass: one thread per (channel, map) sums the workgroup partials in
-// group order and applies the chain rule through the scales.
-WTC_HD WTC_INLINE void wtc_wgrad_finalize_one(int c, int g, int C, int k, int levels, int groups, int plen,
-                                             const float *partial, const float *w_base, const float *bias,
-                                             const float *s_base, const float *w_lvl, const float *s_lvl,
-                                             float *dw_base, float *dbias, float *ds_base, float *dw_lvl,
-                                             float *ds_lvl)
+// Second pass, one 64-lane wave per (channel c, map g): lane t < k*k sums tap
+// t of the workgroup partials in group order (lane k*k the sum of dy for the
+// base map), writes the weight (and bias) gradient, and returns its term of
+// the scale gradient, which the caller adds up with a fixed xor butterfly
+// over the wave (wtc_wgrad_finalize_store takes lane 0's total).
+WTC_HD WTC_INLINE float wtc_wgrad_finalize_lane(int lane, int c, int g, int C, int k, int groups, int plen,
+                                               const float *partial, const float *w_base, const float *bias,
+                                               const float *s_base, const float *w_lvl, const float *s_lvl,
+                                               float *dw_base, float *dbias, float *dw_lvl)
 {
     const int kk = k * k;
     const int off = g == 0 ? 0 : kk + 1 + (g - 1) * kk;
-    float gsum[49];
-    float gb = 0.0f;
-    for (int t = 0; t < kk; ++t) gsum[t] = 0.0f;
-    for (int q = 0; q < groups; ++q) {
-        const float *src = partial + ((int64_t)q * C + c) * plen + off;
-        for (int t = 0; t < kk; ++t) gsum[t] += src[t];
-        if (g == 0) gb += src[kk];
-    }
+    const int nval = g == 0 ? kk + 1 : kk;
+    float gsum = 0.0f;
+    if (lane < nval)
+        for (int q = 0; q < groups; ++q) gsum += partial[((int64_t)q * C + c) * plen + off + lane];
+    float term = 0.0f;
     if (g == 0) {
         const float s0 = s_base[c];
-        const float b0 = bias ? bias[c] : 0.0f;
-        float ds = 0.0f;
-        for (int t = 0; t < kk; ++t) {
-            dw_base[c * kk + t] = s0 * gsum[t];
-            ds = wtc_fma(w_base[c * kk + t], gsum[t], ds);
+        if (lane < kk) {
+            dw_base[c * kk + lane] = s0 * gsum;
+            term = w_base[c * kk + lane] * gsum;
+        } else if (lane == kk) {
+            dbias[c] = s0 * gsum;
+            term = (bias ? bias[c] : 0.0f) * gsum;
         }
-        dbias[c] = s0 * gb;
-        ds_base[c] = wtc_fma(b0, gb, ds);
     } else {
         const int m = (g - 1) / 4 + 1, b = (g - 1) % 4;
         const int64_t ch = (int64_t)(m - 1) * 4 * C + 4 * c + b;
-        const float s = s_lvl[ch];
-        float ds = 0.0f;
-        for (int t = 0; t < kk; ++t) {
-            const float gt = ldexpf(gsum[t], -2 * m);
-            dw_lvl[ch * kk + t] = s * gt;
-            ds = wtc_fma(w_lvl[ch * kk + t], gt, ds);
+        if (lane < kk) {
+            const float gt = ldexpf(gsum, -2 * m);
+            dw_lvl[ch * kk + lane] = s_lvl[ch] * gt;
+            term = w_lvl[ch * kk + lane] * gt;
         }
-        ds_lvl[ch] = ds;
+    }
+    return term;
+}
+
+WTC_HD WTC_INLINE void wtc_wgrad_finalize_store(int c, int g, int C, float total, float *ds_base, float *ds_lvl)
+{
+    if (g == 0) {
+        ds_base[c] = total;
+    } else {
+        const int m = (g - 1) / 4 + 1, b = (g - 1) % 4;
+        ds_lvl[(int64_t)(m - 1) * 4 * C + 4 * c + b] = total;
     }
 }
+
+#ifdef WTC_EMULATE
+// The wave of the second pass on the host: the same per-lane work and the
+// same xor butterfly as the kernel's shuffles.
+static inline void wtc_wgrad_finalize_one(int c, int g, int C, int k, int levels, int groups, int plen,
+                                          const float *partial, const float *w_base, const float *bias,
+                                          const float *s_base, const float *w_lvl, const float *s_lvl,
+                                          float *dw_base, float *dbias, float *ds_base, float *dw_lvl,
+                                          float *ds_lvl)
+{
+    (void)levels;
+    float t[64], u[64];
+    for (int lane = 0; lane < 64; ++lane)
+        t[lane] = wtc_wgrad_finalize_lane(lane, c, g, C, k, groups, plen, partial, w_base, bias, s_base, w_lvl,
+                                          s_lvl, dw_base, dbias, dw_lvl);
+    for (int d = 32; d >= 1; d >>= 1) {
+        for (int lane = 0; lane < 64; ++lane) u[lane] = t[lane] + t[lane ^ d];
+        for (int lane = 0; lane < 64; ++lane) t[lane] = u[lane];
+    }
+    wtc_wgrad_finalize_store(c, g, C, t[0], ds_base, ds_lvl);
+}
+#endif
 
 #endif  // WTCONV_WGRAD_BODY_H
