@@ -27,19 +27,17 @@ __global__ __launch_bounds__(256) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     wtc_whole_table<T, K, BW>(a, ctx);
     for (int img = 0; img < ctx.nimg; ++img) {
         wtc_whole_select<T>(a, ctx, img);
-        wtc_whole_store_input<T, K, BW>(a, ctx);
+        wtc_whole_stage<T, K, BW>(a, ctx);
         wtc_lds_barrier();
         if (img + 1 < ctx.nimg) wtc_whole_load<T, K, BW>(a, ctx, img + 1);
-        wtc_whole_analysis1<T, K>(a, ctx);
-        wtc_lds_barrier();
-        for (int m = 2; m <= a.p.levels; ++m) {
+        for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
             wtc_lds_barrier();
         }
         wtc_whole_conv<T, K, BW>(a, ctx);
         wtc_lds_barrier();
-        // the next image's input store touches only the input map, which the
-        // convolution phase above has finished reading
+        // the next image's staging touches the input and analysis maps, which
+        // the convolution phase above has finished reading
         wtc_whole_out<T, K, BW>(a, ctx);
     }
 }

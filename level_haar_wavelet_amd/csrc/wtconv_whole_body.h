@@ -19,11 +19,15 @@
 //     flight across them;
 //   * LDS is zeroed once: every map keeps a zero border of r pixels, which is
 //     the convolutions' zero padding, and only interiors are rewritten;
-//   * all maps have an odd row pitch, and consecutive lanes take consecutive
-//     2-row blocks, so the 2-row window reads of a wave fall in distinct banks;
-//   * one convolution phase holds the base-convolution blocks (whose results
-//     stay in registers until the synthesis) and every per-level piece of
-//     every level and band, dealt round-robin to the threads.
+//   * every convolution -- the base one at full resolution and the four bands
+//     of every level -- is cut into the same 4x4-output pieces, dealt
+//     round-robin to the threads from a descriptor table built once per
+//     workgroup, so the work is balanced and a wave runs one code path;
+//   * maps are stored with their zero border at (r, r) and 16-byte rows, so a
+//     piece's input window starts on a 16-byte boundary and is read with
+//     128-bit LDS reads (consecutive lanes take consecutive column pieces);
+//   * the base convolution's output goes to LDS like the level outputs, and a
+//     last pass combines them per 2 x BW output block and stores y.
 #ifndef WTCONV_WHOLE_BODY_H
 #define WTCONV_WHOLE_BODY_H
 
@@ -38,52 +42,58 @@ struct WtcWholePlan {
     int32_t planes;      // images per workgroup (same channel)
     int32_t vec;         // activation elements per global chunk
     int32_t out_bw;      // output block width (2, 4 or 8)
-    WtcMap x;            // input, rows h + 4r, image origin at (2r, 2r)
+    int32_t gr;          // input rows per staging group (2 or 4)
+    int32_t groups;      // staging groups per image (one per thread at most)
+    int32_t ws;          // floats per folded kernel (k*k rounded up to 4)
+    WtcMap x;            // input with an r border, origin (r, r)
     WtcMap u[WTC_MAXL + 1];   // U_m plus three detail bands, m = 1..L, origin (r, r)
-    WtcMap z[WTC_MAXL + 1];   // four conv outputs of level m, origin (0, 0)
+    WtcMap z[WTC_MAXL + 1];   // z[0]: base output; z[m]: four conv outputs of level m; origin (0, 0)
     int32_t wf_off;
-    int32_t items;       // convolution items per image: base blocks, then pieces
-    int32_t tab_off;     // item descriptors, 4 ints each
+    int32_t items;       // convolution pieces per image
+    int32_t tab_off;     // piece descriptors, 4 ints each
     int32_t lds_floats;
 };
 
-WTC_PLAN_HD static inline int32_t wtc_odd_pitch(int32_t cols) { return cols | 1; }
+#define WTC_WP 4  // piece side (outputs)
+
+// Rows of 16 bytes, at least `cols` floats.
+WTC_PLAN_HD static inline int32_t wtc_pitch16(int32_t cols) { return wtc_roundup(cols, 4); }
 
 // Fills the LDS layout; returns the number of floats.
 static inline int32_t wtc_whole_layout(WtcWholePlan *p)
 {
-    const int32_t L = p->levels, r = p->k / 2, kk = p->k * p->k;
+    const int32_t L = p->levels, r = p->k / 2, kk = p->k * p->k, P = WTC_WP;
     int32_t off = 0;
+    p->ws = wtc_roundup(kk, 4);
     p->wf_off = off;
-    off += wtc_roundup((1 + 4 * L) * kk, 4);
-    p->x.off = off;
-    p->x.rows = p->h + 4 * r;
-    p->x.pitch = wtc_odd_pitch(wtc_roundup(p->w, 8) + 4 * r);
-    off += p->x.rows * p->x.pitch;
+    off += (1 + 4 * L) * p->ws;
     for (int32_t m = 0; m <= WTC_MAXL; ++m) {
         p->u[m].off = p->u[m].pitch = p->u[m].rows = 0;
         p->z[m] = p->u[m];
     }
+    // input map: the base convolution's pieces read windows of P + 2r rows and
+    // columns starting at multiples of P (stored coordinates)
+    p->x.off = off;
+    p->x.rows = wtc_roundup(p->h, P) + 2 * r;
+    p->x.pitch = wtc_pitch16(wtc_roundup(p->w, P) + 2 * r);
+    off += p->x.rows * p->x.pitch;
     for (int32_t m = 1; m <= L; ++m) {
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
-        // map plus r-wide zero border; room for the ragged last piece
         p->u[m].off = off;
-        p->u[m].rows = wtc_roundup(Hm, WTC_PR) + 2 * r;
-        p->u[m].pitch = wtc_odd_pitch(wtc_roundup(Wm, WTC_PC) + 2 * r);
+        p->u[m].rows = wtc_roundup(Hm, P) + 2 * r;
+        p->u[m].pitch = wtc_pitch16(wtc_roundup(Wm, P) + 2 * r);
         off += 4 * p->u[m].rows * p->u[m].pitch;
     }
-    for (int32_t m = 1; m <= L; ++m) {
+    for (int32_t m = 0; m <= L; ++m) {
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
         p->z[m].off = off;
-        p->z[m].rows = Hm;
-        p->z[m].pitch = wtc_odd_pitch(Wm);
-        off += 4 * p->z[m].rows * p->z[m].pitch;
+        p->z[m].rows = wtc_roundup(Hm, P);
+        p->z[m].pitch = wtc_pitch16(wtc_roundup(Wm, P));
+        off += (m == 0 ? 1 : 4) * p->z[m].rows * p->z[m].pitch;
     }
-    int32_t items = (p->h / 2) * (p->w / p->out_bw);
-    for (int32_t m = 1; m <= L; ++m)
-        items += 4 * (((p->h >> m) + WTC_PR - 1) / WTC_PR) * (((p->w >> m) + WTC_PC - 1) / WTC_PC);
+    int32_t items = ((p->h + P - 1) / P) * ((p->w + P - 1) / P);
+    for (int32_t m = 1; m <= L; ++m) items += 4 * (((p->h >> m) + P - 1) / P) * (((p->w >> m) + P - 1) / P);
     p->items = items;
-    off = wtc_roundup(off, 4);
     p->tab_off = off;
     off += 4 * items;
     p->lds_floats = wtc_roundup(off, 4);
@@ -114,9 +124,12 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     while (vec > 1 && w % vec) vec /= 2;
     p->vec = vec;
     p->out_bw = (w % 8 == 0) ? 8 : (w % 4 == 0) ? 4 : 2;
-    const int64_t chunks = (int64_t)h * (w / vec);
-    if (chunks > (int64_t)WTC_WHOLE_NCH * nthreads) return -1;
-    if (wtc_whole_blocks(p) > nthreads) return -1;  // one base block per thread
+    // a staging group is gr rows x vec columns of the input; with 4 rows and
+    // at least 4 columns its thread computes Haar levels 1 and 2 itself
+    p->gr = (levels >= 2 && vec >= 4 && p->out_bw >= 4) ? 4 : 2;
+    p->groups = (h / p->gr) * (w / vec);
+    if (p->groups > nthreads) return -1;
+    if (wtc_whole_blocks(p) > 2 * nthreads) return -1;
     wtc_whole_layout(p);
     return p->lds_floats <= budget_floats ? 0 : -1;
 }
@@ -138,10 +151,11 @@ struct WtcWholeCtx {
     int tid, nth;
     int c, n0, nimg;  // channel, first image, images of this workgroup
     float bias;
-    // prefetched raw chunk values (as loaded: T)
-    T pre[WTC_WHOLE_NCH][16 / sizeof(T)];
-    // base-convolution result of this thread's block
-    float y0[2][8];
+    // staging group of this thread (gvalid: it has one) and its prefetched
+    // input rows (as loaded: T)
+    int grow, gcol;
+    bool gvalid;
+    T pre[4][16 / sizeof(T)];
 #ifdef WTC_EMULATE
     int64_t lds_n, img_n;
 #endif
@@ -169,6 +183,11 @@ WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     float b = 0.0f;
     if (!p.rotate && a.bias) b = a.s_base[ctx.c] * a.bias[ctx.c];
     ctx.bias = b;
+    const int gpr = p.w / p.vec;
+    const int grp = wtc_min(ctx.tid, p.groups - 1);  // threads past the last group repeat it, unstored
+    ctx.gvalid = ctx.tid < p.groups;
+    ctx.grow = grp / gpr;
+    ctx.gcol = grp - ctx.grow * gpr;
 }
 
 template <typename T>
@@ -207,7 +226,7 @@ WTC_HD WTC_INLINE void wtc_whole_fold(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
             const float s = WTC_PAR(a.s_lvl, ch, (int64_t)p.levels * 4 * C);
             v = ldexpf(s * WTC_PAR(a.w_lvl, (int64_t)ch * kk + se, (int64_t)p.levels * 4 * C * kk), -2 * m);
         }
-        WTC_LDS(ctx, p.wf_off + i) = v;
+        WTC_LDS(ctx, p.wf_off + blk * p.ws + e) = v;
     }
 }
 
@@ -218,21 +237,20 @@ struct WtcVec {
     static constexpr int v = BW < (int)(16 / sizeof(T)) ? BW : (int)(16 / sizeof(T));
 };
 
-// Issue the loads of image `img` of the workgroup into registers.
+// Issue the loads of image `img` of the workgroup into registers: this
+// thread's staging group, gr rows of vec elements (every lane loads a valid
+// group, so that no branch surrounds the loads).
 template <typename T, int K, int BW>
 WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
     const WtcWholePlan &p = a.p;
-    const T *src = a.in + ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
     constexpr int vec = WtcVec<T, BW>::v;
-    const int cpr = p.w / vec, total = p.h * cpr;
+    const T *src = a.in + ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
+    const int64_t e0 = (int64_t)(p.gr * ctx.grow) * p.w + vec * ctx.gcol;
 #pragma unroll
-    for (int q = 0; q < WTC_WHOLE_NCH; ++q) {
-        // every lane loads (a valid chunk) so that no branch surrounds the loads;
-        // lanes past the end repeat the last chunk and do not store it
-        const int idx = wtc_min(ctx.tid + q * ctx.nth, total - 1);
-        {
-            const int64_t e = (int64_t)idx * vec;  // chunks tile the image row-major
+    for (int q = 0; q < 4; ++q) {
+        if (q < p.gr) {
+            const int64_t e = e0 + (int64_t)q * p.w;
 #ifdef WTC_EMULATE
             const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.h * p.w;
             for (int t = 0; t < vec; ++t) ctx.pre[q][t] = wtc_chk(a.in, base + e + t, all, __LINE__);
@@ -257,59 +275,69 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     }
 }
 
-// Write the prefetched chunks into the interior of the input map.
+// Write the prefetched group into the input map and compute Haar level 1
+// (and level 2 when the group has 4 rows) of it straight from registers:
+//   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
+//   U_2 and B_2^1..3 at its 1 x (vec/4) level-2 positions.
 template <typename T, int K, int BW>
-WTC_HD WTC_INLINE void wtc_whole_store_input(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
+WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int R = K / 2;
+    constexpr int vec = WtcVec<T, BW>::v, h1 = vec / 2, h2 = vec / 4 > 0 ? vec / 4 : 1;
     const WtcWholePlan &p = a.p;
-    constexpr int vec = WtcVec<T, BW>::v;
-    const int cpr = p.w / vec, total = p.h * cpr;
-    const WtcMap xm = p.x;
+    if (!ctx.gvalid) return;
+    const WtcMap xm = p.x, u1 = p.u[1];
+    const int st1 = u1.rows * u1.pitch;
+    float x[4][vec];
 #pragma unroll
-    for (int q = 0; q < WTC_WHOLE_NCH; ++q) {
-        const int idx = ctx.tid + q * ctx.nth;
-        if (idx < total) {
-            const int row = idx / cpr, col = (idx - row * cpr) * vec;
-            const int o = xm.off + (row + 2 * R) * xm.pitch + col + 2 * R;
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, o + t) = wtc_to_float(ctx.pre[q][t]);
+        for (int t = 0; t < vec; ++t) x[q][t] = q < p.gr ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+    const int r0 = p.gr * ctx.grow, c0 = vec * ctx.gcol;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < p.gr)
+#pragma unroll
+            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xm.off + (r0 + q + R) * xm.pitch + c0 + t + R) = x[q][t];
+    // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
+    float ll[2][h1];
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+        if (2 * aa < p.gr) {
+            const int i = r0 / 2 + aa;
+#pragma unroll
+            for (int bb = 0; bb < h1; ++bb) {
+                const float x00 = x[2 * aa][2 * bb], x01 = x[2 * aa][2 * bb + 1];
+                const float x10 = x[2 * aa + 1][2 * bb], x11 = x[2 * aa + 1][2 * bb + 1];
+                const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+                const int o = u1.off + (i + R) * u1.pitch + c0 / 2 + bb + R;
+                ll[aa][bb] = sa + sc;
+                WTC_LDS(ctx, o) = sa + sc;
+                WTC_LDS(ctx, o + st1) = sa - sc;
+                WTC_LDS(ctx, o + 2 * st1) = da + dc;
+                WTC_LDS(ctx, o + 3 * st1) = da - dc;
+            }
+        }
+    }
+    if (p.gr == 4 && vec >= 4) {
+        const WtcMap u2 = p.u[2];
+        const int st2 = u2.rows * u2.pitch;
+#pragma unroll
+        for (int bb = 0; bb < h2; ++bb) {
+            const float x00 = ll[0][2 * bb], x01 = ll[0][2 * bb + 1];
+            const float x10 = ll[1][2 * bb], x11 = ll[1][2 * bb + 1];
+            const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+            const int o = u2.off + (ctx.grow + R) * u2.pitch + c0 / 4 + bb + R;
+            WTC_LDS(ctx, o) = sa + sc;
+            WTC_LDS(ctx, o + st2) = sa - sc;
+            WTC_LDS(ctx, o + 2 * st2) = da + dc;
+            WTC_LDS(ctx, o + 3 * st2) = da - dc;
         }
     }
 }
 
-// Level-1 analysis: U_1 and B_1^1..3 from the input map (interior only).
-template <typename T, int K>
-WTC_HD WTC_INLINE void wtc_whole_analysis1(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
-{
-    constexpr int R = K / 2;
-    const WtcWholePlan &p = a.p;
-    const int H1 = p.h >> 1, W1 = p.w >> 1;
-    const WtcMap xm = p.x, um = p.u[1];
-    const int st = um.rows * um.pitch;
-    const int total = H1 * W1;
-    int i = ctx.tid / W1, j = ctx.tid - (ctx.tid / W1) * W1;
-    const int di = ctx.nth / W1, dj = ctx.nth - di * W1;
-    for (int idx = ctx.tid; idx < total; idx += ctx.nth) {
-        const int s = xm.off + (2 * i + 2 * R) * xm.pitch + 2 * j + 2 * R;
-        const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
-        const float x10 = WTC_LDS(ctx, s + xm.pitch), x11 = WTC_LDS(ctx, s + xm.pitch + 1);
-        const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-        const int o = um.off + (i + R) * um.pitch + j + R;
-        WTC_LDS(ctx, o) = sa + sc;
-        WTC_LDS(ctx, o + st) = sa - sc;
-        WTC_LDS(ctx, o + 2 * st) = da + dc;
-        WTC_LDS(ctx, o + 3 * st) = da - dc;
-        i += di;
-        j += dj;
-        if (j >= W1) {
-            j -= W1;
-            ++i;
-        }
-    }
-}
-
-// Level-m analysis (m >= 2) from U_{m-1}.
+// Level-m analysis from U_{m-1} in LDS, for the levels the staging phase did
+// not compute.
 template <typename T, int K>
 WTC_HD WTC_INLINE void wtc_whole_analysis(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int m)
 {
@@ -340,54 +368,41 @@ WTC_HD WTC_INLINE void wtc_whole_analysis(const WtcWholeArgs<T> &a, WtcWholeCtx<
     }
 }
 
-// Item descriptors, built once per workgroup (they depend only on the plan).
-// Items [0, nblk) are base-convolution blocks of 2 x BW outputs, block rows
-// fastest (consecutive lanes take consecutive row pairs: with the odd pitch
-// their window reads fall in distinct banks):
-//   d0 = LDS index of the input window (row 2by - R, column BW bx - R)
-//   d1 = offset of the block's first output in the image
-//   d2 = LDS index of the level-1 outputs of the block's first 2x2 quad
-//   d3 = by | (bx << 16)
-// The remaining items are WTC_PR x WTC_PC pieces of one band of one level,
-// piece rows fastest:
-//   d0 = LDS index of the input window of the band map
-//   d1 = LDS index of the first output in the band's output map
-//   d2 = LDS index of the folded weights | (input pitch << 16)
-//   d3 = valid output rows | (valid columns << 8) | (output pitch << 16)
+// First level the analysis phase computes (the staging phase did the ones
+// below).
+WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p) { return p.gr == 4 ? 3 : 2; }
+
+// Piece descriptors, built once per workgroup (they depend only on the plan).
+// Piece order: the base map (full resolution), then band 0..3 of level 1, 2,
+// ...; inside a map, column pieces fastest.  Four ints:
+//   d0 = LDS index of the input window (stored row P pr, column P pc, i.e.
+//        map element (P pr - r, P pc - r)), a multiple of 4
+//   d1 = LDS index of the first output in the output map
+//   d2 = input pitch | output pitch << 16
+//   d3 = LDS index of the folded weights | (1 << 16 for the base map)
 template <typename T, int K, int BW>
 WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
-    constexpr int R = K / 2, kk = K * K;
+    constexpr int P = WTC_WP;
     const WtcWholePlan &p = a.p;
-    const int nby = p.h / 2, nblk = nby * (p.w / BW);
-    const WtcMap xm = p.x, z1 = p.z[1];
     for (int it = ctx.tid; it < p.items; it += ctx.nth) {
-        int d0, d1, d2, d3;
-        if (it < nblk) {
-            const int by = it % nby, bx = it / nby;
-            d0 = xm.off + (2 * by + R) * xm.pitch + BW * bx + R;
-            d1 = 2 * by * p.w + BW * bx;
-            d2 = z1.off + by * z1.pitch + (BW / 2) * bx;
-            d3 = by | (bx << 16);
-        } else {
-            int rem = it - nblk, m = 1, npr = 0, npc = 0;
-            for (; m <= p.levels; ++m) {
-                npr = ((p.h >> m) + WTC_PR - 1) / WTC_PR;
-                npc = ((p.w >> m) + WTC_PC - 1) / WTC_PC;
-                if (rem < 4 * npr * npc) break;
-                rem -= 4 * npr * npc;
-            }
-            const int b = rem / (npr * npc);
-            rem -= b * npr * npc;
-            const int pc = rem / npr, pr = rem - pc * npr;
-            const WtcMap um = p.u[m], zm = p.z[m];
-            const int Hm = p.h >> m, Wm = p.w >> m;
-            d0 = um.off + b * um.rows * um.pitch + (WTC_PR * pr) * um.pitch + WTC_PC * pc;
-            d1 = zm.off + b * zm.rows * zm.pitch + (WTC_PR * pr) * zm.pitch + WTC_PC * pc;
-            d2 = (p.wf_off + (1 + 4 * (m - 1) + b) * kk) | (um.pitch << 16);
-            d3 = wtc_min(WTC_PR, Hm - WTC_PR * pr) | (wtc_min(WTC_PC, Wm - WTC_PC * pc) << 8) | (zm.pitch << 16);
+        int rem = it, g = 0, npc = 0, npr = 0, m = 0, b = 0;
+        for (;;) {
+            m = g == 0 ? 0 : (g - 1) / 4 + 1;
+            b = g == 0 ? 0 : (g - 1) % 4;
+            npr = ((p.h >> m) + P - 1) / P;
+            npc = ((p.w >> m) + P - 1) / P;
+            if (rem < npr * npc) break;
+            rem -= npr * npc;
+            ++g;
         }
-        int *tab = (int *)&WTC_LDS(ctx, p.tab_off + 4 * it);
+        const int pr = rem / npc, pc = rem - pr * npc;
+        const WtcMap im = m == 0 ? p.x : p.u[m], om = p.z[m];
+        const int d0 = im.off + b * im.rows * im.pitch + (P * pr) * im.pitch + P * pc;
+        const int d1 = om.off + b * om.rows * om.pitch + (P * pr) * om.pitch + P * pc;
+        const int d2 = im.pitch | (om.pitch << 16);
+        const int d3 = (p.wf_off + g * p.ws) | ((g == 0) << 16);
+        int *tab = (int *)&WTC_LDS(ctx, p.tab_off + 4 * it + 3) - 3;
         tab[0] = d0;
         tab[1] = d1;
         tab[2] = d2;
@@ -395,143 +410,183 @@ WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     }
 }
 
-template <typename T>
-WTC_HD WTC_INLINE void wtc_whole_desc(WtcWholeCtx<T> &ctx, int off, int &d0, int &d1, int &d2, int &d3)
+// N consecutive LDS floats starting at a multiple of 4 (16-byte reads).
+template <typename T, int N>
+WTC_HD WTC_INLINE void wtc_lds_row(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N])
 {
 #ifdef WTC_EMULATE
-    const int *t = (const int *)&WTC_LDS(ctx, off + 3) - 3;
+    for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
 #else
-    const int *t = (const int *)&ctx.lds[off];
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    static_assert(N % 4 == 0, "16-byte LDS rows");
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        const v4 v = *(const v4 *)&ctx.lds[idx + 4 * q];
+        dst[4 * q] = v.x;
+        dst[4 * q + 1] = v.y;
+        dst[4 * q + 2] = v.z;
+        dst[4 * q + 3] = v.w;
+    }
 #endif
-    d0 = t[0];
-    d1 = t[1];
-    d2 = t[2];
-    d3 = t[3];
 }
 
-// The convolution phase: each thread takes items tid, tid + nth, ...; its base
-// block (item tid, if any) stays in registers for the synthesis.
+// N consecutive LDS floats starting at an index aligned to min(N, 4).
+template <typename T, int N>
+WTC_HD WTC_INLINE void wtc_lds_vec(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N])
+{
+#ifdef WTC_EMULATE
+    for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
+#else
+    if constexpr (N % 4 == 0) {
+        wtc_lds_row<T, N>(ctx, idx, dst);
+    } else if constexpr (N == 2) {
+        typedef float v2 __attribute__((ext_vector_type(2)));
+        const v2 v = *(const v2 *)&ctx.lds[idx];
+        dst[0] = v.x;
+        dst[1] = v.y;
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) dst[e] = ctx.lds[idx + e];
+    }
+#endif
+}
+
+template <typename T, int N>
+WTC_HD WTC_INLINE void wtc_lds_store4(WtcWholeCtx<T> &ctx, int idx, const float (&src)[N])
+{
+#ifdef WTC_EMULATE
+    for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
+#else
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    static_assert(N % 4 == 0, "16-byte LDS rows");
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+        v4 v;
+        v.x = src[4 * q];
+        v.y = src[4 * q + 1];
+        v.z = src[4 * q + 2];
+        v.w = src[4 * q + 3];
+        *(v4 *)&ctx.lds[idx + 4 * q] = v;
+    }
+#endif
+}
+
+// The convolution phase: every thread computes pieces tid, tid + nth, ...
 template <typename T, int K, int BW>
 WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
-    constexpr int kk = K * K;
+    constexpr int P = WTC_WP, KK = K * K, WS = (KK + 3) / 4 * 4;
+    constexpr int NW = P + K - 1, NR = (NW + 3) / 4 * 4;  // window width, as read
     const WtcWholePlan &p = a.p;
-    const int nblk = (p.h / 2) * (p.w / BW);
-    const WtcMap xm = p.x;
     for (int it = ctx.tid; it < p.items; it += ctx.nth) {
-        int d0, d1, d2, d3;
-        wtc_whole_desc<T>(ctx, p.tab_off + 4 * it, d0, d1, d2, d3);
-        if (it < nblk) {
-            float w0[kk];
-#pragma unroll
-            for (int e = 0; e < kk; ++e) w0[e] = wtc_uniform(WTC_LDS(ctx, p.wf_off + e));
-            float acc[2][BW];
-#pragma unroll
-            for (int dr = 0; dr < 2; ++dr)
-#pragma unroll
-                for (int dc = 0; dc < BW; ++dc) acc[dr][dc] = ctx.bias;
-#pragma unroll
-            for (int t = 0; t < 2 + K - 1; ++t) {
-                float row[BW + K - 1];
-#pragma unroll
-                for (int e = 0; e < BW + K - 1; ++e) row[e] = WTC_LDS(ctx, d0 + t * xm.pitch + e);
-#pragma unroll
-                for (int dr = 0; dr < 2; ++dr) {
-                    const int u = t - dr;
-                    if (u < 0 || u >= K) continue;
-#pragma unroll
-                    for (int v = 0; v < K; ++v)
-#pragma unroll
-                        for (int dc = 0; dc < BW; ++dc) acc[dr][dc] = wtc_fma(w0[u * K + v], row[dc + v], acc[dr][dc]);
-                }
-            }
-#pragma unroll
-            for (int dr = 0; dr < 2; ++dr)
-#pragma unroll
-                for (int dc = 0; dc < BW; ++dc) ctx.y0[dr][dc] = acc[dr][dc];
-        } else {
-            const int wk = d2 & 0xffff, spitch = d2 >> 16;
-            const int vr = d3 & 0xff, vc = (d3 >> 8) & 0xff, zpitch = d3 >> 16;
-            float acc[WTC_PR][WTC_PC];
-#pragma unroll
-            for (int dr = 0; dr < WTC_PR; ++dr)
-#pragma unroll
-                for (int dc = 0; dc < WTC_PC; ++dc) acc[dr][dc] = 0.0f;
-            // wtc_conv_block_lds takes a context only for its LDS pointer
-            WtcCtx<T> lc;
-            lc.lds = ctx.lds;
+        int dsc[4];
+        {
+            float tmp[4];
+            wtc_lds_row<T, 4>(ctx, p.tab_off + 4 * it, tmp);
+            for (int e = 0; e < 4; ++e) {
 #ifdef WTC_EMULATE
-            lc.lds_n = ctx.lds_n;
+                __builtin_memcpy(&dsc[e], &tmp[e], 4);
+#else
+                dsc[e] = __float_as_int(tmp[e]);
 #endif
-            wtc_conv_block_lds<T, K, WTC_PR, WTC_PC>(lc, d0, spitch, wk, acc);
-#pragma unroll
-            for (int dr = 0; dr < WTC_PR; ++dr)
-#pragma unroll
-                for (int dc = 0; dc < WTC_PC; ++dc)
-                    if (dr < vr && dc < vc) WTC_LDS(ctx, d1 + dr * zpitch + dc) = acc[dr][dc];
+            }
         }
+        const int src = dsc[0], dst = dsc[1];
+        const int ip = dsc[2] & 0xffff, op = dsc[2] >> 16;
+        const int wk = dsc[3] & 0xffff;
+        const float init = (dsc[3] >> 16) ? ctx.bias : 0.0f;
+        float wv[WS];
+        wtc_lds_row<T, WS>(ctx, wk, wv);
+        float acc[P][P];
+#pragma unroll
+        for (int dr = 0; dr < P; ++dr)
+#pragma unroll
+            for (int dc = 0; dc < P; ++dc) acc[dr][dc] = init;
+        float row[NR];
+        wtc_lds_row<T, NR>(ctx, src, row);
+#pragma unroll
+        for (int t = 0; t < P + K - 1; ++t) {
+            float nxt[NR];
+            if (t + 1 < P + K - 1) wtc_lds_row<T, NR>(ctx, src + (t + 1) * ip, nxt);
+#pragma unroll
+            for (int dr = 0; dr < P; ++dr) {
+                const int u = t - dr;
+                if (u < 0 || u >= K) continue;
+#pragma unroll
+                for (int v = 0; v < K; ++v)
+#pragma unroll
+                    for (int dc = 0; dc < P; ++dc) acc[dr][dc] = wtc_fma(wv[u * K + v], row[dc + v], acc[dr][dc]);
+            }
+            if (t + 1 < P + K - 1) {
+#pragma unroll
+                for (int e = 0; e < NR; ++e) row[e] = nxt[e];
+            }
+        }
+#pragma unroll
+        for (int dr = 0; dr < P; ++dr) wtc_lds_store4<T, P>(ctx, dst + dr * op, acc[dr]);
     }
 }
 
-// Synthesis and store of this thread's base block: level 1 through the 2x2
-// butterfly, the deeper levels through the closed form with the coordinate
-// bits picking the signs, added to the low-pass input of the butterfly.
+// Synthesis and store, one 2 x BW output block per item (column blocks
+// fastest): base output plus bias (already in the base map), level 1 through
+// the 2x2 butterfly, the deeper levels through the closed form with the
+// coordinate bits picking the signs, added to the low-pass input of the
+// butterfly; one rounding, one store.
 template <typename T, int K, int BW>
 WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
+    constexpr int Q = BW / 2;
     const WtcWholePlan &p = a.p;
-    const int nblk = (p.h / 2) * (p.w / BW);
-    const int it = ctx.tid;
-    if (it >= nblk) return;
-    int d0, d1, d2, d3;
-    wtc_whole_desc<T>(ctx, p.tab_off + 4 * it, d0, d1, d2, d3);
-    const int i1 = d3 & 0xffff, bx = d3 >> 16;
-    const WtcMap z1 = p.z[1];
+    const int nbx = p.w / BW, nblk = (p.h / 2) * nbx;
+    const WtcMap z0 = p.z[0], z1 = p.z[1];
     const int st1 = z1.rows * z1.pitch;
-    float acc[2][BW];
+    for (int it = ctx.tid; it < nblk; it += ctx.nth) {
+        const int by = it / nbx, bx = it - by * nbx;
+        const int i1 = by;
+        float acc[2][BW];
+        wtc_lds_vec<T, BW>(ctx, z0.off + (2 * by) * z0.pitch + BW * bx, acc[0]);
+        wtc_lds_vec<T, BW>(ctx, z0.off + (2 * by + 1) * z0.pitch + BW * bx, acc[1]);
+        float band[4][Q];
+        const int o1 = z1.off + i1 * z1.pitch + Q * bx;
 #pragma unroll
-    for (int dr = 0; dr < 2; ++dr)
+        for (int b = 0; b < 4; ++b) wtc_lds_vec<T, Q>(ctx, o1 + b * st1, band[b]);
+        // deep levels: closed form, signs from the coordinate bits
+        for (int m = 2; m <= p.levels; ++m) {
+            const WtcMap zm = p.z[m];
+            const int sz = zm.rows * zm.pitch;
+            const float sp = ((i1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
+            const int rowo = zm.off + (i1 >> (m - 1)) * zm.pitch;
 #pragma unroll
-        for (int dc = 0; dc < BW; ++dc) acc[dr][dc] = ctx.y0[dr][dc];
-    float deep[BW / 2];
-#pragma unroll
-    for (int q = 0; q < BW / 2; ++q) deep[q] = 0.0f;
-    for (int m = 2; m <= p.levels; ++m) {
-        const WtcMap zm = p.z[m];
-        const int sz = zm.rows * zm.pitch;
-        const float sp = ((i1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
-        const int rowo = zm.off + (i1 >> (m - 1)) * zm.pitch;
-#pragma unroll
-        for (int q = 0; q < BW / 2; ++q) {
-            const int j1 = (BW / 2) * bx + q;
-            const float sq = ((j1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
-            const int oz = rowo + (j1 >> (m - 1));
-            float d = deep[q] + WTC_LDS(ctx, oz);
-            d = wtc_fma(sp, WTC_LDS(ctx, oz + sz), d);
-            d = wtc_fma(sq, WTC_LDS(ctx, oz + 2 * sz), d);
-            deep[q] = wtc_fma(sp * sq, WTC_LDS(ctx, oz + 3 * sz), d);
+            for (int q = 0; q < Q; ++q) {
+                const int j1 = Q * bx + q;
+                const float sq = ((j1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
+                const int oz = rowo + (j1 >> (m - 1));
+                float d = band[0][q] + WTC_LDS(ctx, oz);
+                d = wtc_fma(sp, WTC_LDS(ctx, oz + sz), d);
+                d = wtc_fma(sq, WTC_LDS(ctx, oz + 2 * sz), d);
+                band[0][q] = wtc_fma(sp * sq, WTC_LDS(ctx, oz + 3 * sz), d);
+            }
         }
-    }
 #pragma unroll
-    for (int q = 0; q < BW / 2; ++q) {
-        const int o = d2 + q;
-        const float a0 = WTC_LDS(ctx, o) + deep[q];
-        const float a1 = WTC_LDS(ctx, o + st1), a2 = WTC_LDS(ctx, o + 2 * st1), a3 = WTC_LDS(ctx, o + 3 * st1);
-        const float s01 = a0 + a1, d01 = a0 - a1, s23 = a2 + a3, d23 = a2 - a3;
-        acc[0][2 * q] += s01 + s23;
-        acc[0][2 * q + 1] += s01 - s23;
-        acc[1][2 * q] += d01 + d23;
-        acc[1][2 * q + 1] += d01 - d23;
-    }
+        for (int q = 0; q < Q; ++q) {
+            const float a0 = band[0][q], a1 = band[1][q], a2 = band[2][q], a3 = band[3][q];
+            const float s01 = a0 + a1, d01 = a0 - a1, s23 = a2 + a3, d23 = a2 - a3;
+            acc[0][2 * q] += s01 + s23;
+            acc[0][2 * q + 1] += s01 - s23;
+            acc[1][2 * q] += d01 + d23;
+            acc[1][2 * q + 1] += d01 - d23;
+        }
+        const int64_t o0 = (int64_t)(2 * by) * p.w + BW * bx;
 #ifdef WTC_EMULATE
-    for (int dr = 0; dr < 2; ++dr)
-        for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, d1 + dr * p.w + e) = wtc_from_float<T>(acc[dr][e]);
+        for (int dr = 0; dr < 2; ++dr)
+            for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, o0 + dr * p.w + e) = wtc_from_float<T>(acc[dr][e]);
 #else
-    WtcCtx<T> oc;
-    oc.out = ctx.out;
-    wtc_store_row<T, BW>(oc, d1, acc[0]);
-    wtc_store_row<T, BW>(oc, d1 + p.w, acc[1]);
+        WtcCtx<T> oc;
+        oc.out = ctx.out;
+        wtc_store_row<T, BW>(oc, o0, acc[0]);
+        wtc_store_row<T, BW>(oc, o0 + p.w, acc[1]);
 #endif
+    }
 }
 
 #endif  // WTCONV_WHOLE_BODY_H

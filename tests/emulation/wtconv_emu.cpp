@@ -101,13 +101,11 @@ static void run_whole(const WtcWholeArgs<T> &a)
         for (int img = 0; img < ctx[0].nimg; ++img) {
             for (int t = 0; t < nth; ++t) {
                 wtc_whole_select<T>(a, ctx[t], img);
-                wtc_whole_store_input<T, K, BW>(a, ctx[t]);
+                wtc_whole_stage<T, K, BW>(a, ctx[t]);
             }
-            for (int t = 0; t < nth; ++t) {
+            for (int t = 0; t < nth; ++t)
                 if (img + 1 < ctx[t].nimg) wtc_whole_load<T, K, BW>(a, ctx[t], img + 1);
-                wtc_whole_analysis1<T, K>(a, ctx[t]);
-            }
-            for (int m = 2; m <= p.levels; ++m)
+            for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
             for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW>(a, ctx[t]);
