@@ -21,9 +21,12 @@
 //
 // One workgroup owns one channel and P images.  The correlation work is cut
 // into 4x4 pieces of the dy-side maps ("A" maps: dy itself, then the four
-// bands of every level); thread t owns pieces [Q t, Q t + Q) for the whole
-// life of the workgroup and keeps one k x k (+1) accumulator set per piece, so
-// the cross-thread reduction happens once per workgroup, in a fixed order.
+// bands of every level); thread t owns pieces t, t + nth, t + 2 nth, ... for
+// the whole life of the workgroup and keeps one k x k (+1) accumulator set per
+// piece, so the cross-thread reduction happens once per workgroup, in a fixed
+// order.  Consecutive lanes take horizontally adjacent pieces and every map
+// row starts on a 16-byte boundary, so the 16-byte LDS reads of a wave cover
+// consecutive banks.
 #ifndef WTCONV_WGRAD_BODY_H
 #define WTCONV_WGRAD_BODY_H
 
@@ -60,11 +63,11 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     int32_t off = 0;
     p->x.off = off;
     p->x.rows = wtc_roundup(p->h, P) + 2 * r;
-    p->x.pitch = wtc_roundup(wtc_roundup(p->w, P) + 2 * r, 4) | 1;
+    p->x.pitch = wtc_roundup(wtc_roundup(p->w, P) + 2 * r, 4);
     off += p->x.rows * p->x.pitch;
     p->dy.off = off;
     p->dy.rows = wtc_roundup(p->h, P);
-    p->dy.pitch = wtc_roundup(p->w, P) | 1;
+    p->dy.pitch = wtc_roundup(p->w, P);
     off += p->dy.rows * p->dy.pitch;
     for (int32_t m = 0; m <= WTC_MAXL; ++m) {
         p->u[m].off = p->u[m].pitch = p->u[m].rows = 0;
@@ -74,11 +77,11 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
         p->u[m].off = off;
         p->u[m].rows = wtc_roundup(Hm, P) + 2 * r;
-        p->u[m].pitch = (wtc_roundup(Wm, P) + 2 * r) | 1;
+        p->u[m].pitch = wtc_roundup(wtc_roundup(Wm, P) + 2 * r, 4);
         off += 4 * p->u[m].rows * p->u[m].pitch;
         p->d[m].off = off;
         p->d[m].rows = wtc_roundup(Hm, P);
-        p->d[m].pitch = wtc_roundup(Wm, P) | 1;
+        p->d[m].pitch = wtc_roundup(Wm, P);
         off += 4 * p->d[m].rows * p->d[m].pitch;
     }
     const int32_t maps_end = off;
@@ -226,9 +229,15 @@ WTC_HD WTC_INLINE void wtc_wgrad_store_input(const WtcWgradArgs<T> &a, WtcWgradC
             const int ox = p.x.off + (row + R) * p.x.pitch + col + R;
             const int od = p.dy.off + row * p.dy.pitch + col;
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) {
-                WTC_LDS(ctx, ox + t) = wtc_to_float(ctx.prex[q][t]);
-                WTC_LDS(ctx, od + t) = wtc_to_float(ctx.prey[q][t]);
+            for (int t = 0; t < VEC; ++t) WTC_LDS(ctx, ox + t) = wtc_to_float(ctx.prex[q][t]);
+            if constexpr (VEC % 4 == 0) {
+                float v[VEC];
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) v[t] = wtc_to_float(ctx.prey[q][t]);
+                wtc_lds_store4<T, VEC>(ctx, od, v);
+            } else {
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) WTC_LDS(ctx, od + t) = wtc_to_float(ctx.prey[q][t]);
             }
         }
     }
@@ -331,20 +340,20 @@ WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1,
                                       float (&acc)[K * K + 1])
 {
     constexpr int P = WTC_WG_P;
+    constexpr int NR = (P + K - 1 + 3) / 4 * 4;  // window row, as read (16-byte reads)
     float av[P][P];
 #pragma unroll
-    for (int r = 0; r < P; ++r)
-#pragma unroll
-        for (int c = 0; c < P; ++c) av[r][c] = WTC_LDS(ctx, d1 + r * dp + c);
+    for (int r = 0; r < P; ++r) wtc_lds_row<T, P>(ctx, d1 + r * dp, av[r]);
 #pragma unroll
     for (int r = 0; r < P; ++r)
 #pragma unroll
         for (int c = 0; c < P; ++c) acc[K * K] += av[r][c];
+    float row[NR];
+    wtc_lds_row<T, NR>(ctx, d0, row);
 #pragma unroll
     for (int t = 0; t < P + K - 1; ++t) {
-        float row[P + K - 1];
-#pragma unroll
-        for (int e = 0; e < P + K - 1; ++e) row[e] = WTC_LDS(ctx, d0 + t * xp + e);
+        float nxt[NR];
+        if (t + 1 < P + K - 1) wtc_lds_row<T, NR>(ctx, d0 + (t + 1) * xp, nxt);
 #pragma unroll
         for (int r = 0; r < P; ++r) {
             const int u = t - r;
@@ -353,6 +362,10 @@ WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1,
             for (int v = 0; v < K; ++v)
 #pragma unroll
                 for (int c = 0; c < P; ++c) acc[u * K + v] = wtc_fma(av[r][c], row[c + v], acc[u * K + v]);
+        }
+        if (t + 1 < P + K - 1) {
+#pragma unroll
+            for (int e = 0; e < NR; ++e) row[e] = nxt[e];
         }
     }
 }
@@ -364,10 +377,19 @@ WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx
     const WtcWgradPlan &p = a.p;
 #pragma unroll
     for (int s = 0; s < WTC_WG_QMAX; ++s) {
-        const int it = p.q * ctx.tid + s;
+        const int it = s * ctx.nth + ctx.tid;
         if (s < p.q && it < p.npieces) {
             const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
-            const unsigned t0 = (unsigned)tab[0], t1 = (unsigned)tab[1];
+            unsigned t0, t1;
+#ifdef WTC_EMULATE
+            t0 = (unsigned)tab[0];
+            t1 = (unsigned)tab[1];
+#else
+            typedef unsigned u2 __attribute__((ext_vector_type(2)));
+            const u2 tv = *(const u2 *)tab;
+            t0 = tv.x;
+            t1 = tv.y;
+#endif
             wtc_wgrad_piece<T, K, VEC>(ctx, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
                                       (int)((t1 >> 8) & 0xffu), acc[s]);
         }
@@ -394,9 +416,9 @@ WTC_HD WTC_INLINE void wtc_wgrad_gather(const WtcWgradArgs<T> &a, WtcWgradCtx<T,
     const WtcWgradPlan &p = a.p;
     for (int idx = ctx.tid; idx < p.nmaps * n1; idx += ctx.nth) {
         const int g = idx / n1, e = idx - g * n1;
-        // threads whose piece q t + s lies in [first[g], first[g+1])
-        const int lo = wtc_max(0, (p.first[g] - s + p.q - 1) / p.q);
-        const int hi = wtc_min(p.nthreads, (p.first[g + 1] - s + p.q - 1) / p.q);
+        // threads whose piece s nth + t lies in [first[g], first[g+1])
+        const int lo = wtc_max(0, p.first[g] - s * ctx.nth);
+        const int hi = wtc_min(ctx.nth, p.first[g + 1] - s * ctx.nth);
         float sum = WTC_LDS(ctx, p.res_off + idx);
         for (int t = lo; t < hi; ++t) sum += WTC_LDS(ctx, p.red_off + t * n1 + e);
         WTC_LDS(ctx, p.res_off + idx) = sum;

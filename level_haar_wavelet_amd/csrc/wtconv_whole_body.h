@@ -411,8 +411,8 @@ WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
 }
 
 // N consecutive LDS floats starting at a multiple of 4 (16-byte reads).
-template <typename T, int N>
-WTC_HD WTC_INLINE void wtc_lds_row(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N])
+template <typename T, int N, typename Ctx>
+WTC_HD WTC_INLINE void wtc_lds_row(Ctx &ctx, int idx, float (&dst)[N])
 {
 #ifdef WTC_EMULATE
     for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
@@ -431,8 +431,8 @@ WTC_HD WTC_INLINE void wtc_lds_row(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N]
 }
 
 // N consecutive LDS floats starting at an index aligned to min(N, 4).
-template <typename T, int N>
-WTC_HD WTC_INLINE void wtc_lds_vec(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N])
+template <typename T, int N, typename Ctx>
+WTC_HD WTC_INLINE void wtc_lds_vec(Ctx &ctx, int idx, float (&dst)[N])
 {
 #ifdef WTC_EMULATE
     for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
@@ -451,8 +451,8 @@ WTC_HD WTC_INLINE void wtc_lds_vec(WtcWholeCtx<T> &ctx, int idx, float (&dst)[N]
 #endif
 }
 
-template <typename T, int N>
-WTC_HD WTC_INLINE void wtc_lds_store4(WtcWholeCtx<T> &ctx, int idx, const float (&src)[N])
+template <typename T, int N, typename Ctx>
+WTC_HD WTC_INLINE void wtc_lds_store4(Ctx &ctx, int idx, const float (&src)[N])
 {
 #ifdef WTC_EMULATE
     for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
