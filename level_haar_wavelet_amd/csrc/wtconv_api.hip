@@ -5,6 +5,7 @@
 
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/wtconv.h"
 #include "wtconv_launch.h"
@@ -34,15 +35,21 @@ int lds_budget_floats() { return env_int("WTCONV_LDS_KB", 64, 16, 160) * 1024 / 
 // LDS budget of the whole-plane kernel: two workgroups per compute unit.
 int whole_budget_floats() { return env_int("WTCONV_WHOLE_LDS_KB", 80, 8, 160) * 1024 / 4; }
 
-// Images per workgroup of the whole-plane kernel: as many as keep at least
-// four workgroups per compute unit (WTCONV_PLANES overrides).
-int whole_planes(const wtconv_desc_t *d)
+// Set-up and reduction cost of one workgroup, in units of one image's work
+// (measured on the 56 x 56 and 28 x 28 planes of the stage workloads).
+constexpr double kWholeFixed = 1.0;
+constexpr double kWgradFixed = 1.0;
+
+// Images per workgroup: WTCONV_PLANES overrides; otherwise as many as keep
+// the rounds of resident workgroups few (wtc_choose_planes), with the
+// resident count from HIP's occupancy query (two per compute unit of 256 when
+// that fails).
+int pick_planes(const wtconv_desc_t *d, int resident, double fixed, const char *env)
 {
-    int forced = env_int("WTCONV_PLANES", 0, 1, 64);
+    int forced = env_int(env, 0, 1, 1 << 20);
     if (forced) return forced;
-    for (int p = 8; p > 1; p /= 2)
-        if (d->c * ((d->n + p - 1) / p) >= 1024) return p;
-    return 1;
+    if (resident < 1) resident = 2 * 256;
+    return wtc_choose_planes(d->n, d->c, resident, fixed);
 }
 
 wtconv_status_t check_desc(const wtconv_desc_t *d)
@@ -98,10 +105,13 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
                               (int)d->w, rotate, s);
     } else {
         WtcWholePlan wp;
+        const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
         if (!env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
             wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                                kFusedThreads, whole_planes(d), d->dtype == WTCONV_F32 ? 4 : 2,
-                                whole_budget_floats()) == 0) {
+                                kFusedThreads, 1, eb, whole_budget_floats()) == 0) {
+            const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp), kWholeFixed, "WTCONV_PLANES");
+            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                kFusedThreads, planes, eb, whole_budget_floats());
             e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
             return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
         }
@@ -141,20 +151,15 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
 {
     const int kk = d->k * d->k;
     ch->plen = kk + 1 + 4 * d->levels * kk;
-    int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 64);
-    if (!planes) {
-        planes = 1;
-        for (int p = 8; p > 1; p /= 2)
-            if (d->c * ((d->n + p - 1) / p) >= 1024) {
-                planes = p;
-                break;
-            }
-    }
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
     ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
                 wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels,
-                                    kFusedThreads, planes, d->dtype == WTCONV_F32 ? 4 : 2,
-                                    whole_budget_floats()) == 0;
+                                    kFusedThreads, 1, eb, whole_budget_floats()) == 0;
     if (ch->whole) {
+        const int planes = pick_planes(d, wtc_wgrad_resident(d->dtype, ch->wp), kWgradFixed,
+                                       "WTCONV_WGRAD_PLANES");
+        wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, kFusedThreads,
+                            planes, eb, whole_budget_floats());
         ch->groups = ch->wp.groups;
     } else {
         ch->groups = (int)wgrad_groups(d);
@@ -171,6 +176,40 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
 }
 
 }  // namespace
+
+int wtc_resident_blocks(const void *fn, int nthreads, size_t lds)
+{
+    struct Entry {
+        const void *fn;
+        int dev, nthreads;
+        size_t lds;
+        int resident;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].fn == fn && cache[i].dev == dev && cache[i].nthreads == nthreads && cache[i].lds == lds)
+                return cache[i].resident;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, nthreads, lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();  // leave no error for the next launch check to report
+        return 0;
+    }
+    const int resident = per_cu * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 64) cache[used++] = Entry{fn, dev, nthreads, lds, resident};
+    return resident;
+}
 
 extern "C" {
 

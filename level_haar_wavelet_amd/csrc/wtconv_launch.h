@@ -34,4 +34,13 @@ hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int p
 hipError_t wtc_launch_wgrad_tile(int in_dtype, const WtcWtilePlan &p, const void *x, const void *dy, float *ux,
                                  float *ud, float *partial, hipStream_t stream);
 
+// Workgroups of a kernel (nthreads threads, lds bytes of dynamic LDS) that
+// the current device holds at once: resident per compute unit x compute
+// units; 0 when HIP cannot tell.  Cached per device and configuration.
+int wtc_resident_blocks(const void *fn, int nthreads, size_t lds);
+
+// Resident workgroups of the whole-plane and weight-gradient kernels for a plan.
+int wtc_whole_resident(int dtype, const WtcWholePlan &p);
+int wtc_wgrad_resident(int dtype, const WtcWgradPlan &p);
+
 #endif  // WTCONV_LAUNCH_H

@@ -190,4 +190,27 @@ static inline int wtc_make_fused_plan(WtcFusedPlan *p, int32_t n, int32_t c, int
     }
 }
 
+// Images per workgroup for a grid of C x ceil(N / planes) workgroups of
+// which `slots` run at once: the planes that minimise rounds x (planes +
+// fixed), where fixed is a workgroup's set-up and reduction cost in units of
+// one image's work and rounds = ceil(workgroups / slots).  Ties go to fewer
+// images per workgroup.
+static inline int wtc_choose_planes(int64_t n, int64_t c, int64_t slots, double fixed)
+{
+    if (slots < 1) slots = 1;
+    int best = 1;
+    double best_cost = 0.0;
+    for (int64_t p = 1; p <= n; ++p) {
+        const int64_t groups = (n + p - 1) / p;
+        if (p > 1 && (n + p - 2) / (p - 1) == groups) continue;  // same grid as p - 1
+        const int64_t rounds = (c * groups + slots - 1) / slots;
+        const double cost = (double)rounds * ((double)p + fixed);
+        if (p == 1 || cost < best_cost) {
+            best = (int)p;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 #endif  // WTCONV_PLAN_H

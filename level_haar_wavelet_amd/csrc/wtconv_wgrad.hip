@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
 #pragma unroll
         for (int e = 0; e < K * K + 1; ++e) acc[s][e] = 0.0f;
     for (int img = 0; img < ctx.nimg; ++img) {
-        wtc_wgrad_store_input<T, K, VEC>(a, ctx);
+        wtc_wgrad_stage<T, K, VEC>(a, ctx);
         wtc_lds_barrier_wg();
         if (img + 1 < ctx.nimg) wtc_wgrad_load<T, VEC>(a, ctx, img + 1);
-        for (int m = 1; m <= a.p.levels; ++m) {
+        for (int m = a.p.first_deep; m <= a.p.levels; ++m) {
             wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
             wtc_lds_barrier_wg();
         }
@@ -44,7 +44,9 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
         if (s < a.p.q) {
             wtc_wgrad_park<T, K, VEC>(a, ctx, acc[s]);
             wtc_lds_barrier_wg();
-            wtc_wgrad_gather<T, K, VEC>(a, ctx, s);
+            wtc_wgrad_chunks<T, K, VEC>(a, ctx, s);
+            wtc_lds_barrier_wg();
+            wtc_wgrad_combine<T, K, VEC>(a, ctx, s);
             wtc_lds_barrier_wg();
         }
     }
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k
 }
 
 template <typename T, int K, int VEC>
-static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream)
+static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC>;
@@ -87,33 +89,55 @@ static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream)
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
+    if (resident) {
+        *resident = wtc_resident_blocks(fn, a.p.nthreads, lds);
+        return hipSuccess;
+    }
     const unsigned blocks = (unsigned)(a.p.groups * a.p.c);
     hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int K>
-static hipError_t launch_wgrad_k(const WtcWgradArgs<T> &a, hipStream_t stream)
+static hipError_t launch_wgrad_k(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
     constexpr int VMAX = 16 / sizeof(T);
     switch (a.p.vec) {
-    case VMAX: return launch_wgrad<T, K, VMAX>(a, stream);
-    case VMAX / 2: return launch_wgrad<T, K, VMAX / 2>(a, stream);
-    case VMAX / 4: return launch_wgrad<T, K, VMAX / 4>(a, stream);
-    default: return launch_wgrad<T, K, 1>(a, stream);
+    case VMAX: return launch_wgrad<T, K, VMAX>(a, stream, resident);
+    case VMAX / 2: return launch_wgrad<T, K, VMAX / 2>(a, stream, resident);
+    case VMAX / 4: return launch_wgrad<T, K, VMAX / 4>(a, stream, resident);
+    default: return launch_wgrad<T, K, 1>(a, stream, resident);
     }
 }
 
 template <typename T>
-static hipError_t launch_wgrad_t(const WtcWgradArgs<T> &a, hipStream_t stream)
+static hipError_t launch_wgrad_t(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident = nullptr)
 {
     switch (a.p.k) {
-    case 1: return launch_wgrad_k<T, 1>(a, stream);
-    case 3: return launch_wgrad_k<T, 3>(a, stream);
-    case 5: return launch_wgrad_k<T, 5>(a, stream);
-    case 7: return launch_wgrad_k<T, 7>(a, stream);
+    case 1: return launch_wgrad_k<T, 1>(a, stream, resident);
+    case 3: return launch_wgrad_k<T, 3>(a, stream, resident);
+    case 5: return launch_wgrad_k<T, 5>(a, stream, resident);
+    case 7: return launch_wgrad_k<T, 7>(a, stream, resident);
     default: return hipErrorInvalidValue;
     }
+}
+
+int wtc_wgrad_resident(int dtype, const WtcWgradPlan &p)
+{
+    int r = 0;
+    hipError_t e;
+    if (dtype == 0) {
+        WtcWgradArgs<float> a{nullptr, nullptr, nullptr, p};
+        e = launch_wgrad_t<float>(a, nullptr, &r);
+    } else {
+        WtcWgradArgs<_Float16> a{nullptr, nullptr, nullptr, p};
+        e = launch_wgrad_t<_Float16>(a, nullptr, &r);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return r;
 }
 
 hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,

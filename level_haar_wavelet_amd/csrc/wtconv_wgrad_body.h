@@ -34,7 +34,10 @@
 
 #define WTC_WG_QMAX 3  // pieces per thread
 #define WTC_WG_P 4     // piece side
-#define WTC_WG_NCH 4   // input chunks per thread and image (each of x and dy)
+#define WTC_WG_CH 16   // threads summed by one job of the reduction's first stage
+#define WTC_WG_MAXT 256  // threads per workgroup, at most
+#define WTC_WG_NMAPS (1 + 4 * WTC_MAXL)
+#define WTC_WG_CHMAX (WTC_WG_MAXT / WTC_WG_CH + WTC_WG_NMAPS)  // first-stage jobs of a set, at most
 
 struct WtcWgradPlan {
     int32_t n, c, h, w, k, levels;
@@ -45,7 +48,10 @@ struct WtcWgradPlan {
     int32_t npieces;
     int32_t nmaps;      // 1 + 4L
     int32_t plen;       // floats of one partial result: k*k + 1 + 4L k*k
-    int32_t vec;        // activation elements per global chunk
+    int32_t vec;        // activation elements per staged row segment (at most 16 bytes)
+    int32_t gr;         // rows per staging group (4, 2 or 1)
+    int32_t sgroups;    // staging groups of a plane, (h / gr) (w / vec) <= nthreads
+    int32_t first_deep; // first level computed from LDS (the staging computes the ones before)
     WtcMap x;           // x with an r-wide zero border (origin (r, r))
     WtcMap dy;          // dy (origin (0, 0)), zero beyond the image
     WtcMap u[WTC_MAXL + 1];  // B_m(x): 4 bands with an r border
@@ -53,13 +59,26 @@ struct WtcWgradPlan {
     int32_t first[1 + 4 * WTC_MAXL + 1];  // first piece of every map, then the total
     int32_t tab_off;    // piece descriptors, 2 ints each
     int32_t res_off;    // per-map results, nmaps x (k*k + 1)
-    int32_t red_off;    // reduction scratch, nthreads x (k*k + 1), aliases the maps
+    int32_t red_off;    // parked accumulators, nthreads x n1p (aliases the maps)
+    int32_t csum_off;   // first-stage sums of the reduction (aliases the maps)
+    int32_t ctab_off;   // reduction tables in LDS: per set, chunk[] then mapc[]
     int32_t lds_floats;
+    // Reduction tables (host-built): per set s, the threads of first-stage job
+    // c (t0 | t1 << 16) and, per map, its first job and job count (c0 | n << 16).
+    int32_t nchunks[WTC_WG_QMAX];
+    int32_t chunk[WTC_WG_QMAX][WTC_WG_CHMAX];
+    int32_t mapc[WTC_WG_QMAX][WTC_WG_NMAPS];
 };
+
+// stride of one thread's parked accumulators: k*k + 1 rounded up to odd
+WTC_PLAN_HD static inline int32_t wtc_wgrad_n1p(int32_t k) { return (k * k + 1) | 1; }
 
 static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
 {
     const int32_t L = p->levels, r = p->k / 2, kk = p->k * p->k, P = WTC_WG_P;
+    // Every row starts on a 16-byte boundary.  A piece's x-side window row is
+    // read as roundup(P + k - 1, 4) floats from column 4 pc, which stays inside
+    // the row: the pitch is roundup(roundup(W, 4) + 2r, 4).
     int32_t off = 0;
     p->x.off = off;
     p->x.rows = wtc_roundup(p->h, P) + 2 * r;
@@ -84,7 +103,6 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
         p->d[m].pitch = wtc_roundup(Wm, P);
         off += 4 * p->d[m].rows * p->d[m].pitch;
     }
-    const int32_t maps_end = off;
     // pieces: map 0 is the base (full resolution), map 1 + 4(m-1) + b is band b of level m
     p->nmaps = 1 + 4 * L;
     int32_t np = 0;
@@ -100,14 +118,38 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     off = wtc_roundup(off, 4);
     p->tab_off = off;
     off += 2 * np;
-    // the reduction runs after the last image: its scratch reuses the maps and
-    // the table; the per-map results come after both
+    // the reduction runs after the last image: its buffers reuse the maps and
+    // the table; the per-map results come after both.  A set of pieces splits
+    // into at most nthreads / CH + nmaps first-stage jobs per tap.
     p->red_off = 0;
-    off = wtc_max(off, p->nthreads * (kk + 1));
+    p->csum_off = p->nthreads * wtc_wgrad_n1p(p->k);
+    const int32_t red_end = p->csum_off + (p->nthreads / WTC_WG_CH + p->nmaps) * (kk + 1);
+    off = wtc_max(off, red_end);
     p->res_off = wtc_roundup(off, 4);
     off = p->res_off + p->nmaps * (kk + 1);
-    (void)maps_end;
+    p->ctab_off = off;
+    off += WTC_WG_QMAX * (WTC_WG_CHMAX + WTC_WG_NMAPS);
     p->lds_floats = wtc_roundup(off, 4);
+    // reduction tables: set s holds pieces s nth .. s nth + nth - 1
+    for (int32_t s = 0; s < WTC_WG_QMAX; ++s) {
+        int32_t nc = 0;
+        for (int32_t g = 0; g < WTC_WG_NMAPS; ++g) {
+            int32_t lo = 0, hi = 0;
+            if (g < p->nmaps) {
+                lo = wtc_max(0, p->first[g] - s * p->nthreads);
+                hi = wtc_min(p->nthreads, p->first[g + 1] - s * p->nthreads);
+            }
+            const int32_t cnt = hi > lo ? (hi - lo + WTC_WG_CH - 1) / WTC_WG_CH : 0;
+            p->mapc[s][g] = nc | (cnt << 16);
+            for (int32_t j = 0; j < cnt; ++j) {
+                const int32_t t0 = lo + j * WTC_WG_CH, t1 = wtc_min(hi, t0 + WTC_WG_CH);
+                p->chunk[s][nc + j] = t0 | (t1 << 16);
+            }
+            nc += cnt;
+        }
+        for (int32_t j = nc; j < WTC_WG_CHMAX; ++j) p->chunk[s][j] = 0;
+        p->nchunks[s] = nc;
+    }
     return p->lds_floats;
 }
 
@@ -126,11 +168,15 @@ static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int
     p->groups = (n + p->planes - 1) / p->planes;
     if (levels < 0 || levels > WTC_MAXL) return -1;
     if (h % (1 << levels) || w % (1 << levels)) return -1;
+    if (nthreads % WTC_WG_CH || nthreads > WTC_WG_MAXT) return -1;
     int32_t vec = 16 / elem_bytes;
     while (vec > 1 && w % vec) vec /= 2;
     p->vec = vec;
-    const int64_t chunks = (int64_t)h * (w / vec);
-    if (chunks > (int64_t)WTC_WG_NCH * nthreads) return -1;
+    p->gr = h % 4 == 0 ? 4 : (h % 2 == 0 ? 2 : 1);
+    if (levels >= 1 && (p->gr < 2 || vec < 2)) return -1;
+    p->sgroups = (h / p->gr) * (w / vec);
+    if (p->sgroups > nthreads) return -1;
+    p->first_deep = (levels >= 2 && p->gr == 4 && vec >= 4) ? 3 : 2;
     wtc_wgrad_layout(p);
     if (p->q > WTC_WG_QMAX) return -1;
     // descriptor fields: pitches below 256, LDS indexes below 65536
@@ -151,12 +197,60 @@ struct WtcWgradCtx {
     float *lds;
     int tid, nth;
     int c, n0, nimg, group;
-    T prex[WTC_WG_NCH][VEC];
-    T prey[WTC_WG_NCH][VEC];
+    int grow, gcol;  // this thread's staging group
+    bool gvalid;
+    T prex[4][VEC];
+    T prey[4][VEC];
 #ifdef WTC_EMULATE
     int64_t lds_n;
 #endif
 };
+
+// N floats to LDS at an index that is a multiple of A (16-, 8- or 4-byte stores).
+template <int N, int A, typename Ctx>
+WTC_HD WTC_INLINE void wtc_lds_put(Ctx &ctx, int idx, const float (&src)[N])
+{
+#ifdef WTC_EMULATE
+    if (idx % A) {
+        fprintf(stderr, "wtconv emulation: LDS index %d not a multiple of %d\n", idx, A);
+        abort();
+    }
+    for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
+#else
+    if constexpr (A >= 4 && N % 4 == 0) {
+        typedef float v4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            v4 v;
+            v.x = src[4 * q];
+            v.y = src[4 * q + 1];
+            v.z = src[4 * q + 2];
+            v.w = src[4 * q + 3];
+            *(v4 *)&ctx.lds[idx + 4 * q] = v;
+        }
+    } else if constexpr (A >= 2 && N % 2 == 0) {
+        typedef float v2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int q = 0; q < N / 2; ++q) {
+            v2 v;
+            v.x = src[2 * q];
+            v.y = src[2 * q + 1];
+            *(v2 *)&ctx.lds[idx + 2 * q] = v;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) ctx.lds[idx + e] = src[e];
+    }
+#endif
+}
+
+// largest of 4, 2, 1 dividing both a and b (a, b powers of two or 0 for "any")
+WTC_HD constexpr int wtc_align_of(int a, int b)
+{
+    const int la = a == 0 ? 4 : (a % 4 == 0 ? 4 : (a % 2 == 0 ? 2 : 1));
+    const int lb = b == 0 ? 4 : (b % 4 == 0 ? 4 : (b % 2 == 0 ? 2 : 1));
+    return la < lb ? la : lb;
+}
 
 template <typename T, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_setup(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int bid)
@@ -166,85 +260,149 @@ WTC_HD WTC_INLINE void wtc_wgrad_setup(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
     ctx.group = bid / p.c;
     ctx.n0 = ctx.group * p.planes;
     ctx.nimg = wtc_min(p.planes, p.n - ctx.n0);
+    const int g = wtc_min(ctx.tid, p.sgroups - 1), cpr = p.w / VEC;
+    ctx.grow = g / cpr;
+    ctx.gcol = g - ctx.grow * cpr;
+    ctx.gvalid = ctx.tid < p.sgroups;
 }
 
 template <typename T, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_zero(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
 {
-    for (int i = ctx.tid; i < a.p.lds_floats; i += ctx.nth) WTC_LDS(ctx, i) = 0.0f;
+    const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 4 * ctx.tid; i < a.p.lds_floats; i += 4 * ctx.nth) wtc_lds_put<4, 4>(ctx, i, z);
 }
 
-// Loads of one image of x and dy into registers (every lane loads a valid chunk).
+// Loads of this thread's staging group (gr rows of VEC elements) of image
+// `img`, x and dy, into registers; every lane loads a valid group.
 template <typename T, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int img)
 {
     const WtcWgradPlan &p = a.p;
     const int64_t plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
-    const int cpr = p.w / VEC, total = p.h * cpr;
+    const int64_t e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
 #pragma unroll
-    for (int q = 0; q < WTC_WG_NCH; ++q) {
-        const int idx = wtc_min(ctx.tid + q * ctx.nth, total - 1);
-        const int64_t e = plane + (int64_t)idx * VEC;
+    for (int q = 0; q < 4; ++q) {
+        if (q < p.gr) {
+            const int64_t e = e0 + (int64_t)q * p.w;
 #ifdef WTC_EMULATE
-        const int64_t all = (int64_t)p.n * p.c * p.h * p.w;
-        for (int t = 0; t < VEC; ++t) {
-            ctx.prex[q][t] = wtc_chk(a.x, e + t, all, __LINE__);
-            ctx.prey[q][t] = wtc_chk(a.dy, e + t, all, __LINE__);
-        }
-#else
-        if constexpr (VEC * sizeof(T) == 16) {
-            typedef float v4 __attribute__((ext_vector_type(4)));
-            v4 d0 = __builtin_nontemporal_load((const v4 *)(a.x + e));
-            v4 d1 = __builtin_nontemporal_load((const v4 *)(a.dy + e));
-            __builtin_memcpy(&ctx.prex[q][0], &d0, 16);
-            __builtin_memcpy(&ctx.prey[q][0], &d1, 16);
-        } else if constexpr (VEC * sizeof(T) == 8) {
-            typedef float v2 __attribute__((ext_vector_type(2)));
-            v2 d0 = __builtin_nontemporal_load((const v2 *)(a.x + e));
-            v2 d1 = __builtin_nontemporal_load((const v2 *)(a.dy + e));
-            __builtin_memcpy(&ctx.prex[q][0], &d0, 8);
-            __builtin_memcpy(&ctx.prey[q][0], &d1, 8);
-        } else {
-#pragma unroll
+            const int64_t all = (int64_t)p.n * p.c * p.h * p.w;
             for (int t = 0; t < VEC; ++t) {
-                ctx.prex[q][t] = a.x[e + t];
-                ctx.prey[q][t] = a.dy[e + t];
+                ctx.prex[q][t] = wtc_chk(a.x, e + t, all, __LINE__);
+                ctx.prey[q][t] = wtc_chk(a.dy, e + t, all, __LINE__);
             }
-        }
+#else
+            if constexpr (VEC * sizeof(T) == 16) {
+                typedef float v4 __attribute__((ext_vector_type(4)));
+                v4 d0 = __builtin_nontemporal_load((const v4 *)(a.x + e));
+                v4 d1 = __builtin_nontemporal_load((const v4 *)(a.dy + e));
+                __builtin_memcpy(&ctx.prex[q][0], &d0, 16);
+                __builtin_memcpy(&ctx.prey[q][0], &d1, 16);
+            } else if constexpr (VEC * sizeof(T) == 8) {
+                typedef float v2 __attribute__((ext_vector_type(2)));
+                v2 d0 = __builtin_nontemporal_load((const v2 *)(a.x + e));
+                v2 d1 = __builtin_nontemporal_load((const v2 *)(a.dy + e));
+                __builtin_memcpy(&ctx.prex[q][0], &d0, 8);
+                __builtin_memcpy(&ctx.prey[q][0], &d1, 8);
+            } else {
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) {
+                    ctx.prex[q][t] = a.x[e + t];
+                    ctx.prey[q][t] = a.dy[e + t];
+                }
+            }
 #endif
+        }
     }
 }
 
+// One 2x2 Haar step on four pairs of rows held in registers: out[b][j] for
+// band b (LL, top-bottom, left-right, diagonal) at column j of the half rows.
+template <int N>
+WTC_HD WTC_INLINE void wtc_haar_rows(const float (&top)[2 * N], const float (&bot)[2 * N], float (&out)[4][N])
+{
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const float x00 = top[2 * j], x01 = top[2 * j + 1], x10 = bot[2 * j], x11 = bot[2 * j + 1];
+        const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+        out[0][j] = sa + sc;
+        out[1][j] = sa - sc;
+        out[2][j] = da + dc;
+        out[3][j] = da - dc;
+    }
+}
+
+// Write the prefetched groups of x (bordered map) and dy, and compute Haar
+// level 1 (and level 2 when the group has 4 rows and at least 4 columns) of
+// both straight from registers.
 template <typename T, int K, int VEC>
-WTC_HD WTC_INLINE void wtc_wgrad_store_input(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
+WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
 {
     constexpr int R = K / 2;
     const WtcWgradPlan &p = a.p;
-    const int cpr = p.w / VEC, total = p.h * cpr;
+    if (!ctx.gvalid) return;
+    float xv[4][VEC], dv[4][VEC];
 #pragma unroll
-    for (int q = 0; q < WTC_WG_NCH; ++q) {
-        const int idx = ctx.tid + q * ctx.nth;
-        if (idx < total) {
-            const int row = idx / cpr, col = (idx - row * cpr) * VEC;
-            const int ox = p.x.off + (row + R) * p.x.pitch + col + R;
-            const int od = p.dy.off + row * p.dy.pitch + col;
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int t = 0; t < VEC; ++t) WTC_LDS(ctx, ox + t) = wtc_to_float(ctx.prex[q][t]);
-            if constexpr (VEC % 4 == 0) {
-                float v[VEC];
+        for (int t = 0; t < VEC; ++t) {
+            xv[q][t] = q < p.gr ? wtc_to_float(ctx.prex[q][t]) : 0.0f;
+            dv[q][t] = q < p.gr ? wtc_to_float(ctx.prey[q][t]) : 0.0f;
+        }
+    const int r0 = p.gr * ctx.grow, c0 = VEC * ctx.gcol;
 #pragma unroll
-                for (int t = 0; t < VEC; ++t) v[t] = wtc_to_float(ctx.prey[q][t]);
-                wtc_lds_store4<T, VEC>(ctx, od, v);
-            } else {
+    for (int q = 0; q < 4; ++q) {
+        if (q < p.gr) {
+            wtc_lds_put<VEC, wtc_align_of(VEC, R)>(ctx, p.x.off + (r0 + q + R) * p.x.pitch + c0 + R, xv[q]);
+            wtc_lds_put<VEC, wtc_align_of(VEC, 0)>(ctx, p.dy.off + (r0 + q) * p.dy.pitch + c0, dv[q]);
+        }
+    }
+    if constexpr (VEC >= 2) {
+        if (p.levels < 1) return;
+        constexpr int H1 = VEC / 2;
+        const WtcMap u1 = p.u[1], d1 = p.d[1];
+        const int su = u1.rows * u1.pitch, sd = d1.rows * d1.pitch;
+        float llx[2][H1], lld[2][H1];
 #pragma unroll
-                for (int t = 0; t < VEC; ++t) WTC_LDS(ctx, od + t) = wtc_to_float(ctx.prey[q][t]);
+        for (int aa = 0; aa < 2; ++aa) {
+            if (2 * aa < p.gr) {
+                const int i = r0 / 2 + aa;
+                float bx[4][H1], bd[4][H1];
+                wtc_haar_rows<H1>(xv[2 * aa], xv[2 * aa + 1], bx);
+                wtc_haar_rows<H1>(dv[2 * aa], dv[2 * aa + 1], bd);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    wtc_lds_put<H1, wtc_align_of(H1, R)>(ctx, u1.off + b * su + (i + R) * u1.pitch + c0 / 2 + R,
+                                                         bx[b]);
+                    wtc_lds_put<H1, wtc_align_of(H1, 0)>(ctx, d1.off + b * sd + i * d1.pitch + c0 / 2, bd[b]);
+                }
+#pragma unroll
+                for (int j = 0; j < H1; ++j) {
+                    llx[aa][j] = bx[0][j];
+                    lld[aa][j] = bd[0][j];
+                }
+            }
+        }
+        if constexpr (VEC >= 4) {
+            if (p.first_deep != 3) return;
+            constexpr int H2 = VEC / 4;
+            const WtcMap u2 = p.u[2], d2 = p.d[2];
+            const int su2 = u2.rows * u2.pitch, sd2 = d2.rows * d2.pitch;
+            float bx[4][H2], bd[4][H2];
+            wtc_haar_rows<H2>(llx[0], llx[1], bx);
+            wtc_haar_rows<H2>(lld[0], lld[1], bd);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                wtc_lds_put<H2, wtc_align_of(H2, R)>(ctx, u2.off + b * su2 + (ctx.grow + R) * u2.pitch + c0 / 4 + R,
+                                                     bx[b]);
+                wtc_lds_put<H2, wtc_align_of(H2, 0)>(ctx, d2.off + b * sd2 + ctx.grow * d2.pitch + c0 / 4, bd[b]);
             }
         }
     }
 }
 
-// Haar level m of both pyramids: x side from x (m = 1) or U_{m-1}(x) into the
-// bordered maps, dy side into the interior maps.
+// Haar level m (m >= first_deep) of both pyramids from level m - 1 in LDS:
+// x side into the bordered maps, dy side into the interior maps.
 template <typename T, int K, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_analysis(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int m)
 {
@@ -252,27 +410,18 @@ WTC_HD WTC_INLINE void wtc_wgrad_analysis(const WtcWgradArgs<T> &a, WtcWgradCtx<
     const WtcWgradPlan &p = a.p;
     const int Hm = p.h >> m, Wm = p.w >> m;
     const WtcMap ux = p.u[m], ud = p.d[m];
-    int sx, sxp, sd, sdp;  // source origins (index of element (0, 0)) and pitches
-    if (m == 1) {
-        sx = p.x.off + R * p.x.pitch + R;
-        sxp = p.x.pitch;
-        sd = p.dy.off;
-        sdp = p.dy.pitch;
-    } else {
-        sx = p.u[m - 1].off + R * p.u[m - 1].pitch + R;
-        sxp = p.u[m - 1].pitch;
-        sd = p.d[m - 1].off;
-        sdp = p.d[m - 1].pitch;
-    }
+    const int sx = p.u[m - 1].off + R * p.u[m - 1].pitch + R, sxp = p.u[m - 1].pitch;
+    const int sd = p.d[m - 1].off, sdp = p.d[m - 1].pitch;
     const int stx = ux.rows * ux.pitch, std_ = ud.rows * ud.pitch;
     const int total = Hm * Wm;
-    int i = ctx.tid / Wm, j = ctx.tid - (ctx.tid / Wm) * Wm;
-    const int di = ctx.nth / Wm, dj = ctx.nth - di * Wm;
     for (int idx = ctx.tid; idx < total; idx += ctx.nth) {
+        const int i = idx / Wm, j = idx - i * Wm;
+        const int s0 = sx + (2 * i) * sxp + 2 * j, s1 = sd + (2 * i) * sdp + 2 * j;
+        const float x00 = WTC_LDS(ctx, s0), x01 = WTC_LDS(ctx, s0 + 1);
+        const float x10 = WTC_LDS(ctx, s0 + sxp), x11 = WTC_LDS(ctx, s0 + sxp + 1);
+        const float y00 = WTC_LDS(ctx, s1), y01 = WTC_LDS(ctx, s1 + 1);
+        const float y10 = WTC_LDS(ctx, s1 + sdp), y11 = WTC_LDS(ctx, s1 + sdp + 1);
         {
-            const int s = sx + (2 * i) * sxp + 2 * j;
-            const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
-            const float x10 = WTC_LDS(ctx, s + sxp), x11 = WTC_LDS(ctx, s + sxp + 1);
             const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
             const int o = ux.off + (i + R) * ux.pitch + j + R;
             WTC_LDS(ctx, o) = sa + sc;
@@ -281,21 +430,12 @@ WTC_HD WTC_INLINE void wtc_wgrad_analysis(const WtcWgradArgs<T> &a, WtcWgradCtx<
             WTC_LDS(ctx, o + 3 * stx) = da - dc;
         }
         {
-            const int s = sd + (2 * i) * sdp + 2 * j;
-            const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
-            const float x10 = WTC_LDS(ctx, s + sdp), x11 = WTC_LDS(ctx, s + sdp + 1);
-            const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
+            const float sa = y00 + y01, sc = y10 + y11, da = y00 - y01, dc = y10 - y11;
             const int o = ud.off + i * ud.pitch + j;
             WTC_LDS(ctx, o) = sa + sc;
             WTC_LDS(ctx, o + std_) = sa - sc;
             WTC_LDS(ctx, o + 2 * std_) = da + dc;
             WTC_LDS(ctx, o + 3 * std_) = da - dc;
-        }
-        i += di;
-        j += dj;
-        if (j >= Wm) {
-            j -= Wm;
-            ++i;
         }
     }
 }
@@ -330,6 +470,12 @@ WTC_HD WTC_INLINE void wtc_wgrad_table(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
         int *tab = (int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
         tab[0] = (int)((unsigned)d0 | ((unsigned)d1 << 16));
         tab[1] = (d2 & 0xff) | (((d2 >> 16) & 0xff) << 8) | (g << 16);
+    }
+    constexpr int per = WTC_WG_CHMAX + WTC_WG_NMAPS;
+    for (int i = ctx.tid; i < WTC_WG_QMAX * per; i += ctx.nth) {
+        const int s = i / per, j = i - s * per;
+        const int v = j < WTC_WG_CHMAX ? p.chunk[s][j] : p.mapc[s][j - WTC_WG_CHMAX];
+        *(int *)&WTC_LDS(ctx, p.ctab_off + i) = v;
     }
 }
 
@@ -396,31 +542,54 @@ WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx
     }
 }
 
-// After the last image: per set s, every thread parks its accumulators in
-// LDS, then one thread per (map, tap) sums the threads that own pieces of
-// that map, in thread order, into the per-map result.
+// After the last image, per set s of pieces (piece s nth + t on thread t):
+// every thread parks its accumulators in LDS (park); first-stage jobs sum the
+// parked values of up to CH consecutive threads of one map, in thread order
+// (chunks); then every (map, tap) adds its chunk sums, in chunk order, to the
+// per-map result (combine).  The order of every addition is fixed.
 template <typename T, int K, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_park(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx,
                                      const float (&acc)[K * K + 1])
 {
-    constexpr int n1 = K * K + 1;
+    constexpr int n1 = K * K + 1, n1p = n1 | 1;
     const WtcWgradPlan &p = a.p;
 #pragma unroll
-    for (int e = 0; e < n1; ++e) WTC_LDS(ctx, p.red_off + ctx.tid * n1 + e) = acc[e];
+    for (int e = 0; e < n1; ++e) WTC_LDS(ctx, p.red_off + ctx.tid * n1p + e) = acc[e];
 }
 
 template <typename T, int K, int VEC>
-WTC_HD WTC_INLINE void wtc_wgrad_gather(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int s)
+WTC_HD WTC_INLINE void wtc_wgrad_chunks(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int s)
+{
+    constexpr int n1 = K * K + 1, n1p = n1 | 1, CH = WTC_WG_CH;
+    const WtcWgradPlan &p = a.p;
+    const int tab = p.ctab_off + s * (WTC_WG_CHMAX + WTC_WG_NMAPS);
+    for (int j = ctx.tid; j < p.nchunks[s] * n1; j += ctx.nth) {
+        const int c = j / n1, e = j - c * n1;
+        const int word = *(const int *)&WTC_LDS(ctx, tab + c);
+        const int t0 = word & 0xffff, t1 = word >> 16;
+        float sum = 0.0f;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int t = t0 + u;
+            const float v = WTC_LDS(ctx, p.red_off + wtc_min(t, t1 - 1) * n1p + e);
+            sum += t < t1 ? v : 0.0f;
+        }
+        WTC_LDS(ctx, p.csum_off + j) = sum;
+    }
+}
+
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_combine(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int s)
 {
     constexpr int n1 = K * K + 1;
     const WtcWgradPlan &p = a.p;
+    const int tab = p.ctab_off + s * (WTC_WG_CHMAX + WTC_WG_NMAPS) + WTC_WG_CHMAX;
     for (int idx = ctx.tid; idx < p.nmaps * n1; idx += ctx.nth) {
         const int g = idx / n1, e = idx - g * n1;
-        // threads whose piece s nth + t lies in [first[g], first[g+1])
-        const int lo = wtc_max(0, p.first[g] - s * ctx.nth);
-        const int hi = wtc_min(ctx.nth, p.first[g + 1] - s * ctx.nth);
+        const int word = *(const int *)&WTC_LDS(ctx, tab + g);
+        const int c0 = word & 0xffff, cnt = word >> 16;
         float sum = WTC_LDS(ctx, p.res_off + idx);
-        for (int t = lo; t < hi; ++t) sum += WTC_LDS(ctx, p.red_off + t * n1 + e);
+        for (int c = c0; c < c0 + cnt; ++c) sum += WTC_LDS(ctx, p.csum_off + c * n1 + e);
         WTC_LDS(ctx, p.res_off + idx) = sum;
     }
 }

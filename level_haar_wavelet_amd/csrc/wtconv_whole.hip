@@ -43,13 +43,17 @@ __global__ __launch_bounds__(256) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 }
 
 template <typename T, int K, int BW>
-static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream)
+static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
+    }
+    if (resident) {
+        *resident = wtc_resident_blocks(fn, a.p.nthreads, lds);
+        return hipSuccess;
     }
     const unsigned groups = (unsigned)((a.p.n + a.p.planes - 1) / a.p.planes);
     const unsigned blocks = groups * (unsigned)a.p.c;
@@ -58,23 +62,23 @@ static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream)
 }
 
 template <typename T, int K>
-static hipError_t launch_k(const WtcWholeArgs<T> &a, hipStream_t stream)
+static hipError_t launch_k(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     switch (a.p.out_bw) {
-    case 8: return launch_bw<T, K, 8>(a, stream);
-    case 4: return launch_bw<T, K, 4>(a, stream);
-    default: return launch_bw<T, K, 2>(a, stream);
+    case 8: return launch_bw<T, K, 8>(a, stream, resident);
+    case 4: return launch_bw<T, K, 4>(a, stream, resident);
+    default: return launch_bw<T, K, 2>(a, stream, resident);
     }
 }
 
 template <typename T>
-static hipError_t launch_t(const WtcWholeArgs<T> &a, hipStream_t stream)
+static hipError_t launch_t(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident = nullptr)
 {
     switch (a.p.k) {
-    case 1: return launch_k<T, 1>(a, stream);
-    case 3: return launch_k<T, 3>(a, stream);
-    case 5: return launch_k<T, 5>(a, stream);
-    case 7: return launch_k<T, 7>(a, stream);
+    case 1: return launch_k<T, 1>(a, stream, resident);
+    case 3: return launch_k<T, 3>(a, stream, resident);
+    case 5: return launch_k<T, 5>(a, stream, resident);
+    case 7: return launch_k<T, 7>(a, stream, resident);
     default: return hipErrorInvalidValue;
     }
 }
@@ -89,4 +93,22 @@ hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, vo
     }
     WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
     return launch_t<_Float16>(a, stream);
+}
+
+int wtc_whole_resident(int dtype, const WtcWholePlan &p)
+{
+    int r = 0;
+    hipError_t e;
+    if (dtype == 0) {
+        WtcWholeArgs<float> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
+        e = launch_t<float>(a, nullptr, &r);
+    } else {
+        WtcWholeArgs<_Float16> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
+        e = launch_t<_Float16>(a, nullptr, &r);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return r;
 }

@@ -125,6 +125,12 @@ def wgrad_plan(n, c, h, w, k, levels, nthreads=256, planes=1, dtype="f32", budge
     return d
 
 
+def choose_planes(n, c, slots, fixed):
+    lib = _load()
+    lib.emu_choose_planes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    return lib.emu_choose_planes(n, c, slots, fixed)
+
+
 def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nthreads=256, planes=1,
           budget_floats=40960, tiled=False):
     """Parameter gradients through the emulated fused weight-gradient kernel."""

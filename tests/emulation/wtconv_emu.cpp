@@ -160,16 +160,17 @@ static void run_wgrad(const WtcWgradArgs<T> &a)
         for (int t = 0; t < nth; ++t) wtc_wgrad_zero<T, VEC>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_wgrad_table<T, K, VEC>(a, ctx[t]);
         for (int img = 0; img < ctx[0].nimg; ++img) {
-            for (int t = 0; t < nth; ++t) wtc_wgrad_store_input<T, K, VEC>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_stage<T, K, VEC>(a, ctx[t]);
             for (int t = 0; t < nth; ++t)
                 if (img + 1 < ctx[t].nimg) wtc_wgrad_load<T, VEC>(a, ctx[t], img + 1);
-            for (int m = 1; m <= p.levels; ++m)
+            for (int m = p.first_deep; m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_wgrad_analysis<T, K, VEC>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_wgrad_correlate<T, K, VEC>(a, ctx[t], A(t));
         }
         for (int s = 0; s < p.q; ++s) {
             for (int t = 0; t < nth; ++t) wtc_wgrad_park<T, K, VEC>(a, ctx[t], A(t)[s]);
-            for (int t = 0; t < nth; ++t) wtc_wgrad_gather<T, K, VEC>(a, ctx[t], s);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_chunks<T, K, VEC>(a, ctx[t], s);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_combine<T, K, VEC>(a, ctx[t], s);
         }
         for (int t = 0; t < nth; ++t) wtc_wgrad_write<T, K, VEC>(a, ctx[t]);
     }
@@ -337,6 +338,9 @@ int emu_wgrad_plan(int n, int c, int h, int w, int k, int levels, int nthreads, 
     out[5] = p.vec;
     return rc;
 }
+
+// Images per workgroup chosen for a grid of c x ceil(n / planes) workgroups.
+int emu_choose_planes(int n, int c, int slots, double fixed) { return wtc_choose_planes(n, c, slots, fixed); }
 
 // Whole-plane plan: out[0..6] = planes, vec, out_bw, lds_floats, blocks, nthreads, ok.
 int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int planes, int ebytes,

@@ -76,6 +76,9 @@ WGRAD_CASES = [
     (3, 2, 28, 28, 5, 2, "f16", 2),
     (2, 2, 56, 56, 5, 3, "f32", 2),
     (1, 2, 64, 96, 5, 4, "f16", 3),
+    (2, 2, 14, 10, 7, 1, "f32", 2),   # staging groups of 2 rows, 2 columns
+    (3, 2, 12, 12, 1, 2, "f16", 1),
+    (2, 1, 24, 40, 3, 2, "f32", 2),   # odd border width
 ]
 
 
@@ -94,3 +97,24 @@ def test_emulated_weight_gradients_match_oracle(orc, case, tiled):
             continue
         assert not np.isnan(gg).any()
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
+
+
+def _rounds_cost(n, c, slots, fixed, p):
+    groups = -(-n // p)
+    return -(-c * groups // slots) * (p + fixed)
+
+
+@pytest.mark.parametrize("n,c,slots", [(64, 96, 512), (64, 192, 512), (64, 192, 1024), (16, 256, 512),
+                                       (1, 7, 512), (5, 3, 512), (300, 2, 4)])
+def test_choose_planes_minimises_rounds_cost(n, c, slots):
+    """The planes chooser against brute force over every planes value."""
+    for fixed in (0.0, 1.0, 3.0):
+        got = emu.choose_planes(n, c, slots, fixed)
+        assert 1 <= got <= n
+        best = min(_rounds_cost(n, c, slots, fixed, p) for p in range(1, n + 1))
+        assert _rounds_cost(n, c, slots, fixed, got) == best
+
+
+def test_choose_planes_fills_one_round():
+    # 96 channels x 64 images on 512 resident workgroups: 5 groups of 13 images run in one round
+    assert emu.choose_planes(64, 96, 512, 1.0) == 13
