@@ -133,9 +133,10 @@ def run_gpu(args, wl):
             torch.cuda.synchronize()
             ms_total += evs[i][0].elapsed_time(evs[i][3])
         wall = time.perf_counter() - t0
-    per = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]
-    avg = [sum(p[j] for p in per) / len(per) * 1000.0 for j in range(3)]  # us per op
-    return {"ms_per_step": ms_total / args.steps, "us_ops": avg, "wall_s": wall}
+    per = [[e[j].elapsed_time(e[j + 1]) * 1000.0 for j in range(3)] for e in evs]  # us per op and step
+    med = [sorted(p[j] for p in per)[len(per) // 2] for j in range(3)]
+    mean = [sum(p[j] for p in per) / len(per) for j in range(3)]
+    return {"ms_per_step": ms_total / args.steps, "us_ops": med, "us_ops_mean": mean, "wall_s": wall}
 
 
 def cpu_baseline(wl, images, min_seconds=2.0):
@@ -176,8 +177,8 @@ def cpu_baseline(wl, images, min_seconds=2.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="stage1")
     ap.add_argument("--levels", type=int, default=None)
     ap.add_argument("--dtype", default=None)
@@ -243,6 +244,8 @@ def main():
         "us_bwd_data": round(us_b, 2),
         "us_bwd_weight": round(us_w, 2),
         "us_fwd_bwd": round(us_f + us_b + us_w, 2),
+        "us_per_op": "median over the timed steps (events around each call); means %s" % (
+            ", ".join("%.2f" % v for v in res["us_ops_mean"])),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "modeled_bytes_per_step": step_bytes,
         "mall_flush": bool(args.mall_flush),
