@@ -17,6 +17,8 @@ hipError_t wtc_launch_dwconv(int dtype, int k, const void *in, void *out, const 
 namespace {
 
 constexpr int kFusedThreads = 256;
+constexpr int kWholeThreads = 256;     // whole-plane forward / data backward: 256 or 512 threads
+constexpr int kWholeWideItems = 384;  // convolution pieces per image from which 512 threads pay
 constexpr int kMaxLdsFloats = 160 * 1024 / 4;
 
 // LDS budget of one fused workgroup.  The default keeps two workgroups per
@@ -106,12 +108,20 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     } else {
         WtcWholePlan wp;
         const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
-        if (!env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
-            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                                kFusedThreads, 1, eb, whole_budget_floats()) == 0) {
+        // 256 threads, or 512 when a plane has enough convolution pieces to
+        // keep them busy (more waves in flight hide the latency of the
+        // staging and output passes); WTCONV_WHOLE_THREADS overrides
+        int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
+        bool fits = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
+                    wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                        wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()) == 0;
+        if (fits && !wth) wth = wp.items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
+        if (fits &&
+            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1,
+                                eb, whole_budget_floats()) == 0) {
             const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp), kWholeFixed, "WTCONV_PLANES");
-            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                                kFusedThreads, planes, eb, whole_budget_floats());
+            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth,
+                                planes, eb, whole_budget_floats());
             e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
             return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
         }

@@ -12,7 +12,7 @@
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <typename T, int K, int BW>
-__global__ __launch_bounds__(256) void wtconv_whole_kernel(WtcWholeArgs<T> a)
+__global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
     WtcWholeCtx<T> ctx;

@@ -19,6 +19,10 @@
 //     flight across them;
 //   * LDS is zeroed once: every map keeps a zero border of r pixels, which is
 //     the convolutions' zero padding, and only interiors are rewritten;
+//   * each thread stages a group of gr rows x vec columns of the input (one
+//     16-byte load per row) and computes Haar level 1, and level 2 when the
+//     group has 4 rows and 4 columns, from those registers; deeper levels are
+//     computed from LDS;
 //   * every convolution -- the base one at full resolution and the four bands
 //     of every level -- is cut into the same 4x4-output pieces, dealt
 //     round-robin to the threads from a descriptor table built once per

@@ -118,3 +118,13 @@ def test_choose_planes_minimises_rounds_cost(n, c, slots):
 def test_choose_planes_fills_one_round():
     # 96 channels x 64 images on 512 resident workgroups: 5 groups of 13 images run in one round
     assert emu.choose_planes(64, 96, 512, 1.0) == 13
+
+
+@pytest.mark.parametrize("nthreads,planes", [(512, 2), (128, 3)])
+def test_emulated_whole_plane_thread_counts(orc, nthreads, planes):
+    n, c, h, w, k, L = 5, 2, 32, 32, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, seed=nthreads + planes)
+    y = emu.whole(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, nthreads=nthreads,
+                  planes=planes, budget_floats=1 << 16)
+    ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    _check(y, ref)

@@ -55,6 +55,34 @@ def test_small_shapes(orc, case):
     assert_close(dx, ref_dx, dt, "dx")
 
 
+WIDE = [
+    # n, c, h, w, k, L, dtype, threads, planes
+    (3, 4, 16, 16, 5, 2, "f32", 512, 2),
+    (5, 2, 56, 56, 5, 3, "f32", 512, 3),
+    (2, 3, 24, 40, 3, 3, "f16", 512, 1),
+    (5, 2, 56, 56, 5, 3, "f32", 256, 2),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "x".join(map(str, c)))
+def test_whole_plane_thread_counts_and_image_groups(orc, case, monkeypatch):
+    """The whole-plane kernel at 256 and 512 threads and with image groups
+    that leave a ragged last group."""
+    n, c, h, w, k, L, dt, th, planes = case
+    _log("case %s" % (case,))
+    monkeypatch.setenv("WTCONV_WHOLE_THREADS", str(th))
+    monkeypatch.setenv("WTCONV_PLANES", str(planes))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + th + planes)
+    d = DevInputs(inp, dt)
+    y = forward(d)
+    dx = backward_data(d)
+    torch.cuda.synchronize()
+    ref_y = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    ref_dx = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(y, ref_y, dt, "y")
+    assert_close(dx, ref_dx, dt, "dx")
+
+
 def test_no_bias_and_forced_tiling(orc, monkeypatch):
     """Small LDS budget: several tiles per plane, strips, XCD remap of tiles."""
     monkeypatch.setenv("WTCONV_LDS_KB", "16")
