@@ -42,6 +42,12 @@
 #define WTC_INLINE inline
 static inline float wtc_fma(float a, float b, float c) { return fmaf(a, b, c); }
 static inline float wtc_uniform(float v) { return v; }
+// product of two non-negative ints below 2^23 (LDS and in-plane indexes)
+static inline int wtc_mul24(int a, int b)
+{
+    assert(a >= 0 && b >= 0 && a < (1 << 23) && b < (1 << 23));
+    return a * b;
+}
 template <typename P>
 static inline P &wtc_chk(P *base, int64_t i, int64_t n, int line)
 {
@@ -61,6 +67,9 @@ static inline P &wtc_chk(P *base, int64_t i, int64_t n, int line)
 #define WTC_HD __device__
 #define WTC_INLINE __forceinline__
 static __device__ __forceinline__ float wtc_fma(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+// Product of two non-negative ints below 2^23 (LDS and in-plane indexes):
+// the full-rate 24-bit multiply instead of the quarter-rate 32-bit one.
+static __device__ __forceinline__ int wtc_mul24(int a, int b) { return __mul24(a, b); }
 // A value that is the same in every lane, moved to a scalar register.
 static __device__ __forceinline__ float wtc_uniform(float v)
 {

@@ -36,7 +36,8 @@ struct WtcWtilePlan {
     int32_t nmaps_here;      // 1 (last step) or 4
     int32_t first[5];
     int32_t plen;
-    WtcMap x;                // U_j(x) over the tile plus 2r (origin (2r, 2r))
+    WtcMap x;                // U_j(x) over the tile plus 2r (origin (2r, 2r + xs))
+    int32_t xs;              // left pad of the x map: correlation windows start on 16-byte boundaries
     WtcMap dy;               // U_j(dy) over the tile
     WtcMap bx;               // 3 detail bands of level j+1 of x, tile/2 plus r (origin (r, r))
     WtcMap bd;               // 3 detail bands of level j+1 of dy, tile/2
@@ -49,24 +50,29 @@ static inline int32_t wtc_wtile_layout(WtcWtilePlan *p)
     const int32_t r = p->k / 2, kk = p->k * p->k, P = WTC_WG_P;
     const int32_t TH = p->th, TW = p->tw, last = p->step == p->levels;
     int32_t off = 0;
+    // Rows are 16-byte aligned and the shared piece routine reads a window
+    // row as roundup(P + k - 1, 4) floats from a 16-byte boundary: the x map
+    // is shifted right by xs so that a window (starting r columns left of its
+    // piece) starts on one, and every pitch leaves room for the last read.
+    p->xs = (4 - r % 4) % 4;
     p->x.off = off;
     p->x.rows = wtc_roundup(TH, P) + 4 * r;
-    p->x.pitch = (wtc_roundup(TW, P) + 4 * r) | 1;
+    p->x.pitch = wtc_roundup(p->xs + wtc_roundup(TW, P) + 4 * r, 4);
     off += p->x.rows * p->x.pitch;
     p->dy.off = off;
     p->dy.rows = wtc_roundup(TH, P);
-    p->dy.pitch = wtc_roundup(TW, P) | 1;
+    p->dy.pitch = wtc_roundup(TW, P);
     off += p->dy.rows * p->dy.pitch;
     p->bx.off = p->bx.rows = p->bx.pitch = 0;
     p->bd = p->bx;
     if (!last) {
         p->bx.off = off;
         p->bx.rows = wtc_roundup(TH / 2, P) + 2 * r;
-        p->bx.pitch = (wtc_roundup(TW / 2, P) + 2 * r) | 1;
+        p->bx.pitch = wtc_roundup(wtc_roundup(TW / 2, P) + 2 * r, 4);
         off += 3 * p->bx.rows * p->bx.pitch;
         p->bd.off = off;
         p->bd.rows = wtc_roundup(TH / 2, P);
-        p->bd.pitch = wtc_roundup(TW / 2, P) | 1;
+        p->bd.pitch = wtc_roundup(TW / 2, P);
         off += 3 * p->bd.rows * p->bd.pitch;
     }
     p->nmaps_here = last ? 1 : 4;
@@ -228,8 +234,8 @@ WTC_HD WTC_INLINE void wtc_wtile_table(const WtcWtileArgs<TI> &a, WtcWtileCtx &c
         const int pr = rem / npc, pc = rem - pr * npc;
         int d0, d1, xp, dp;
         if (g == 0) {
-            // x origin (2R, 2R): element (i0 - R, j0 - R) sits at (i0 + R, j0 + R)
-            d0 = p.x.off + (P * pr + R) * p.x.pitch + P * pc + R;
+            // x origin (2R, 2R + xs): element (i0 - R, j0 - R) sits at (i0 + R, j0 + R + xs)
+            d0 = p.x.off + (P * pr + R) * p.x.pitch + P * pc + R + p.xs;
             d1 = p.dy.off + (P * pr) * p.dy.pitch + P * pc;
             xp = p.x.pitch;
             dp = p.dy.pitch;
@@ -264,7 +270,7 @@ WTC_HD WTC_INLINE void wtc_wtile_stage(const WtcWtileArgs<TI> &a, WtcWtileCtx &c
         const int hh = ty0 - 2 * R + ri, ww = tx0 - 2 * R + ci;
         float v = 0.0f;
         if (hh >= 0 && hh < p.h && ww >= 0 && ww < p.w) v = wtc_to_float(WTC_PAR(a.x, base + (int64_t)hh * p.w + ww, all));
-        WTC_LDS(ctx, p.x.off + ri * p.x.pitch + ci) = v;
+        WTC_LDS(ctx, p.x.off + ri * p.x.pitch + ci + p.xs) = v;
     }
     for (int idx = ctx.tid; idx < p.th * p.tw; idx += ctx.nth) {
         const int ri = idx / p.tw, ci = idx - ri * p.tw;
@@ -296,7 +302,7 @@ WTC_HD WTC_INLINE void wtc_wtile_analysis(const WtcWtileArgs<TI> &a, WtcWtileCtx
         float b1 = 0.0f, b2 = 0.0f, b3 = 0.0f, ll = 0.0f;
         if (i >= 0 && i < h1 && j >= 0 && j < w1) {
             // full-resolution row 2i is staged row 2i - (ty0 - 2R) = 2 ri
-            const int s = p.x.off + (2 * ri) * p.x.pitch + 2 * ci;
+            const int s = p.x.off + (2 * ri) * p.x.pitch + 2 * ci + p.xs;
             const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
             const float x10 = WTC_LDS(ctx, s + p.x.pitch), x11 = WTC_LDS(ctx, s + p.x.pitch + 1);
             const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;

@@ -25,20 +25,30 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(a, ctx);
     wtc_whole_table<T, K, BW>(a, ctx);
+    // Software pipeline over the images: image i+1 is staged (its input map
+    // and first Haar levels written) in the same barrier interval as image i's
+    // output pass, and the input of image i+2 is requested between the two,
+    // so the wait for a prefetched input never waits for output stores issued
+    // just before it (loads and stores share one counter) and the loads do
+    // not queue behind the stores.
+    wtc_whole_stage<T, K, BW>(a, ctx);
+    wtc_lds_barrier();
+    if (ctx.nimg > 1) wtc_whole_load<T, K, BW>(a, ctx, 1);
     for (int img = 0; img < ctx.nimg; ++img) {
-        wtc_whole_select<T>(a, ctx, img);
-        wtc_whole_stage<T, K, BW>(a, ctx);
-        wtc_lds_barrier();
-        if (img + 1 < ctx.nimg) wtc_whole_load<T, K, BW>(a, ctx, img + 1);
         for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
             wtc_lds_barrier();
         }
         wtc_whole_conv<T, K, BW>(a, ctx);
         wtc_lds_barrier();
-        // the next image's staging touches the input and analysis maps, which
-        // the convolution phase above has finished reading
+        // the convolutions above have finished reading the input and analysis
+        // maps, which the staging of the next image overwrites; the output
+        // pass reads only the convolution outputs
+        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW>(a, ctx);
+        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW>(a, ctx, img + 2);
+        wtc_whole_select<T>(a, ctx, img);
         wtc_whole_out<T, K, BW>(a, ctx);
+        wtc_lds_barrier();
     }
 }
 

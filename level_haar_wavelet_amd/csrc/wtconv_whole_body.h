@@ -124,12 +124,18 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     p->planes = planes < 1 ? 1 : (planes > n ? n : planes);
     if (levels < 1 || levels > WTC_MAXL) return -1;
     if (h % (1 << levels) || w % (1 << levels)) return -1;
-    int32_t vec = 16 / elem_bytes;
-    while (vec > 1 && w % vec) vec /= 2;
+    // Output blocks of 2 x BW with BW the 16-byte store width (4 fp32, 8
+    // fp16) where the row allows, doubled when blocks would be more than two
+    // per thread; the kernel stages rows in segments of vec = min(BW, 16-byte
+    // width) elements, a compile-time function of its BW.
+    const int32_t wide = 16 / elem_bytes;
+    int32_t bw = wide < 8 ? wide : 8;
+    while (bw > 2 && w % bw) bw /= 2;
+    if (bw < 8 && (h / 2) * (w / bw) > 2 * nthreads && w % (2 * bw) == 0) bw *= 2;
+    if (w % bw) return -1;
+    p->out_bw = bw;
+    const int32_t vec = bw < wide ? bw : wide;
     p->vec = vec;
-    p->out_bw = (w % 8 == 0) ? 8 : (w % 4 == 0) ? 4 : 2;
-    // a staging group is gr rows x vec columns of the input; with 4 rows and
-    // at least 4 columns its thread computes Haar levels 1 and 2 itself
     p->gr = (levels >= 2 && vec >= 4 && p->out_bw >= 4) ? 4 : 2;
     p->groups = (h / p->gr) * (w / vec);
     if (p->groups > nthreads) return -1;
@@ -159,6 +165,7 @@ struct WtcWholeCtx {
     // input rows (as loaded: T)
     int grow, gcol;
     bool gvalid;
+    int oblk;  // this thread's first output block: row << 16 | column (set once)
     T pre[4][16 / sizeof(T)];
 #ifdef WTC_EMULATE
     int64_t lds_n, img_n;
@@ -192,6 +199,8 @@ WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     ctx.gvalid = ctx.tid < p.groups;
     ctx.grow = grp / gpr;
     ctx.gcol = grp - ctx.grow * gpr;
+    const int nbx = p.w / p.out_bw, by = ctx.tid / nbx;
+    ctx.oblk = (by << 16) | (ctx.tid - by * nbx);
 }
 
 template <typename T>
@@ -302,7 +311,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     for (int q = 0; q < 4; ++q)
         if (q < p.gr)
 #pragma unroll
-            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xm.off + (r0 + q + R) * xm.pitch + c0 + t + R) = x[q][t];
+            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xm.off + wtc_mul24(r0 + q + R, xm.pitch) + c0 + t + R) = x[q][t];
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
 #pragma unroll
@@ -314,7 +323,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
                 const float x00 = x[2 * aa][2 * bb], x01 = x[2 * aa][2 * bb + 1];
                 const float x10 = x[2 * aa + 1][2 * bb], x11 = x[2 * aa + 1][2 * bb + 1];
                 const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-                const int o = u1.off + (i + R) * u1.pitch + c0 / 2 + bb + R;
+                const int o = u1.off + wtc_mul24(i + R, u1.pitch) + c0 / 2 + bb + R;
                 ll[aa][bb] = sa + sc;
                 WTC_LDS(ctx, o) = sa + sc;
                 WTC_LDS(ctx, o + st1) = sa - sc;
@@ -331,7 +340,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
             const float x00 = ll[0][2 * bb], x01 = ll[0][2 * bb + 1];
             const float x10 = ll[1][2 * bb], x11 = ll[1][2 * bb + 1];
             const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-            const int o = u2.off + (ctx.grow + R) * u2.pitch + c0 / 4 + bb + R;
+            const int o = u2.off + wtc_mul24(ctx.grow + R, u2.pitch) + c0 / 4 + bb + R;
             WTC_LDS(ctx, o) = sa + sc;
             WTC_LDS(ctx, o + st2) = sa - sc;
             WTC_LDS(ctx, o + 2 * st2) = da + dc;
@@ -354,11 +363,11 @@ WTC_HD WTC_INLINE void wtc_whole_analysis(const WtcWholeArgs<T> &a, WtcWholeCtx<
     int i = ctx.tid / Wm, j = ctx.tid - (ctx.tid / Wm) * Wm;
     const int di = ctx.nth / Wm, dj = ctx.nth - di * Wm;
     for (int idx = ctx.tid; idx < total; idx += ctx.nth) {
-        const int s = sm.off + (2 * i + R) * sm.pitch + 2 * j + R;
+        const int s = sm.off + wtc_mul24(2 * i + R, sm.pitch) + 2 * j + R;
         const float x00 = WTC_LDS(ctx, s), x01 = WTC_LDS(ctx, s + 1);
         const float x10 = WTC_LDS(ctx, s + sm.pitch), x11 = WTC_LDS(ctx, s + sm.pitch + 1);
         const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-        const int o = um.off + (i + R) * um.pitch + j + R;
+        const int o = um.off + wtc_mul24(i + R, um.pitch) + j + R;
         WTC_LDS(ctx, o) = sa + sc;
         WTC_LDS(ctx, o + st) = sa - sc;
         WTC_LDS(ctx, o + 2 * st) = da + dc;
@@ -415,10 +424,23 @@ WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
 }
 
 // N consecutive LDS floats starting at a multiple of 4 (16-byte reads).
+#ifdef WTC_EMULATE
+// the vector LDS accesses need their natural alignment (16 or 8 bytes)
+static inline void wtc_check_align(int idx, int n, int line)
+{
+    const int a = n % 4 == 0 ? 4 : (n == 2 ? 2 : 1);
+    if (idx % a) {
+        fprintf(stderr, "wtconv emulation: LDS index %d of a %d-float access not aligned (line %d)\n", idx, n, line);
+        abort();
+    }
+}
+#endif
+
 template <typename T, int N, typename Ctx>
 WTC_HD WTC_INLINE void wtc_lds_row(Ctx &ctx, int idx, float (&dst)[N])
 {
 #ifdef WTC_EMULATE
+    wtc_check_align(idx, N, __LINE__);
     for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
 #else
     typedef float v4 __attribute__((ext_vector_type(4)));
@@ -439,6 +461,7 @@ template <typename T, int N, typename Ctx>
 WTC_HD WTC_INLINE void wtc_lds_vec(Ctx &ctx, int idx, float (&dst)[N])
 {
 #ifdef WTC_EMULATE
+    wtc_check_align(idx, N, __LINE__);
     for (int e = 0; e < N; ++e) dst[e] = WTC_LDS(ctx, idx + e);
 #else
     if constexpr (N % 4 == 0) {
@@ -459,6 +482,7 @@ template <typename T, int N, typename Ctx>
 WTC_HD WTC_INLINE void wtc_lds_store4(Ctx &ctx, int idx, const float (&src)[N])
 {
 #ifdef WTC_EMULATE
+    wtc_check_align(idx, N, __LINE__);
     for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
 #else
     typedef float v4 __attribute__((ext_vector_type(4)));
@@ -545,30 +569,53 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
     const WtcMap z0 = p.z[0], z1 = p.z[1];
     const int st1 = z1.rows * z1.pitch;
     for (int it = ctx.tid; it < nblk; it += ctx.nth) {
-        const int by = it / nbx, bx = it - by * nbx;
+        // the first block's coordinates were computed once per workgroup
+        const int by = it == ctx.tid ? ctx.oblk >> 16 : it / nbx;
+        const int bx = it == ctx.tid ? ctx.oblk & 0xffff : it - by * nbx;
         const int i1 = by;
         float acc[2][BW];
-        wtc_lds_vec<T, BW>(ctx, z0.off + (2 * by) * z0.pitch + BW * bx, acc[0]);
-        wtc_lds_vec<T, BW>(ctx, z0.off + (2 * by + 1) * z0.pitch + BW * bx, acc[1]);
+        const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
+        wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
+        wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
         float band[4][Q];
-        const int o1 = z1.off + i1 * z1.pitch + Q * bx;
+        const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
 #pragma unroll
         for (int b = 0; b < 4; ++b) wtc_lds_vec<T, Q>(ctx, o1 + b * st1, band[b]);
-        // deep levels: closed form, signs from the coordinate bits
-        for (int m = 2; m <= p.levels; ++m) {
+        // deep levels, closed form: level m adds, to the low-pass value of
+        // level-1 cell (i1, j1), the four band outputs of level-m cell
+        // (i1 >> (m-1), j1 >> (m-1)) with signs from bit m-2 of i1 (sp) and of
+        // j1 (sq).  The block's Q level-1 cells (Q <= 4, starting at a
+        // multiple of Q) span Q/2 cells of level 2 and one cell of every
+        // deeper level, and each is read once.
+        static_assert(Q <= 4, "one cell of level 3 and deeper per block");
+        if (p.levels >= 2) {
+            constexpr int C2 = Q >= 2 ? Q / 2 : 1;
+            const WtcMap z2 = p.z[2];
+            const int sz = z2.rows * z2.pitch;
+            const float sp = (i1 & 1) ? -1.0f : 1.0f;
+            const int oz = z2.off + wtc_mul24(i1 >> 1, z2.pitch) + (Q * bx) / 2;
+            float zc[4][C2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wtc_lds_vec<T, C2>(ctx, oz + b * sz, zc[b]);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int c = Q >= 2 ? q / 2 : 0;
+                const float sq = Q >= 2 ? ((q & 1) ? -1.0f : 1.0f) : ((bx & 1) ? -1.0f : 1.0f);
+                const float t0 = wtc_fma(sp, zc[1][c], zc[0][c]), t1 = wtc_fma(sp, zc[3][c], zc[2][c]);
+                band[0][q] += wtc_fma(sq, t1, t0);
+            }
+        }
+        for (int m = 3; m <= p.levels; ++m) {
             const WtcMap zm = p.z[m];
             const int sz = zm.rows * zm.pitch;
             const float sp = ((i1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
-            const int rowo = zm.off + (i1 >> (m - 1)) * zm.pitch;
+            const int oz = zm.off + wtc_mul24(i1 >> (m - 1), zm.pitch) + ((Q * bx) >> (m - 1));
+            const float t0 = wtc_fma(sp, WTC_LDS(ctx, oz + sz), WTC_LDS(ctx, oz));
+            const float t1 = wtc_fma(sp, WTC_LDS(ctx, oz + 3 * sz), WTC_LDS(ctx, oz + 2 * sz));
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                const int j1 = Q * bx + q;
-                const float sq = ((j1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
-                const int oz = rowo + (j1 >> (m - 1));
-                float d = band[0][q] + WTC_LDS(ctx, oz);
-                d = wtc_fma(sp, WTC_LDS(ctx, oz + sz), d);
-                d = wtc_fma(sq, WTC_LDS(ctx, oz + 2 * sz), d);
-                band[0][q] = wtc_fma(sp * sq, WTC_LDS(ctx, oz + 3 * sz), d);
+                const float sq = (((Q * bx + q) >> (m - 2)) & 1) ? -1.0f : 1.0f;
+                band[0][q] += wtc_fma(sq, t1, t0);
             }
         }
 #pragma unroll
@@ -580,7 +627,7 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
             acc[1][2 * q] += d01 + d23;
             acc[1][2 * q + 1] += d01 - d23;
         }
-        const int64_t o0 = (int64_t)(2 * by) * p.w + BW * bx;
+        const int64_t o0 = wtc_mul24(2 * by, p.w) + BW * bx;
 #ifdef WTC_EMULATE
         for (int dr = 0; dr < 2; ++dr)
             for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, o0 + dr * p.w + e) = wtc_from_float<T>(acc[dr][e]);

@@ -98,17 +98,24 @@ static void run_whole(const WtcWholeArgs<T> &a)
         for (int t = 0; t < nth; ++t) wtc_whole_init<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_fold<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_table<T, K, BW>(a, ctx[t]);
+        // the kernel's software pipeline: image i+1 is staged in the same
+        // barrier interval as image i's output pass (here every staging runs
+        // first, so a staging write that the output pass reads would show)
+        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t)
+            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW>(a, ctx[t], 1);
         for (int img = 0; img < ctx[0].nimg; ++img) {
-            for (int t = 0; t < nth; ++t) {
-                wtc_whole_select<T>(a, ctx[t], img);
-                wtc_whole_stage<T, K, BW>(a, ctx[t]);
-            }
-            for (int t = 0; t < nth; ++t)
-                if (img + 1 < ctx[t].nimg) wtc_whole_load<T, K, BW>(a, ctx[t], img + 1);
             for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
-            for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t) {
+                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW>(a, ctx[t]);
+                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW>(a, ctx[t], img + 2);
+            }
+            for (int t = 0; t < nth; ++t) {
+                wtc_whole_select<T>(a, ctx[t], img);
+                wtc_whole_out<T, K, BW>(a, ctx[t]);
+            }
         }
     }
 }

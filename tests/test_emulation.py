@@ -128,3 +128,20 @@ def test_emulated_whole_plane_thread_counts(orc, nthreads, planes):
                   planes=planes, budget_floats=1 << 16)
     ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
     _check(y, ref)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 16, 16, 5, 2), (1, 2, 28, 28, 5, 2), (1, 2, 24, 40, 3, 3), (1, 1, 32, 64, 7, 4)])
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_whole_plane_fp16(orc, shape, rotate):
+    """The whole-plane kernel with fp16 activations: staging segment width and
+    output block width follow the dtype."""
+    n, c, h, w, k, L = shape
+    inp = make_inputs(n, c, h, w, k, L, dtype="f16", seed=h + w + rotate)
+    y = emu.whole(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate, dtype="f16",
+                  budget_floats=1 << 16)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.x, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel <= 5e-3, rel
