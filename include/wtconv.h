@@ -123,6 +123,36 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
                                        float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
                                        size_t workspace_bytes, wtconv_stream_t stream);
 
+/* ---- Unfused baseline (test and benchmark use only) ----------------------
+ * The same layer composed of separate kernels with every intermediate in HBM:
+ * per level a Haar analysis pass, a depthwise convolution pass and a scale
+ * pass, then per level (deepest first) an add of the low-pass band and a
+ * synthesis pass, and the base convolution, scale and final add (the
+ * composition the pages measure the fused kernel against: technical summary,
+ * Problem Statement, and its count of element moves).  The backward calls are
+ * the step-by-step adjoints of that composition.  Same arguments as the fused
+ * calls; the caller allocates one workspace of wtconv_unfused_workspace_size()
+ * bytes (256-byte aligned) and passes the same workspace to all three calls:
+ * the forward leaves its intermediates there and both backward calls read
+ * them, so a backward call must follow a forward on the same inputs and
+ * parameters.  Intermediates are stored in the activation type.  Errors:
+ * WTCONV_ERR_SHAPE for an invalid descriptor, WTCONV_ERR_NULL for a missing
+ * pointer, WTCONV_ERR_WORKSPACE when the workspace is too small,
+ * WTCONV_ERR_HIP for a launch error. */
+wtconv_status_t wtconv_unfused_workspace_size(const wtconv_desc_t *desc, size_t *bytes);
+wtconv_status_t wtconv_unfused_forward(const wtconv_desc_t *desc, const void *x, const float *w_base,
+                                       const float *bias, const float *s_base, const float *w_lvl,
+                                       const float *s_lvl, void *y, void *workspace, size_t workspace_bytes,
+                                       wtconv_stream_t stream);
+wtconv_status_t wtconv_unfused_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
+                                             const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
+                                             void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
+wtconv_status_t wtconv_unfused_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                               const float *w_base, const float *bias, const float *s_base,
+                                               const float *w_lvl, const float *s_lvl, float *dw_base,
+                                               float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                                               void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char *wtconv_status_string(wtconv_status_t status);
 

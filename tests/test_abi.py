@@ -99,3 +99,26 @@ def test_alias_and_alignment_are_rejected(lib):
     misaligned = lib.wtconv_forward(ctypes.byref(d), ctypes.c_void_p(0x100004), p, None, p, p, p,
                                     ctypes.c_void_p(0x900000), None, 0, None)
     assert misaligned == 3
+
+
+def test_unfused_binding_names_match_the_abi():
+    from level_haar_wavelet_amd import unfused
+
+    for name in unfused.__all__:
+        if name.startswith("wtconv_"):
+            assert name in declared_functions(), name
+
+
+def test_unfused_validation_before_any_launch(lib):
+    import ctypes
+
+    size = ctypes.c_size_t(0)
+    good = _native.desc(2, 3, 16, 16, 5, 2, _native.F32)
+    assert lib.wtconv_unfused_workspace_size(ctypes.byref(good), ctypes.byref(size)) == 0 and size.value > 0
+    bad = _native.desc(2, 3, 18, 16, 5, 2, _native.F32)  # 18 not divisible by 4
+    assert lib.wtconv_unfused_workspace_size(ctypes.byref(bad), ctypes.byref(size)) == 2
+    # null pointers and a short workspace are rejected before anything is launched
+    assert lib.wtconv_unfused_forward(ctypes.byref(good), None, None, None, None, None, None, None, None, 0,
+                                      None) == 1
+    one = ctypes.c_void_p(16)
+    assert lib.wtconv_unfused_forward(ctypes.byref(good), one, one, None, one, one, one, one, one, 8, None) == 4
