@@ -139,6 +139,76 @@ def run_gpu(args, wl):
     return {"ms_per_step": ms_total / args.steps, "us_ops": med, "us_ops_mean": mean, "wall_s": wall}
 
 
+def run_unfused(args, wl):
+    """The same step on the unfused baseline (separate kernels, intermediates in
+    HBM; wtconv_unfused_*), timed the same way, and the peak device memory of
+    one forward + backward of each path (torch.cuda.max_memory_allocated above
+    what the inputs, outputs and parameters already hold, workspaces included)."""
+    import torch
+
+    import level_haar_wavelet_amd as wt
+    from level_haar_wavelet_amd import _native
+    from level_haar_wavelet_amd import unfused as uf
+    from level_haar_wavelet_amd.synthetic import make_inputs
+
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
+    T = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev, dtype=dt)
+    x, dy = T(inp.x, tdt), T(inp.dy, tdt)
+    w0, b0, s0, wl_, sl_ = T(inp.w_base), T(inp.bias), T(inp.s_base), T(inp.w_lvl), T(inp.s_lvl)
+    y, dx = torch.empty_like(x), torch.empty_like(dy)
+    grads = (torch.empty_like(w0), torch.empty_like(b0), torch.empty_like(s0), torch.empty_like(wl_),
+             torch.empty_like(sl_))
+    if wl.levels == 0:
+        wl_ = sl_ = None
+        grads = grads[:3] + (None, None)
+    stream = torch.cuda.current_stream()
+
+    def peak(fn):
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() - base
+
+    def fused_step():
+        n = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, 0 if wl.dtype == "f32" else 1,
+                                     _native.OP_BWD_WEIGHT)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=stream)
+        wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=stream)
+        wt.wtconv_backward_weight(x, dy, w0, b0, s0, wl_, sl_, workspace=ws, grads=grads, stream=stream)
+
+    def unfused_step(ws=None):
+        ws = uf.workspace(x, wl.k, wl.levels) if ws is None else ws
+        uf.wtconv_unfused_forward(x, w0, b0, s0, wl_, sl_, ws, y=y, stream=stream)
+        uf.wtconv_unfused_backward_data(dy, w0, s0, wl_, sl_, ws, dx=dx, stream=stream)
+        uf.wtconv_unfused_backward_weight(x, dy, w0, b0, s0, wl_, sl_, ws, grads=grads, stream=stream)
+
+    mem_fused, mem_unfused = peak(fused_step), peak(unfused_step)
+    ws = uf.workspace(x, wl.k, wl.levels)
+    ops = (lambda: uf.wtconv_unfused_forward(x, w0, b0, s0, wl_, sl_, ws, y=y, stream=stream),
+           lambda: uf.wtconv_unfused_backward_data(dy, w0, s0, wl_, sl_, ws, dx=dx, stream=stream),
+           lambda: uf.wtconv_unfused_backward_weight(x, dy, w0, b0, s0, wl_, sl_, ws, grads=grads, stream=stream))
+    for _ in range(max(2, args.warmup // 2)):
+        unfused_step(ws)
+    steps = max(5, args.steps // 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(stream)
+        for j, op in enumerate(ops):
+            op()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [[e[j].elapsed_time(e[j + 1]) * 1000.0 for j in range(3)] for e in evs]
+    med = [sorted(p[j] for p in per)[len(per) // 2] for j in range(3)]
+    return {"us_ops": med, "steps": steps, "peak_mem_fused_bytes": int(mem_fused),
+            "peak_mem_unfused_bytes": int(mem_unfused)}
+
+
 def cpu_baseline(wl, images, min_seconds=2.0):
     """The CPU oracle (as it stands) on `images` images of the workload: one
     forward, data backward and weight backward, repeated until at least
@@ -186,6 +256,8 @@ def main():
     ap.add_argument("--mall-flush", action="store_true")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-baseline comparison")
+    ap.add_argument("--no-comparator", action="store_true", help="skip the 7x7 depthwise comparator")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -262,6 +334,35 @@ def main():
             "source_digest": digest,
         },
     }
+    if not args.no_unfused:
+        u = run_unfused(args, wl)
+        uf, ub, uw = u["us_ops"]
+        line["unfused_baseline"] = {
+            "what": "the same layer as separate kernels with every intermediate in HBM (wtconv_unfused_*), "
+                    "timed the same way (medians over %d steps)" % u["steps"],
+            "us_fwd": round(uf, 2), "us_bwd_data": round(ub, 2), "us_bwd_weight": round(uw, 2),
+            "us_fwd_bwd": round(uf + ub + uw, 2),
+            "speedup_fwd": round(uf / us_f, 3), "speedup_fwd_bwd": round((uf + ub + uw) / (us_f + us_b + us_w), 3),
+            "peak_mem_fused_MB": round(u["peak_mem_fused_bytes"] / 2 ** 20, 1),
+            "peak_mem_unfused_MB": round(u["peak_mem_unfused_bytes"] / 2 ** 20, 1),
+        }
+    if not args.no_comparator:
+        # the same shape through a plain 7 x 7 depthwise convolution with bias
+        # and scale (the library at L = 0, k = 7): the layer the method's
+        # accuracy and cost are compared with
+        import dataclasses
+
+        dw = dataclasses.replace(wl, name=wl.name + "-dw7x7", k=7, levels=0)
+        r7 = run_gpu(args, dw)
+        f7, b7, w7 = r7["us_ops"]
+        line["dw7x7_comparator"] = {
+            "what": "7x7 depthwise conv (+bias, scale) on the same tensors, same timing",
+            "us_fwd": round(f7, 2), "us_bwd_data": round(b7, 2), "us_bwd_weight": round(w7, 2),
+            "us_fwd_bwd": round(f7 + b7 + w7, 2),
+            "flops_per_element": 2 * 49, "wtconv_flops_per_element": round(conv_flops(wl) / wl.elems, 2),
+            "wtconv_over_dw7x7_fwd": round(us_f / f7, 3),
+            "wtconv_over_dw7x7_fwd_bwd": round((us_f + us_b + us_w) / (f7 + b7 + w7), 3),
+        }
     if args.cpu_sample > 0:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)

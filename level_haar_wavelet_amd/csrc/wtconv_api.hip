@@ -102,29 +102,29 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     if (overlaps(in, out, act_bytes(d))) return WTCONV_ERR_ALIAS;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if (d->levels == 0) {
+    // the whole-plane kernel when a plane fits one workgroup (any L, even
+    // sides for L = 0); otherwise the row-band kernel for L = 0 and the
+    // strip kernel for L >= 1
+    WtcWholePlan wp;
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    // 256 threads, or 512 when a plane has enough convolution pieces to
+    // keep them busy (more waves in flight hide the latency of the
+    // staging and output passes); WTCONV_WHOLE_THREADS overrides
+    int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
+    bool fits = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
+                wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                    wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()) == 0;
+    if (fits && !wth) wth = wp.items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
+    if (fits && wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth,
+                                    1, eb, whole_budget_floats()) == 0) {
+        const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp), kWholeFixed, "WTCONV_PLANES");
+        wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, planes,
+                            eb, whole_budget_floats());
+        e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
+    } else if (d->levels == 0) {
         e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
                               (int)d->w, rotate, s);
     } else {
-        WtcWholePlan wp;
-        const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
-        // 256 threads, or 512 when a plane has enough convolution pieces to
-        // keep them busy (more waves in flight hide the latency of the
-        // staging and output passes); WTCONV_WHOLE_THREADS overrides
-        int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
-        bool fits = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
-                    wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                                        wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()) == 0;
-        if (fits && !wth) wth = wp.items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
-        if (fits &&
-            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1,
-                                eb, whole_budget_floats()) == 0) {
-            const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp), kWholeFixed, "WTCONV_PLANES");
-            wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth,
-                                planes, eb, whole_budget_floats());
-            e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
-            return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
-        }
         WtcFusedPlan p;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                 kFusedThreads, lds_budget_floats()) &&

@@ -220,6 +220,7 @@ struct Layout {
     int64_t D[WTCONV_MAX_LEVELS + 1], Dz[WTCONV_MAX_LEVELS + 1], dY[WTCONV_MAX_LEVELS + 1];
     int64_t S[WTCONV_MAX_LEVELS + 1], Sa[WTCONV_MAX_LEVELS + 1], Db, Ds;
     int64_t elems;      // activation-type elements
+    int64_t ones_off;   // byte offset of 4C floats of 1.0 (unit scales of the convolution steps)
     int64_t part_off;   // byte offset of the float partials
     int64_t groups;
     size_t bytes;
@@ -256,7 +257,8 @@ void make_layout(const wtconv_desc_t *d, Layout *L)
     L->elems = off;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
     L->groups = d->n < 16 ? d->n : 16;
-    L->part_off = (off * eb + 255) / 256 * 256;
+    L->ones_off = (off * eb + 255) / 256 * 256;
+    L->part_off = L->ones_off + (4 * d->c * 4 + 255) / 256 * 256;
     const int64_t kk1 = (int64_t)d->k * d->k + 1;
     L->bytes = (size_t)(L->part_off + L->groups * 4 * d->c * kk1 * 4);
 }
@@ -270,10 +272,23 @@ bool desc_ok(const wtconv_desc_t *d)
     return d->dtype == WTCONV_F32 || d->dtype == WTCONV_F16;
 }
 
-template <typename T>
-void dwconv(int k, const T *in, T *out, const float *wt, const float *bias, int C, int64_t P, int h, int w,
-                  int rotate, hipStream_t s)
+__global__ void k_fill(float *p, int n, float v)
 {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+// One convolution step: the library's own depthwise convolution (the layer at
+// L = 0 with unit scales: wtconv_forward / wtconv_backward_data), so that the
+// baseline's convolutions are as fast as the fused path's; the plain kernel
+// above if that call declines the shape.
+template <typename T>
+void dwconv(int k, const T *in, T *out, const float *wt, const float *bias, const float *ones, int C, int64_t P,
+            int h, int w, int rotate, hipStream_t s)
+{
+    const wtconv_desc_t cd{P / C, C, h, w, k, 0, sizeof(T) == 4 ? WTCONV_F32 : WTCONV_F16};
+    const wtconv_status_t st = rotate ? wtconv_backward_data(&cd, in, wt, ones, nullptr, nullptr, out, nullptr, 0, s)
+                                      : wtconv_forward(&cd, in, wt, bias, ones, nullptr, nullptr, out, nullptr, 0, s);
+    if (st == WTCONV_OK) return;
     const unsigned g = grid_for(P * h * w);
     switch (k) {
     case 1: hipLaunchKernelGGL((k_dwconv<T, 1>), dim3(g), dim3(kThreads), 0, s, in, out, wt, bias, C, P, h, w, rotate); break;
@@ -306,6 +321,8 @@ wtconv_status_t forward_t(const wtconv_desc_t *d, const T *x, const float *w0, c
     make_layout(d, &L);
     const int C = (int)d->c, k = d->k, Lv = d->levels;
     const int64_t NC = d->n * d->c, kk = (int64_t)k * k;
+    float *ones = (float *)((char *)ws + L.ones_off);
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(kThreads), 0, s, ones, 4 * C, 1.0f);
     for (int l = 1; l <= Lv; ++l) {
         const int h = (int)(d->h >> (l - 1)), w = (int)(d->w >> (l - 1));
         const int64_t q = NC * plane_elems(d, l);
@@ -313,8 +330,8 @@ wtconv_status_t forward_t(const wtconv_desc_t *d, const T *x, const float *w0, c
         const int64_t istride = l == 1 ? (int64_t)h * w : 4 * (int64_t)h * w;
         hipLaunchKernelGGL(k_analysis<T>, dim3(grid_for(q)), dim3(kThreads), 0, s, src, istride, ws + L.Y[l],
                            4 * plane_elems(d, l), NC, h, w);
-        dwconv<T>(k, ws + L.Y[l], ws + L.Zc[l], wl + (int64_t)(l - 1) * 4 * C * kk, nullptr, 4 * C, 4 * NC, h / 2,
-                  w / 2, 0, s);
+        dwconv<T>(k, ws + L.Y[l], ws + L.Zc[l], wl + (int64_t)(l - 1) * 4 * C * kk, nullptr, ones, 4 * C, 4 * NC,
+                  h / 2, w / 2, 0, s);
         hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(4 * q)), dim3(kThreads), 0, s, ws + L.Zc[l],
                            sl + (int64_t)(l - 1) * 4 * C, (const T *)nullptr, ws + L.Zs[l], 4 * C, 4 * NC,
                            plane_elems(d, l));
@@ -334,7 +351,7 @@ wtconv_status_t forward_t(const wtconv_desc_t *d, const T *x, const float *w0, c
         }
     }
     const int64_t E = NC * d->h * d->w, hw = d->h * d->w;
-    dwconv<T>(k, x, ws + L.Bc, w0, b0, C, NC, (int)d->h, (int)d->w, 0, s);
+    dwconv<T>(k, x, ws + L.Bc, w0, b0, ones, C, NC, (int)d->h, (int)d->w, 0, s);
     hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(E)), dim3(kThreads), 0, s, ws + L.Bc, s0,
                        Lv ? (const T *)(ws + L.Nx[1]) : (const T *)nullptr, y, C, NC, hw);
     return hipGetLastError() == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
@@ -364,12 +381,14 @@ wtconv_status_t backward_data_t(const wtconv_desc_t *d, const T *dy, const float
     make_layout(d, &L);
     const int C = (int)d->c, k = d->k, Lv = d->levels;
     const int64_t NC = d->n * d->c, kk = (int64_t)k * k;
+    float *ones = (float *)((char *)ws + L.ones_off);
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(kThreads), 0, s, ones, 4 * C, 1.0f);
     wavelet_adjoint_bands<T>(d, L, dy, ws, s);
     for (int l = 1; l <= Lv; ++l) {
         const int64_t per = plane_elems(d, l);
         hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(4 * NC * per)), dim3(kThreads), 0, s, ws + L.D[l],
                            sl + (int64_t)(l - 1) * 4 * C, (const T *)nullptr, ws + L.Dz[l], 4 * C, 4 * NC, per);
-        dwconv<T>(k, ws + L.Dz[l], ws + L.dY[l], wl + (int64_t)(l - 1) * 4 * C * kk, nullptr, 4 * C, 4 * NC,
+        dwconv<T>(k, ws + L.Dz[l], ws + L.dY[l], wl + (int64_t)(l - 1) * 4 * C * kk, nullptr, ones, 4 * C, 4 * NC,
                   (int)(d->h >> l), (int)(d->w >> l), 1, s);
     }
     // from the deepest level up: the low-pass band of dY_l also receives the
@@ -391,7 +410,7 @@ wtconv_status_t backward_data_t(const wtconv_desc_t *d, const T *dy, const float
     const int64_t E = NC * d->h * d->w, hw = d->h * d->w;
     hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(E)), dim3(kThreads), 0, s, dy, s0, (const T *)nullptr,
                        ws + L.Ds, C, NC, hw);
-    dwconv<T>(k, ws + L.Ds, Lv ? ws + L.Db : dx, w0, nullptr, C, NC, (int)d->h, (int)d->w, 1, s);
+    dwconv<T>(k, ws + L.Ds, Lv ? ws + L.Db : dx, w0, nullptr, ones, C, NC, (int)d->h, (int)d->w, 1, s);
     if (Lv)
         hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(E)), dim3(kThreads), 0, s, ws + L.Db, (const float *)nullptr,
                            (const T *)(ws + L.S[1]), dx, C, NC, hw);

@@ -106,6 +106,11 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
 
 static inline int32_t wtc_whole_blocks(const WtcWholePlan *p) { return (p->h / 2) * (p->w / p->out_bw); }
 
+// The staging phase computes Haar level 2 too (4-row groups of at least 4
+// columns); the analysis phase then starts at level 3.
+WTC_HD WTC_INLINE bool wtc_whole_stage_l2(const WtcWholePlan &p) { return p.gr == 4 && p.vec >= 4 && p.levels >= 2; }
+WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p) { return wtc_whole_stage_l2(p) ? 3 : 2; }
+
 // Plan of the whole-plane kernel, or -1 when the plane does not fit (LDS,
 // per-thread chunk or block limits).  `planes` is the requested number of
 // images per workgroup (clamped to n).
@@ -122,8 +127,11 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     p->rotate = rotate;
     p->nthreads = nthreads;
     p->planes = planes < 1 ? 1 : (planes > n ? n : planes);
-    if (levels < 1 || levels > WTC_MAXL) return -1;
-    if (h % (1 << levels) || w % (1 << levels)) return -1;
+    // L = 0 (a plain depthwise convolution) needs even sides: the staging and
+    // output passes work on 2-row groups and blocks
+    if (levels < 0 || levels > WTC_MAXL) return -1;
+    if (h % (2 << levels) && levels == 0) return -1;
+    if (h % (1 << levels) || w % (1 << levels) || w % 2) return -1;
     // Output blocks of 2 x BW with BW the 16-byte store width (4 fp32, 8
     // fp16) where the row allows, doubled when blocks would be more than two
     // per thread; the kernel stages rows in segments of vec = min(BW, 16-byte
@@ -136,7 +144,9 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     p->out_bw = bw;
     const int32_t vec = bw < wide ? bw : wide;
     p->vec = vec;
-    p->gr = (levels >= 2 && vec >= 4 && p->out_bw >= 4) ? 4 : 2;
+    // staging groups of 4 rows where the height allows (their threads also
+    // compute Haar level 2 when L >= 2 and vec >= 4), else 2
+    p->gr = (h % 4 == 0 && vec >= 2) ? 4 : 2;
     p->groups = (h / p->gr) * (w / vec);
     if (p->groups > nthreads) return -1;
     if (wtc_whole_blocks(p) > 2 * nthreads) return -1;
@@ -312,6 +322,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
         if (q < p.gr)
 #pragma unroll
             for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xm.off + wtc_mul24(r0 + q + R, xm.pitch) + c0 + t + R) = x[q][t];
+    if (p.levels < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
 #pragma unroll
@@ -332,7 +343,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
             }
         }
     }
-    if (p.gr == 4 && vec >= 4) {
+    if (vec >= 4 && wtc_whole_stage_l2(p)) {
         const WtcMap u2 = p.u[2];
         const int st2 = u2.rows * u2.pitch;
 #pragma unroll
@@ -380,10 +391,6 @@ WTC_HD WTC_INLINE void wtc_whole_analysis(const WtcWholeArgs<T> &a, WtcWholeCtx<
         }
     }
 }
-
-// First level the analysis phase computes (the staging phase did the ones
-// below).
-WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p) { return p.gr == 4 ? 3 : 2; }
 
 // Piece descriptors, built once per workgroup (they depend only on the plan).
 // Piece order: the base map (full resolution), then band 0..3 of level 1, 2,
@@ -578,9 +585,16 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
         wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
         float band[4][Q];
-        const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
+        if (p.levels >= 1) {
+            const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) wtc_lds_vec<T, Q>(ctx, o1 + b * st1, band[b]);
+            for (int b = 0; b < 4; ++b) wtc_lds_vec<T, Q>(ctx, o1 + b * st1, band[b]);
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int q = 0; q < Q; ++q) band[b][q] = 0.0f;
+        }
         // deep levels, closed form: level m adds, to the low-pass value of
         // level-1 cell (i1, j1), the four band outputs of level-m cell
         // (i1 >> (m-1), j1 >> (m-1)) with signs from bit m-2 of i1 (sp) and of

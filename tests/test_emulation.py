@@ -145,3 +145,23 @@ def test_emulated_whole_plane_fp16(orc, shape, rotate):
         ref = orc.backward_data(inp.x, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
     rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
     assert rel <= 5e-3, rel
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 16, 16, 7, 0, "f32"), (1, 2, 14, 10, 3, 0, "f32"), (2, 2, 12, 20, 5, 0, "f16"),
+                                   (1, 2, 28, 28, 5, 1, "f32"), (1, 2, 20, 12, 3, 1, "f16")])
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_whole_plane_levels_0_and_1(orc, shape, rotate):
+    """L = 0 (the plain depthwise convolution) and L = 1 through the whole-plane
+    kernel, with 2- and 4-row staging groups."""
+    n, c, h, w, k, L, dt = shape
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h * w + rotate)
+    y = emu.whole(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate, dtype=dt,
+                  budget_floats=1 << 16)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.x, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    if dt == "f32":
+        _check(y, ref)
+    else:
+        assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
