@@ -53,11 +53,10 @@ template <typename T>
 __global__ void k_analysis(const T *in, int64_t istride, T *out, int64_t ostride, int64_t P, int h, int w)
 {
     const int h2 = h / 2, w2 = w / 2;
-    const int64_t per = (int64_t)h2 * w2, total = P * per;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = t / per;
-        const int r = (int)(t - p * per);
-        const int i = r / w2, j = r - (r / w2) * w2;
+    const uint32_t per = (uint32_t)(h2 * w2), total = (uint32_t)(P * per);
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+        const uint32_t p = t / per, r = t - p * per;
+        const uint32_t i = r / (uint32_t)w2, j = r - i * (uint32_t)w2;
         const T *s = in + p * istride + (int64_t)(2 * i) * w + 2 * j;
         const float a = ld(s, 0), b = ld(s, 1), c = ld(s, w), d = ld(s, w + 1);
         T *o = out + p * ostride + (int64_t)i * w2 + j;
@@ -75,15 +74,14 @@ template <typename T>
 __global__ void k_synthesis(const T *ll, int64_t lstride, const T *bands, int64_t bstride, T *out, int64_t P, int h,
                             int w)
 {
-    const int64_t per = (int64_t)h * w, total = P * per;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = t / per;
-        const int r = (int)(t - p * per);
-        const int i = r / w, j = r - (r / w) * w;
+    const uint32_t per = (uint32_t)(h * w), total = (uint32_t)(P * per);
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+        const uint32_t p = t / per, r = t - p * per;
+        const uint32_t i = r / (uint32_t)w, j = r - i * (uint32_t)w;
         const float a0 = ld(ll, p * lstride + r);
         const T *bb = bands + p * bstride + r;
         const float a1 = ld(bb, per), a2 = ld(bb, 2 * per), a3 = ld(bb, 3 * per);
-        T *o = out + p * (4 * per) + (int64_t)(2 * i) * (2 * w) + 2 * j;
+        T *o = out + (int64_t)p * (4 * per) + (int64_t)(2 * i) * (2 * w) + 2 * j;
         st(o, 0, 0.5f * (a0 + a1 + a2 + a3));
         st(o, 1, 0.5f * (a0 + a1 - a2 - a3));
         st(o, 2 * w, 0.5f * (a0 - a1 + a2 - a3));
@@ -126,9 +124,9 @@ __global__ void k_dwconv(const T *in, T *out, const float *wt, const float *bias
 template <typename T>
 __global__ void k_scale_add(const T *in, const float *s, const T *add, T *out, int C, int64_t P, int64_t per)
 {
-    const int64_t total = P * per;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int c = (int)((t / per) % C);
+    const uint32_t total = (uint32_t)(P * per), per32 = (uint32_t)per;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+        const uint32_t c = (t / per32) % (uint32_t)C;
         float v = (s ? s[c] : 1.0f) * ld(in, t);
         if (add) v += ld(add, t);
         st(out, t, v);
@@ -139,9 +137,9 @@ __global__ void k_scale_add(const T *in, const float *s, const T *add, T *out, i
 template <typename T>
 __global__ void k_add_strided(const T *a, int64_t astride, const T *b, int64_t bstride, T *out, int64_t P, int64_t per)
 {
-    const int64_t total = P * per;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = t / per, r = t - p * per;
+    const uint32_t total = (uint32_t)(P * per), per32 = (uint32_t)per;
+    for (uint32_t t = blockIdx.x * blockDim.x + threadIdx.x; t < total; t += gridDim.x * blockDim.x) {
+        const uint32_t p = t / per32, r = t - p * per32;
         st(out, t, ld(a, p * astride + r) + ld(b, p * bstride + r));
     }
 }
@@ -221,6 +219,10 @@ struct Layout {
     int64_t S[WTCONV_MAX_LEVELS + 1], Sa[WTCONV_MAX_LEVELS + 1], Db, Ds;
     int64_t elems;      // activation-type elements
     int64_t ones_off;   // byte offset of 4C floats of 1.0 (unit scales of the convolution steps)
+    int64_t zw_off;     // byte offset of 4C k^2 zero weights (the correlation steps' unused scale term)
+    int64_t sdb_off;    // byte offset of 2 x 4C scratch floats (their unused bias and scale outputs)
+    int64_t fws_off;    // byte offset of the correlation steps' own workspace, fws_bytes long
+    int64_t fws_bytes;
     int64_t part_off;   // byte offset of the float partials
     int64_t groups;
     size_t bytes;
@@ -258,7 +260,21 @@ void make_layout(const wtconv_desc_t *d, Layout *L)
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
     L->groups = d->n < 16 ? d->n : 16;
     L->ones_off = (off * eb + 255) / 256 * 256;
-    L->part_off = L->ones_off + (4 * d->c * 4 + 255) / 256 * 256;
+    L->zw_off = L->ones_off + (4 * d->c * 4 + 255) / 256 * 256;
+    L->sdb_off = L->zw_off + (4 * d->c * d->k * d->k * 4 + 255) / 256 * 256;
+    L->fws_off = L->sdb_off + (2 * 4 * d->c * 4 + 255) / 256 * 256;
+    // the correlation steps run the library's weight-gradient path at L = 0
+    // (k x k for the weights, 1 x 1 for the scales) on every level's shape
+    int64_t fws = 0;
+    for (int l = 0; l <= d->levels; ++l) {
+        for (int kk : {d->k, 1}) {
+            const wtconv_desc_t cd{d->n, l == 0 ? d->c : 4 * d->c, d->h >> l, d->w >> l, kk, 0, d->dtype};
+            size_t b = 0;
+            if (wtconv_workspace_size(&cd, WTCONV_OP_BWD_WEIGHT, &b) == WTCONV_OK && (int64_t)b > fws) fws = (int64_t)b;
+        }
+    }
+    L->fws_bytes = fws;
+    L->part_off = L->fws_off + (fws + 255) / 256 * 256;
     const int64_t kk1 = (int64_t)d->k * d->k + 1;
     L->bytes = (size_t)(L->part_off + L->groups * 4 * d->c * kk1 * 4);
 }
@@ -269,6 +285,7 @@ bool desc_ok(const wtconv_desc_t *d)
     if (d->levels < 0 || d->levels > WTCONV_MAX_LEVELS) return false;
     if (d->h % ((int64_t)1 << d->levels) || d->w % ((int64_t)1 << d->levels)) return false;
     if (d->k != 1 && d->k != 3 && d->k != 5 && d->k != 7) return false;
+    if (d->n * d->c * d->h * d->w >= ((int64_t)1 << 31)) return false;  // 32-bit element indexes
     return d->dtype == WTCONV_F32 || d->dtype == WTCONV_F16;
 }
 
@@ -296,6 +313,27 @@ void dwconv(int k, const T *in, T *out, const float *wt, const float *bias, cons
     case 5: hipLaunchKernelGGL((k_dwconv<T, 5>), dim3(g), dim3(kThreads), 0, s, in, out, wt, bias, C, P, h, w, rotate); break;
     default: hipLaunchKernelGGL((k_dwconv<T, 7>), dim3(g), dim3(kThreads), 0, s, in, out, wt, bias, C, P, h, w, rotate); break;
     }
+}
+
+template <typename T>
+void corr(int k, const T *dz, const float *scale, const T *a, float *part, int C, int N, int G, int h, int w,
+                float *out, float *outb, hipStream_t s);
+
+// One correlation step through the library's weight-gradient path at L = 0
+// with unit scales and zero weights: dw = G (the k x k correlation of dz with
+// a), db = sum dz.  dz must already carry its scale.  Falls back to the plain
+// kernel above if that call declines the shape.
+template <typename T>
+void corr_lib(int k, const T *dz, const T *a, const Layout &L, T *ws, float *part, int C, int N, int G, int h, int w,
+              float *out, float *outb, hipStream_t s)
+{
+    char *base = (char *)ws;
+    float *ones = (float *)(base + L.ones_off), *zw = (float *)(base + L.zw_off), *sdb = (float *)(base + L.sdb_off);
+    const wtconv_desc_t cd{N, C, h, w, k, 0, sizeof(T) == 4 ? WTCONV_F32 : WTCONV_F16};
+    const wtconv_status_t st =
+        wtconv_backward_weight(&cd, a, dz, zw, nullptr, ones, nullptr, nullptr, out, outb ? outb : sdb, sdb + C,
+                               nullptr, nullptr, base + L.fws_off, (size_t)L.fws_bytes, s);
+    if (st != WTCONV_OK) corr<T>(k, dz, nullptr, a, part, C, N, G, h, w, out, outb, s);
 }
 
 template <typename T>
@@ -427,18 +465,29 @@ wtconv_status_t backward_weight_t(const wtconv_desc_t *d, const T *x, const T *d
     const int C = (int)d->c, k = d->k, Lv = d->levels, N = (int)d->n, G = (int)L.groups;
     const int64_t kk = (int64_t)k * k;
     float *part = (float *)((char *)ws + L.part_off);
+    const int64_t NC = d->n * d->c;
+    hipLaunchKernelGGL(k_fill, dim3(1), dim3(kThreads), 0, s, (float *)((char *)ws + L.ones_off), 4 * C, 1.0f);
+    hipLaunchKernelGGL(k_fill, dim3(4), dim3(kThreads), 0, s, (float *)((char *)ws + L.zw_off), (int)(4 * C * kk),
+                       0.0f);
     wavelet_adjoint_bands<T>(d, L, dy, ws, s);
     for (int l = 1; l <= Lv; ++l) {
         const int h = (int)(d->h >> l), w = (int)(d->w >> l);
-        // dW_l = corr(s_l D_l, Y_l); ds_l = <D_l, Zc_l>
-        corr<T>(k, ws + L.D[l], sl + (int64_t)(l - 1) * 4 * C, ws + L.Y[l], part, 4 * C, N, G, h, w,
-                dwl + (int64_t)(l - 1) * 4 * C * kk, nullptr, s);
-        corr<T>(1, ws + L.D[l], nullptr, ws + L.Zc[l], part, 4 * C, N, G, h, w, dsl + (int64_t)(l - 1) * 4 * C,
-                nullptr, s);
+        const int64_t per = plane_elems(d, l);
+        // dW_l = corr(s_l D_l, Y_l) (the scale backward, then the convolution's
+        // weight gradient); ds_l = <D_l, Zc_l>
+        hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(4 * NC * per)), dim3(kThreads), 0, s, ws + L.D[l],
+                           sl + (int64_t)(l - 1) * 4 * C, (const T *)nullptr, ws + L.Dz[l], 4 * C, 4 * NC, per);
+        corr_lib<T>(k, ws + L.Dz[l], ws + L.Y[l], L, ws, part, 4 * C, N, G, h, w,
+                    dwl + (int64_t)(l - 1) * 4 * C * kk, nullptr, s);
+        corr_lib<T>(1, ws + L.D[l], ws + L.Zc[l], L, ws, part, 4 * C, N, G, h, w, dsl + (int64_t)(l - 1) * 4 * C,
+                    nullptr, s);
     }
     // base: dW0 = corr(s0 dy, x), db0 = sum s0 dy, ds0 = <dy, Bc> (Bc = W0 (*) x + b0)
-    corr<T>(k, dy, s0, x, part, C, N, G, (int)d->h, (int)d->w, dw0, db0, s);
-    corr<T>(1, dy, nullptr, ws + L.Bc, part, C, N, G, (int)d->h, (int)d->w, ds0, nullptr, s);
+    const int64_t E = NC * d->h * d->w;
+    hipLaunchKernelGGL(k_scale_add<T>, dim3(grid_for(E)), dim3(kThreads), 0, s, dy, s0, (const T *)nullptr, ws + L.Ds,
+                       C, NC, d->h * d->w);
+    corr_lib<T>(k, ws + L.Ds, x, L, ws, part, C, N, G, (int)d->h, (int)d->w, dw0, db0, s);
+    corr_lib<T>(1, dy, ws + L.Bc, L, ws, part, C, N, G, (int)d->h, (int)d->w, ds0, nullptr, s);
     return hipGetLastError() == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
 }
 
