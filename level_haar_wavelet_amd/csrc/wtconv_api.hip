@@ -162,14 +162,19 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     const int kk = d->k * d->k;
     ch->plen = kk + 1 + 4 * d->levels * kk;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    // 256 threads (512 threads with one accumulator set each measured no
+    // faster at the 56 x 56 planes); WTCONV_WGRAD_THREADS overrides
+    const int wth = env_int("WTCONV_WGRAD_THREADS", kFusedThreads, 64, 512);
     ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
-                wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels,
-                                    kFusedThreads, 1, eb, whole_budget_floats()) == 0;
+                wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1,
+                                    eb, whole_budget_floats()) == 0;
     if (ch->whole) {
+        wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1, eb,
+                            whole_budget_floats());
         const int planes = pick_planes(d, wtc_wgrad_resident(d->dtype, ch->wp), kWgradFixed,
                                        "WTCONV_WGRAD_PLANES");
-        wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, kFusedThreads,
-                            planes, eb, whole_budget_floats());
+        wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, planes, eb,
+                            whole_budget_floats());
         ch->groups = ch->wp.groups;
     } else {
         ch->groups = (int)wgrad_groups(d);

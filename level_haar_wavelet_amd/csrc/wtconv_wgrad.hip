@@ -10,8 +10,11 @@
 
 static __device__ __forceinline__ void wtc_lds_barrier_wg() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename T, int K, int VEC>
-__global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
+// Q: accumulator sets per thread the kernel holds (1, or WTC_WG_QMAX for q = 2..3).
+// With one set (fp32, k <= 5) the kernel is held to 128 VGPRs: two 512-thread workgroups
+// (four waves per SIMD) share a compute unit.
+template <typename T, int K, int VEC, int Q>
+__global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
     WtcWgradCtx<T, VEC> ctx;
@@ -23,9 +26,9 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
     wtc_wgrad_zero<T, VEC>(a, ctx);
     wtc_lds_barrier_wg();
     wtc_wgrad_table<T, K, VEC>(a, ctx);
-    float acc[WTC_WG_QMAX][K * K + 1];
+    float acc[Q][K * K + 1];
 #pragma unroll
-    for (int s = 0; s < WTC_WG_QMAX; ++s)
+    for (int s = 0; s < Q; ++s)
 #pragma unroll
         for (int e = 0; e < K * K + 1; ++e) acc[s][e] = 0.0f;
     for (int img = 0; img < ctx.nimg; ++img) {
@@ -36,11 +39,11 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
             wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
             wtc_lds_barrier_wg();
         }
-        wtc_wgrad_correlate<T, K, VEC>(a, ctx, acc);
+        wtc_wgrad_correlate<T, K, VEC, Q>(a, ctx, acc);
         wtc_lds_barrier_wg();
     }
 #pragma unroll
-    for (int s = 0; s < WTC_WG_QMAX; ++s) {
+    for (int s = 0; s < Q; ++s) {
         if (s < a.p.q) {
             wtc_wgrad_park<T, K, VEC>(a, ctx, acc[s]);
             wtc_lds_barrier_wg();
@@ -80,11 +83,11 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k
     if (lane == 0) wtc_wgrad_finalize_store(c, g, C, term, ds_base, ds_lvl);
 }
 
-template <typename T, int K, int VEC>
-static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
+template <typename T, int K, int VEC, int Q>
+static hipError_t launch_wgrad_q(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC>;
+    const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC, Q>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -94,8 +97,15 @@ static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int
         return hipSuccess;
     }
     const unsigned blocks = (unsigned)(a.p.groups * a.p.c);
-    hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC, Q>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <typename T, int K, int VEC>
+static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
+{
+    return a.p.q == 1 ? launch_wgrad_q<T, K, VEC, 1>(a, stream, resident)
+                      : launch_wgrad_q<T, K, VEC, WTC_WG_QMAX>(a, stream, resident);
 }
 
 template <typename T, int K>

@@ -35,7 +35,7 @@
 #define WTC_WG_QMAX 3  // pieces per thread
 #define WTC_WG_P 4     // piece side
 #define WTC_WG_CH 16   // threads summed by one job of the reduction's first stage
-#define WTC_WG_MAXT 256  // threads per workgroup, at most
+#define WTC_WG_MAXT 512  // threads per workgroup, at most
 #define WTC_WG_NMAPS (1 + 4 * WTC_MAXL)
 #define WTC_WG_CHMAX (WTC_WG_MAXT / WTC_WG_CH + WTC_WG_NMAPS)  // first-stage jobs of a set, at most
 
@@ -516,13 +516,14 @@ WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1,
     }
 }
 
-template <typename T, int K, int VEC>
+// Q: accumulator sets the kernel holds (at least the plan's q)
+template <typename T, int K, int VEC, int Q>
 WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx,
-                                          float (&acc)[WTC_WG_QMAX][K * K + 1])
+                                          float (&acc)[Q][K * K + 1])
 {
     const WtcWgradPlan &p = a.p;
 #pragma unroll
-    for (int s = 0; s < WTC_WG_QMAX; ++s) {
+    for (int s = 0; s < Q; ++s) {
         const int it = s * ctx.nth + ctx.tid;
         if (s < p.q && it < p.npieces) {
             const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;

@@ -172,7 +172,7 @@ static void run_wgrad(const WtcWgradArgs<T> &a)
                 if (img + 1 < ctx[t].nimg) wtc_wgrad_load<T, VEC>(a, ctx[t], img + 1);
             for (int m = p.first_deep; m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_wgrad_analysis<T, K, VEC>(a, ctx[t], m);
-            for (int t = 0; t < nth; ++t) wtc_wgrad_correlate<T, K, VEC>(a, ctx[t], A(t));
+            for (int t = 0; t < nth; ++t) wtc_wgrad_correlate<T, K, VEC, WTC_WG_QMAX>(a, ctx[t], A(t));
         }
         for (int s = 0; s < p.q; ++s) {
             for (int t = 0; t < nth; ++t) wtc_wgrad_park<T, K, VEC>(a, ctx[t], A(t)[s]);
