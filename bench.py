@@ -90,6 +90,11 @@ def run_gpu(args, wl):
     ws_bytes = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, 0 if wl.dtype == "f32" else 1,
                                         _native.OP_BWD_WEIGHT)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    # forward / data-backward workspaces (planes too large for one workgroup keep
+    # their level-1 low-pass map and deeper levels' term there), allocated once
+    wsf = [torch.empty(max(wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels,
+                                                    0 if wl.dtype == "f32" else 1, op), 1),
+                       dtype=torch.uint8, device=dev) for op in (_native.OP_FWD, _native.OP_BWD_DATA)]
     grads = (torch.empty_like(w0), torch.empty_like(b0), torch.empty_like(s0), torch.empty_like(wl_),
              torch.empty_like(sl_))
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.mall_flush else None
@@ -98,10 +103,10 @@ def run_gpu(args, wl):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=stream)
+        wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=stream, workspace=wsf[0])
         if ev:
             ev[1].record(stream)
-        wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=stream)
+        wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=stream, workspace=wsf[1])
         if ev:
             ev[2].record(stream)
         wt.wtconv_backward_weight(x, dy, w0, b0, s0, wl_, sl_, workspace=ws, grads=grads, stream=stream)

@@ -87,8 +87,10 @@ typedef struct {
 /* hipStream_t without pulling in the HIP headers. */
 typedef struct ihipStream_t *wtconv_stream_t;
 
-/* Bytes of device workspace `op` needs for `desc` (0 for the forward and the
- * data backward).  Errors as for the op itself. */
+/* Bytes of device workspace `op` needs for `desc` on the current device.  The
+ * forward and the data backward need none when a plane fits one workgroup
+ * (or L <= 1); for larger planes with L >= 2 they keep the level-1 low-pass
+ * map and the deeper levels' term there.  Errors as for the op itself. */
 wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op, size_t *bytes);
 
 /* y = WTConv(x).  The per-channel scales are folded into the weights (and the

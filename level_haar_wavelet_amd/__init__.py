@@ -74,7 +74,20 @@ def wtconv_workspace_size(shape, k, levels, dtype_code, op) -> int:
     return out.value
 
 
-def wtconv_forward(x, w_base, bias, s_base, w_lvl, s_lvl, y=None, stream=None):
+def _workspace_for(lib, d, op, workspace, device):
+    """The caller's workspace, or a new one when the op needs one (planes too
+    large for one workgroup with L >= 2 keep the level-1 low-pass map and the
+    deeper levels' term there)."""
+    need = ctypes.c_size_t(0)
+    _native.check(lib.wtconv_workspace_size(ctypes.byref(d), op, ctypes.byref(need)), "wtconv_workspace_size")
+    if need.value == 0:
+        return None, 0
+    if workspace is None:
+        workspace = _torch().empty(need.value, dtype=_torch().uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def wtconv_forward(x, w_base, bias, s_base, w_lvl, s_lvl, y=None, stream=None, workspace=None):
     """y = WTConv(x), enqueued on `stream` (default: torch's current stream)."""
     lib = _native.load()
     for t, name in ((w_base, "w_base"), (bias, "bias"), (s_base, "s_base"), (w_lvl, "w_lvl"), (s_lvl, "s_lvl")):
@@ -82,13 +95,14 @@ def wtconv_forward(x, w_base, bias, s_base, w_lvl, s_lvl, y=None, stream=None):
     d = _desc_for(x, w_base, _levels_of(w_lvl))
     if y is None:
         y = _torch().empty_like(x)
+    ws, nbytes = _workspace_for(lib, d, _native.OP_FWD, workspace, x.device)
     st = lib.wtconv_forward(ctypes.byref(d), _ptr(x), _ptr(w_base), _ptr(bias), _ptr(s_base), _ptr(w_lvl),
-                            _ptr(s_lvl), _ptr(y), None, 0, _stream(stream))
+                            _ptr(s_lvl), _ptr(y), _ptr(ws), nbytes, _stream(stream))
     _native.check(st, "wtconv_forward")
     return y
 
 
-def wtconv_backward_data(dy, w_base, s_base, w_lvl, s_lvl, dx=None, stream=None):
+def wtconv_backward_data(dy, w_base, s_base, w_lvl, s_lvl, dx=None, stream=None, workspace=None):
     """dx = d<dy, WTConv(x)>/dx, enqueued on `stream`."""
     lib = _native.load()
     for t, name in ((w_base, "w_base"), (s_base, "s_base"), (w_lvl, "w_lvl"), (s_lvl, "s_lvl")):
@@ -96,8 +110,9 @@ def wtconv_backward_data(dy, w_base, s_base, w_lvl, s_lvl, dx=None, stream=None)
     d = _desc_for(dy, w_base, _levels_of(w_lvl))
     if dx is None:
         dx = _torch().empty_like(dy)
+    ws, nbytes = _workspace_for(lib, d, _native.OP_BWD_DATA, workspace, dy.device)
     st = lib.wtconv_backward_data(ctypes.byref(d), _ptr(dy), _ptr(w_base), _ptr(s_base), _ptr(w_lvl), _ptr(s_lvl),
-                                  _ptr(dx), None, 0, _stream(stream))
+                                  _ptr(dx), _ptr(ws), nbytes, _stream(stream))
     _native.check(st, "wtconv_backward_data")
     return dx
 

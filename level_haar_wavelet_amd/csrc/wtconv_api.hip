@@ -90,9 +90,78 @@ wtconv_status_t check_params(const wtconv_desc_t *d, const float *w_base, const 
     return WTCONV_OK;
 }
 
+// Whole-plane plan for d (256 threads, or 512 when a plane has enough
+// convolution pieces to keep them busy: more waves in flight hide the latency
+// of the staging and output passes; WTCONV_WHOLE_THREADS overrides), with its
+// images per workgroup; false if a plane does not fit one workgroup.
+bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp)
+{
+    if (env_int("WTCONV_NO_WHOLE", 0, 0, 1)) return false;
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
+    if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                            wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()))
+        return false;
+    if (!wth) wth = wp->items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
+    if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1, eb,
+                            whole_budget_floats()))
+        return false;
+    const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp[0]), kWholeFixed, "WTCONV_PLANES");
+    wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, planes, eb,
+                        whole_budget_floats());
+    return true;
+}
+
+// Tiled plan for planes too large for one workgroup (L >= 1): the base and
+// level-1 convolutions on tiles, the deeper levels from the level-1 low-pass
+// map by a separate call.  Tile shapes are tried in order (about 256 pieces
+// per tile first); false if none fits or WTCONV_NO_TILES is set.
+bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp)
+{
+    if (d->levels < 1 || env_int("WTCONV_NO_TILES", 0, 0, 1)) return false;
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    static const int shapes[][2] = {{64, 32}, {32, 64}, {32, 32}, {64, 64}, {16, 32}, {32, 16}, {16, 16}};
+    for (const auto &sh : shapes) {
+        if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
+        if (wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, rotate,
+                                     kFusedThreads, 1, eb, whole_budget_floats()))
+            continue;
+        const int resident = wtc_whole_resident(d->dtype, tp[0]);
+        int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
+        if (!planes) planes = wtc_choose_planes(tp->units, d->c, resident > 0 ? resident : 512, kWholeFixed);
+        wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, rotate,
+                                 kFusedThreads, planes, eb, whole_budget_floats());
+        return true;
+    }
+    return false;
+}
+
+// The deeper levels (L >= 2) of a tiled pass are the layer with L - 1 levels
+// on the level-1 low-pass map, with the level weights and scales from level 2
+// on and a zero base scale.
+wtconv_desc_t deeper_desc(const wtconv_desc_t *d)
+{
+    wtconv_desc_t s = *d;
+    s.h = d->h / 2;
+    s.w = d->w / 2;
+    s.levels = d->levels - 1;
+    return s;
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t pass_workspace(const wtconv_desc_t *d, int rotate)
+{
+    WtcWholePlan wp;
+    if (whole_choice(d, rotate, &wp) || d->levels < 2 || !tile_choice(d, rotate, &wp)) return 0;
+    const wtconv_desc_t sd = deeper_desc(d);
+    const size_t quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * (d->dtype == WTCONV_F32 ? 4 : 2));
+    return 2 * quarter + align256((size_t)d->c * 4) + pass_workspace(&sd, rotate);
+}
+
 wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *w_base, const float *bias,
                            const float *s_base, const float *w_lvl, const float *s_lvl, void *out, int rotate,
-                           wtconv_stream_t stream)
+                           void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
 {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
@@ -103,27 +172,38 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     // the whole-plane kernel when a plane fits one workgroup (any L, even
-    // sides for L = 0); otherwise the row-band kernel for L = 0 and the
-    // strip kernel for L >= 1
+    // sides for L = 0); else tiles for L >= 1, the row-band kernel for L = 0
+    // and the strip kernel where no tile shape fits
     WtcWholePlan wp;
-    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
-    // 256 threads, or 512 when a plane has enough convolution pieces to
-    // keep them busy (more waves in flight hide the latency of the
-    // staging and output passes); WTCONV_WHOLE_THREADS overrides
-    int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
-    bool fits = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
-                wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                                    wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()) == 0;
-    if (fits && !wth) wth = wp.items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
-    if (fits && wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth,
-                                    1, eb, whole_budget_floats()) == 0) {
-        const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp), kWholeFixed, "WTCONV_PLANES");
-        wtc_make_whole_plan(&wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, planes,
-                            eb, whole_budget_floats());
+    if (whole_choice(d, rotate, &wp)) {
         e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
     } else if (d->levels == 0) {
         e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
                               (int)d->w, rotate, s);
+    } else if (tile_choice(d, rotate, &wp)) {
+        const void *low = nullptr;
+        if (d->levels >= 2) {
+            const size_t need = pass_workspace(d, rotate);
+            if (!workspace || workspace_bytes < need) return WTCONV_ERR_WORKSPACE;
+            if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
+            const wtconv_desc_t sd = deeper_desc(d);
+            const size_t quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * (d->dtype == WTCONV_F32 ? 4 : 2));
+            char *ws = (char *)workspace;
+            void *ll = ws, *deep = ws + quarter;
+            float *zeros = (float *)(ws + 2 * quarter);
+            char *sub = ws + 2 * quarter + align256((size_t)d->c * 4);
+            const int64_t kk = (int64_t)d->k * d->k;
+            if ((e = wtc_launch_lowpass(d->dtype, in, ll, d->n * d->c, (int)d->h, (int)d->w, s)) != hipSuccess ||
+                (e = wtc_launch_fill(zeros, d->c, 0.0f, s)) != hipSuccess)
+                return WTCONV_ERR_HIP;
+            const float *wl2 = w_lvl + 4 * d->c * kk, *sl2 = s_lvl + 4 * d->c;
+            st = rotate ? wtconv_backward_data(&sd, ll, w_base, zeros, wl2, sl2, deep, sub, need - (sub - ws), stream)
+                        : wtconv_forward(&sd, ll, w_base, nullptr, zeros, wl2, sl2, deep, sub, need - (sub - ws),
+                                         stream);
+            if (st != WTCONV_OK) return st;
+            low = deep;
+        }
+        e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s, low);
     } else {
         WtcFusedPlan p;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
@@ -234,8 +314,8 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     if (st != WTCONV_OK) return st;
     if (!bytes) return WTCONV_ERR_NULL;
     switch (op) {
-    case WTCONV_OP_FWD:
-    case WTCONV_OP_BWD_DATA: *bytes = 0; return WTCONV_OK;
+    case WTCONV_OP_FWD: *bytes = pass_workspace(desc, 0); return WTCONV_OK;
+    case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1); return WTCONV_OK;
     case WTCONV_OP_BWD_WEIGHT: {
         WgradChoice ch;
         if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
@@ -295,18 +375,14 @@ wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const f
                                const float *s_base, const float *w_lvl, const float *s_lvl, void *y,
                                void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
-    return fused_pass(desc, x, w_base, bias, s_base, w_lvl, s_lvl, y, 0, stream);
+    return fused_pass(desc, x, w_base, bias, s_base, w_lvl, s_lvl, y, 0, workspace, workspace_bytes, stream);
 }
 
 wtconv_status_t wtconv_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
                                      const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
                                      void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
-    return fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, stream);
+    return fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, workspace, workspace_bytes, stream);
 }
 
 const char *wtconv_status_string(wtconv_status_t status)

@@ -15,10 +15,19 @@ hipError_t wtc_launch_fused(int dtype, const WtcFusedPlan &p, const void *in, vo
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                             hipStream_t stream);
 
-// Whole-plane fused forward / data backward, per plan p.
+// Whole-plane fused forward / data backward, per plan p; for a tiled plan,
+// `low` is the deeper levels' low-pass term at level-1 resolution (or null).
 hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, void *out, const float *w_base,
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
-                            hipStream_t stream);
+                            hipStream_t stream, const void *low = nullptr);
+
+// Level-1 low-pass band (orthonormal, (a + b + c + d) / 2 of every 2x2 block)
+// of `planes` planes of h x w (even), into planes of (h/2) x (w/2).
+hipError_t wtc_launch_lowpass(int dtype, const void *in, void *out, int64_t planes, int h, int w,
+                              hipStream_t stream);
+
+// n floats set to v (a kernel, so that callers may capture it in a graph).
+hipError_t wtc_launch_fill(float *p, int64_t n, float v, hipStream_t stream);
 
 // Fused parameter-gradient correlations (partials per workgroup) and the
 // fixed-order reduction with the chain rule.

@@ -11,7 +11,7 @@
 // clobber keeps the compiler from moving LDS accesses across it.
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename T, int K, int BW>
+template <typename T, int K, int BW, bool TL>
 __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     ctx.tid = threadIdx.x;
     ctx.nth = blockDim.x;
     wtc_whole_setup<T>(a, ctx, blockIdx.x);
-    wtc_whole_load<T, K, BW>(a, ctx, 0);
+    wtc_whole_load<T, K, BW, TL>(a, ctx, 0);
     wtc_whole_init<T, K>(a, ctx);
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(a, ctx);
@@ -31,9 +31,9 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     // so the wait for a prefetched input never waits for output stores issued
     // just before it (loads and stores share one counter) and the loads do
     // not queue behind the stores.
-    wtc_whole_stage<T, K, BW>(a, ctx);
+    wtc_whole_stage<T, K, BW, TL>(a, ctx);
     wtc_lds_barrier();
-    if (ctx.nimg > 1) wtc_whole_load<T, K, BW>(a, ctx, 1);
+    if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL>(a, ctx, 1);
     for (int img = 0; img < ctx.nimg; ++img) {
         for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
@@ -44,19 +44,19 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
         // the convolutions above have finished reading the input and analysis
         // maps, which the staging of the next image overwrites; the output
         // pass reads only the convolution outputs
-        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW>(a, ctx);
-        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW>(a, ctx, img + 2);
+        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL>(a, ctx);
+        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL>(a, ctx, img + 2);
         wtc_whole_select<T>(a, ctx, img);
-        wtc_whole_out<T, K, BW>(a, ctx);
+        wtc_whole_out<T, K, BW, TL>(a, ctx);
         wtc_lds_barrier();
     }
 }
 
-template <typename T, int K, int BW>
-static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
+template <typename T, int K, int BW, bool TL>
+static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW>;
+    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -65,10 +65,16 @@ static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *r
         *resident = wtc_resident_blocks(fn, a.p.nthreads, lds);
         return hipSuccess;
     }
-    const unsigned groups = (unsigned)((a.p.n + a.p.planes - 1) / a.p.planes);
+    const unsigned groups = (unsigned)((a.p.units + a.p.planes - 1) / a.p.planes);
     const unsigned blocks = groups * (unsigned)a.p.c;
-    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
+}
+
+template <typename T, int K, int BW>
+static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
+{
+    return a.p.tiled ? launch_tl<T, K, BW, true>(a, stream, resident) : launch_tl<T, K, BW, false>(a, stream, resident);
 }
 
 template <typename T, int K>
@@ -95,13 +101,15 @@ static hipError_t launch_t(const WtcWholeArgs<T> &a, hipStream_t stream, int *re
 
 hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, void *out, const float *w_base,
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
-                            hipStream_t stream)
+                            hipStream_t stream, const void *low)
 {
     if (dtype == 0) {
-        WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
+                              (const float *)low};
         return launch_t<float>(a, stream);
     }
-    WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
+                             (const _Float16 *)low};
     return launch_t<_Float16>(a, stream);
 }
 

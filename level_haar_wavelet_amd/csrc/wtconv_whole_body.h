@@ -56,6 +56,17 @@ struct WtcWholePlan {
     int32_t items;       // convolution pieces per image
     int32_t tab_off;     // piece descriptors, 4 ints each
     int32_t lds_floats;
+    // Tiling, for planes too large for one workgroup: h x w above is then one
+    // tile of an ih x iw image and a unit of work is one (image, tile); lh
+    // input rows and columns around the tile are loaded too (zero outside the
+    // image), the maps are stored from origins that keep the convolution
+    // windows on 16-byte boundaries, L is 1, and the low-pass contribution of
+    // the deeper levels, computed beforehand at level-1 resolution, is added
+    // before level 1's synthesis.  Untiled: ih = h, iw = w, one tile, lh = 0.
+    int32_t tiled, ih, iw, tiles_x, tiles_y, units;
+    int32_t lh;          // loaded halo (input pixels, a multiple of 4 and of vec)
+    int32_t xr, xc;      // stored row / column of tile element (0, 0) in the input map
+    int32_t u1r, u1c;    // the same for the level-1 maps (deeper maps: (r, r))
 };
 
 #define WTC_WP 4  // piece side (outputs)
@@ -75,17 +86,20 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
         p->u[m].off = p->u[m].pitch = p->u[m].rows = 0;
         p->z[m] = p->u[m];
     }
-    // input map: the base convolution's pieces read windows of P + 2r rows and
-    // columns starting at multiples of P (stored coordinates)
+    // input map: the base convolution's pieces read windows of P + 2r rows
+    // (and roundup(P + 2r, 4) columns, as read) starting r before multiples of
+    // P; the map holds the loaded region (the tile plus lh) and every window
+    const int32_t NR = wtc_roundup(P + 2 * r, 4);
     p->x.off = off;
-    p->x.rows = wtc_roundup(p->h, P) + 2 * r;
-    p->x.pitch = wtc_pitch16(wtc_roundup(p->w, P) + 2 * r);
+    p->x.rows = wtc_max(p->lh + p->h + p->xr, wtc_roundup(p->h, P) - P - r + p->xr + P + 2 * r);
+    p->x.pitch = wtc_pitch16(wtc_max(p->lh + p->w + p->xc, wtc_roundup(p->w, P) - P - r + p->xc + NR));
     off += p->x.rows * p->x.pitch;
     for (int32_t m = 1; m <= L; ++m) {
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
+        const int32_t orow = m == 1 ? p->u1r : r, ocol = m == 1 ? p->u1c : r, lm = m == 1 ? p->lh / 2 : 0;
         p->u[m].off = off;
-        p->u[m].rows = wtc_roundup(Hm, P) + 2 * r;
-        p->u[m].pitch = wtc_pitch16(wtc_roundup(Wm, P) + 2 * r);
+        p->u[m].rows = wtc_max(lm + Hm + orow, wtc_roundup(Hm, P) - P - r + orow + P + 2 * r);
+        p->u[m].pitch = wtc_pitch16(wtc_max(lm + Wm + ocol, wtc_roundup(Wm, P) - P - r + ocol + NR));
         off += 4 * p->u[m].rows * p->u[m].pitch;
     }
     for (int32_t m = 0; m <= L; ++m) {
@@ -111,13 +125,14 @@ static inline int32_t wtc_whole_blocks(const WtcWholePlan *p) { return (p->h / 2
 WTC_HD WTC_INLINE bool wtc_whole_stage_l2(const WtcWholePlan &p) { return p.gr == 4 && p.vec >= 4 && p.levels >= 2; }
 WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p) { return wtc_whole_stage_l2(p) ? 3 : 2; }
 
-// Plan of the whole-plane kernel, or -1 when the plane does not fit (LDS,
-// per-thread chunk or block limits).  `planes` is the requested number of
-// images per workgroup (clamped to n).
-static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
-                                      int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
-                                      int32_t elem_bytes, int32_t budget_floats)
+// Plan of the whole-plane kernel on h x w planes (or tiles), or -1 when it
+// does not fit (LDS, per-thread chunk or block limits).  `planes` is the
+// requested number of units (images, or (image, tile) pairs) per workgroup.
+static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
+                                        int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
+                                        int32_t elem_bytes, int32_t budget_floats, int32_t ih, int32_t iw)
 {
+    const int32_t r = k / 2;
     p->n = n;
     p->c = c;
     p->h = h;
@@ -126,10 +141,18 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     p->levels = levels;
     p->rotate = rotate;
     p->nthreads = nthreads;
-    p->planes = planes < 1 ? 1 : (planes > n ? n : planes);
+    p->tiled = ih != h || iw != w;
+    p->ih = ih;
+    p->iw = iw;
+    if (h < 1 || w < 1 || ih % h || iw % w) return -1;
+    p->tiles_y = ih / h;
+    p->tiles_x = iw / w;
+    p->units = n * p->tiles_y * p->tiles_x;
+    p->planes = planes < 1 ? 1 : (planes > p->units ? p->units : planes);
     // L = 0 (a plain depthwise convolution) needs even sides: the staging and
     // output passes work on 2-row groups and blocks
     if (levels < 0 || levels > WTC_MAXL) return -1;
+    if (p->tiled && levels != 1) return -1;
     if (h % (2 << levels) && levels == 0) return -1;
     if (h % (1 << levels) || w % (1 << levels) || w % 2) return -1;
     // Output blocks of 2 x BW with BW the 16-byte store width (4 fp32, 8
@@ -147,11 +170,43 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
     // staging groups of 4 rows where the height allows (their threads also
     // compute Haar level 2 when L >= 2 and vec >= 4), else 2
     p->gr = (h % 4 == 0 && vec >= 2) ? 4 : 2;
-    p->groups = (h / p->gr) * (w / vec);
+    if (p->tiled) {
+        // the tile plus 2r input pixels (level 1's convolution needs r level-1
+        // pixels around the tile), rounded to whole staging segments and groups
+        p->lh = wtc_roundup(wtc_max(2 * r, 1), wtc_max(4, vec));
+        p->xr = p->lh;
+        p->xc = p->lh + r;
+        p->u1r = p->lh / 2;
+        p->u1c = p->lh / 2 + ((r - p->lh / 2) % 4 + 4) % 4;
+        if (p->gr != 4 || h % 4 || w % vec) return -1;
+    } else {
+        p->lh = 0;
+        p->xr = p->xc = p->u1r = p->u1c = r;
+    }
+    p->groups = ((h + 2 * p->lh) / p->gr) * ((w + 2 * p->lh) / vec);
     if (p->groups > nthreads) return -1;
     if (wtc_whole_blocks(p) > 2 * nthreads) return -1;
     wtc_whole_layout(p);
     return p->lds_floats <= budget_floats ? 0 : -1;
+}
+
+static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
+                                      int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
+                                      int32_t elem_bytes, int32_t budget_floats)
+{
+    return wtc_whole_plan_common(p, n, c, h, w, k, levels, rotate, nthreads, planes, elem_bytes, budget_floats, h,
+                                 w);
+}
+
+// Tiled plan: th x tw tiles of ih x iw images, L = 1 (plus the added low-pass
+// term of the deeper levels).
+static inline int wtc_make_whole_tile_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
+                                           int32_t th, int32_t tw, int32_t k, int32_t rotate, int32_t nthreads,
+                                           int32_t planes, int32_t elem_bytes, int32_t budget_floats)
+{
+    if (th == ih && tw == iw) return -1;
+    return wtc_whole_plan_common(p, n, c, th, tw, k, 1, rotate, nthreads, planes, elem_bytes, budget_floats, ih,
+                                 iw);
 }
 
 template <typename T>
@@ -160,6 +215,9 @@ struct WtcWholeArgs {
     T *out;
     const float *w_base, *bias, *s_base, *w_lvl, *s_lvl;
     WtcWholePlan p;
+    // tiled plans: the deeper levels' low-pass contribution at level-1
+    // resolution, (N, C, ih/2, iw/2) orthonormal, or null
+    const T *low = nullptr;
 };
 
 // Per-thread state of the whole-plane kernel.
@@ -176,6 +234,9 @@ struct WtcWholeCtx {
     int grow, gcol;
     bool gvalid;
     int oblk;  // this thread's first output block: row << 16 | column (set once)
+    int ty0, tx0;  // current unit's tile origin in the image
+    int64_t plane;  // current unit's plane index (n * C + c)
+    int vmask;     // rows of the prefetched group that lie in the image (bit q)
     T pre[4][16 / sizeof(T)];
 #ifdef WTC_EMULATE
     int64_t lds_n, img_n;
@@ -194,17 +255,17 @@ template <typename T>
 WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int bid)
 {
     const WtcWholePlan &p = a.p;
-    const int groups = (p.n + p.planes - 1) / p.planes;
-    // consecutive workgroups take consecutive channels of the same image group
+    // consecutive workgroups take consecutive channels of the same group of
+    // units (images, or (image, tile) pairs with the tiles of an image
+    // consecutive)
     ctx.c = bid % p.c;
     const int g = bid / p.c;
     ctx.n0 = g * p.planes;
-    ctx.nimg = wtc_min(p.planes, p.n - ctx.n0);
-    (void)groups;
+    ctx.nimg = wtc_min(p.planes, p.units - ctx.n0);
     float b = 0.0f;
     if (!p.rotate && a.bias) b = a.s_base[ctx.c] * a.bias[ctx.c];
     ctx.bias = b;
-    const int gpr = p.w / p.vec;
+    const int gpr = (p.w + 2 * p.lh) / p.vec;
     const int grp = wtc_min(ctx.tid, p.groups - 1);  // threads past the last group repeat it, unstored
     ctx.gvalid = ctx.tid < p.groups;
     ctx.grow = grp / gpr;
@@ -213,13 +274,27 @@ WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     ctx.oblk = (by << 16) | (ctx.tid - by * nbx);
 }
 
+// Image plane and tile origin of unit `u` of the workgroup.
+template <typename T>
+WTC_HD WTC_INLINE void wtc_whole_unit(const WtcWholeArgs<T> &a, const WtcWholeCtx<T> &ctx, int u, int64_t &plane,
+                                      int &ty0, int &tx0)
+{
+    const WtcWholePlan &p = a.p;
+    const int tiles = p.tiles_x * p.tiles_y, unit = ctx.n0 + u;
+    const int img = unit / tiles, t = unit - img * tiles;
+    const int ty = t / p.tiles_x;
+    plane = (int64_t)img * p.c + ctx.c;
+    ty0 = ty * p.h;
+    tx0 = (t - ty * p.tiles_x) * p.w;
+}
+
 template <typename T>
 WTC_HD WTC_INLINE void wtc_whole_select(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
-    const int64_t hw = (int64_t)a.p.h * a.p.w;
-    const int64_t plane = (int64_t)(ctx.n0 + img) * a.p.c + ctx.c;
-    ctx.in = a.in + plane * hw;
-    ctx.out = a.out + plane * hw;
+    const int64_t hw = (int64_t)a.p.ih * a.p.iw;
+    wtc_whole_unit(a, ctx, img, ctx.plane, ctx.ty0, ctx.tx0);
+    ctx.in = a.in + ctx.plane * hw;
+    ctx.out = a.out + ctx.plane * hw;
 }
 
 // Phase: zero all of LDS (once per workgroup) and fold the channel's weights.
@@ -263,19 +338,48 @@ struct WtcVec {
 // Issue the loads of image `img` of the workgroup into registers: this
 // thread's staging group, gr rows of vec elements (every lane loads a valid
 // group, so that no branch surrounds the loads).
-template <typename T, int K, int BW>
+// TL: tiled plan (halo loads, bounds, shifted map origins, the added
+// low-pass term); untiled plans compile without any of it.
+template <typename T, int K, int BW, bool TL>
 WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
     const WtcWholePlan &p = a.p;
     constexpr int vec = WtcVec<T, BW>::v;
-    const T *src = a.in + ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
-    const int64_t e0 = (int64_t)(p.gr * ctx.grow) * p.w + vec * ctx.gcol;
+#ifndef WTC_EMULATE
+    // Everything still in flight here was issued a phase or more ago (the
+    // previous prefetch, consumed by the staging just before, and older
+    // output stores): waiting for it now costs nothing and tells the
+    // compiler's wait insertion that the prefetch registers are free, so the
+    // loads below issue back to back (vmcnt 0, expcnt and lgkmcnt unchanged).
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+    int64_t plane;
+    int ty0 = 0, tx0 = 0;
+    if constexpr (TL)
+        wtc_whole_unit(a, ctx, img, plane, ty0, tx0);
+    else
+        plane = (int64_t)(ctx.n0 + img) * p.c + ctx.c;
+    const T *src = a.in + plane * ((int64_t)p.ih * p.iw);
+    // image row / column of the group's first element; in tiled plans rows
+    // and segments outside the image load a clamped address and are zeroed
+    // when staged
+    const int lh = TL ? p.lh : 0;
+    const int row0 = ty0 - lh + p.gr * ctx.grow, col = tx0 - lh + vec * ctx.gcol;
+    const bool colok = !TL || (col >= 0 && col < p.iw);
+    const int ccol = TL ? wtc_min(wtc_max(col, 0), p.iw - vec) : col;
+    int vm = 0;
+    // untiled: one base offset plus q rows (the address stays in one register
+    // pair, so no prefetch load waits on the one before it)
+    const int64_t e0 = (int64_t)row0 * p.iw + col;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (q < p.gr) {
-            const int64_t e = e0 + (int64_t)q * p.w;
+            const int row = row0 + q;
+            vm |= (!TL || (colok && row >= 0 && row < p.ih)) ? (1 << q) : 0;
+            const int64_t e = TL ? (int64_t)wtc_min(wtc_max(row, 0), p.ih - 1) * p.iw + ccol
+                                 : e0 + (int64_t)q * p.iw;
 #ifdef WTC_EMULATE
-            const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.h * p.w;
+            const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.ih * p.iw;
             for (int t = 0; t < vec; ++t) ctx.pre[q][t] = wtc_chk(a.in, base + e + t, all, __LINE__);
 #else
             if constexpr (vec * sizeof(T) == 16) {
@@ -296,13 +400,14 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 #endif
         }
     }
+    ctx.vmask = vm;
 }
 
 // Write the prefetched group into the input map and compute Haar level 1
 // (and level 2 when the group has 4 rows) of it straight from registers:
 //   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
 //   U_2 and B_2^1..3 at its 1 x (vec/4) level-2 positions.
-template <typename T, int K, int BW>
+template <typename T, int K, int BW, bool TL>
 WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int R = K / 2;
@@ -315,26 +420,32 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int t = 0; t < vec; ++t) x[q][t] = q < p.gr ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+        for (int t = 0; t < vec; ++t)
+            x[q][t] = (q < p.gr && (!TL || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+    // r0, c0: the group's position in the loaded region (the tile plus lh);
+    // map origins are the plan's in tiled plans, (r, r) otherwise
+    const int lh = TL ? p.lh : 0, xr = TL ? p.xr : R, xc = TL ? p.xc : R;
+    const int u1r = TL ? p.u1r : R, u1c = TL ? p.u1c : R;
     const int r0 = p.gr * ctx.grow, c0 = vec * ctx.gcol;
+    const int xo = xm.off + wtc_mul24(r0 - lh + xr, xm.pitch) + c0 - lh + xc;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         if (q < p.gr)
 #pragma unroll
-            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xm.off + wtc_mul24(r0 + q + R, xm.pitch) + c0 + t + R) = x[q][t];
+            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xo + wtc_mul24(q, xm.pitch) + t) = x[q][t];
     if (p.levels < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
         if (2 * aa < p.gr) {
-            const int i = r0 / 2 + aa;
+            const int i = (r0 - lh) / 2 + aa;
 #pragma unroll
             for (int bb = 0; bb < h1; ++bb) {
                 const float x00 = x[2 * aa][2 * bb], x01 = x[2 * aa][2 * bb + 1];
                 const float x10 = x[2 * aa + 1][2 * bb], x11 = x[2 * aa + 1][2 * bb + 1];
                 const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-                const int o = u1.off + wtc_mul24(i + R, u1.pitch) + c0 / 2 + bb + R;
+                const int o = u1.off + wtc_mul24(i + u1r, u1.pitch) + (c0 - lh) / 2 + bb + u1c;
                 ll[aa][bb] = sa + sc;
                 WTC_LDS(ctx, o) = sa + sc;
                 WTC_LDS(ctx, o + st1) = sa - sc;
@@ -418,7 +529,10 @@ WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
         }
         const int pr = rem / npc, pc = rem - pr * npc;
         const WtcMap im = m == 0 ? p.x : p.u[m], om = p.z[m];
-        const int d0 = im.off + b * im.rows * im.pitch + (P * pr) * im.pitch + P * pc;
+        // window of output (P pr, P pc): map element (P pr - r, P pc - r),
+        // stored at that plus the map's origin
+        const int orow = m == 0 ? p.xr : (m == 1 ? p.u1r : K / 2), ocol = m == 0 ? p.xc : (m == 1 ? p.u1c : K / 2);
+        const int d0 = im.off + b * im.rows * im.pitch + (P * pr - K / 2 + orow) * im.pitch + P * pc - K / 2 + ocol;
         const int d1 = om.off + b * om.rows * om.pitch + (P * pr) * om.pitch + P * pc;
         const int d2 = im.pitch | (om.pitch << 16);
         const int d3 = (p.wf_off + g * p.ws) | ((g == 0) << 16);
@@ -567,7 +681,7 @@ WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 // the 2x2 butterfly, the deeper levels through the closed form with the
 // coordinate bits picking the signs, added to the low-pass input of the
 // butterfly; one rounding, one store.
-template <typename T, int K, int BW>
+template <typename T, int K, int BW, bool TL>
 WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int Q = BW / 2;
@@ -632,6 +746,22 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
                 band[0][q] += wtc_fma(sq, t1, t0);
             }
         }
+        if (TL && a.low) {
+            // the deeper levels' low-pass term (orthonormal) enters level 1's
+            // synthesis as half its value in these unnormalised sums
+            const int64_t lo = ctx.plane * ((int64_t)(p.ih / 2) * (p.iw / 2)) +
+                               (int64_t)(ctx.ty0 / 2 + i1) * (p.iw / 2) + ctx.tx0 / 2 + Q * bx;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+#ifdef WTC_EMULATE
+                const float v = wtc_to_float(
+                    wtc_chk(a.low, lo + q, (int64_t)p.n * p.c * (p.ih / 2) * (p.iw / 2), __LINE__));
+#else
+                const float v = wtc_to_float(a.low[lo + q]);
+#endif
+                band[0][q] = wtc_fma(0.5f, v, band[0][q]);
+            }
+        }
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             const float a0 = band[0][q], a1 = band[1][q], a2 = band[2][q], a3 = band[3][q];
@@ -641,15 +771,16 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
             acc[1][2 * q] += d01 + d23;
             acc[1][2 * q + 1] += d01 - d23;
         }
-        const int64_t o0 = wtc_mul24(2 * by, p.w) + BW * bx;
+        const int64_t o0 = TL ? (int64_t)(ctx.ty0 + 2 * by) * p.iw + ctx.tx0 + BW * bx
+                              : (int64_t)wtc_mul24(2 * by, p.w) + BW * bx;
 #ifdef WTC_EMULATE
         for (int dr = 0; dr < 2; ++dr)
-            for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, o0 + dr * p.w + e) = wtc_from_float<T>(acc[dr][e]);
+            for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, o0 + dr * p.iw + e) = wtc_from_float<T>(acc[dr][e]);
 #else
         WtcCtx<T> oc;
         oc.out = ctx.out;
         wtc_store_row<T, BW>(oc, o0, acc[0]);
-        wtc_store_row<T, BW>(oc, o0 + p.w, acc[1]);
+        wtc_store_row<T, BW>(oc, o0 + p.iw, acc[1]);
 #endif
     }
 }

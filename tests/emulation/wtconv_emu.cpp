@@ -74,11 +74,11 @@ static int run_t(const WtcFusedArgs<T> &a)
     }
 }
 
-template <typename T, int K, int BW>
+template <typename T, int K, int BW, bool TL>
 static void run_whole(const WtcWholeArgs<T> &a)
 {
     const WtcWholePlan &p = a.p;
-    const int groups = (p.n + p.planes - 1) / p.planes;
+    const int groups = (p.units + p.planes - 1) / p.planes;
     const int nblocks = groups * p.c;
     std::vector<float> lds((size_t)p.lds_floats);
     const int nth = p.nthreads;
@@ -91,30 +91,30 @@ static void run_whole(const WtcWholeArgs<T> &a)
             ctx[t].tid = t;
             ctx[t].nth = nth;
             ctx[t].lds_n = p.lds_floats;
-            ctx[t].img_n = (int64_t)p.h * p.w;
+            ctx[t].img_n = (int64_t)p.ih * p.iw;
             wtc_whole_setup<T>(a, ctx[t], bid);
         }
-        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, TL>(a, ctx[t], 0);
         for (int t = 0; t < nth; ++t) wtc_whole_init<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_fold<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_table<T, K, BW>(a, ctx[t]);
         // the kernel's software pipeline: image i+1 is staged in the same
         // barrier interval as image i's output pass (here every staging runs
         // first, so a staging write that the output pass reads would show)
-        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
         for (int t = 0; t < nth; ++t)
-            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW>(a, ctx[t], 1);
+            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL>(a, ctx[t], 1);
         for (int img = 0; img < ctx[0].nimg; ++img) {
             for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
             for (int t = 0; t < nth; ++t) {
-                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW>(a, ctx[t]);
-                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW>(a, ctx[t], img + 2);
+                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
+                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL>(a, ctx[t], img + 2);
             }
             for (int t = 0; t < nth; ++t) {
                 wtc_whole_select<T>(a, ctx[t], img);
-                wtc_whole_out<T, K, BW>(a, ctx[t]);
+                wtc_whole_out<T, K, BW, TL>(a, ctx[t]);
             }
         }
     }
@@ -123,10 +123,18 @@ static void run_whole(const WtcWholeArgs<T> &a)
 template <typename T, int K>
 static void run_whole_k(const WtcWholeArgs<T> &a)
 {
+    if (a.p.tiled) {
+        switch (a.p.out_bw) {
+        case 8: run_whole<T, K, 8, true>(a); break;
+        case 4: run_whole<T, K, 4, true>(a); break;
+        default: run_whole<T, K, 2, true>(a); break;
+        }
+        return;
+    }
     switch (a.p.out_bw) {
-    case 8: run_whole<T, K, 8>(a); break;
-    case 4: run_whole<T, K, 4>(a); break;
-    default: run_whole<T, K, 2>(a); break;
+    case 8: run_whole<T, K, 8, false>(a); break;
+    case 4: run_whole<T, K, 4, false>(a); break;
+    default: run_whole<T, K, 2, false>(a); break;
     }
 }
 
@@ -378,6 +386,26 @@ int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, 
         return run_whole_t<float>(a);
     }
     WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return run_whole_t<_Float16>(a);
+}
+
+// The tiled whole-plane pass (L = 1 plus the deeper levels' low-pass term
+// `low`, (N, C, ih/2, iw/2), or null) on host arrays.
+int emu_whole_tiled(int dtype, const void *in, void *out, const void *low, int n, int c, int ih, int iw, int th,
+                    int tw, int k, int rotate, const float *w_base, const float *bias, const float *s_base,
+                    const float *w_lvl, const float *s_lvl, int nthreads, int planes, int budget_floats)
+{
+    WtcWholePlan p;
+    if (wtc_make_whole_tile_plan(&p, n, c, ih, iw, th, tw, k, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
+                                 budget_floats))
+        return -1;
+    if (dtype == 0) {
+        WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
+                              (const float *)low};
+        return run_whole_t<float>(a);
+    }
+    WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
+                             (const _Float16 *)low};
     return run_whole_t<_Float16>(a);
 }
 

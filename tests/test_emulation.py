@@ -165,3 +165,49 @@ def test_emulated_whole_plane_levels_0_and_1(orc, shape, rotate):
         _check(y, ref)
     else:
         assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
+
+
+def _lowpass(a):
+    """Level-1 orthonormal low-pass band of (N, C, H, W): half the 2x2 block sums."""
+    return 0.5 * (a[:, :, 0::2, 0::2] + a[:, :, 0::2, 1::2] + a[:, :, 1::2, 0::2] + a[:, :, 1::2, 1::2])
+
+
+TILED = [
+    # n, c, h, w, k, L, th, tw, dtype
+    (2, 2, 64, 64, 5, 1, 32, 16, "f32"),
+    (1, 2, 64, 96, 5, 3, 32, 32, "f32"),
+    (2, 1, 48, 64, 3, 2, 16, 32, "f32"),
+    (1, 2, 64, 64, 7, 4, 32, 32, "f32"),
+    (1, 2, 64, 128, 5, 2, 32, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
+    """Planes too large for one workgroup: the base and level-1 convolutions on
+    tiles with halos, plus the deeper levels' contribution, which is the layer
+    with L - 1 levels (weights and scales from level 2 on, base scale 0) on
+    the level-1 low-pass map.  The deeper term is taken from the oracle here;
+    the result must equal the oracle's full layer."""
+    n, c, h, w, k, L, th, tw, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + L + rotate)
+    src = inp.x
+    low = None
+    if L >= 2:
+        zero = np.zeros_like(inp.s_base)
+        ll = _lowpass(src)
+        if rotate == 0:
+            low = orc.forward(ll, inp.w_base, None, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
+        else:
+            low = orc.backward_data(ll, inp.w_base, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
+    y = emu.whole_tiled(src, low, inp.w_base, inp.bias, inp.s_base, inp.w_lvl[:1], inp.s_lvl[:1], k, th, tw,
+                        rotate=rotate, dtype=dt, planes=3, budget_floats=1 << 16)
+    if rotate == 0:
+        ref = orc.forward(src, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(src, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    if dt == "f32":
+        _check(y, ref)
+    else:
+        assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3

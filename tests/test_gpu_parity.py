@@ -83,9 +83,34 @@ def test_whole_plane_thread_counts_and_image_groups(orc, case, monkeypatch):
     assert_close(dx, ref_dx, dt, "dx")
 
 
+TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
+         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32")]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
+def test_tiled_planes(orc, case, monkeypatch):
+    """The path for planes too large for one workgroup, forced on small planes:
+    base and level-1 convolutions on tiles with halos, the deeper levels from
+    the level-1 low-pass map through a nested call (itself tiled)."""
+    n, c, h, w, k, L, dt = case
+    _log("case %s" % (case,))
+    monkeypatch.setenv("WTCONV_NO_WHOLE", "1")
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h * w + L)
+    d = DevInputs(inp, dt)
+    y = forward(d)
+    dx = backward_data(d)
+    torch.cuda.synchronize()
+    ref_y = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    ref_dx = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(y, ref_y, dt, "y")
+    assert_close(dx, ref_dx, dt, "dx")
+
+
 def test_no_bias_and_forced_tiling(orc, monkeypatch):
-    """Small LDS budget: several tiles per plane, strips, XCD remap of tiles."""
+    """The strip kernel (used where no tile shape divides the plane), small LDS
+    budget: several tiles per plane, strips, XCD remap of tiles."""
     monkeypatch.setenv("WTCONV_LDS_KB", "16")
+    monkeypatch.setenv("WTCONV_NO_TILES", "1")  # the strip kernel (planes no tile shape divides)
     n, c, h, w, k, L = 1, 8, 128, 96, 5, 3
     inp = make_inputs(n, c, h, w, k, L, seed=77)
     inp.bias = None
