@@ -220,11 +220,15 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
 // otherwise the level-by-level tiled steps.  Both write partial rows
 // [groups][C][plen] that the finalize pass reduces.
 struct WgradChoice {
-    bool whole;
+    bool whole;        // one plane per workgroup
+    bool tiles;        // planes too large: base and level 1 on tiles (wp), deeper levels nested
     WtcWgradPlan wp;
     int groups;
-    int plen;
+    int plen;          // partial-row length of the kernel that writes them
     WtcWtileCarve cv;
+    size_t part_bytes; // partial rows (tiles: at the start of the workspace)
+    size_t quarter;    // tiles, L >= 2: bytes of one level-1 low-pass map
+    size_t sub_bytes;  // tiles, L >= 2: the nested call's workspace
     size_t total_bytes;
 };
 
@@ -248,6 +252,44 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
                 wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1,
                                     eb, whole_budget_floats()) == 0;
+    ch->tiles = false;
+    if (!ch->whole && d->levels >= 1 && !env_int("WTCONV_NO_TILES", 0, 0, 1)) {
+        // planes too large for one workgroup: base and level-1 correlations on
+        // tiles (L = 1 partial rows); levels 2..L are the layer with L - 1
+        // levels on the level-1 low-pass maps of x and dy, a nested call
+        static const int shapes[][2] = {{64, 32}, {32, 64}, {32, 32}, {64, 64}, {16, 32}, {32, 16}, {16, 16}};
+        for (const auto &sh : shapes) {
+            if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
+            if (wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
+                                         kFusedThreads, 1, eb, whole_budget_floats()))
+                continue;
+            const int resident = wtc_wgrad_resident(d->dtype, ch->wp);
+            int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 1 << 20);
+            if (!planes) planes = wtc_choose_planes(ch->wp.units, d->c, resident > 0 ? resident : 512, kWgradFixed);
+            wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
+                                     kFusedThreads, planes, eb, whole_budget_floats());
+            ch->tiles = true;
+            break;
+        }
+    }
+    if (ch->tiles) {
+        ch->groups = ch->wp.groups;
+        ch->plen = 5 * kk + 1;
+        ch->part_bytes = align256((size_t)ch->groups * d->c * ch->plen * 4);
+        ch->quarter = ch->sub_bytes = 0;
+        if (d->levels >= 2) {
+            const wtconv_desc_t sd = deeper_desc(d);
+            ch->quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * eb);
+            size_t sub = 0;
+            wtconv_status_t st = wtconv_workspace_size(&sd, WTCONV_OP_BWD_WEIGHT, &sub);
+            if (st != WTCONV_OK) return st;
+            ch->sub_bytes = sub;
+        }
+        // partials | LL(x) | LL(dy) | scratch base gradients (C k^2 + 2C floats) | nested workspace
+        ch->total_bytes = ch->part_bytes + 2 * ch->quarter +
+                          (d->levels >= 2 ? align256((size_t)d->c * (kk + 2) * 4) + ch->sub_bytes : 0);
+        return WTCONV_OK;
+    }
     if (ch->whole) {
         wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1, eb,
                             whole_budget_floats());
@@ -346,6 +388,27 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
     char *ws = (char *)workspace;
     float *partial = (float *)ws;
     hipError_t e = hipSuccess;
+    if (ch.tiles) {
+        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
+        if (e == hipSuccess)
+            e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, 1, ch.groups, ch.plen, partial, w_base, bias,
+                                          s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
+        if (e != hipSuccess) return WTCONV_ERR_HIP;
+        if (desc->levels < 2) return WTCONV_OK;
+        const wtconv_desc_t sd = deeper_desc(desc);
+        char *llx = ws + ch.part_bytes, *lld = llx + ch.quarter;
+        float *scratch = (float *)(lld + ch.quarter);
+        char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
+        if ((e = wtc_launch_lowpass(desc->dtype, x, llx, desc->n * desc->c, (int)desc->h, (int)desc->w, s)) !=
+                hipSuccess ||
+            (e = wtc_launch_lowpass(desc->dtype, dy, lld, desc->n * desc->c, (int)desc->h, (int)desc->w, s)) !=
+                hipSuccess)
+            return WTCONV_ERR_HIP;
+        const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
+        return wtconv_backward_weight(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C,
+                                      scratch, scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk,
+                                      ds_lvl + 4 * C, sub, ch.sub_bytes, stream);
+    }
     if (ch.whole) {
         e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
     } else {

@@ -13,7 +13,7 @@ static __device__ __forceinline__ void wtc_lds_barrier_wg() { asm volatile("s_wa
 // Q: accumulator sets per thread the kernel holds (1, or WTC_WG_QMAX for q = 2..3).
 // With one set (fp32, k <= 5) the kernel is held to 128 VGPRs: two 512-thread workgroups
 // (four waves per SIMD) share a compute unit.
-template <typename T, int K, int VEC, int Q>
+template <typename T, int K, int VEC, int Q, bool TL>
 __global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
@@ -22,7 +22,7 @@ __global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) 
     ctx.tid = threadIdx.x;
     ctx.nth = blockDim.x;
     wtc_wgrad_setup<T, VEC>(a, ctx, blockIdx.x);
-    wtc_wgrad_load<T, VEC>(a, ctx, 0);
+    wtc_wgrad_load<T, VEC, TL>(a, ctx, 0);
     wtc_wgrad_zero<T, VEC>(a, ctx);
     wtc_lds_barrier_wg();
     wtc_wgrad_table<T, K, VEC>(a, ctx);
@@ -32,9 +32,9 @@ __global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) 
 #pragma unroll
         for (int e = 0; e < K * K + 1; ++e) acc[s][e] = 0.0f;
     for (int img = 0; img < ctx.nimg; ++img) {
-        wtc_wgrad_stage<T, K, VEC>(a, ctx);
+        wtc_wgrad_stage<T, K, VEC, TL>(a, ctx);
         wtc_lds_barrier_wg();
-        if (img + 1 < ctx.nimg) wtc_wgrad_load<T, VEC>(a, ctx, img + 1);
+        if (img + 1 < ctx.nimg) wtc_wgrad_load<T, VEC, TL>(a, ctx, img + 1);
         for (int m = a.p.first_deep; m <= a.p.levels; ++m) {
             wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
             wtc_lds_barrier_wg();
@@ -83,11 +83,11 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k
     if (lane == 0) wtc_wgrad_finalize_store(c, g, C, term, ds_base, ds_lvl);
 }
 
-template <typename T, int K, int VEC, int Q>
+template <typename T, int K, int VEC, int Q, bool TL>
 static hipError_t launch_wgrad_q(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC, Q>;
+    const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC, Q, TL>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -97,15 +97,15 @@ static hipError_t launch_wgrad_q(const WtcWgradArgs<T> &a, hipStream_t stream, i
         return hipSuccess;
     }
     const unsigned blocks = (unsigned)(a.p.groups * a.p.c);
-    hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC, Q>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_wgrad_kernel<T, K, VEC, Q, TL>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int K, int VEC>
+template <typename T, int K, int VEC, bool TL = false>
 static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
-    return a.p.q == 1 ? launch_wgrad_q<T, K, VEC, 1>(a, stream, resident)
-                      : launch_wgrad_q<T, K, VEC, WTC_WG_QMAX>(a, stream, resident);
+    return a.p.q == 1 ? launch_wgrad_q<T, K, VEC, 1, TL>(a, stream, resident)
+                      : launch_wgrad_q<T, K, VEC, WTC_WG_QMAX, TL>(a, stream, resident);
 }
 
 template <typename T, int K>
@@ -113,7 +113,9 @@ static hipError_t launch_wgrad_k(const WtcWgradArgs<T> &a, hipStream_t stream, i
 {
     constexpr int VMAX = 16 / sizeof(T);
     switch (a.p.vec) {
-    case VMAX: return launch_wgrad<T, K, VMAX>(a, stream, resident);
+    // tiled plans always stage 16-byte segments
+    case VMAX: return a.p.tiled ? launch_wgrad<T, K, VMAX, true>(a, stream, resident)
+                                : launch_wgrad<T, K, VMAX>(a, stream, resident);
     case VMAX / 2: return launch_wgrad<T, K, VMAX / 2>(a, stream, resident);
     case VMAX / 4: return launch_wgrad<T, K, VMAX / 4>(a, stream, resident);
     default: return launch_wgrad<T, K, 1>(a, stream, resident);

@@ -68,6 +68,15 @@ struct WtcWgradPlan {
     int32_t nchunks[WTC_WG_QMAX];
     int32_t chunk[WTC_WG_QMAX][WTC_WG_CHMAX];
     int32_t mapc[WTC_WG_QMAX][WTC_WG_NMAPS];
+    // Tiling, for planes too large for one workgroup: h x w above is one tile
+    // of an ih x iw image and a unit of work is one (image, tile); the x side
+    // is loaded with lh pixels around the tile (zero outside the image) and
+    // stored from origins that keep the correlation windows on 16-byte
+    // boundaries; the dy side is the tile only; L is 1 (the deeper levels are
+    // a separate call on the level-1 low-pass maps).  Untiled: ih = h, iw = w,
+    // one tile, lh = 0, origins (r, r).
+    int32_t tiled, ih, iw, tiles_x, tiles_y, units;
+    int32_t lh, xr, xc, u1r, u1c;
 };
 
 // stride of one thread's parked accumulators: k*k + 1 rounded up to odd
@@ -80,9 +89,10 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     // read as roundup(P + k - 1, 4) floats from column 4 pc, which stays inside
     // the row: the pitch is roundup(roundup(W, 4) + 2r, 4).
     int32_t off = 0;
+    const int32_t NR = wtc_roundup(P + 2 * r, 4);  // window row, as read
     p->x.off = off;
-    p->x.rows = wtc_roundup(p->h, P) + 2 * r;
-    p->x.pitch = wtc_roundup(wtc_roundup(p->w, P) + 2 * r, 4);
+    p->x.rows = wtc_max(p->lh + p->h + p->xr, wtc_roundup(p->h, P) - P - r + p->xr + P + 2 * r);
+    p->x.pitch = wtc_roundup(wtc_max(p->lh + p->w + p->xc, wtc_roundup(p->w, P) - P - r + p->xc + NR), 4);
     off += p->x.rows * p->x.pitch;
     p->dy.off = off;
     p->dy.rows = wtc_roundup(p->h, P);
@@ -94,9 +104,10 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     }
     for (int32_t m = 1; m <= L; ++m) {
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
+        const int32_t orow = m == 1 ? p->u1r : r, ocol = m == 1 ? p->u1c : r, lm = m == 1 ? p->lh / 2 : 0;
         p->u[m].off = off;
-        p->u[m].rows = wtc_roundup(Hm, P) + 2 * r;
-        p->u[m].pitch = wtc_roundup(wtc_roundup(Wm, P) + 2 * r, 4);
+        p->u[m].rows = wtc_max(lm + Hm + orow, wtc_roundup(Hm, P) - P - r + orow + P + 2 * r);
+        p->u[m].pitch = wtc_roundup(wtc_max(lm + Wm + ocol, wtc_roundup(Wm, P) - P - r + ocol + NR), 4);
         off += 4 * p->u[m].rows * p->u[m].pitch;
         p->d[m].off = off;
         p->d[m].rows = wtc_roundup(Hm, P);
@@ -153,10 +164,11 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     return p->lds_floats;
 }
 
-static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
-                                      int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
-                                      int32_t budget_floats)
+static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
+                                        int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
+                                        int32_t budget_floats, int32_t ih, int32_t iw)
 {
+    const int32_t r = k / 2;
     p->n = n;
     p->c = c;
     p->h = h;
@@ -164,9 +176,17 @@ static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int
     p->k = k;
     p->levels = levels;
     p->nthreads = nthreads;
-    p->planes = planes < 1 ? 1 : (planes > n ? n : planes);
-    p->groups = (n + p->planes - 1) / p->planes;
+    p->tiled = ih != h || iw != w;
+    p->ih = ih;
+    p->iw = iw;
+    if (h < 1 || w < 1 || ih % h || iw % w) return -1;
+    p->tiles_y = ih / h;
+    p->tiles_x = iw / w;
+    p->units = n * p->tiles_y * p->tiles_x;
+    p->planes = planes < 1 ? 1 : (planes > p->units ? p->units : planes);
+    p->groups = (p->units + p->planes - 1) / p->planes;
     if (levels < 0 || levels > WTC_MAXL) return -1;
+    if (p->tiled && levels != 1) return -1;
     if (h % (1 << levels) || w % (1 << levels)) return -1;
     if (nthreads % WTC_WG_CH || nthreads > WTC_WG_MAXT) return -1;
     int32_t vec = 16 / elem_bytes;
@@ -174,7 +194,20 @@ static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int
     p->vec = vec;
     p->gr = h % 4 == 0 ? 4 : (h % 2 == 0 ? 2 : 1);
     if (levels >= 1 && (p->gr < 2 || vec < 2)) return -1;
-    p->sgroups = (h / p->gr) * (w / vec);
+    if (p->tiled) {
+        // x loaded with 2r pixels around the tile (level 1's windows need r
+        // level-1 pixels), rounded to whole staging groups and segments
+        if (p->gr != 4 || vec != 16 / elem_bytes) return -1;
+        p->lh = wtc_roundup(wtc_max(2 * r, 1), wtc_max(4, vec));
+        p->xr = p->lh;
+        p->xc = p->lh + r;
+        p->u1r = p->lh / 2;
+        p->u1c = p->lh / 2 + ((r - p->lh / 2) % 4 + 4) % 4;
+    } else {
+        p->lh = 0;
+        p->xr = p->xc = p->u1r = p->u1c = r;
+    }
+    p->sgroups = ((h + 2 * p->lh) / p->gr) * ((w + 2 * p->lh) / vec);
     if (p->sgroups > nthreads) return -1;
     p->first_deep = (levels >= 2 && p->gr == 4 && vec >= 4) ? 3 : 2;
     wtc_wgrad_layout(p);
@@ -182,6 +215,22 @@ static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int
     // descriptor fields: pitches below 256, LDS indexes below 65536
     if (p->x.pitch > 255 || p->dy.pitch > 255 || p->lds_floats > 65535) return -1;
     return p->lds_floats <= budget_floats ? 0 : -1;
+}
+
+static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
+                                      int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
+                                      int32_t budget_floats)
+{
+    return wtc_wgrad_plan_common(p, n, c, h, w, k, levels, nthreads, planes, elem_bytes, budget_floats, h, w);
+}
+
+// Tiled plan: th x tw tiles of ih x iw images, L = 1.
+static inline int wtc_make_wgrad_tile_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
+                                           int32_t th, int32_t tw, int32_t k, int32_t nthreads, int32_t planes,
+                                           int32_t elem_bytes, int32_t budget_floats)
+{
+    if (th == ih && tw == iw) return -1;
+    return wtc_wgrad_plan_common(p, n, c, th, tw, k, 1, nthreads, planes, elem_bytes, budget_floats, ih, iw);
 }
 
 template <typename T>
@@ -199,6 +248,7 @@ struct WtcWgradCtx {
     int c, n0, nimg, group;
     int grow, gcol;  // this thread's staging group
     bool gvalid;
+    int vmask;       // rows of the prefetched group that lie in the image (bit q)
     T prex[4][VEC];
     T prey[4][VEC];
 #ifdef WTC_EMULATE
@@ -259,8 +309,8 @@ WTC_HD WTC_INLINE void wtc_wgrad_setup(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
     ctx.c = bid % p.c;
     ctx.group = bid / p.c;
     ctx.n0 = ctx.group * p.planes;
-    ctx.nimg = wtc_min(p.planes, p.n - ctx.n0);
-    const int g = wtc_min(ctx.tid, p.sgroups - 1), cpr = p.w / VEC;
+    ctx.nimg = wtc_min(p.planes, p.units - ctx.n0);
+    const int g = wtc_min(ctx.tid, p.sgroups - 1), cpr = (p.w + 2 * p.lh) / VEC;
     ctx.grow = g / cpr;
     ctx.gcol = g - ctx.grow * cpr;
     ctx.gvalid = ctx.tid < p.sgroups;
@@ -275,18 +325,46 @@ WTC_HD WTC_INLINE void wtc_wgrad_zero(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
 
 // Loads of this thread's staging group (gr rows of VEC elements) of image
 // `img`, x and dy, into registers; every lane loads a valid group.
-template <typename T, int VEC>
+// TL: tiled plan (units of (image, tile), halo loads with bounds, shifted
+// origins); untiled plans compile without any of it.
+template <typename T, int VEC, bool TL = false>
 WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int img)
 {
     const WtcWgradPlan &p = a.p;
-    const int64_t plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
-    const int64_t e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
+#ifndef WTC_EMULATE
+    // everything in flight was issued a phase or more ago: one wait here keeps
+    // the compiler from draining each load before the next (vmcnt 0 only)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+    int64_t plane, e0;
+    int row0 = 0, col = 0;
+    if constexpr (TL) {
+        const int tiles = p.tiles_x * p.tiles_y, unit = ctx.n0 + img;
+        const int im = unit / tiles, t = unit - im * tiles, ty = t / p.tiles_x;
+        plane = ((int64_t)im * p.c + ctx.c) * ((int64_t)p.ih * p.iw);
+        row0 = ty * p.h - p.lh + p.gr * ctx.grow;
+        col = (t - ty * p.tiles_x) * p.w - p.lh + VEC * ctx.gcol;
+        e0 = plane;
+    } else {
+        plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
+        e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
+    }
+    const bool colok = col >= 0 && col < p.iw;
+    int vm = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (q < p.gr) {
-            const int64_t e = e0 + (int64_t)q * p.w;
+            int64_t e;
+            if constexpr (TL) {
+                const int row = row0 + q;
+                vm |= (colok && row >= 0 && row < p.ih) ? (1 << q) : 0;
+                e = e0 + (int64_t)wtc_min(wtc_max(row, 0), p.ih - 1) * p.iw + wtc_min(wtc_max(col, 0), p.iw - VEC);
+            } else {
+                vm |= 1 << q;
+                e = e0 + (int64_t)q * p.w;
+            }
 #ifdef WTC_EMULATE
-            const int64_t all = (int64_t)p.n * p.c * p.h * p.w;
+            const int64_t all = (int64_t)p.n * p.c * p.ih * p.iw;
             for (int t = 0; t < VEC; ++t) {
                 ctx.prex[q][t] = wtc_chk(a.x, e + t, all, __LINE__);
                 ctx.prey[q][t] = wtc_chk(a.dy, e + t, all, __LINE__);
@@ -314,6 +392,7 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
 #endif
         }
     }
+    ctx.vmask = vm;
 }
 
 // One 2x2 Haar step on four pairs of rows held in registers: out[b][j] for
@@ -335,7 +414,7 @@ WTC_HD WTC_INLINE void wtc_haar_rows(const float (&top)[2 * N], const float (&bo
 // Write the prefetched groups of x (bordered map) and dy, and compute Haar
 // level 1 (and level 2 when the group has 4 rows and at least 4 columns) of
 // both straight from registers.
-template <typename T, int K, int VEC>
+template <typename T, int K, int VEC, bool TL = false>
 WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx)
 {
     constexpr int R = K / 2;
@@ -346,15 +425,35 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < VEC; ++t) {
-            xv[q][t] = q < p.gr ? wtc_to_float(ctx.prex[q][t]) : 0.0f;
-            dv[q][t] = q < p.gr ? wtc_to_float(ctx.prey[q][t]) : 0.0f;
+            const bool ok = q < p.gr && (!TL || ((ctx.vmask >> q) & 1));
+            xv[q][t] = ok ? wtc_to_float(ctx.prex[q][t]) : 0.0f;
+            dv[q][t] = ok ? wtc_to_float(ctx.prey[q][t]) : 0.0f;
         }
-    const int r0 = p.gr * ctx.grow, c0 = VEC * ctx.gcol;
+    // (r0, c0): the group in the loaded region; tiled: (r0 - lh, c0 - lh) in
+    // the tile, dy stored only for groups inside the tile
+    const int lh = TL ? p.lh : 0;
+    const int r0 = p.gr * ctx.grow - lh, c0 = VEC * ctx.gcol - lh;
+    const bool dyin = !TL || (r0 >= 0 && r0 < p.h && c0 >= 0 && c0 < p.w);
+    if constexpr (TL) {
+        // x at the plan's origin; windows start 16-byte aligned, the stores
+        // themselves are 4-byte
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (q < p.gr) {
-            wtc_lds_put<VEC, wtc_align_of(VEC, R)>(ctx, p.x.off + (r0 + q + R) * p.x.pitch + c0 + R, xv[q]);
-            wtc_lds_put<VEC, wtc_align_of(VEC, 0)>(ctx, p.dy.off + (r0 + q) * p.dy.pitch + c0, dv[q]);
+        for (int q = 0; q < 4; ++q)
+            if (q < p.gr)
+#pragma unroll
+                for (int t = 0; t < VEC; ++t) WTC_LDS(ctx, p.x.off + (r0 + q + p.xr) * p.x.pitch + c0 + t + p.xc) = xv[q][t];
+        if (dyin) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < p.gr) wtc_lds_put<VEC, wtc_align_of(VEC, 0)>(ctx, p.dy.off + (r0 + q) * p.dy.pitch + c0, dv[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q < p.gr) {
+                wtc_lds_put<VEC, wtc_align_of(VEC, R)>(ctx, p.x.off + (r0 + q + R) * p.x.pitch + c0 + R, xv[q]);
+                wtc_lds_put<VEC, wtc_align_of(VEC, 0)>(ctx, p.dy.off + (r0 + q) * p.dy.pitch + c0, dv[q]);
+            }
         }
     }
     if constexpr (VEC >= 2) {
@@ -372,9 +471,12 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
                 wtc_haar_rows<H1>(dv[2 * aa], dv[2 * aa + 1], bd);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    wtc_lds_put<H1, wtc_align_of(H1, R)>(ctx, u1.off + b * su + (i + R) * u1.pitch + c0 / 2 + R,
+                    // x side at the level-1 origin (u1r, u1c): (r, r) untiled,
+                    // u1c = r (mod 4) tiled, so the alignment class is the same
+                    const int u1r = TL ? p.u1r : R, u1c = TL ? p.u1c : R;
+                    wtc_lds_put<H1, wtc_align_of(H1, R)>(ctx, u1.off + b * su + (i + u1r) * u1.pitch + c0 / 2 + u1c,
                                                          bx[b]);
-                    wtc_lds_put<H1, wtc_align_of(H1, 0)>(ctx, d1.off + b * sd + i * d1.pitch + c0 / 2, bd[b]);
+                    if (dyin) wtc_lds_put<H1, wtc_align_of(H1, 0)>(ctx, d1.off + b * sd + i * d1.pitch + c0 / 2, bd[b]);
                 }
 #pragma unroll
                 for (int j = 0; j < H1; ++j) {
@@ -457,13 +559,14 @@ WTC_HD WTC_INLINE void wtc_wgrad_table(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
         const int pr = rem / npc, pc = rem - pr * npc;
         int d0, d1, d2;
         if (m == 0) {
-            // x map origin (r, r): element (i0 - r, j0 - r) sits at (i0, j0)
-            d0 = p.x.off + (P * pr) * p.x.pitch + P * pc;
+            // x map origin (xr, xc): element (i0 - r, j0 - r) sits at (i0 - r + xr, j0 - r + xc)
+            d0 = p.x.off + (P * pr - K / 2 + p.xr) * p.x.pitch + P * pc - K / 2 + p.xc;
             d1 = p.dy.off + (P * pr) * p.dy.pitch + P * pc;
             d2 = p.x.pitch | (p.dy.pitch << 16);
         } else {
             const WtcMap ux = p.u[m], ud = p.d[m];
-            d0 = ux.off + b * ux.rows * ux.pitch + (P * pr) * ux.pitch + P * pc;
+            const int orow = m == 1 ? p.u1r : K / 2, ocol = m == 1 ? p.u1c : K / 2;
+            d0 = ux.off + b * ux.rows * ux.pitch + (P * pr - K / 2 + orow) * ux.pitch + P * pc - K / 2 + ocol;
             d1 = ud.off + b * ud.rows * ud.pitch + (P * pr) * ud.pitch + P * pc;
             d2 = ux.pitch | (ud.pitch << 16);
         }

@@ -51,6 +51,8 @@ def _load():
         lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 8 + [vp] * 5 + [ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
+        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 7 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad_tiles.restype = ci
         lib.emu_whole_plan.restype = ci
         lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
         lib.emu_wgrad.restype = ci
@@ -135,6 +137,27 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
     if rc != 0:
         raise ValueError("emu_whole_tiled failed: %d" % rc)
     return out.astype(np.float64)
+
+
+def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32", nthreads=256, planes=1,
+                budget_floats=40960):
+    """Base and level-1 parameter gradients through the emulated tiled
+    weight-gradient pass (w_lvl / s_lvl: level 1 only)."""
+    lib = _load()
+    n, c, ih, iw = x.shape
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    dyin = np.ascontiguousarray(dy, dtype=npdt)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    outs = [np.full((c, k, k), np.nan, np.float32), np.full((c,), np.nan, np.float32),
+            np.full((c,), np.nan, np.float32), np.full((1, 4 * c, k, k), np.nan, np.float32),
+            np.full((1, 4 * c), np.nan, np.float32)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.emu_wgrad_tiles(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, ih, iw, th, tw, k,
+                             *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes, budget_floats)
+    if rc != 0:
+        raise ValueError("emu_wgrad_tiles failed: %d" % rc)
+    return [o.astype(np.float64) for o in outs]
 
 
 def wgrad_plan(n, c, h, w, k, levels, nthreads=256, planes=1, dtype="f32", budget_floats=40960):

@@ -150,7 +150,7 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
     }
 }
 
-template <typename T, int K, int VEC>
+template <typename T, int K, int VEC, bool TL = false>
 static void run_wgrad(const WtcWgradArgs<T> &a)
 {
     const WtcWgradPlan &p = a.p;
@@ -171,13 +171,13 @@ static void run_wgrad(const WtcWgradArgs<T> &a)
             ctx[t].lds_n = p.lds_floats;
             wtc_wgrad_setup<T, VEC>(a, ctx[t], bid);
         }
-        for (int t = 0; t < nth; ++t) wtc_wgrad_load<T, VEC>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_wgrad_load<T, VEC, TL>(a, ctx[t], 0);
         for (int t = 0; t < nth; ++t) wtc_wgrad_zero<T, VEC>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_wgrad_table<T, K, VEC>(a, ctx[t]);
         for (int img = 0; img < ctx[0].nimg; ++img) {
-            for (int t = 0; t < nth; ++t) wtc_wgrad_stage<T, K, VEC>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_stage<T, K, VEC, TL>(a, ctx[t]);
             for (int t = 0; t < nth; ++t)
-                if (img + 1 < ctx[t].nimg) wtc_wgrad_load<T, VEC>(a, ctx[t], img + 1);
+                if (img + 1 < ctx[t].nimg) wtc_wgrad_load<T, VEC, TL>(a, ctx[t], img + 1);
             for (int m = p.first_deep; m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_wgrad_analysis<T, K, VEC>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_wgrad_correlate<T, K, VEC, WTC_WG_QMAX>(a, ctx[t], A(t));
@@ -196,7 +196,12 @@ static void run_wgrad_k(const WtcWgradArgs<T> &a)
 {
     constexpr int VMAX = 16 / sizeof(T);
     switch (a.p.vec) {
-    case VMAX: run_wgrad<T, K, VMAX>(a); break;
+    case VMAX:
+        if (a.p.tiled)
+            run_wgrad<T, K, VMAX, true>(a);
+        else
+            run_wgrad<T, K, VMAX>(a);
+        break;
     case VMAX / 2: run_wgrad<T, K, VMAX / 2>(a); break;
     case VMAX / 4: run_wgrad<T, K, VMAX / 4>(a); break;
     default: run_wgrad<T, K, 1>(a); break;
@@ -337,6 +342,33 @@ int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int
         for (int g = 0; g < 1 + 4 * levels; ++g)
             wtc_wgrad_finalize_one(cc, g, c, k, levels, p.groups, p.plen, partial.data(), w_base, bias, s_base,
                                    w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
+    return 0;
+}
+
+// The tiled weight-gradient pass (base and level-1 correlations on th x tw
+// tiles of ih x iw images, L = 1) on host arrays, with its finalize.
+int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int ih, int iw, int th, int tw, int k,
+                    const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
+                    const float *s_lvl, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                    int nthreads, int planes, int budget_floats)
+{
+    WtcWgradPlan p;
+    if (wtc_make_wgrad_tile_plan(&p, n, c, ih, iw, th, tw, k, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats))
+        return -1;
+    std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
+    int rc;
+    if (dtype == 0) {
+        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial.data(), p};
+        rc = run_wgrad_t<float>(a);
+    } else {
+        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p};
+        rc = run_wgrad_t<_Float16>(a);
+    }
+    if (rc) return rc;
+    for (int cc = 0; cc < c; ++cc)
+        for (int g = 0; g < 5; ++g)
+            wtc_wgrad_finalize_one(cc, g, c, k, 1, p.groups, p.plen, partial.data(), w_base, bias, s_base, w_lvl,
+                                   s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
     return 0;
 }
 

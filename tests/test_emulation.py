@@ -211,3 +211,42 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
         _check(y, ref)
     else:
         assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
+
+
+WGRAD_TILED = [
+    # n, c, h, w, k, th, tw, dtype
+    (2, 2, 64, 64, 5, 32, 16, "f32"),
+    (3, 1, 48, 64, 3, 16, 32, "f32"),
+    (1, 2, 64, 64, 7, 32, 32, "f32"),
+    (2, 2, 64, 128, 5, 32, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", WGRAD_TILED, ids=lambda c: "x".join(map(str, c)))
+def test_emulated_tiled_weight_gradients_levels_0_and_1(orc, case):
+    """Planes too large for one workgroup: base and level-1 parameter gradients
+    from correlations on tiles (x with halos, dy inside the tile)."""
+    n, c, h, w, k, th, tw, dt = case
+    inp = make_inputs(n, c, h, w, k, 1, dtype=dt, seed=h + w + k)
+    got = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, th, tw,
+                          dtype=dt, planes=3, budget_floats=1 << 16)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, 1)
+    for gg, rr in zip(got, ref):
+        assert not np.isnan(gg).any()
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
+
+
+@pytest.mark.parametrize("L", [2, 3, 4])
+def test_deeper_level_gradients_are_the_layer_on_the_low_pass_maps(orc, L):
+    """The decomposition the large-plane weight gradient relies on, checked on
+    the oracle alone: the level-2..L gradients of the layer equal the level
+    gradients of the (L-1)-level layer on the level-1 low-pass maps of x and dy
+    (weights and scales from level 2 on)."""
+    n, c, h, w, k = 2, 3, 32, 32, 5
+    inp = make_inputs(n, c, h, w, k, L, seed=40 + L)
+    full = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    x64, dy64 = inp.x.astype(np.float64), inp.dy.astype(np.float64)
+    sub = orc.backward_weight(_lowpass(x64), _lowpass(dy64), inp.w_base, None, inp.s_base, inp.w_lvl[1:],
+                              inp.s_lvl[1:], k, L - 1)
+    assert np.abs(full[3][1:] - sub[3]).max() <= 1e-12 * (1 + np.abs(full[3]).max())
+    assert np.abs(full[4][1:] - sub[4]).max() <= 1e-12 * (1 + np.abs(full[4]).max())

@@ -54,6 +54,7 @@ def test_small_shapes(orc, case):
 
 
 def test_tiled_path_forced(orc, monkeypatch):
+    """The level-by-level kernel (planes that no tile shape divides)."""
     monkeypatch.setenv("WTCONV_NO_WHOLE", "1")
     n, c, h, w, k, L = 3, 4, 56, 56, 5, 3
     inp = make_inputs(n, c, h, w, k, L, seed=11)
@@ -61,6 +62,25 @@ def test_tiled_path_forced(orc, monkeypatch):
     got = backward_weight(d)
     torch.cuda.synchronize()
     assert_grads_close(got, _oracle(orc, inp, k, L), "f32", "forced tiled")
+
+
+TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
+         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32")]
+
+
+@pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
+def test_tiled_planes_forced(orc, case, monkeypatch):
+    """The path for planes too large for one workgroup, forced on small planes:
+    base and level-1 correlations on tiles, levels 2..L through a nested call
+    on the level-1 low-pass maps of x and dy."""
+    monkeypatch.setenv("WTCONV_NO_WHOLE", "1")
+    n, c, h, w, k, L, dt = case
+    print("case", case, flush=True)
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + k + L)
+    d = DevInputs(inp, dt)
+    got = backward_weight(d)
+    torch.cuda.synchronize()
+    assert_grads_close(got, _oracle(orc, inp, k, L), dt, str(case))
 
 
 def test_deterministic(orc):
