@@ -34,8 +34,12 @@ int env_int(const char *name, int dflt, int lo, int hi)
 
 int lds_budget_floats() { return env_int("WTCONV_LDS_KB", 64, 16, 160) * 1024 / 4; }
 
-// LDS budget of the whole-plane kernel: two workgroups per compute unit.
-int whole_budget_floats() { return env_int("WTCONV_WHOLE_LDS_KB", 80, 8, 160) * 1024 / 4; }
+// LDS budget of the whole-plane kernel: all of a compute unit's 160 KB.  Planes
+// up to 80 KB still run two workgroups per compute unit (the images per
+// workgroup follow the occupancy); larger ones run one rather than being
+// tiled (one per CU measured about 10 % faster than tiles plus a nested call
+// on the 64 x 64 planes of a 128 x 128 layer).  WTCONV_WHOLE_LDS_KB overrides.
+int whole_budget_floats() { return env_int("WTCONV_WHOLE_LDS_KB", 160, 8, 160) * 1024 / 4; }
 
 // Set-up and reduction cost of one workgroup, in units of one image's work
 // (measured on the 56 x 56 and 28 x 28 planes of the stage workloads).
