@@ -111,13 +111,11 @@ static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int
 template <typename T, int K>
 static hipError_t launch_wgrad_k(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
-    constexpr int VMAX = 16 / sizeof(T);
     switch (a.p.vec) {
-    // tiled plans always stage 16-byte segments
-    case VMAX: return a.p.tiled ? launch_wgrad<T, K, VMAX, true>(a, stream, resident)
-                                : launch_wgrad<T, K, VMAX>(a, stream, resident);
-    case VMAX / 2: return launch_wgrad<T, K, VMAX / 2>(a, stream, resident);
-    case VMAX / 4: return launch_wgrad<T, K, VMAX / 4>(a, stream, resident);
+    // tiled plans always stage 4-element segments
+    case 4: return a.p.tiled ? launch_wgrad<T, K, 4, true>(a, stream, resident)
+                             : launch_wgrad<T, K, 4>(a, stream, resident);
+    case 2: return launch_wgrad<T, K, 2>(a, stream, resident);
     default: return launch_wgrad<T, K, 1>(a, stream, resident);
     }
 }

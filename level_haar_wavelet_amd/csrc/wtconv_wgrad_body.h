@@ -189,7 +189,10 @@ static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, i
     if (p->tiled && levels != 1) return -1;
     if (h % (1 << levels) || w % (1 << levels)) return -1;
     if (nthreads % WTC_WG_CH || nthreads > WTC_WG_MAXT) return -1;
-    int32_t vec = 16 / elem_bytes;
+    // 4-element segments in both storage types (16 bytes of fp32, 8 of
+    // fp16): with 8 fp16 per thread the staging's LDS writes from lanes 32
+    // bytes apart conflict twice as often
+    int32_t vec = 16 / elem_bytes < 4 ? 16 / elem_bytes : 4;
     while (vec > 1 && w % vec) vec /= 2;
     p->vec = vec;
     p->gr = h % 4 == 0 ? 4 : (h % 2 == 0 ? 2 : 1);
@@ -197,7 +200,7 @@ static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, i
     if (p->tiled) {
         // x loaded with 2r pixels around the tile (level 1's windows need r
         // level-1 pixels), rounded to whole staging groups and segments
-        if (p->gr != 4 || vec != 16 / elem_bytes) return -1;
+        if (p->gr != 4 || vec != 4) return -1;
         p->lh = wtc_roundup(wtc_max(2 * r, 1), wtc_max(4, vec));
         p->xr = p->lh;
         p->xc = p->lh + r;

@@ -155,12 +155,14 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     if (p->tiled && levels != 1) return -1;
     if (h % (2 << levels) && levels == 0) return -1;
     if (h % (1 << levels) || w % (1 << levels) || w % 2) return -1;
-    // Output blocks of 2 x BW with BW the 16-byte store width (4 fp32, 8
-    // fp16) where the row allows, doubled when blocks would be more than two
+    // Output blocks of 2 x BW with BW = 4 (16-byte fp32 stores, 8-byte fp16
+    // ones) where the row allows, doubled when blocks would be more than two
     // per thread; the kernel stages rows in segments of vec = min(BW, 16-byte
-    // width) elements, a compile-time function of its BW.
+    // width) elements, a compile-time function of its BW.  Wider default
+    // blocks are slower: 8-element fp16 segments put the staging's LDS writes
+    // 32 bytes apart across lanes and double their bank conflicts.
     const int32_t wide = 16 / elem_bytes;
-    int32_t bw = wide < 8 ? wide : 8;
+    int32_t bw = 4;
     while (bw > 2 && w % bw) bw /= 2;
     if (bw < 8 && (h / 2) * (w / bw) > 2 * nthreads && w % (2 * bw) == 0) bw *= 2;
     if (w % bw) return -1;

@@ -194,16 +194,14 @@ static void run_wgrad(const WtcWgradArgs<T> &a)
 template <typename T, int K>
 static void run_wgrad_k(const WtcWgradArgs<T> &a)
 {
-    constexpr int VMAX = 16 / sizeof(T);
     switch (a.p.vec) {
-    case VMAX:
+    case 4:
         if (a.p.tiled)
-            run_wgrad<T, K, VMAX, true>(a);
+            run_wgrad<T, K, 4, true>(a);
         else
-            run_wgrad<T, K, VMAX>(a);
+            run_wgrad<T, K, 4>(a);
         break;
-    case VMAX / 2: run_wgrad<T, K, VMAX / 2>(a); break;
-    case VMAX / 4: run_wgrad<T, K, VMAX / 4>(a); break;
+    case 2: run_wgrad<T, K, 2>(a); break;
     default: run_wgrad<T, K, 1>(a); break;
     }
 }
