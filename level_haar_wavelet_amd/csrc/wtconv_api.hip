@@ -122,18 +122,21 @@ bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp)
 // per tile first); false if none fits or WTCONV_NO_TILES is set.
 bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp)
 {
-    if (d->levels < 1 || env_int("WTCONV_NO_TILES", 0, 0, 1)) return false;
+    if (env_int("WTCONV_NO_TILES", 0, 0, 1)) return false;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    // the tiles carry the base convolution and level 1; deeper levels are the
+    // nested call on the level-1 low-pass map
+    const int tl = d->levels >= 1 ? 1 : 0;
     static const int shapes[][2] = {{64, 32}, {32, 64}, {32, 32}, {64, 64}, {16, 32}, {32, 16}, {16, 16}};
     for (const auto &sh : shapes) {
         if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
-        if (wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, rotate,
-                                     kFusedThreads, 1, eb, whole_budget_floats()))
+        if (wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl,
+                                     rotate, kFusedThreads, 1, eb, whole_budget_floats()))
             continue;
         const int resident = wtc_whole_resident(d->dtype, tp[0]);
         int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
         if (!planes) planes = wtc_choose_planes(tp->units, d->c, resident > 0 ? resident : 512, kWholeFixed);
-        wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, rotate,
+        wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl, rotate,
                                  kFusedThreads, planes, eb, whole_budget_floats());
         return true;
     }
@@ -176,14 +179,11 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     // the whole-plane kernel when a plane fits one workgroup (any L, even
-    // sides for L = 0); else tiles for L >= 1, the row-band kernel for L = 0
-    // and the strip kernel where no tile shape fits
+    // sides for L = 0); else tiles where a tile shape divides the plane; else
+    // the row-band kernel for L = 0 and the strip kernel for L >= 1
     WtcWholePlan wp;
     if (whole_choice(d, rotate, &wp)) {
         e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
-    } else if (d->levels == 0) {
-        e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
-                              (int)d->w, rotate, s);
     } else if (tile_choice(d, rotate, &wp)) {
         const void *low = nullptr;
         if (d->levels >= 2) {
@@ -208,6 +208,9 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
             low = deep;
         }
         e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s, low);
+    } else if (d->levels == 0) {
+        e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
+                              (int)d->w, rotate, s);
     } else {
         WtcFusedPlan p;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
@@ -257,7 +260,9 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
                 wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1,
                                     eb, whole_budget_floats()) == 0;
     ch->tiles = false;
-    if (!ch->whole && d->levels >= 1 && !env_int("WTCONV_NO_TILES", 0, 0, 1)) {
+    // levels carried by the tiles (base and level 1; L = 0: the base alone)
+    const int tl = d->levels >= 1 ? 1 : 0;
+    if (!ch->whole && !env_int("WTCONV_NO_TILES", 0, 0, 1)) {
         // planes too large for one workgroup: base and level-1 correlations on
         // tiles (L = 1 partial rows); levels 2..L are the layer with L - 1
         // levels on the level-1 low-pass maps of x and dy, a nested call
@@ -265,20 +270,20 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
         for (const auto &sh : shapes) {
             if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
             if (wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                         kFusedThreads, 1, eb, whole_budget_floats()))
+                                         tl, kFusedThreads, 1, eb, whole_budget_floats()))
                 continue;
             const int resident = wtc_wgrad_resident(d->dtype, ch->wp);
             int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 1 << 20);
             if (!planes) planes = wtc_choose_planes(ch->wp.units, d->c, resident > 0 ? resident : 512, kWgradFixed);
             wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                     kFusedThreads, planes, eb, whole_budget_floats());
+                                     tl, kFusedThreads, planes, eb, whole_budget_floats());
             ch->tiles = true;
             break;
         }
     }
     if (ch->tiles) {
         ch->groups = ch->wp.groups;
-        ch->plen = 5 * kk + 1;
+        ch->plen = (1 + 4 * tl) * kk + 1;
         ch->part_bytes = align256((size_t)ch->groups * d->c * ch->plen * 4);
         ch->quarter = ch->sub_bytes = 0;
         if (d->levels >= 2) {
@@ -395,8 +400,9 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
     if (ch.tiles) {
         e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
         if (e == hipSuccess)
-            e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, 1, ch.groups, ch.plen, partial, w_base, bias,
-                                          s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
+            e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels >= 1 ? 1 : 0, ch.groups, ch.plen,
+                                          partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
+                                          dw_lvl, ds_lvl, s);
         if (e != hipSuccess) return WTCONV_ERR_HIP;
         if (desc->levels < 2) return WTCONV_OK;
         const wtconv_desc_t sd = deeper_desc(desc);

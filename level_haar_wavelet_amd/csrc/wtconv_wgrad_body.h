@@ -186,7 +186,7 @@ static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, i
     p->planes = planes < 1 ? 1 : (planes > p->units ? p->units : planes);
     p->groups = (p->units + p->planes - 1) / p->planes;
     if (levels < 0 || levels > WTC_MAXL) return -1;
-    if (p->tiled && levels != 1) return -1;
+    if (p->tiled && levels > 1) return -1;
     if (h % (1 << levels) || w % (1 << levels)) return -1;
     if (nthreads % WTC_WG_CH || nthreads > WTC_WG_MAXT) return -1;
     // 4-element segments in both storage types (16 bytes of fp32, 8 of
@@ -227,13 +227,14 @@ static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int
     return wtc_wgrad_plan_common(p, n, c, h, w, k, levels, nthreads, planes, elem_bytes, budget_floats, h, w);
 }
 
-// Tiled plan: th x tw tiles of ih x iw images, L = 1.
+// Tiled plan: th x tw tiles of ih x iw images, L = 1 (base and level-1
+// gradients) or L = 0.
 static inline int wtc_make_wgrad_tile_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
-                                           int32_t th, int32_t tw, int32_t k, int32_t nthreads, int32_t planes,
-                                           int32_t elem_bytes, int32_t budget_floats)
+                                           int32_t th, int32_t tw, int32_t k, int32_t levels, int32_t nthreads,
+                                           int32_t planes, int32_t elem_bytes, int32_t budget_floats)
 {
     if (th == ih && tw == iw) return -1;
-    return wtc_wgrad_plan_common(p, n, c, th, tw, k, 1, nthreads, planes, elem_bytes, budget_floats, ih, iw);
+    return wtc_wgrad_plan_common(p, n, c, th, tw, k, levels, nthreads, planes, elem_bytes, budget_floats, ih, iw);
 }
 
 template <typename T>

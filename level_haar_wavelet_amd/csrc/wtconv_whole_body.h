@@ -152,7 +152,7 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     // L = 0 (a plain depthwise convolution) needs even sides: the staging and
     // output passes work on 2-row groups and blocks
     if (levels < 0 || levels > WTC_MAXL) return -1;
-    if (p->tiled && levels != 1) return -1;
+    if (p->tiled && levels > 1) return -1;
     if (h % (2 << levels) && levels == 0) return -1;
     if (h % (1 << levels) || w % (1 << levels) || w % 2) return -1;
     // Output blocks of 2 x BW with BW = 4 (16-byte fp32 stores, 8-byte fp16
@@ -201,14 +201,15 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
 }
 
 // Tiled plan: th x tw tiles of ih x iw images, L = 1 (plus the added low-pass
-// term of the deeper levels).
+// term of the deeper levels) or L = 0 (a plain depthwise convolution).
 static inline int wtc_make_whole_tile_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
-                                           int32_t th, int32_t tw, int32_t k, int32_t rotate, int32_t nthreads,
-                                           int32_t planes, int32_t elem_bytes, int32_t budget_floats)
+                                           int32_t th, int32_t tw, int32_t k, int32_t levels, int32_t rotate,
+                                           int32_t nthreads, int32_t planes, int32_t elem_bytes,
+                                           int32_t budget_floats)
 {
     if (th == ih && tw == iw) return -1;
-    return wtc_whole_plan_common(p, n, c, th, tw, k, 1, rotate, nthreads, planes, elem_bytes, budget_floats, ih,
-                                 iw);
+    return wtc_whole_plan_common(p, n, c, th, tw, k, levels, rotate, nthreads, planes, elem_bytes, budget_floats,
+                                 ih, iw);
 }
 
 template <typename T>

@@ -48,10 +48,10 @@ def _load():
         lib.emu_fused_plan.restype = ci
         lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci]
         lib.emu_whole.restype = ci
-        lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 8 + [vp] * 5 + [ci, ci, ci]
+        lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
-        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 7 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 10 + [ci, ci, ci]
         lib.emu_wgrad_tiles.restype = ci
         lib.emu_whole_plan.restype = ci
         lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
@@ -123,7 +123,8 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
                 budget_floats=40960):
     """Run the tiled whole-plane kernel (base and level-1 convolutions on th x tw
     tiles, plus the deeper levels' low-pass term `low`) on the CPU emulation.
-    w_lvl / s_lvl: the level-1 weights and scales (1, 4C, k, k) / (1, 4C)."""
+    w_lvl / s_lvl: the level-1 weights and scales (1, 4C, k, k) / (1, 4C), or
+    None for L = 0 (the base convolution alone)."""
     lib = _load()
     n, c, ih, iw = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -132,8 +133,9 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
     out = np.full_like(xin, np.nan)
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
+    levels = 0 if w_lvl is None else 1
     rc = lib.emu_whole_tiled(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, ptr(lin), n, c, ih, iw,
-                             th, tw, k, rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats)
+                             th, tw, k, levels, rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats)
     if rc != 0:
         raise ValueError("emu_whole_tiled failed: %d" % rc)
     return out.astype(np.float64)
@@ -142,19 +144,21 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
 def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32", nthreads=256, planes=1,
                 budget_floats=40960):
     """Base and level-1 parameter gradients through the emulated tiled
-    weight-gradient pass (w_lvl / s_lvl: level 1 only)."""
+    weight-gradient pass (w_lvl / s_lvl: level 1 only, or None for L = 0)."""
     lib = _load()
     n, c, ih, iw = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
     xin = np.ascontiguousarray(x, dtype=npdt)
     dyin = np.ascontiguousarray(dy, dtype=npdt)
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    levels = 0 if w_lvl is None else 1
     outs = [np.full((c, k, k), np.nan, np.float32), np.full((c,), np.nan, np.float32),
             np.full((c,), np.nan, np.float32), np.full((1, 4 * c, k, k), np.nan, np.float32),
-            np.full((1, 4 * c), np.nan, np.float32)]
+            np.full((1, 4 * c), np.nan, np.float32)][:3 + 2 * levels]
     ptr = lambda a: None if a is None else a.ctypes.data
+    optr = [o.ctypes.data for o in outs] + [None] * (5 - len(outs))
     rc = lib.emu_wgrad_tiles(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, ih, iw, th, tw, k,
-                             *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes, budget_floats)
+                             levels, *[ptr(a) for a in keep], *optr, nthreads, planes, budget_floats)
     if rc != 0:
         raise ValueError("emu_wgrad_tiles failed: %d" % rc)
     return [o.astype(np.float64) for o in outs]

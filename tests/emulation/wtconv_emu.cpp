@@ -346,12 +346,13 @@ int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int
 // The tiled weight-gradient pass (base and level-1 correlations on th x tw
 // tiles of ih x iw images, L = 1) on host arrays, with its finalize.
 int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int ih, int iw, int th, int tw, int k,
-                    const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
+                    int levels, const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
                     const float *s_lvl, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
                     int nthreads, int planes, int budget_floats)
 {
     WtcWgradPlan p;
-    if (wtc_make_wgrad_tile_plan(&p, n, c, ih, iw, th, tw, k, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats))
+    if (wtc_make_wgrad_tile_plan(&p, n, c, ih, iw, th, tw, k, levels, nthreads, planes, dtype == 0 ? 4 : 2,
+                                 budget_floats))
         return -1;
     std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
     int rc;
@@ -364,8 +365,8 @@ int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int 
     }
     if (rc) return rc;
     for (int cc = 0; cc < c; ++cc)
-        for (int g = 0; g < 5; ++g)
-            wtc_wgrad_finalize_one(cc, g, c, k, 1, p.groups, p.plen, partial.data(), w_base, bias, s_base, w_lvl,
+        for (int g = 0; g < 1 + 4 * levels; ++g)
+            wtc_wgrad_finalize_one(cc, g, c, k, levels, p.groups, p.plen, partial.data(), w_base, bias, s_base, w_lvl,
                                    s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
     return 0;
 }
@@ -422,11 +423,11 @@ int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, 
 // The tiled whole-plane pass (L = 1 plus the deeper levels' low-pass term
 // `low`, (N, C, ih/2, iw/2), or null) on host arrays.
 int emu_whole_tiled(int dtype, const void *in, void *out, const void *low, int n, int c, int ih, int iw, int th,
-                    int tw, int k, int rotate, const float *w_base, const float *bias, const float *s_base,
+                    int tw, int k, int levels, int rotate, const float *w_base, const float *bias, const float *s_base,
                     const float *w_lvl, const float *s_lvl, int nthreads, int planes, int budget_floats)
 {
     WtcWholePlan p;
-    if (wtc_make_whole_tile_plan(&p, n, c, ih, iw, th, tw, k, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
+    if (wtc_make_whole_tile_plan(&p, n, c, ih, iw, th, tw, k, levels, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
                                  budget_floats))
         return -1;
     if (dtype == 0) {

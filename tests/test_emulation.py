@@ -174,6 +174,8 @@ def _lowpass(a):
 
 TILED = [
     # n, c, h, w, k, L, th, tw, dtype
+    (2, 2, 64, 64, 7, 0, 32, 32, "f32"),
+    (1, 3, 32, 64, 5, 0, 16, 32, "f16"),
     (2, 2, 64, 64, 5, 1, 32, 16, "f32"),
     (1, 2, 64, 96, 5, 3, 32, 32, "f32"),
     (2, 1, 48, 64, 3, 2, 16, 32, "f32"),
@@ -201,7 +203,8 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
             low = orc.forward(ll, inp.w_base, None, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
         else:
             low = orc.backward_data(ll, inp.w_base, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
-    y = emu.whole_tiled(src, low, inp.w_base, inp.bias, inp.s_base, inp.w_lvl[:1], inp.s_lvl[:1], k, th, tw,
+    wl1, sl1 = (inp.w_lvl[:1], inp.s_lvl[:1]) if L else (None, None)
+    y = emu.whole_tiled(src, low, inp.w_base, inp.bias, inp.s_base, wl1, sl1, k, th, tw,
                         rotate=rotate, dtype=dt, planes=3, budget_floats=1 << 16)
     if rotate == 0:
         ref = orc.forward(src, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
@@ -214,23 +217,27 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
 
 
 WGRAD_TILED = [
-    # n, c, h, w, k, th, tw, dtype
-    (2, 2, 64, 64, 5, 32, 16, "f32"),
-    (3, 1, 48, 64, 3, 16, 32, "f32"),
-    (1, 2, 64, 64, 7, 32, 32, "f32"),
-    (2, 2, 64, 128, 5, 32, 64, "f16"),
+    # n, c, h, w, k, L (0 or 1), th, tw, dtype
+    (2, 2, 64, 64, 5, 1, 32, 16, "f32"),
+    (3, 1, 48, 64, 3, 1, 16, 32, "f32"),
+    (1, 2, 64, 64, 7, 1, 32, 32, "f32"),
+    (2, 2, 64, 128, 5, 1, 32, 64, "f16"),
+    (2, 2, 64, 64, 7, 0, 32, 32, "f32"),
+    (1, 3, 32, 64, 5, 0, 16, 32, "f16"),
 ]
 
 
 @pytest.mark.parametrize("case", WGRAD_TILED, ids=lambda c: "x".join(map(str, c)))
 def test_emulated_tiled_weight_gradients_levels_0_and_1(orc, case):
     """Planes too large for one workgroup: base and level-1 parameter gradients
-    from correlations on tiles (x with halos, dy inside the tile)."""
-    n, c, h, w, k, th, tw, dt = case
-    inp = make_inputs(n, c, h, w, k, 1, dtype=dt, seed=h + w + k)
-    got = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, th, tw,
+    from correlations on tiles (x with halos, dy inside the tile); L = 0 is a
+    plain depthwise convolution's gradients."""
+    n, c, h, w, k, L, th, tw, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + k)
+    wl, sl = (inp.w_lvl, inp.s_lvl) if L else (None, None)
+    got = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, wl, sl, k, th, tw,
                           dtype=dt, planes=3, budget_floats=1 << 16)
-    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, 1)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, wl, sl, k, L)
     for gg, rr in zip(got, ref):
         assert not np.isnan(gg).any()
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6

@@ -65,7 +65,8 @@ def test_tiled_path_forced(orc, monkeypatch):
 
 
 TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
-         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32")]
+         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32"),
+         (2, 3, 64, 64, 7, 0, "f32"), (1, 4, 32, 64, 5, 0, "f16")]  # L = 0: a depthwise conv on tiles
 
 
 @pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
