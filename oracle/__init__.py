@@ -148,21 +148,23 @@ def backward_weight(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, nthrea
 
 
 def level_outputs(xplane, wl_c, sl_c, k, levels):
-    """Scaled band outputs Z_l^b of one plane: list over l of arrays (4, H>>l, W>>l)."""
+    """Scaled band outputs Z_l^b of one plane: list over l of arrays
+    (4, ceil(H / 2^l), ceil(W / 2^l))."""
     lib = _load()
     h, w = xplane.shape
     xd, px = _d(xplane)
     wd, pw = _d(np.reshape(wl_c, (levels, 4, k, k)))
     sd, ps = _d(np.reshape(sl_c, (levels, 4)))
-    total = sum(4 * (h >> l) * (w >> l) for l in range(1, levels + 1))
+    dim = lambda n, l: -(-n // (1 << l))
+    total = sum(4 * dim(h, l) * dim(w, l) for l in range(1, levels + 1))
     z = np.empty(total)
     rc = lib.oracle_wtconv_level_outputs(h, w, k, levels, px, pw, ps,
                                          z.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     _check(rc, "oracle_wtconv_level_outputs")
     out, off = [], 0
     for l in range(1, levels + 1):
-        m = 4 * (h >> l) * (w >> l)
-        out.append(z[off:off + m].reshape(4, h >> l, w >> l))
+        m = 4 * dim(h, l) * dim(w, l)
+        out.append(z[off:off + m].reshape(4, dim(h, l), dim(w, l)))
         off += m
     del xd, wd, sd
     return out

@@ -55,7 +55,11 @@
  *     ([method 3]);
  *   - every convolution is a cross-correlation with zero 'same' padding and
  *     stride 1 at the resolution of its own level; k is odd;
- *   - H and W must be divisible by 2^L.
+ *   - a map with an odd side is padded with one zero row at the bottom and/or
+ *     one zero column at the right before its Haar analysis, and the synthesis
+ *     of that level is cropped back to the map's size, so level l is
+ *     ceil(H / 2^l) x ceil(W / 2^l) (when 2^L divides H and W nothing is
+ *     padded).
  *
  * Parameter layout (all double here):
  *   w_base [C][k][k], bias [C] (may be NULL = zero), s_base [C],
@@ -74,20 +78,32 @@
 /* Building blocks on one (h x w) map                                         */
 /* ------------------------------------------------------------------------ */
 
-/* One level of the 2D Haar analysis [method 1].  in is h x w (both even); each
- * 2x2 block (a b / c d) gives one coefficient in each of the four bands:
+/* Side of a level-l map of an h-pixel side: ceil(h / 2^l) (an odd side is
+ * padded by one zero before each analysis). */
+static int64_t lvl_dim(int64_t h, int l) { return (h + ((int64_t)1 << l) - 1) >> l; }
+
+/* Pixel (i, j) of an h x w map, zero outside it (the zero padding of an odd
+ * side). */
+static double px(const double *in, int64_t h, int64_t w, int64_t i, int64_t j)
+{
+    return (i < h && j < w) ? in[i * w + j] : 0.0;
+}
+
+/* One level of the 2D Haar analysis [method 1].  in is h x w; each 2x2 block
+ * (a b / c d) gives one coefficient in each of the four bands:
  *   band 0 = (a+b+c+d)/2, band 1 = (a+b-c-d)/2, band 2 = (a-b+c-d)/2,
  *   band 3 = (a-b-c+d)/2.
- * out holds the 4 bands one after another, each (h/2) x (w/2). */
+ * out holds the 4 bands one after another, each ceil(h/2) x ceil(w/2); pixels
+ * past an odd side count as zero. */
 static void haar_analysis(const double *in, int64_t h, int64_t w, double *out)
 {
-    int64_t h2 = h / 2, w2 = w / 2, m = h2 * w2;
+    int64_t h2 = lvl_dim(h, 1), w2 = lvl_dim(w, 1), m = h2 * w2;
     for (int64_t i = 0; i < h2; i++) {
         for (int64_t j = 0; j < w2; j++) {
-            double a = in[(2 * i) * w + 2 * j];
-            double b = in[(2 * i) * w + 2 * j + 1];
-            double c = in[(2 * i + 1) * w + 2 * j];
-            double d = in[(2 * i + 1) * w + 2 * j + 1];
+            double a = px(in, h, w, 2 * i, 2 * j);
+            double b = px(in, h, w, 2 * i, 2 * j + 1);
+            double c = px(in, h, w, 2 * i + 1, 2 * j);
+            double d = px(in, h, w, 2 * i + 1, 2 * j + 1);
             out[0 * m + i * w2 + j] = 0.5 * (a + b + c + d);
             out[1 * m + i * w2 + j] = 0.5 * (a + b - c - d);
             out[2 * m + i * w2 + j] = 0.5 * (a - b + c - d);
@@ -97,11 +113,12 @@ static void haar_analysis(const double *in, int64_t h, int64_t w, double *out)
 }
 
 /* Adjoint of haar_analysis: each band coefficient is scattered back onto its
- * 2x2 block with the same +-1/2 weights it was gathered with.  out is h x w
+ * 2x2 block with the same +-1/2 weights it was gathered with; what falls on the
+ * zero padding is dropped (the adjoint of padding is cropping).  out is h x w
  * and is overwritten. */
 static void haar_analysis_adjoint(const double *bands, int64_t h, int64_t w, double *out)
 {
-    int64_t h2 = h / 2, w2 = w / 2, m = h2 * w2;
+    int64_t h2 = lvl_dim(h, 1), w2 = lvl_dim(w, 1), m = h2 * w2;
     memset(out, 0, (size_t)(h * w) * sizeof(double));
     for (int64_t i = 0; i < h2; i++) {
         for (int64_t j = 0; j < w2; j++) {
@@ -109,51 +126,56 @@ static void haar_analysis_adjoint(const double *bands, int64_t h, int64_t w, dou
             double g1 = bands[1 * m + i * w2 + j];
             double g2 = bands[2 * m + i * w2 + j];
             double g3 = bands[3 * m + i * w2 + j];
+            int row1 = 2 * i + 1 < h, col1 = 2 * j + 1 < w;
             /* a: coefficient +1/2 in all four bands */
             out[(2 * i) * w + 2 * j] += 0.5 * g0 + 0.5 * g1 + 0.5 * g2 + 0.5 * g3;
             /* b: +, +, -, - */
-            out[(2 * i) * w + 2 * j + 1] += 0.5 * g0 + 0.5 * g1 - 0.5 * g2 - 0.5 * g3;
+            if (col1) out[(2 * i) * w + 2 * j + 1] += 0.5 * g0 + 0.5 * g1 - 0.5 * g2 - 0.5 * g3;
             /* c: +, -, +, - */
-            out[(2 * i + 1) * w + 2 * j] += 0.5 * g0 - 0.5 * g1 + 0.5 * g2 - 0.5 * g3;
+            if (row1) out[(2 * i + 1) * w + 2 * j] += 0.5 * g0 - 0.5 * g1 + 0.5 * g2 - 0.5 * g3;
             /* d: +, -, -, + */
-            out[(2 * i + 1) * w + 2 * j + 1] += 0.5 * g0 - 0.5 * g1 - 0.5 * g2 + 0.5 * g3;
+            if (row1 && col1) out[(2 * i + 1) * w + 2 * j + 1] += 0.5 * g0 - 0.5 * g1 - 0.5 * g2 + 0.5 * g3;
         }
     }
 }
 
 /* One level of the Haar synthesis (the inverse of haar_analysis, which is an
  * orthogonal map, so the synthesis is the transposed analysis) [method 2].
- * bands: 4 maps of h2 x w2; out: (2 h2) x (2 w2), overwritten.  The pixel at
- * row parity p and column parity q of block (i, j) is
+ * bands: 4 maps of h2 x w2, the analysis of an h x w map (h2 = ceil(h/2),
+ * w2 = ceil(w/2)); out: h x w, overwritten, i.e. the (2 h2) x (2 w2)
+ * reconstruction cropped back to the analysed map.  The pixel at row parity p
+ * and column parity q of block (i, j) is
  *   (band0 + (-1)^p band1 + (-1)^q band2 + (-1)^(p+q) band3) / 2. */
-static void haar_synthesis(const double *bands, int64_t h2, int64_t w2, double *out)
+static void haar_synthesis(const double *bands, int64_t h2, int64_t w2, int64_t h, int64_t w, double *out)
 {
-    int64_t m = h2 * w2, w = 2 * w2;
+    int64_t m = h2 * w2;
     for (int64_t i = 0; i < h2; i++) {
         for (int64_t j = 0; j < w2; j++) {
             double b0 = bands[0 * m + i * w2 + j];
             double b1 = bands[1 * m + i * w2 + j];
             double b2 = bands[2 * m + i * w2 + j];
             double b3 = bands[3 * m + i * w2 + j];
+            int row1 = 2 * i + 1 < h, col1 = 2 * j + 1 < w;
             out[(2 * i) * w + 2 * j] = 0.5 * (b0 + b1 + b2 + b3);
-            out[(2 * i) * w + 2 * j + 1] = 0.5 * (b0 + b1 - b2 - b3);
-            out[(2 * i + 1) * w + 2 * j] = 0.5 * (b0 - b1 + b2 - b3);
-            out[(2 * i + 1) * w + 2 * j + 1] = 0.5 * (b0 - b1 - b2 + b3);
+            if (col1) out[(2 * i) * w + 2 * j + 1] = 0.5 * (b0 + b1 - b2 - b3);
+            if (row1) out[(2 * i + 1) * w + 2 * j] = 0.5 * (b0 - b1 + b2 - b3);
+            if (row1 && col1) out[(2 * i + 1) * w + 2 * j + 1] = 0.5 * (b0 - b1 - b2 + b3);
         }
     }
 }
 
 /* Adjoint of haar_synthesis: gathers the gradient of the four pixels of each
- * block back into the four band coefficients with the synthesis weights. */
-static void haar_synthesis_adjoint(const double *g, int64_t h2, int64_t w2, double *bands)
+ * block back into the four band coefficients with the synthesis weights; g is
+ * h x w, and the pixels the crop removed contribute zero. */
+static void haar_synthesis_adjoint(const double *g, int64_t h2, int64_t w2, int64_t h, int64_t w, double *bands)
 {
-    int64_t m = h2 * w2, w = 2 * w2;
+    int64_t m = h2 * w2;
     for (int64_t i = 0; i < h2; i++) {
         for (int64_t j = 0; j < w2; j++) {
-            double ga = g[(2 * i) * w + 2 * j];       /* p=0, q=0 */
-            double gb = g[(2 * i) * w + 2 * j + 1];   /* p=0, q=1 */
-            double gc = g[(2 * i + 1) * w + 2 * j];   /* p=1, q=0 */
-            double gd = g[(2 * i + 1) * w + 2 * j + 1]; /* p=1, q=1 */
+            double ga = px(g, h, w, 2 * i, 2 * j);         /* p=0, q=0 */
+            double gb = px(g, h, w, 2 * i, 2 * j + 1);     /* p=0, q=1 */
+            double gc = px(g, h, w, 2 * i + 1, 2 * j);     /* p=1, q=0 */
+            double gd = px(g, h, w, 2 * i + 1, 2 * j + 1); /* p=1, q=1 */
             bands[0 * m + i * w2 + j] = 0.5 * (ga + gb + gc + gd);
             bands[1 * m + i * w2 + j] = 0.5 * (ga + gb - gc - gd);
             bands[2 * m + i * w2 + j] = 0.5 * (ga - gb + gc - gd);
@@ -259,8 +281,8 @@ static void gather_params(chan_params *p, int64_t C, int64_t c, int k, int level
     }
 }
 
-/* Sizes of the level maps: level l is (h >> l) x (w >> l). */
-static int64_t map_elems(int64_t h, int64_t w, int l) { return (h >> l) * (w >> l); }
+/* Sizes of the level maps: level l is ceil(h / 2^l) x ceil(w / 2^l). */
+static int64_t map_elems(int64_t h, int64_t w, int l) { return lvl_dim(h, l) * lvl_dim(w, l); }
 
 /* Offsets into one buffer holding, for l = 1..L, the 4 band maps of level l. */
 static int64_t level_offset(int64_t h, int64_t w, int l)
@@ -282,8 +304,8 @@ static void plane_analysis(const chan_params *p, int64_t h, int64_t w, const dou
     int64_t kk = (int64_t)k * k;
     const double *ll = x;
     for (int l = 1; l <= p->levels; l++) {
-        int64_t hp = h >> (l - 1), wp = w >> (l - 1);
-        int64_t hl = h >> l, wl = w >> l, m = hl * wl;
+        int64_t hp = lvl_dim(h, l - 1), wp = lvl_dim(w, l - 1);
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l), m = hl * wl;
         double *al = a + level_offset(h, w, l);
         haar_analysis(ll, hp, wp, al);
         if (zc) {
@@ -319,11 +341,12 @@ static void plane_forward(const chan_params *p, int64_t h, int64_t w, const doub
      * R_l = synthesis(Z_l^0 + R_{l+1}, Z_l^1, Z_l^2, Z_l^3). */
     memset(r, 0, (size_t)map_elems(h, w, L) * sizeof(double));
     for (int l = L; l >= 1; l--) {
-        int64_t hl = h >> l, wl = w >> l, m = hl * wl;
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l), m = hl * wl;
+        int64_t hp = lvl_dim(h, l - 1), wp = lvl_dim(w, l - 1);
         double *zl = zc + level_offset(h, w, l);
         for (int64_t i = 0; i < m; i++) zl[i] += r[i]; /* into the low-pass band */
-        haar_synthesis(zl, hl, wl, t);
-        memcpy(r, t, (size_t)(4 * m) * sizeof(double));
+        haar_synthesis(zl, hl, wl, hp, wp, t);          /* cropped to level l-1 */
+        memcpy(r, t, (size_t)(hp * wp) * sizeof(double));
     }
     for (int64_t i = 0; i < hw; i++) y[i] += r[i];
 }
@@ -349,15 +372,15 @@ static void plane_backward_data(const chan_params *p, int64_t h, int64_t w, cons
      * the gradient of its four inputs; the low-pass one is also dR_{l+1}. */
     const double *dr = dy;
     for (int l = 1; l <= L; l++) {
-        int64_t hl = h >> l, wl = w >> l;
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l);
         double *dzl = dz + level_offset(h, w, l);
-        haar_synthesis_adjoint(dr, hl, wl, dzl);
+        haar_synthesis_adjoint(dr, hl, wl, lvl_dim(h, l - 1), lvl_dim(w, l - 1), dzl);
         dr = dzl; /* band 0 map = gradient of R_{l+1} */
     }
 
     /* scaled convs: Z = s * Zc, Zc = W (*) A  ->  dA = adjoint(W)(s * dZ) */
     for (int l = 1; l <= L; l++) {
-        int64_t hl = h >> l, wl = w >> l, m = hl * wl;
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l), m = hl * wl;
         double *dzl = dz + level_offset(h, w, l);
         double *dal = da + level_offset(h, w, l);
         for (int b = 0; b < 4; b++) {
@@ -370,7 +393,7 @@ static void plane_backward_data(const chan_params *p, int64_t h, int64_t w, cons
      * dLL_L = 0; dLL_{l-1} = analysis_adjoint(dA_l with dLL_l added to band 0). */
     memset(dll, 0, (size_t)map_elems(h, w, L) * sizeof(double));
     for (int l = L; l >= 1; l--) {
-        int64_t hp = h >> (l - 1), wp = w >> (l - 1), m = map_elems(h, w, l);
+        int64_t hp = lvl_dim(h, l - 1), wp = lvl_dim(w, l - 1), m = map_elems(h, w, l);
         double *dal = da + level_offset(h, w, l);
         for (int64_t i = 0; i < m; i++) dal[i] += dll[i];
         haar_analysis_adjoint(dal, hp, wp, t);
@@ -412,16 +435,16 @@ static void plane_backward_weight(const chan_params *p, int64_t h, int64_t w, co
     /* gradient at every Z_l (same reverse cascade as the data part) */
     const double *dr = dy;
     for (int l = 1; l <= L; l++) {
-        int64_t hl = h >> l, wl = w >> l;
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l);
         double *dzl = dz + level_offset(h, w, l);
-        haar_synthesis_adjoint(dr, hl, wl, dzl);
+        haar_synthesis_adjoint(dr, hl, wl, lvl_dim(h, l - 1), lvl_dim(w, l - 1), dzl);
         dr = dzl;
     }
 
     /* Z = s * Zc:  ds = sum dZ * Zc;  dW = sum (s dZ) * A(shift) */
     double *gw = g + kk + 2, *gs = g + kk + 2 + (int64_t)L * 4 * kk;
     for (int l = 1; l <= L; l++) {
-        int64_t hl = h >> l, wl = w >> l, m = hl * wl;
+        int64_t hl = lvl_dim(h, l), wl = lvl_dim(w, l), m = hl * wl;
         double *al = a + level_offset(h, w, l);
         double *zl = zc + level_offset(h, w, l);
         double *dzl = dz + level_offset(h, w, l);
@@ -484,7 +507,6 @@ static int check_args(int64_t n, int64_t c, int64_t h, int64_t w, int k, int lev
 {
     if (n < 0 || c < 0 || h < 0 || w < 0) return -1;
     if (k < 1 || (k % 2) == 0 || levels < 0 || levels > 15) return -1;
-    if ((h % ((int64_t)1 << levels)) != 0 || (w % ((int64_t)1 << levels)) != 0) return -1;
     return 0;
 }
 
@@ -593,7 +615,7 @@ int oracle_wtconv_backward_weight(int64_t n, int64_t c, int64_t h, int64_t w, in
 
 /* The scaled per-level band outputs Z_l^b = s_l^b * (W_l^b (*) A_l^b) of one
  * plane, for l = 1..L and b = 0..3, written one after another (level 1 band 0
- * first; each map (h>>l) x (w>>l)).  wl: [L][4][k][k] and sl: [L][4] of this
+ * first; each map ceil(h/2^l) x ceil(w/2^l)).  wl: [L][4][k][k] and sl: [L][4] of this
  * channel.  Lets a test evaluate the closed-form synthesis on the oracle's own
  * band outputs. */
 int oracle_wtconv_level_outputs(int64_t h, int64_t w, int k, int levels, const double *x, const double *wl,
@@ -635,7 +657,7 @@ int oracle_haar_analysis(const double *in, int64_t h, int64_t w, double *bands)
 int oracle_haar_synthesis(const double *bands, int64_t h2, int64_t w2, double *out)
 {
     if (!bands || !out || h2 < 1 || w2 < 1) return -1;
-    haar_synthesis(bands, h2, w2, out);
+    haar_synthesis(bands, h2, w2, 2 * h2, 2 * w2, out);
     return 0;
 }
 

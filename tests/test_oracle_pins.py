@@ -361,7 +361,129 @@ def test_backward_data_by_finite_differences(orc):
 
 def test_rejects_bad_shapes(orc):
     x = np.zeros((1, 1, 12, 12))
-    with pytest.raises(ValueError):
-        orc.forward(x, np.zeros((1, 3, 3)), None, np.ones(1), np.zeros((3, 4, 3, 3)), np.ones((3, 4)), 3, 3)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError):  # even kernel side
         orc.forward(x, np.zeros((1, 4, 4)), None, np.ones(1), None, None, 4, 0)
+    with pytest.raises(ValueError):  # more levels than the oracle keeps
+        orc.forward(x, np.zeros((1, 3, 3)), None, np.ones(1), np.zeros((16, 4, 3, 3)), np.ones((16, 4)), 3, 16)
+
+
+# ---------------------------------------------------------------------------
+# Sides not divisible by 2^L: each odd map is padded with one zero row at the
+# bottom / one zero column at the right before its analysis, and that level's
+# synthesis is cropped back (level l is ceil(H / 2^l) x ceil(W / 2^l))
+# ---------------------------------------------------------------------------
+
+def _padded_blockmean_up(x, f):
+    """Mean over the f x f blocks of x zero-padded at the bottom and right to
+    multiples of f (a block that sticks out still divides by f^2), spread back
+    over its pixels and cropped to x's size."""
+    *lead, h, w = x.shape
+    hp, wp = -(-h // f) * f, -(-w // f) * f
+    xp = np.zeros((*lead, hp, wp))
+    xp[..., :h, :w] = x
+    return _up(_blockmean(xp, f), f)[..., :h, :w]
+
+
+@pytest.mark.parametrize("levels,h,w", [(1, 7, 10), (2, 13, 22), (3, 9, 17), (4, 21, 6), (3, 3, 5)])
+def test_ragged_identity_kernels_give_zero_padded_block_means(orc, levels, h, w):
+    """k = 1, unit level weights, scale a_l on all four bands, no base path: level
+    l reconstructs its (cropped) input map exactly, so y = sum_l a_l times the
+    2^(l-1) block means of x with zeros past the bottom and right edges."""
+    rng = np.random.default_rng(200 + levels + h)
+    n, c = 2, 2
+    x = rng.standard_normal((n, c, h, w))
+    a = rng.uniform(0.5, 2.0, size=levels)
+    wl = np.ones((levels, 4 * c, 1, 1))
+    sl = np.repeat(a[:, None], 4 * c, axis=1)
+    y = orc.forward(x, np.ones((c, 1, 1)), None, np.zeros(c), wl, sl, 1, levels)
+    ref = sum(a[l - 1] * _padded_blockmean_up(x, 2 ** (l - 1)) for l in range(1, levels + 1))
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("levels,h,w", [(1, 7, 10), (2, 13, 22), (3, 9, 17), (3, 5, 3)])
+def test_ragged_lowpass_only_gives_zero_padded_block_means(orc, levels, h, w):
+    """Only the low-pass band scaled: y = sum_l a_l times the 2^l block means of
+    the zero-padded x (the padding of every level is where the closed form puts
+    it: bottom and right, blocks anchored at the top-left corner)."""
+    rng = np.random.default_rng(210 + levels + w)
+    n, c = 1, 3
+    x = rng.standard_normal((n, c, h, w))
+    a = rng.uniform(0.5, 2.0, size=levels)
+    wl = np.ones((levels, 4 * c, 1, 1))
+    sl = np.zeros((levels, 4 * c))
+    sl[:, 0::4] = a[:, None]
+    y = orc.forward(x, np.ones((c, 1, 1)), None, np.zeros(c), wl, sl, 1, levels)
+    ref = sum(a[l - 1] * _padded_blockmean_up(x, 2 ** l) for l in range(1, levels + 1))
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("k,L,h,w", [(3, 2, 7, 10), (5, 3, 9, 5), (3, 3, 3, 6)])
+def test_ragged_dense_matrix_forward_and_backward_data(orc, k, L, h, w):
+    """Brute force on ragged planes: dx is the transpose of the probed forward
+    matrix, and that transpose is the layer with 180-degree kernels."""
+    rng = np.random.default_rng(220 + k + h)
+    w0, b0, s0, wl, sl = _rand_params(rng, 1, k, L)
+    M = _dense_matrix(orc, h, w, k, L, w0, s0, wl, sl)
+    x = rng.standard_normal((1, 1, h, w))
+    dy = rng.standard_normal((1, 1, h, w))
+    y = orc.forward(x, w0, b0, s0, wl, sl, k, L)
+    np.testing.assert_allclose(y.reshape(-1), M @ x.reshape(-1) + s0[0] * b0[0], rtol=0, atol=1e-12)
+    dx = orc.backward_data(dy, w0, s0, wl, sl, k, L)
+    np.testing.assert_allclose(dx.reshape(-1), M.T @ dy.reshape(-1), rtol=0, atol=1e-12)
+    Mt = _dense_matrix(orc, h, w, k, L, w0[:, ::-1, ::-1], s0, wl[:, :, ::-1, ::-1], sl)
+    np.testing.assert_allclose(Mt, M.T, rtol=0, atol=1e-12)
+
+
+def test_ragged_parameter_gradients_by_finite_differences(orc):
+    """Every parameter gradient on a ragged plane against exact central
+    differences of the (parameter-wise affine) loss <dy, y>."""
+    rng = np.random.default_rng(230)
+    n, c, h, w, k, L = 2, 2, 7, 11, 3, 2
+    x = rng.standard_normal((n, c, h, w))
+    dy = rng.standard_normal((n, c, h, w))
+    params = list(_rand_params(rng, c, k, L))
+    grads = orc.backward_weight(x, dy, *params, k, L)
+
+    def loss(p):
+        return float((orc.forward(x, *p, k, L) * dy).sum())
+
+    for pi, g in enumerate(grads):
+        flat = params[pi].reshape(-1)
+        fd = np.empty(flat.size)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + 0.5
+            lp = loss(params)
+            flat[i] = old - 0.5
+            lm = loss(params)
+            flat[i] = old
+            fd[i] = lp - lm
+        np.testing.assert_allclose(np.asarray(g).reshape(-1), fd, rtol=0, atol=1e-10 * (1 + np.abs(fd).max()))
+
+
+@pytest.mark.parametrize("k,L,h,w,extra", [(5, 2, 13, 22, 0), (3, 3, 9, 17, 0), (5, 3, 10, 7, 8), (7, 1, 5, 9, 2)])
+def test_ragged_equals_layer_on_zero_padded_input(orc, k, L, h, w, extra):
+    """Padding every odd level map by one zero row / column is the same as
+    padding x once with zeros at the bottom and right to a multiple of 2^L (or
+    further) and cropping: the padded pixels only ever feed outputs that are
+    cropped away, and every level's zero 'same' padding sees zeros either way.
+    So the ragged layer equals the (already pinned) divisible layer on the
+    zero-padded input, cropped; its data backward equals the divisible one on
+    the zero-padded dy, cropped; its parameter gradients are those of the
+    padded pair (x, dy)."""
+    rng = np.random.default_rng(240 + h + w + extra)
+    n, c = 2, 2
+    x = rng.standard_normal((n, c, h, w))
+    dy = rng.standard_normal((n, c, h, w))
+    params = _rand_params(rng, c, k, L)
+    f = 2 ** L
+    hp, wp = -(-h // f) * f + extra, -(-w // f) * f + extra
+    pad = lambda a: np.pad(a, ((0, 0), (0, 0), (0, hp - h), (0, wp - w)))
+    y = orc.forward(x, *params, k, L)
+    np.testing.assert_allclose(y, orc.forward(pad(x), *params, k, L)[:, :, :h, :w], rtol=0, atol=1e-12)
+    w0, _, s0, wl, sl = params
+    dx = orc.backward_data(dy, w0, s0, wl, sl, k, L)
+    np.testing.assert_allclose(dx, orc.backward_data(pad(dy), w0, s0, wl, sl, k, L)[:, :, :h, :w], rtol=0,
+                               atol=1e-12)
+    for g, gp in zip(orc.backward_weight(x, dy, *params, k, L), orc.backward_weight(pad(x), pad(dy), *params, k, L)):
+        np.testing.assert_allclose(g, gp, rtol=1e-12, atol=1e-10)
