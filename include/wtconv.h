@@ -31,7 +31,17 @@
  *                accumulated.  dw/ds are gradients of the raw (unfolded)
  *                weights and scales.
  * Shape rules  n, c, h, w >= 1; k in {1, 3, 5, 7}; 0 <= L <= WTCONV_MAX_LEVELS;
- *              h and w divisible by 2^L and h, w <= WTCONV_MAX_SIDE.
+ *              h, w and their round-up to multiples of 2^L <= WTCONV_MAX_SIDE.
+ * Odd maps     Where 2^L does not divide h or w, every level map with an odd
+ *              side is padded with one zero row (bottom) / column (right)
+ *              before its Haar analysis and that level's synthesis is cropped
+ *              back, so level l is ceil(h / 2^l) x ceil(w / 2^l) (the pages do
+ *              not treat odd sides; this is the reading taken).  The library
+ *              computes it as the layer on copies zero-padded to multiples of
+ *              2^L, cropped, which is the same operator; all three calls then
+ *              need a workspace (two padded activation copies plus the padded
+ *              layer's own workspace).  The unfused baseline requires 2^L to
+ *              divide h and w.
  * fp16 mode    fp16 storage of activations only: every product and sum is fp32,
  *              each output element is rounded once to fp16 (round to nearest
  *              even).
@@ -89,8 +99,10 @@ typedef struct ihipStream_t *wtconv_stream_t;
 
 /* Bytes of device workspace `op` needs for `desc` on the current device.  The
  * forward and the data backward need none when a plane fits one workgroup
- * (or L <= 1); for larger planes with L >= 2 they keep the level-1 low-pass
- * map and the deeper levels' term there.  Errors as for the op itself. */
+ * (or L <= 1) and 2^L divides h and w; for larger planes with L >= 2 they keep
+ * the level-1 low-pass map and the deeper levels' term there, and for sides
+ * 2^L does not divide the zero-padded copies of the input and output.  Errors
+ * as for the op itself. */
 wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op, size_t *bytes);
 
 /* y = WTConv(x).  The per-channel scales are folded into the weights (and the

@@ -64,8 +64,6 @@ wtconv_status_t check_desc(const wtconv_desc_t *d)
     if (d->n < 1 || d->c < 1 || d->h < 1 || d->w < 1) return WTCONV_ERR_SHAPE;
     if (d->h > WTCONV_MAX_SIDE || d->w > WTCONV_MAX_SIDE) return WTCONV_ERR_SHAPE;
     if (d->levels < 0 || d->levels > WTCONV_MAX_LEVELS) return WTCONV_ERR_SHAPE;
-    const int64_t g = (int64_t)1 << d->levels;
-    if (d->h % g || d->w % g) return WTCONV_ERR_SHAPE;
     if (d->k != 1 && d->k != 3 && d->k != 5 && d->k != 7) return WTCONV_ERR_UNSUPPORTED;
     if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_F16) return WTCONV_ERR_UNSUPPORTED;
     if (d->n * d->c > (int64_t)1 << 24) return WTCONV_ERR_SHAPE;  // grid size
@@ -76,6 +74,25 @@ wtconv_status_t check_desc(const wtconv_desc_t *d)
 size_t act_bytes(const wtconv_desc_t *d)
 {
     return (size_t)(d->n * d->c * d->h * d->w) * (d->dtype == WTCONV_F32 ? 4 : 2);
+}
+
+// Sides that 2^L does not divide: the layer is computed on copies zero-padded
+// at the bottom and right to multiples of 2^L (equal to padding every odd level
+// map by one zero before its analysis and cropping that level's synthesis),
+// kept in the workspace ahead of the padded layer's own workspace.
+bool ragged(const wtconv_desc_t *d)
+{
+    const int64_t g = (int64_t)1 << d->levels;
+    return d->h % g || d->w % g;
+}
+
+wtconv_desc_t padded_desc(const wtconv_desc_t *d)
+{
+    const int64_t g = (int64_t)1 << d->levels;
+    wtconv_desc_t s = *d;
+    s.h = (d->h + g - 1) / g * g;
+    s.w = (d->w + g - 1) / g * g;
+    return s;
 }
 
 bool overlaps(const void *a, const void *b, size_t bytes)
@@ -159,6 +176,10 @@ size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t pass_workspace(const wtconv_desc_t *d, int rotate)
 {
+    if (ragged(d)) {
+        const wtconv_desc_t pd = padded_desc(d);
+        return 2 * align256(act_bytes(&pd)) + pass_workspace(&pd, rotate);
+    }
     WtcWholePlan wp;
     if (whole_choice(d, rotate, &wp) || d->levels < 2 || !tile_choice(d, rotate, &wp)) return 0;
     const wtconv_desc_t sd = deeper_desc(d);
@@ -178,6 +199,24 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     if (overlaps(in, out, act_bytes(d))) return WTCONV_ERR_ALIAS;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    if (ragged(d)) {
+        // zero-padded copy in, the padded layer, crop out
+        const wtconv_desc_t pd = padded_desc(d);
+        if ((st = check_desc(&pd)) != WTCONV_OK) return st;
+        const size_t a = align256(act_bytes(&pd)), inner = pass_workspace(&pd, rotate);
+        if (!workspace || workspace_bytes < 2 * a + inner) return WTCONV_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
+        char *ws = (char *)workspace;
+        if (wtc_launch_repack(d->dtype, in, ws, d->n * d->c, (int)d->h, (int)d->w, (int)pd.h, (int)pd.w, s) !=
+            hipSuccess)
+            return WTCONV_ERR_HIP;
+        st = fused_pass(&pd, ws, w_base, bias, s_base, w_lvl, s_lvl, ws + a, rotate, ws + 2 * a, inner, stream);
+        if (st != WTCONV_OK) return st;
+        return wtc_launch_repack(d->dtype, ws + a, out, d->n * d->c, (int)pd.h, (int)pd.w, (int)d->h, (int)d->w,
+                                 s) == hipSuccess
+                   ? WTCONV_OK
+                   : WTCONV_ERR_HIP;
+    }
     // the whole-plane kernel when a plane fits one workgroup (any L, even
     // sides for L = 0); else tiles where a tile shape divides the plane; else
     // the row-band kernel for L = 0 and the strip kernel for L >= 1
@@ -369,8 +408,11 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1); return WTCONV_OK;
     case WTCONV_OP_BWD_WEIGHT: {
         WgradChoice ch;
-        if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
-        *bytes = ch.total_bytes;
+        const wtconv_desc_t pd = padded_desc(desc);
+        if ((st = check_desc(&pd)) != WTCONV_OK) return st;
+        if ((st = choose_wgrad(&pd, &ch)) != WTCONV_OK) return st;
+        // ragged sides: zero-padded copies of x and dy ahead of the padded call's workspace
+        *bytes = (ragged(desc) ? 2 * align256(act_bytes(&pd)) : 0) + ch.total_bytes;
         return WTCONV_OK;
     }
     default: return WTCONV_ERR_UNSUPPORTED;
@@ -389,6 +431,26 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
     if ((st = check_params(desc, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
     if (desc->levels > 0 && (!dw_lvl || !ds_lvl)) return WTCONV_ERR_NULL;
     if (!aligned16(x) || !aligned16(dy)) return WTCONV_ERR_UNSUPPORTED;
+    if (ragged(desc)) {
+        // the gradients of the layer on zero-padded copies of x and dy
+        const wtconv_desc_t pd = padded_desc(desc);
+        if ((st = check_desc(&pd)) != WTCONV_OK) return st;
+        size_t need = 0;
+        if ((st = wtconv_workspace_size(desc, WTCONV_OP_BWD_WEIGHT, &need)) != WTCONV_OK) return st;
+        if (!workspace || workspace_bytes < need) return WTCONV_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
+        const size_t a = align256(act_bytes(&pd));
+        char *ws = (char *)workspace;
+        hipStream_t s = (hipStream_t)stream;
+        const int64_t planes = desc->n * desc->c;
+        if (wtc_launch_repack(desc->dtype, x, ws, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w, s) !=
+                hipSuccess ||
+            wtc_launch_repack(desc->dtype, dy, ws + a, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w,
+                              s) != hipSuccess)
+            return WTCONV_ERR_HIP;
+        return wtconv_backward_weight(&pd, ws, ws + a, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
+                                      dw_lvl, ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream);
+    }
     WgradChoice ch;
     if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
     if (!workspace || workspace_bytes < ch.total_bytes) return WTCONV_ERR_WORKSPACE;

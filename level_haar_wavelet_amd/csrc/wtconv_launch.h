@@ -29,6 +29,11 @@ hipError_t wtc_launch_lowpass(int dtype, const void *in, void *out, int64_t plan
 // n floats set to v (a kernel, so that callers may capture it in a graph).
 hipError_t wtc_launch_fill(float *p, int64_t n, float v, hipStream_t stream);
 
+// The hout x wout window of each of `planes` planes of hin x win: zero-padded
+// (at the bottom and right) or cropped copy.
+hipError_t wtc_launch_repack(int dtype, const void *in, void *out, int64_t planes, int hin, int win, int hout,
+                             int wout, hipStream_t stream);
+
 // Fused parameter-gradient correlations (partials per workgroup) and the
 // fixed-order reduction with the chain rule.
 hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,

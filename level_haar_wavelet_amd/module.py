@@ -22,8 +22,9 @@ __all__ = ["WTConvFunction", "WTConv2d"]
 class WTConvFunction(torch.autograd.Function):
     """y = WTConv(x; w_base, bias, s_base, w_lvl, s_lvl).
 
-    x: (N, C, H, W) float32 or float16, contiguous, on the GPU; H and W
-    divisible by 2^L.  Parameters are float32: w_base (C, k, k), bias (C,) or
+    x: (N, C, H, W) float32 or float16, contiguous, on the GPU (sides 2^L
+    does not divide: odd level maps zero-padded at the bottom / right, each
+    level's synthesis cropped back).  Parameters are float32: w_base (C, k, k), bias (C,) or
     None, s_base (C,), w_lvl (L, 4C, k, k) and s_lvl (L, 4C), or None for
     both when L = 0.
     """

@@ -58,7 +58,6 @@ def _ws(lib, d, op=0):
     ((2, 8, 16, 16, 5, 2, 0), 0),
     ((2, 8, 16, 16, 4, 2, 0), 3),    # even k
     ((2, 8, 16, 16, 9, 2, 0), 3),    # k not built
-    ((2, 8, 18, 16, 5, 2, 0), 2),    # 18 not divisible by 4
     ((2, 8, 16, 16, 5, 7, 0), 2),    # too many levels
     ((2, 8, 16, 16, 5, -1, 0), 2),
     ((0, 8, 16, 16, 5, 2, 0), 2),
@@ -70,6 +69,23 @@ def test_validation(lib, shape, expect):
     assert st == expect
     if expect == 0:
         assert val == 0
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 18, 16, 5, 2, 0), (1, 3, 7, 9, 3, 3, 1), (2, 2, 5, 12, 5, 1, 0)])
+def test_ragged_sides_take_padded_copies_in_the_workspace(lib, shape):
+    """Sides 2^L does not divide are accepted; every op then needs room for
+    two zero-padded activation copies (256-byte aligned) ahead of the padded
+    layer's own workspace."""
+    n, c, h, w, k, L, dt = shape
+    g = 2 ** L
+    hp, wp = -(-h // g) * g, -(-w // g) * g
+    copy = -(-(n * c * hp * wp * (4 if dt == 0 else 2)) // 256) * 256
+    padded = _native.desc(n, c, hp, wp, k, L, dt)
+    for op in (0, 1, 2):
+        st, val = _ws(lib, _native.desc(*shape), op)
+        st_p, val_p = _ws(lib, padded, op)
+        assert st == 0 and st_p == 0
+        assert val == 2 * copy + val_p
 
 
 def test_null_arguments_are_rejected_before_any_launch(lib):
@@ -84,8 +100,14 @@ def test_null_arguments_are_rejected_before_any_launch(lib):
     assert lib.wtconv_forward(ctypes.byref(d), vp(), vp(), None, vp(), None, vp(), ctypes.c_void_p(0x20000),
                               None, 0, None) == 1
     # bad shape wins over anything else
-    bad = _native.desc(2, 8, 18, 16, 5, 2, 0)
+    bad = _native.desc(2, 8, 16, 16, 5, 7, 0)
     assert lib.wtconv_backward_data(ctypes.byref(bad), vp(), vp(), vp(), vp(), vp(), vp(), None, 0, None) == 2
+    # odd sides without the workspace for their padded copies
+    rag = _native.desc(2, 8, 18, 16, 5, 2, 0)
+    assert lib.wtconv_forward(ctypes.byref(rag), vp(), vp(), None, vp(), vp(), vp(), ctypes.c_void_p(0x200000),
+                              None, 0, None) == 4
+    assert lib.wtconv_backward_weight(ctypes.byref(rag), vp(), ctypes.c_void_p(0x200000), vp(), None, vp(), vp(),
+                                      vp(), vp(), vp(), vp(), vp(), vp(), None, 0, None) == 4
 
 
 def test_alias_and_alignment_are_rejected(lib):
@@ -115,7 +137,7 @@ def test_unfused_validation_before_any_launch(lib):
     size = ctypes.c_size_t(0)
     good = _native.desc(2, 3, 16, 16, 5, 2, _native.F32)
     assert lib.wtconv_unfused_workspace_size(ctypes.byref(good), ctypes.byref(size)) == 0 and size.value > 0
-    bad = _native.desc(2, 3, 18, 16, 5, 2, _native.F32)  # 18 not divisible by 4
+    bad = _native.desc(2, 3, 18, 16, 5, 2, _native.F32)  # 18 not divisible by 4 (the baseline needs it)
     assert lib.wtconv_unfused_workspace_size(ctypes.byref(bad), ctypes.byref(size)) == 2
     # null pointers and a short workspace are rejected before anything is launched
     assert lib.wtconv_unfused_forward(ctypes.byref(good), None, None, None, None, None, None, None, None, 0,
