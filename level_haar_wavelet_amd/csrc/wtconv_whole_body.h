@@ -48,6 +48,7 @@ struct WtcWholePlan {
     int32_t out_bw;      // output block width (2, 4 or 8)
     int32_t gr;          // input rows per staging group (2 or 4)
     int32_t groups;      // staging groups per image (one per thread at most)
+    int32_t stage_l3;    // the staging also computes Haar level 3 (2 x 2 groups per lane quad)
     int32_t ws;          // floats per folded kernel (k*k rounded up to 4)
     WtcMap x;            // input with an r border, origin (r, r)
     WtcMap u[WTC_MAXL + 1];   // U_m plus three detail bands, m = 1..L, origin (r, r)
@@ -123,7 +124,10 @@ static inline int32_t wtc_whole_blocks(const WtcWholePlan *p) { return (p->h / 2
 // The staging phase computes Haar level 2 too (4-row groups of at least 4
 // columns); the analysis phase then starts at level 3.
 WTC_HD WTC_INLINE bool wtc_whole_stage_l2(const WtcWholePlan &p) { return p.gr == 4 && p.vec >= 4 && p.levels >= 2; }
-WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p) { return wtc_whole_stage_l2(p) ? 3 : 2; }
+WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p)
+{
+    return p.stage_l3 ? 4 : (wtc_whole_stage_l2(p) ? 3 : 2);
+}
 
 // Plan of the whole-plane kernel on h x w planes (or tiles), or -1 when it
 // does not fit (LDS, per-thread chunk or block limits).  `planes` is the
@@ -185,6 +189,10 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
         p->lh = 0;
         p->xr = p->xc = p->u1r = p->u1c = r;
     }
+    // with L >= 3 and 4 x 4 groups (so 2^3 divides both sides and the group
+    // grid has even sides), the four lanes of a quad take a 2 x 2 block of
+    // groups and compute Haar level 3 from their level-2 sums by lane exchange
+    p->stage_l3 = !p->tiled && levels >= 3 && p->gr == 4 && vec == 4;
     p->groups = ((h + 2 * p->lh) / p->gr) * ((w + 2 * p->lh) / vec);
     if (p->groups > nthreads) return -1;
     if (wtc_whole_blocks(p) > 2 * nthreads) return -1;
@@ -240,6 +248,7 @@ struct WtcWholeCtx {
     int ty0, tx0;  // current unit's tile origin in the image
     int64_t plane;  // current unit's plane index (n * C + c)
     int vmask;     // rows of the prefetched group that lie in the image (bit q)
+    float u2;      // the group's level-2 low-pass sum (for level 3 across the lane quad)
     T pre[4][16 / sizeof(T)];
 #ifdef WTC_EMULATE
     int64_t lds_n, img_n;
@@ -271,8 +280,16 @@ WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     const int gpr = (p.w + 2 * p.lh) / p.vec;
     const int grp = wtc_min(ctx.tid, p.groups - 1);  // threads past the last group repeat it, unstored
     ctx.gvalid = ctx.tid < p.groups;
-    ctx.grow = grp / gpr;
-    ctx.gcol = grp - ctx.grow * gpr;
+    if (p.stage_l3) {
+        // lane quad q takes groups (2 qr + dr, 2 qc + dc), dr, dc from lane bits
+        // 1 and 0 (the group count is a multiple of 4, so quads are whole)
+        const int q = grp >> 2, qr = q / (gpr / 2), qc = q - qr * (gpr / 2);
+        ctx.grow = 2 * qr + ((grp >> 1) & 1);
+        ctx.gcol = 2 * qc + (grp & 1);
+    } else {
+        ctx.grow = grp / gpr;
+        ctx.gcol = grp - ctx.grow * gpr;
+    }
     const int nbx = p.w / p.out_bw, by = ctx.tid / nbx;
     ctx.oblk = (by << 16) | (ctx.tid - by * nbx);
 }
@@ -406,6 +423,22 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     ctx.vmask = vm;
 }
 
+// Haar level 3 of a 2 x 2 block of staging groups from the level-2 sums
+// v[0..3] of its four lanes (top-left, top-right, bottom-left, bottom-right):
+// lane dr dc of the quad writes band 2 dr + dc of the block's level-3 cell.
+template <typename T>
+WTC_HD WTC_INLINE void wtc_whole_stage_l3(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, const float (&v)[4])
+{
+    const WtcWholePlan &p = a.p;
+    const int R = p.k / 2;
+    const WtcMap u3 = p.u[3];
+    const float sa = v[0] + v[1], sc = v[2] + v[3], da = v[0] - v[1], dc = v[2] - v[3];
+    const int band = 2 * (ctx.grow & 1) + (ctx.gcol & 1);
+    const float val = band == 0 ? sa + sc : (band == 1 ? sa - sc : (band == 2 ? da + dc : da - dc));
+    const int o = u3.off + band * u3.rows * u3.pitch + wtc_mul24((ctx.grow >> 1) + R, u3.pitch) + (ctx.gcol >> 1) + R;
+    WTC_LDS(ctx, o) = val;
+}
+
 // Write the prefetched group into the input map and compute Haar level 1
 // (and level 2 when the group has 4 rows) of it straight from registers:
 //   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
@@ -470,8 +503,21 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
             WTC_LDS(ctx, o + st2) = sa - sc;
             WTC_LDS(ctx, o + 2 * st2) = da + dc;
             WTC_LDS(ctx, o + 3 * st2) = da - dc;
+            ctx.u2 = sa + sc;
         }
     }
+#ifndef WTC_EMULATE
+    if (p.stage_l3) {
+        // the quad's four level-2 sums (lanes: top-left, top-right,
+        // bottom-left, bottom-right), broadcast within the quad by DPP
+        float v[4];
+        v[0] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ctx.u2), 0x00, 0xf, 0xf, false));
+        v[1] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ctx.u2), 0x55, 0xf, 0xf, false));
+        v[2] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ctx.u2), 0xaa, 0xf, 0xf, false));
+        v[3] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ctx.u2), 0xff, 0xf, 0xf, false));
+        wtc_whole_stage_l3(a, ctx, v);
+    }
+#endif
 }
 
 // Level-m analysis from U_{m-1} in LDS, for the levels the staging phase did

@@ -95,10 +95,10 @@ def fused(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
 
 
 def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f32", budget_floats=40960):
-    out = (ctypes.c_int * 7)()
+    out = (ctypes.c_int * 8)()
     rc = _load().emu_whole_plan(n, c, h, w, k, levels, rotate, nthreads, planes, 4 if dtype == "f32" else 2,
                                 budget_floats, out)
-    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok")
+    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok", "stage_l3")
     return dict(zip(keys, list(out)))
 
 

@@ -74,6 +74,23 @@ static int run_t(const WtcFusedArgs<T> &a)
     }
 }
 
+// Haar level 3 across lane quads (the kernel exchanges the quad's level-2 sums
+// by DPP right after staging; here every thread has staged first).
+template <typename T>
+static void emu_stage_l3(const WtcWholeArgs<T> &a, std::vector<WtcWholeCtx<T>> &ctx)
+{
+    for (size_t t = 0; t < ctx.size(); ++t) {
+        if (!ctx[t].gvalid) continue;
+        float v[4];
+        for (int j = 0; j < 4; ++j) {
+            const WtcWholeCtx<T> &o = ctx[(t & ~(size_t)3) | (size_t)j];
+            if (!o.gvalid) abort();  // quads are whole
+            v[j] = o.u2;
+        }
+        wtc_whole_stage_l3(a, ctx[t], v);
+    }
+}
+
 template <typename T, int K, int BW, bool TL>
 static void run_whole(const WtcWholeArgs<T> &a)
 {
@@ -102,6 +119,7 @@ static void run_whole(const WtcWholeArgs<T> &a)
         // barrier interval as image i's output pass (here every staging runs
         // first, so a staging write that the output pass reads would show)
         for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
+        if (p.stage_l3) emu_stage_l3(a, ctx);
         for (int t = 0; t < nth; ++t)
             if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL>(a, ctx[t], 1);
         for (int img = 0; img < ctx[0].nimg; ++img) {
@@ -112,6 +130,7 @@ static void run_whole(const WtcWholeArgs<T> &a)
                 if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
                 if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL>(a, ctx[t], img + 2);
             }
+            if (p.stage_l3 && img + 1 < ctx[0].nimg) emu_stage_l3(a, ctx);
             for (int t = 0; t < nth; ++t) {
                 wtc_whole_select<T>(a, ctx[t], img);
                 wtc_whole_out<T, K, BW, TL>(a, ctx[t]);
@@ -401,6 +420,7 @@ int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, in
     out[4] = p.items;
     out[5] = p.nthreads;
     out[6] = rc == 0;
+    out[7] = p.stage_l3;
     return rc;
 }
 

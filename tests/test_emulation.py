@@ -130,6 +130,28 @@ def test_emulated_whole_plane_thread_counts(orc, nthreads, planes):
     _check(y, ref)
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 56, 56, 5, 3, "f32", 512), (2, 2, 48, 16, 3, 4, "f32", 256),
+                                   (1, 2, 16, 40, 7, 3, "f16", 256), (3, 1, 32, 32, 1, 5, "f32", 128)])
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_whole_plane_level3_from_lane_quads(orc, shape, rotate):
+    """L >= 3 with 4 x 4 staging groups: the four lanes of a quad stage a 2 x 2
+    block of groups and build Haar level 3 from their level-2 sums (DPP in
+    the kernel; here after every thread has staged)."""
+    n, c, h, w, k, L, dt, nth = shape
+    assert emu.whole_plan(n, c, h, w, k, L, nthreads=nth, dtype=dt, budget_floats=1 << 16)["stage_l3"] == 1
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + 3 * w + rotate)
+    y = emu.whole(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate, dtype=dt,
+                  nthreads=nth, planes=2, budget_floats=1 << 16)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.x, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    if dt == "f32":
+        _check(y, ref)
+    else:
+        assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
+
+
 @pytest.mark.parametrize("shape", [(2, 3, 16, 16, 5, 2), (1, 2, 28, 28, 5, 2), (1, 2, 24, 40, 3, 3), (1, 1, 32, 64, 7, 4)])
 @pytest.mark.parametrize("rotate", [0, 1])
 def test_emulated_whole_plane_fp16(orc, shape, rotate):
