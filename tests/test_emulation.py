@@ -79,6 +79,8 @@ WGRAD_CASES = [
     (2, 2, 14, 10, 7, 1, "f32", 2),   # staging groups of 2 rows, 2 columns
     (3, 2, 12, 12, 1, 2, "f16", 1),
     (2, 1, 24, 40, 3, 2, "f32", 2),   # odd border width
+    (2, 2, 32, 48, 7, 3, "f32", 2),
+    (2, 1, 32, 32, 1, 5, "f32", 2),
 ]
 
 
