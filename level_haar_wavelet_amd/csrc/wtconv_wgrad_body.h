@@ -260,52 +260,6 @@ struct WtcWgradCtx {
 #endif
 };
 
-// N floats to LDS at an index that is a multiple of A (16-, 8- or 4-byte stores).
-template <int N, int A, typename Ctx>
-WTC_HD WTC_INLINE void wtc_lds_put(Ctx &ctx, int idx, const float (&src)[N])
-{
-#ifdef WTC_EMULATE
-    if (idx % A) {
-        fprintf(stderr, "wtconv emulation: LDS index %d not a multiple of %d\n", idx, A);
-        abort();
-    }
-    for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
-#else
-    if constexpr (A >= 4 && N % 4 == 0) {
-        typedef float v4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-        for (int q = 0; q < N / 4; ++q) {
-            v4 v;
-            v.x = src[4 * q];
-            v.y = src[4 * q + 1];
-            v.z = src[4 * q + 2];
-            v.w = src[4 * q + 3];
-            *(v4 *)&ctx.lds[idx + 4 * q] = v;
-        }
-    } else if constexpr (A >= 2 && N % 2 == 0) {
-        typedef float v2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-        for (int q = 0; q < N / 2; ++q) {
-            v2 v;
-            v.x = src[2 * q];
-            v.y = src[2 * q + 1];
-            *(v2 *)&ctx.lds[idx + 2 * q] = v;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < N; ++e) ctx.lds[idx + e] = src[e];
-    }
-#endif
-}
-
-// largest of 4, 2, 1 dividing both a and b (a, b powers of two or 0 for "any")
-WTC_HD constexpr int wtc_align_of(int a, int b)
-{
-    const int la = a == 0 ? 4 : (a % 4 == 0 ? 4 : (a % 2 == 0 ? 2 : 1));
-    const int lb = b == 0 ? 4 : (b % 4 == 0 ? 4 : (b % 2 == 0 ? 2 : 1));
-    return la < lb ? la : lb;
-}
-
 template <typename T, int VEC>
 WTC_HD WTC_INLINE void wtc_wgrad_setup(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx, int bid)
 {

@@ -423,6 +423,52 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     ctx.vmask = vm;
 }
 
+// N floats to LDS at an index that is a multiple of A (16-, 8- or 4-byte stores).
+template <int N, int A, typename Ctx>
+WTC_HD WTC_INLINE void wtc_lds_put(Ctx &ctx, int idx, const float (&src)[N])
+{
+#ifdef WTC_EMULATE
+    if (idx % A) {
+        fprintf(stderr, "wtconv emulation: LDS index %d not a multiple of %d\n", idx, A);
+        abort();
+    }
+    for (int e = 0; e < N; ++e) WTC_LDS(ctx, idx + e) = src[e];
+#else
+    if constexpr (A >= 4 && N % 4 == 0) {
+        typedef float v4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q) {
+            v4 v;
+            v.x = src[4 * q];
+            v.y = src[4 * q + 1];
+            v.z = src[4 * q + 2];
+            v.w = src[4 * q + 3];
+            *(v4 *)&ctx.lds[idx + 4 * q] = v;
+        }
+    } else if constexpr (A >= 2 && N % 2 == 0) {
+        typedef float v2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+        for (int q = 0; q < N / 2; ++q) {
+            v2 v;
+            v.x = src[2 * q];
+            v.y = src[2 * q + 1];
+            *(v2 *)&ctx.lds[idx + 2 * q] = v;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) ctx.lds[idx + e] = src[e];
+    }
+#endif
+}
+
+// largest of 4, 2, 1 dividing both a and b (a, b powers of two or 0 for "any")
+WTC_HD constexpr int wtc_align_of(int a, int b)
+{
+    const int la = a == 0 ? 4 : (a % 4 == 0 ? 4 : (a % 2 == 0 ? 2 : 1));
+    const int lb = b == 0 ? 4 : (b % 4 == 0 ? 4 : (b % 2 == 0 ? 2 : 1));
+    return la < lb ? la : lb;
+}
+
 // Haar level 3 of a 2 x 2 block of staging groups from the level-2 sums
 // v[0..3] of its four lanes (top-left, top-right, bottom-left, bottom-right):
 // lane dr dc of the quad writes band 2 dr + dc of the block's level-3 cell.
@@ -464,11 +510,12 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     const int u1r = TL ? p.u1r : R, u1c = TL ? p.u1c : R;
     const int r0 = p.gr * ctx.grow, c0 = vec * ctx.gcol;
     const int xo = xm.off + wtc_mul24(r0 - lh + xr, xm.pitch) + c0 - lh + xc;
+    // the x map's origin column is r (mod 4) and c0 a multiple of vec: 8-byte
+    // stores for even r (two per 4-element row: half the bank conflicts of
+    // 4-byte stores from lanes 16 bytes apart)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        if (q < p.gr)
-#pragma unroll
-            for (int t = 0; t < vec; ++t) WTC_LDS(ctx, xo + wtc_mul24(q, xm.pitch) + t) = x[q][t];
+        if (q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
     if (p.levels < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
@@ -476,18 +523,22 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     for (int aa = 0; aa < 2; ++aa) {
         if (2 * aa < p.gr) {
             const int i = (r0 - lh) / 2 + aa;
+            float bnd[4][h1];
 #pragma unroll
             for (int bb = 0; bb < h1; ++bb) {
                 const float x00 = x[2 * aa][2 * bb], x01 = x[2 * aa][2 * bb + 1];
                 const float x10 = x[2 * aa + 1][2 * bb], x11 = x[2 * aa + 1][2 * bb + 1];
                 const float sa = x00 + x01, sc = x10 + x11, da = x00 - x01, dc = x10 - x11;
-                const int o = u1.off + wtc_mul24(i + u1r, u1.pitch) + (c0 - lh) / 2 + bb + u1c;
                 ll[aa][bb] = sa + sc;
-                WTC_LDS(ctx, o) = sa + sc;
-                WTC_LDS(ctx, o + st1) = sa - sc;
-                WTC_LDS(ctx, o + 2 * st1) = da + dc;
-                WTC_LDS(ctx, o + 3 * st1) = da - dc;
+                bnd[0][bb] = sa + sc;
+                bnd[1][bb] = sa - sc;
+                bnd[2][bb] = da + dc;
+                bnd[3][bb] = da - dc;
             }
+            // origin column u1c = r (mod 4), (c0 - lh) / 2 a multiple of h1
+            const int o = u1.off + wtc_mul24(i + u1r, u1.pitch) + (c0 - lh) / 2 + u1c;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) wtc_lds_put<h1, wtc_align_of(h1, R)>(ctx, o + b * st1, bnd[b]);
         }
     }
     if (vec >= 4 && wtc_whole_stage_l2(p)) {
