@@ -140,6 +140,9 @@ bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp)
 // and data backward (sweep L = 1 fp32: 184 -> 172 us against 64 x 32), 16 x 128
 // for the weight backward (265 -> 214 us).  WTCONV_TILE=<rows>x<cols> puts one
 // shape first (tuning).
+// Threads of a tiled workgroup (WTCONV_TILE_THREADS: 256 or 512).
+int tile_threads() { return env_int("WTCONV_TILE_THREADS", kFusedThreads, 256, 512) >= 512 ? 512 : 256; }
+
 struct TileShapes {
     int n;
     int s[10][2];
@@ -186,13 +189,13 @@ bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp)
         const int *sh = shapes.s[si];
         if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
         if (wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl,
-                                     rotate, kFusedThreads, 1, eb, whole_budget_floats()))
+                                     rotate, tile_threads(), 1, eb, whole_budget_floats()))
             continue;
         const int resident = wtc_whole_resident(d->dtype, tp[0]);
         int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
         if (!planes) planes = wtc_choose_planes(tp->units, d->c, resident > 0 ? resident : 512, kWholeFixed);
         wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl, rotate,
-                                 kFusedThreads, planes, eb, whole_budget_floats());
+                                 tile_threads(), planes, eb, whole_budget_floats());
         return true;
     }
     return false;
@@ -348,13 +351,13 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
             const int *sh = shapes.s[si];
             if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
             if (wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                         tl, kFusedThreads, 1, eb, whole_budget_floats()))
+                                         tl, tile_threads(), 1, eb, whole_budget_floats()))
                 continue;
             const int resident = wtc_wgrad_resident(d->dtype, ch->wp);
             int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 1 << 20);
             if (!planes) planes = wtc_choose_planes(ch->wp.units, d->c, resident > 0 ? resident : 512, kWgradFixed);
             wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                     tl, kFusedThreads, planes, eb, whole_budget_floats());
+                                     tl, tile_threads(), planes, eb, whole_budget_floats());
             ch->tiles = true;
             break;
         }
