@@ -333,12 +333,18 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     const int kk = d->k * d->k;
     ch->plen = kk + 1 + 4 * d->levels * kk;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
-    // 256 threads (512 threads with one accumulator set each measured no
-    // faster at the 56 x 56 planes); WTCONV_WGRAD_THREADS overrides
-    const int wth = env_int("WTCONV_WGRAD_THREADS", kFusedThreads, 64, 512);
+    // 256 threads, 512 when a plane has more than two pieces per thread of 256
+    // (64 x 64 planes: 3 % faster; at the 56 x 56 and 28 x 28 planes 512
+    // threads measured slower); WTCONV_WGRAD_THREADS overrides
+    const int forced_wth = env_int("WTCONV_WGRAD_THREADS", 0, 64, 512);
+    int wth = forced_wth ? forced_wth : kFusedThreads;
     ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
                 wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1,
                                     eb, whole_budget_floats()) == 0;
+    if (ch->whole && !forced_wth && ch->wp.npieces > 2 * kFusedThreads &&
+        wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels,
+                            2 * kFusedThreads, 1, eb, whole_budget_floats()) == 0)
+        wth = 2 * kFusedThreads;
     ch->tiles = false;
     // levels carried by the tiles (base and level 1; L = 0: the base alone)
     const int tl = d->levels >= 1 ? 1 : 0;
