@@ -240,6 +240,18 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
         assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
 
 
+def test_emulated_tiled_pass_with_two_output_blocks_per_thread(orc):
+    """Tiles with more output blocks than threads (64 x 64 tiles, 384 threads):
+    a thread's second output block, with its own deeper-levels term."""
+    n, c, h, w, k, L, th, tw = 1, 2, 128, 128, 5, 3, 64, 64
+    inp = make_inputs(n, c, h, w, k, L, seed=321)
+    zero = np.zeros_like(inp.s_base)
+    low = orc.forward(_lowpass(inp.x), inp.w_base, None, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
+    y = emu.whole_tiled(inp.x, low, inp.w_base, inp.bias, inp.s_base, inp.w_lvl[:1], inp.s_lvl[:1], k, th, tw,
+                        nthreads=384, planes=2, budget_floats=1 << 16)
+    _check(y, orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L))
+
+
 WGRAD_TILED = [
     # n, c, h, w, k, L (0 or 1), th, tw, dtype
     (2, 2, 64, 64, 5, 1, 32, 16, "f32"),
