@@ -20,9 +20,11 @@
 //   * LDS is zeroed once: every map keeps a zero border of r pixels, which is
 //     the convolutions' zero padding, and only interiors are rewritten;
 //   * each thread stages a group of gr rows x vec columns of the input (one
-//     16-byte load per row) and computes Haar level 1, and level 2 when the
-//     group has 4 rows and 4 columns, from those registers; deeper levels are
-//     computed from LDS;
+//     load of at most 16 bytes per row; 4 columns where the width allows) and
+//     computes Haar level 1, and level 2 when the group has 4 rows and 4
+//     columns, from those registers; with L >= 3 the four lanes of a quad hold
+//     a 2 x 2 block of groups and build level 3 by DPP exchange; deeper levels
+//     are computed from LDS;
 //   * every convolution -- the base one at full resolution and the four bands
 //     of every level -- is cut into the same 4x4-output pieces, dealt
 //     round-robin to the threads from a descriptor table built once per
@@ -37,7 +39,6 @@
 
 #include "wtconv_fused_body.h"
 
-#define WTC_WHOLE_NCH 4   // 16-byte (or smaller) input chunks per thread and image
 
 struct WtcWholePlan {
     int32_t n, c, h, w, k, levels;
