@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -37,16 +38,24 @@ HBM_PEAK_GBS = 8000.0
 VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 PACKED_FP32_PUBLISHED_TFLOPS = 157.3
 
-KERNEL_SOURCES = ("wtconv_whole_body.h", "wtconv_whole.hip", "wtconv_wgrad_body.h", "wtconv_wgrad.hip",
-                  "wtconv_fused_body.h", "wtconv_fused.hip", "wtconv_plan.h", "wtconv_wgrad_tile_body.h",
-                  "wtconv_wgrad_tile.hip", "wtconv_api.hip")
+CSRC = os.path.join(ROOT, "level_haar_wavelet_amd", "csrc")
+
+
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment-only edit keeps the digest of code the counters were taken on."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def source_digest() -> str:
+    """Digest of every kernel and launch source of the library (code only)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "level_haar_wavelet_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -55,3 +55,16 @@ def test_cpu_baseline_times_the_oracle_on_a_bounded_sample():
     out = bench.cpu_baseline(wl, images=1, min_seconds=0.05)
     assert out["kind"] == "oracle" and out["cores"] >= 1 and out["value"] > 0
     assert "1 of %d images" % wl.n in out["sample"]
+
+
+def test_source_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    src = tmp_path / "csrc"
+    src.mkdir()
+    (src / "k.hip").write_text("int f(int a) { return a * 2; }  // doubles\n")
+    (src / "k.h").write_text("/* header */\n#define N 4\n")
+    monkeypatch.setattr(bench, "CSRC", str(src))
+    d0 = bench.source_digest()
+    (src / "k.hip").write_text("// a new comment\nint f(int a)\n{\n    return a * 2;  /* doubles */\n}\n")
+    assert bench.source_digest() == d0
+    (src / "k.hip").write_text("int f(int a) { return a * 3; }\n")
+    assert bench.source_digest() != d0
