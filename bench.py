@@ -160,6 +160,30 @@ def run_gpu(args, wl):
     return {"ms_per_step": ms_total / args.steps, "us_ops": med, "us_ops_mean": mean, "wall_s": wall}
 
 
+def stream_copy_gbs(nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate on this GPU (bytes read + written per second,
+    median of `reps` timed copies of `nbytes`): the practical HBM ceiling the
+    achieved GB/s is read against."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    torch.cuda.empty_cache()
+    times.sort()
+    return 2.0 * nbytes / times[len(times) // 2] / 1e9
+
+
 def run_unfused(args, wl):
     """The same step on the unfused baseline (separate kernels, intermediates in
     HBM; wtconv_unfused_*), timed the same way, and the peak device memory of
@@ -345,6 +369,7 @@ def main():
         "us_per_op": "median over the timed steps (events around each call); means %s" % (
             ", ".join("%.2f" % v for v in res["us_ops_mean"])),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "stream_copy_GBs": round(stream_copy_gbs(), 1),
         "modeled_bytes_per_step": step_bytes,
         "mall_flush": bool(args.mall_flush),
         "roofline": {
