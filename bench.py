@@ -65,19 +65,177 @@ def conv_flops(wl) -> float:
     return 2.0 * wl.k * wl.k * (1.0 + s) * wl.elems
 
 
-def measured_traffic(kernel: str, digest: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if
-    it was taken on the current kernel sources (else None)."""
+def measured_traffic(kernel: str, digest: str, workload: str):
+    """HBM bytes per launch of `kernel` (an op) on `workload` from the
+    committed counter summary, if it was taken on the current kernel sources
+    (else None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
-            d = json.load(fh)
-    except (OSError, ValueError):
+            d = json.load(fh).get(workload, {})
+    except (OSError, ValueError, AttributeError):
         return None
     if d.get("source_digest") != digest:
         return None
     k = d.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def workload_name(wl) -> str:
+    return "%s %dx%dx%dx%d k=%d L=%d %s" % (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels,
+                                           "fp32" if wl.dtype == "f32" else "fp16 storage")
+
+
+def _short_kernel(name: str) -> str:
+    """Kernel name without the return type and the parameter list, as profilers
+    print it in either form."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _counter_means(folder: str) -> dict:
+    """Mean counter value per dispatch for each kernel, from the
+    *counter_collection.csv files that `rocprofv3 --pmc` wrote under folder."""
+    import csv
+    import glob
+
+    sums = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                key = (_short_kernel(row["Kernel_Name"]), row["Counter_Name"])
+                acc = sums.setdefault(key, {})
+                acc[row["Dispatch_Id"]] = acc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    return {key: sum(v.values()) / len(v) for key, v in sums.items()}
+
+
+def traffic_summary(folder: str, workload: str, copy_bytes: int, outdir: str = None) -> dict:
+    """Writes profiles/hbm_traffic.json and profiles/<workload>_hbm_traffic.md
+    from four counter runs under folder: fetch/ and write/ (FETCH_SIZE and
+    WRITE_SIZE of the bench), cfetch/ and cwrite/ (the same counters over a
+    plain device copy of copy_bytes bytes, which scales KiB to bytes)."""
+    from level_haar_wavelet_amd.synthetic import WORKLOADS
+
+    outdir = outdir or os.path.join(ROOT, "profiles")
+    wl = WORKLOADS[workload]
+    fetch, write = _counter_means(os.path.join(folder, "fetch")), _counter_means(os.path.join(folder, "write"))
+    cf, cw = _counter_means(os.path.join(folder, "cfetch")), _counter_means(os.path.join(folder, "cwrite"))
+    copy_f = max(v for (k, c), v in cf.items() if c == "FETCH_SIZE")
+    copy_w = max(v for (k, c), v in cw.items() if c == "WRITE_SIZE")
+    ff, fw = copy_bytes / 1024.0 / copy_f, copy_bytes / 1024.0 / copy_w
+    kernels = {}
+    for (k, c), v in sorted(fetch.items()):
+        if c == "FETCH_SIZE" and k.startswith(("wtconv_", "lowpass_")):
+            kernels[k] = {"fetch_kib": v, "write_kib": write.get((k, "WRITE_SIZE"), 0.0),
+                          "fetch_bytes": v * 1024.0 * ff, "write_bytes": write.get((k, "WRITE_SIZE"), 0.0) * 1024.0 * fw}
+    whole = [k for k in kernels if k.startswith("wtconv_whole_kernel")]
+    wgrad = [k for k in kernels if k.startswith("wtconv_wgrad_kernel")]
+    fin = [k for k in kernels if k.startswith("wtconv_wgrad_finalize")]
+    out = {"source_digest": source_digest(), "workload": workload_name(wl), "fetch_factor": ff, "write_factor": fw,
+           "kernels": {k: {"fetch_bytes": v["fetch_bytes"], "write_bytes": v["write_bytes"]} for k, v in kernels.items()}}
+    # per-op bytes where each op is one kernel launch (plus the reduction pass)
+    if len(whole) == 1 and len(wgrad) == 1 and not any(k.startswith("lowpass_") for k in kernels):
+        wb = kernels[whole[0]]["fetch_bytes"] + kernels[whole[0]]["write_bytes"]
+        gb = sum(kernels[k]["fetch_bytes"] + kernels[k]["write_bytes"] for k in wgrad + fin)
+        out["kernels"]["wtconv_forward"] = {"bytes_per_launch": wb}
+        out["kernels"]["wtconv_backward_data"] = {"bytes_per_launch": wb}
+        out["kernels"]["wtconv_backward_weight"] = {"bytes_per_launch": gb}
+    # one entry per workload, merged into what the file already holds
+    jpath = os.path.join(outdir, "hbm_traffic.json")
+    try:
+        with open(jpath) as fh:
+            allw = json.load(fh)
+        if "source_digest" in allw:  # a single-workload file of an earlier format
+            allw = {}
+    except (OSError, ValueError):
+        allw = {}
+    allw[out["workload"]] = out
+    with open(jpath, "w") as fh:
+        json.dump(allw, fh, indent=1)
+    E, e = wl.elems, wl.ebytes
+    bench = ("python3 bench.py --workload %s --steps 2 --warmup 1 --cpu-sample 0 --no-unfused --no-comparator"
+             % workload)
+    lines = ["# HBM traffic per launch: %s" % out["workload"], "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 counter runs, each scaled by what "
+             "the same counter reads for a plain %d-byte device copy (`bench.py --copy-calibration %d`): "
+             "FETCH_SIZE reads %.0f KiB for the copy's %.0f KiB (factor %.4f), WRITE_SIZE %.0f KiB (factor %.4f)."
+             % (copy_bytes, copy_bytes, copy_f, copy_bytes / 1024.0, ff, copy_w, fw), "",
+             "Commands (from the repository root; OUT is any output folder):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- " + bench,
+             "    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- " + bench,
+             "    rocprofv3 --pmc FETCH_SIZE -d OUT/cfetch -o cfetch --output-format csv -- "
+             "python3 bench.py --copy-calibration %d" % copy_bytes,
+             "    rocprofv3 --pmc WRITE_SIZE -d OUT/cwrite -o cwrite --output-format csv -- "
+             "python3 bench.py --copy-calibration %d" % copy_bytes,
+             "    python3 bench.py --traffic-summary OUT --workload %s --copy-calibration %d" % (workload, copy_bytes),
+             "", "| kernel | FETCH KiB | WRITE KiB | fetch bytes (scaled) | write bytes (scaled) |",
+             "|---|---|---|---|---|"]
+    for k, v in kernels.items():
+        lines.append("| `%s` | %.0f | %.0f | %.4g | %.4g |" % (k, v["fetch_kib"], v["write_kib"], v["fetch_bytes"],
+                                                               v["write_bytes"]))
+    lines += ["", "Counters per dispatch, averaged over all launches of a kernel (sizes mixed where one op "
+              "launches it at several sizes).", "",
+              "Modeled minimum per launch: forward or data backward %.4g bytes (read E e, write E e), weight "
+              "backward %.4g bytes (read 2 E e)." % (2.0 * E * e, 2.0 * E * e), "",
+              "Source digest of the kernels counted: `%s` (bench.py reports `traffic` only while the library "
+              "sources still hash to it)." % out["source_digest"]]
+    with open(os.path.join(outdir, "%s_hbm_traffic.md" % workload), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return out
+
+
+def trace_summary(folder: str, workload: str, outdir: str = None) -> str:
+    """Writes profiles/<workload>_kernel_trace.md from the *kernel_stats.csv of
+    a `rocprofv3 --kernel-trace --stats` run under folder, with the bench line
+    folder/bench.json (a plain run of the same build) if present."""
+    import csv
+    import glob
+
+    from level_haar_wavelet_amd.synthetic import WORKLOADS
+
+    outdir = outdir or os.path.join(ROOT, "profiles")
+    wl = WORKLOADS[workload]
+    name = workload_name(wl)
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True):
+        with open(path, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    cmd = ("rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- python3 bench.py --workload %s "
+           "--steps 5 --warmup 2 --cpu-sample 0 --no-unfused --no-comparator" % workload)
+    lines = ["# Kernel durations: %s (MI355X)" % name, "", "Commands (from the repository root; OUT is any output "
+             "folder):", "", "    " + cmd,
+             "    python3 bench.py --workload %s > OUT/kt/bench.json" % workload,
+             "    python3 bench.py --trace-summary OUT/kt --workload %s" % workload, "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
+            _short_kernel(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    lines += ["", "Before the 2 warm-up and 5 timed steps, bench.py runs the step for 0.5 s untimed (clock ramp), "
+              "so the call counts are those of about half a second of steps.  A kernel launched at several sizes "
+              "within one op (a tiled pass and the nested call on its level-1 low-pass map) is averaged over all "
+              "its launches."]
+    bj = os.path.join(folder, "bench.json")
+    if os.path.exists(bj):
+        with open(bj) as fh:
+            line = [ln for ln in fh.read().splitlines() if ln.startswith("{")][-1]
+        lines += ["", "bench.py line of the same build (`python3 bench.py --workload %s`):" % workload, "", "```",
+                  line, "```"]
+    path = os.path.join(outdir, "%s_kernel_trace.md" % workload)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
 
 
 def run_gpu(args, wl):
@@ -303,6 +461,10 @@ def main():
     ap.add_argument("--mall-flush", action="store_true")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--trace-summary", default=None,
+                    help="folder of a kernel-trace run: write the kernel-duration summary under profiles/ and exit")
+    ap.add_argument("--traffic-summary", default=None,
+                    help="folder of the four counter runs: write the HBM-traffic summaries under profiles/ and exit")
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-baseline comparison")
     ap.add_argument("--no-comparator", action="store_true", help="skip the 7x7 depthwise comparator")
     args = ap.parse_args()
@@ -312,6 +474,15 @@ def main():
               "(the layer needs no collective for forward or data backward; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.workload))
+        return
+
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(args.traffic_summary, args.workload, args.copy_calibration or (1 << 30)),
+                         indent=1))
+        return
 
     if args.copy_calibration:
         import torch
@@ -343,7 +514,7 @@ def main():
     dominant = max(ops, key=ops.get)
     achieved = flops / (ops[dominant] * 1e-6) / 1e12
     digest = source_digest()
-    traffic = measured_traffic(dominant, digest)
+    traffic = measured_traffic(dominant, digest, workload_name(wl))
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -358,8 +529,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": "%s %dx%dx%dx%d k=%d L=%d %s" % (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels,
-                                                                 "fp32" if wl.dtype == "f32" else "fp16 storage"),
+        "config": {"workload": workload_name(wl),
                    "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w, "k": wl.k, "levels": wl.levels,
                    "parallelism": "single GPU"},
         "us_fwd": round(us_f, 2),

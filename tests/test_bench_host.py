@@ -42,12 +42,15 @@ def test_counter_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_pa
     prof = tmp_path / "profiles"
     prof.mkdir()
     digest = bench.source_digest()
+    wname = bench.workload_name(WORKLOADS["stage1"])
     (prof / "hbm_traffic.json").write_text(json.dumps(
-        {"source_digest": digest, "kernels": {"wtconv_forward": {"bytes_per_launch": 123.0}}}))
+        {wname: {"source_digest": digest, "kernels": {"wtconv_forward": {"bytes_per_launch": 123.0}}}}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.measured_traffic("wtconv_forward", digest) == 123.0
-    assert bench.measured_traffic("wtconv_forward", "0" * 16) is None
-    assert bench.measured_traffic("wtconv_backward_weight", digest) is None
+    assert bench.measured_traffic("wtconv_forward", digest, wname) == 123.0
+    assert bench.measured_traffic("wtconv_forward", "0" * 16, wname) is None
+    assert bench.measured_traffic("wtconv_backward_weight", digest, wname) is None
+    # counters of another workload are not this one's
+    assert bench.measured_traffic("wtconv_forward", digest, bench.workload_name(WORKLOADS["stage2"])) is None
 
 
 def test_cpu_baseline_times_the_oracle_on_a_bounded_sample():
@@ -68,3 +71,44 @@ def test_source_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.source_digest() == d0
     (src / "k.hip").write_text("int f(int a) { return a * 3; }\n")
     assert bench.source_digest() != d0
+
+
+def _write_counters(folder, rows):
+    import csv
+
+    os.makedirs(folder, exist_ok=True)
+    with open(os.path.join(folder, "x_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)  # quotes the kernel names, which hold commas
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_traffic_summary_scales_counters_by_the_copy_calibration(tmp_path):
+    # a 1 MiB copy whose FETCH_SIZE reads half its bytes (factor 2) and whose
+    # WRITE_SIZE reads them exactly (factor 1); two dispatches per kernel
+    copy = 1 << 20
+    whole, wgrad, fin = ("wtconv_whole_kernel<float, 5, 4, false>", "wtconv_wgrad_kernel<float, 5, 4, 3, false>",
+                         "wtconv_wgrad_finalize_kernel")
+    _write_counters(tmp_path / "fetch", [(1, "void %s(WtcWholeArgs<float>)" % whole, "FETCH_SIZE", 100), (2, whole, "FETCH_SIZE", 300),
+                                         (3, wgrad, "FETCH_SIZE", 50), (4, fin, "FETCH_SIZE", 2),
+                                         (5, "copyBuffer", "FETCH_SIZE", 7)])
+    _write_counters(tmp_path / "write", [(1, whole, "WRITE_SIZE", 10), (2, whole, "WRITE_SIZE", 30),
+                                         (3, wgrad, "WRITE_SIZE", 4), (4, fin, "WRITE_SIZE", 1)])
+    _write_counters(tmp_path / "cfetch", [(1, "copyBuffer", "FETCH_SIZE", 512)])
+    _write_counters(tmp_path / "cwrite", [(1, "copyBuffer", "WRITE_SIZE", 1024)])
+    out = bench.traffic_summary(str(tmp_path), "stage1", copy, outdir=str(tmp_path))
+    assert out["fetch_factor"] == pytest.approx(2.0) and out["write_factor"] == pytest.approx(1.0)
+    k = out["kernels"]
+    assert k[whole]["fetch_bytes"] == pytest.approx(200 * 1024 * 2.0)
+    assert k[whole]["write_bytes"] == pytest.approx(20 * 1024)
+    assert k["wtconv_forward"]["bytes_per_launch"] == pytest.approx((400 + 20) * 1024)
+    assert k["wtconv_backward_weight"]["bytes_per_launch"] == pytest.approx((100 + 4 + 4 + 1) * 1024)
+    assert "copyBuffer" not in k
+    assert out["source_digest"] == bench.source_digest()
+    saved = json.load(open(tmp_path / "hbm_traffic.json"))
+    assert saved == {out["workload"]: json.loads(json.dumps(out))}
+    # a second workload is merged in, the first kept
+    out2 = bench.traffic_summary(str(tmp_path), "stage2", copy, outdir=str(tmp_path))
+    saved = json.load(open(tmp_path / "hbm_traffic.json"))
+    assert set(saved) == {out["workload"], out2["workload"]}
+    assert (tmp_path / "stage1_hbm_traffic.md").read_text().count("rocprofv3 --pmc") == 4
