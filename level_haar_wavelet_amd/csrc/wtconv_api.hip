@@ -508,7 +508,11 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
     float *partial = (float *)ws;
     hipError_t e = hipSuccess;
     if (ch.tiles) {
-        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
+        // with L >= 2 the tiles also write the level-1 low-pass maps of x and
+        // dy (every tile its interior), the inputs of the nested call
+        char *llx = desc->levels >= 2 ? ws + ch.part_bytes : nullptr;
+        char *lld = desc->levels >= 2 ? llx + ch.quarter : nullptr;
+        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s, llx, lld);
         if (e == hipSuccess)
             e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels >= 1 ? 1 : 0, ch.groups, ch.plen,
                                           partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
@@ -516,14 +520,8 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
         if (e != hipSuccess) return WTCONV_ERR_HIP;
         if (desc->levels < 2) return WTCONV_OK;
         const wtconv_desc_t sd = deeper_desc(desc);
-        char *llx = ws + ch.part_bytes, *lld = llx + ch.quarter;
         float *scratch = (float *)(lld + ch.quarter);
         char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
-        if ((e = wtc_launch_lowpass(desc->dtype, x, llx, desc->n * desc->c, (int)desc->h, (int)desc->w, s)) !=
-                hipSuccess ||
-            (e = wtc_launch_lowpass(desc->dtype, dy, lld, desc->n * desc->c, (int)desc->h, (int)desc->w, s)) !=
-                hipSuccess)
-            return WTCONV_ERR_HIP;
         const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
         return wtconv_backward_weight(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C,
                                       scratch, scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk,

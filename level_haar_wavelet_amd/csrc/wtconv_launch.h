@@ -35,9 +35,11 @@ hipError_t wtc_launch_repack(int dtype, const void *in, void *out, int64_t plane
                              int wout, hipStream_t stream);
 
 // Fused parameter-gradient correlations (partials per workgroup) and the
-// fixed-order reduction with the chain rule.
+// fixed-order reduction with the chain rule.  Tiled plans may also write the
+// level-1 low-pass maps of x and dy (llx, lld: (N, C, ih/2, iw/2), both or
+// neither).
 hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,
-                            hipStream_t stream);
+                            hipStream_t stream, void *llx = nullptr, void *lld = nullptr);
 hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int plen, const float *partial,
                                      const float *w_base, const float *bias, const float *s_base,
                                      const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,

@@ -151,13 +151,15 @@ int wtc_wgrad_resident(int dtype, const WtcWgradPlan &p)
 }
 
 hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,
-                            hipStream_t stream)
+                            hipStream_t stream, void *llx, void *lld)
 {
+    if ((llx != nullptr) != (lld != nullptr) || (llx && !p.tiled)) return hipErrorInvalidValue;
     if (dtype == 0) {
-        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial, p};
+        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial, p, (float *)llx, (float *)lld};
         return launch_wgrad_t<float>(a, stream);
     }
-    WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial, p};
+    WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial, p, (_Float16 *)llx,
+                             (_Float16 *)lld};
     return launch_wgrad_t<_Float16>(a, stream);
 }
 

@@ -243,6 +243,11 @@ struct WtcWgradArgs {
     const T *dy;
     float *partial;  // [groups][C][plen]
     WtcWgradPlan p;
+    // tiled plans: the level-1 low-pass maps of x and dy, (N, C, ih/2, iw/2)
+    // orthonormal, written for every tile's interior (the input of the deeper
+    // levels' gradients), or null
+    T *llx = nullptr;
+    T *lld = nullptr;
 };
 
 template <typename T, int VEC>
@@ -253,6 +258,7 @@ struct WtcWgradCtx {
     int grow, gcol;  // this thread's staging group
     bool gvalid;
     int vmask;       // rows of the prefetched group that lie in the image (bit q)
+    int64_t llo;     // tiled: the prefetched unit's tile origin in the level-1 low-pass maps
     T prex[4][VEC];
     T prey[4][VEC];
 #ifdef WTC_EMULATE
@@ -303,6 +309,8 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
         row0 = ty * p.h - p.lh + p.gr * ctx.grow;
         col = (t - ty * p.tiles_x) * p.w - p.lh + VEC * ctx.gcol;
         e0 = plane;
+        ctx.llo = ((int64_t)im * p.c + ctx.c) * ((int64_t)(p.ih / 2) * (p.iw / 2)) +
+                  (int64_t)(ty * p.h / 2) * (p.iw / 2) + (t - ty * p.tiles_x) * p.w / 2;
     } else {
         plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
         e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
@@ -455,6 +463,25 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
                 for (int j = 0; j < H1; ++j) {
                     llx[aa][j] = bx[0][j];
                     lld[aa][j] = bd[0][j];
+                }
+                if constexpr (TL) {
+                    // the tile interior's level-1 low-pass values, (a + b + c + d) / 2
+                    if (dyin && a.llx) {
+                        const int64_t o = ctx.llo + (int64_t)i * (p.iw / 2) + c0 / 2;
+#ifdef WTC_EMULATE
+                        const int64_t all = (int64_t)p.n * p.c * (p.ih / 2) * (p.iw / 2);
+                        for (int j = 0; j < H1; ++j) {
+                            wtc_chk(a.llx, o + j, all, __LINE__) = wtc_from_float<T>(0.5f * bx[0][j]);
+                            wtc_chk(a.lld, o + j, all, __LINE__) = wtc_from_float<T>(0.5f * bd[0][j]);
+                        }
+#else
+#pragma unroll
+                        for (int j = 0; j < H1; ++j) {
+                            a.llx[o + j] = wtc_from_float<T>(0.5f * bx[0][j]);
+                            a.lld[o + j] = wtc_from_float<T>(0.5f * bd[0][j]);
+                        }
+#endif
+                    }
                 }
             }
         }

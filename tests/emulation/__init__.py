@@ -51,7 +51,7 @@ def _load():
         lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
-        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 12 + [ci, ci, ci]
         lib.emu_wgrad_tiles.restype = ci
         lib.emu_whole_plan.restype = ci
         lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
@@ -142,9 +142,10 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
 
 
 def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32", nthreads=256, planes=1,
-                budget_floats=40960):
+                budget_floats=40960, lowpass=False):
     """Base and level-1 parameter gradients through the emulated tiled
-    weight-gradient pass (w_lvl / s_lvl: level 1 only, or None for L = 0)."""
+    weight-gradient pass (w_lvl / s_lvl: level 1 only, or None for L = 0);
+    with lowpass=True also the level-1 low-pass maps of x and dy it writes."""
     lib = _load()
     n, c, ih, iw = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -157,11 +158,14 @@ def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32
             np.full((1, 4 * c), np.nan, np.float32)][:3 + 2 * levels]
     ptr = lambda a: None if a is None else a.ctypes.data
     optr = [o.ctypes.data for o in outs] + [None] * (5 - len(outs))
+    lls = [np.full((n, c, ih // 2, iw // 2), np.nan, npdt) for _ in range(2)] if lowpass else [None, None]
     rc = lib.emu_wgrad_tiles(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, ih, iw, th, tw, k,
-                             levels, *[ptr(a) for a in keep], *optr, nthreads, planes, budget_floats)
+                             levels, *[ptr(a) for a in keep], *optr, *[ptr(a) for a in lls], nthreads, planes,
+                             budget_floats)
     if rc != 0:
         raise ValueError("emu_wgrad_tiles failed: %d" % rc)
-    return [o.astype(np.float64) for o in outs]
+    res = [o.astype(np.float64) for o in outs]
+    return (res, [a.astype(np.float64) for a in lls]) if lowpass else res
 
 
 def wgrad_plan(n, c, h, w, k, levels, nthreads=256, planes=1, dtype="f32", budget_floats=40960):

@@ -363,11 +363,12 @@ int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int
 }
 
 // The tiled weight-gradient pass (base and level-1 correlations on th x tw
-// tiles of ih x iw images, L = 1) on host arrays, with its finalize.
+// tiles of ih x iw images, L = 1) on host arrays, with its finalize; llx and
+// lld (both or neither) receive the level-1 low-pass maps of x and dy.
 int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int ih, int iw, int th, int tw, int k,
                     int levels, const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
                     const float *s_lvl, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
-                    int nthreads, int planes, int budget_floats)
+                    void *llx, void *lld, int nthreads, int planes, int budget_floats)
 {
     WtcWgradPlan p;
     if (wtc_make_wgrad_tile_plan(&p, n, c, ih, iw, th, tw, k, levels, nthreads, planes, dtype == 0 ? 4 : 2,
@@ -376,10 +377,11 @@ int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int 
     std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
     int rc;
     if (dtype == 0) {
-        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial.data(), p};
+        WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial.data(), p, (float *)llx, (float *)lld};
         rc = run_wgrad_t<float>(a);
     } else {
-        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p};
+        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p, (_Float16 *)llx,
+                                 (_Float16 *)lld};
         rc = run_wgrad_t<_Float16>(a);
     }
     if (rc) return rc;

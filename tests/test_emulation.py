@@ -279,6 +279,28 @@ def test_emulated_tiled_weight_gradients_levels_0_and_1(orc, case):
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
 
 
+@pytest.mark.parametrize("case", [c for c in WGRAD_TILED if c[5] == 1], ids=lambda c: "x".join(map(str, c)))
+def test_emulated_tiled_weight_gradients_write_the_low_pass_maps(orc, case):
+    """With L >= 2 the tiled weight-gradient pass also writes the level-1
+    low-pass maps of x and dy (every tile its interior), which feed the nested
+    call for the deeper levels: every element written once, equal to the
+    oracle's Haar analysis, and the gradients unchanged."""
+    n, c, h, w, k, L, th, tw, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + k)
+    got, (llx, lld) = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k,
+                                      th, tw, dtype=dt, planes=3, budget_floats=1 << 16, lowpass=True)
+    plain = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, th, tw,
+                            dtype=dt, planes=3, budget_floats=1 << 16)
+    for gg, pp in zip(got, plain):
+        assert np.array_equal(gg, pp)
+    tol = 1e-6 if dt == "f32" else 1e-3
+    for src, ll in ((inp.x, llx), (inp.dy, lld)):
+        assert not np.isnan(ll).any()
+        ref = np.stack([np.stack([orc.haar_analysis(src[i, j].astype(np.float64))[0] for j in range(c)])
+                        for i in range(n)])
+        assert np.abs(ll - ref).max() <= tol * (1 + np.abs(ref).max())
+
+
 @pytest.mark.parametrize("L", [2, 3, 4])
 def test_deeper_level_gradients_are_the_layer_on_the_low_pass_maps(orc, L):
     """The decomposition the large-plane weight gradient relies on, checked on
