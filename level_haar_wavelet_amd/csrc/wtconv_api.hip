@@ -116,21 +116,26 @@ wtconv_status_t check_params(const wtconv_desc_t *d, const float *w_base, const 
 // convolution pieces to keep them busy: more waves in flight hide the latency
 // of the staging and output passes; WTCONV_WHOLE_THREADS overrides), with its
 // images per workgroup; false if a plane does not fit one workgroup.
-bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp)
+bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp, int nobase = 0)
 {
     if (env_int("WTCONV_NO_WHOLE", 0, 0, 1)) return false;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
     int wth = env_int("WTCONV_WHOLE_THREADS", 0, 64, 512);
+    // the thread count follows the pieces of the layer with its base path
+    // (without it, the 64 x 64 nested planes of L = 3 measured 2 % slower
+    // on the 256 threads their fewer pieces would pick)
     if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                            wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()))
+                            wth ? wth : kWholeThreads, 1, eb, whole_budget_floats()) &&
+        (!nobase || wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                        wth ? wth : kWholeThreads, 1, eb, whole_budget_floats(), nobase)))
         return false;
     if (!wth) wth = wp->items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
     if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1, eb,
-                            whole_budget_floats()))
+                            whole_budget_floats(), nobase))
         return false;
     const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp[0]), kWholeFixed, "WTCONV_PLANES");
     wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, planes, eb,
-                        whole_budget_floats());
+                        whole_budget_floats(), nobase);
     return true;
 }
 
@@ -177,7 +182,7 @@ TileShapes tile_shapes(bool wgrad)
 // convolutions on tiles, the deeper levels from the level-1 low-pass map by a
 // separate call (L = 0: the base convolution alone).  Tile shapes are tried
 // in the order of tile_shapes(); false if none fits or WTCONV_NO_TILES is set.
-bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp)
+bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp, int nobase = 0)
 {
     if (env_int("WTCONV_NO_TILES", 0, 0, 1)) return false;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
@@ -189,13 +194,13 @@ bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp)
         const int *sh = shapes.s[si];
         if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
         if (wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl,
-                                     rotate, tile_threads(), 1, eb, whole_budget_floats()))
+                                     rotate, tile_threads(), 1, eb, whole_budget_floats(), nobase))
             continue;
         const int resident = wtc_whole_resident(d->dtype, tp[0]);
         int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
         if (!planes) planes = wtc_choose_planes(tp->units, d->c, resident > 0 ? resident : 512, kWholeFixed);
         wtc_make_whole_tile_plan(tp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, tl, rotate,
-                                 tile_threads(), planes, eb, whole_budget_floats());
+                                 tile_threads(), planes, eb, whole_budget_floats(), nobase);
         return true;
     }
     return false;
@@ -228,9 +233,14 @@ size_t pass_workspace(const wtconv_desc_t *d, int rotate)
     return 2 * quarter + align256((size_t)d->c * 4) + pass_workspace(&sd, rotate);
 }
 
+// zero_base (C floats of scratch, or null): the base path is zero, as in the
+// nested call for the deeper levels of a larger layer (w_base, bias and
+// s_base are then not read); the whole-plane and tiled kernels skip it, the
+// other paths run with a zero base scale written there.
 wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *w_base, const float *bias,
                            const float *s_base, const float *w_lvl, const float *s_lvl, void *out, int rotate,
-                           void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
+                           void *workspace, size_t workspace_bytes, wtconv_stream_t stream,
+                           float *zero_base = nullptr)
 {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
@@ -251,7 +261,8 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
         if (wtc_launch_repack(d->dtype, in, ws, d->n * d->c, (int)d->h, (int)d->w, (int)pd.h, (int)pd.w, s) !=
             hipSuccess)
             return WTCONV_ERR_HIP;
-        st = fused_pass(&pd, ws, w_base, bias, s_base, w_lvl, s_lvl, ws + a, rotate, ws + 2 * a, inner, stream);
+        st = fused_pass(&pd, ws, w_base, bias, s_base, w_lvl, s_lvl, ws + a, rotate, ws + 2 * a, inner, stream,
+                        zero_base);
         if (st != WTCONV_OK) return st;
         return wtc_launch_repack(d->dtype, ws + a, out, d->n * d->c, (int)pd.h, (int)pd.w, (int)d->h, (int)d->w,
                                  s) == hipSuccess
@@ -261,10 +272,11 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     // the whole-plane kernel when a plane fits one workgroup (any L, even
     // sides for L = 0); else tiles where a tile shape divides the plane; else
     // the row-band kernel for L = 0 and the strip kernel for L >= 1
+    const int nobase = zero_base != nullptr && d->levels >= 1;
     WtcWholePlan wp;
-    if (whole_choice(d, rotate, &wp)) {
+    if (whole_choice(d, rotate, &wp, nobase)) {
         e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
-    } else if (tile_choice(d, rotate, &wp)) {
+    } else if (tile_choice(d, rotate, &wp, nobase)) {
         const void *low = nullptr;
         if (d->levels >= 2) {
             const size_t need = pass_workspace(d, rotate);
@@ -277,13 +289,12 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
             float *zeros = (float *)(ws + 2 * quarter);
             char *sub = ws + 2 * quarter + align256((size_t)d->c * 4);
             const int64_t kk = (int64_t)d->k * d->k;
-            if ((e = wtc_launch_lowpass(d->dtype, in, ll, d->n * d->c, (int)d->h, (int)d->w, s)) != hipSuccess ||
-                (e = wtc_launch_fill(zeros, d->c, 0.0f, s)) != hipSuccess)
+            if ((e = wtc_launch_lowpass(d->dtype, in, ll, d->n * d->c, (int)d->h, (int)d->w, s)) != hipSuccess)
                 return WTCONV_ERR_HIP;
+            // the deeper levels: the layer with L - 1 levels and no base path
             const float *wl2 = w_lvl + 4 * d->c * kk, *sl2 = s_lvl + 4 * d->c;
-            st = rotate ? wtconv_backward_data(&sd, ll, w_base, zeros, wl2, sl2, deep, sub, need - (sub - ws), stream)
-                        : wtconv_forward(&sd, ll, w_base, nullptr, zeros, wl2, sl2, deep, sub, need - (sub - ws),
-                                         stream);
+            st = fused_pass(&sd, ll, w_base, nullptr, zeros, wl2, sl2, deep, rotate, sub, need - (sub - ws), stream,
+                            zeros);
             if (st != WTCONV_OK) return st;
             low = deep;
         }
@@ -292,6 +303,11 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
         e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
                               (int)d->w, rotate, s);
     } else {
+        if (nobase) {
+            if (wtc_launch_fill(zero_base, d->c, 0.0f, s) != hipSuccess) return WTCONV_ERR_HIP;
+            s_base = zero_base;
+            bias = nullptr;
+        }
         WtcFusedPlan p;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                 kFusedThreads, lds_budget_floats()) &&

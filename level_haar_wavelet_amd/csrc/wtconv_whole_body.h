@@ -69,6 +69,9 @@ struct WtcWholePlan {
     int32_t lh;          // loaded halo (input pixels, a multiple of 4 and of vec)
     int32_t xr, xc;      // stored row / column of tile element (0, 0) in the input map
     int32_t u1r, u1c;    // the same for the level-1 maps (deeper maps: (r, r))
+    // the base path is known to be zero (the deeper levels of a larger layer,
+    // whose base scale is 0): no base convolution pieces, no base output read
+    int32_t nobase;
 };
 
 #define WTC_WP 4  // piece side (outputs)
@@ -111,7 +114,7 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
         p->z[m].pitch = wtc_pitch16(wtc_roundup(Wm, P));
         off += (m == 0 ? 1 : 4) * p->z[m].rows * p->z[m].pitch;
     }
-    int32_t items = ((p->h + P - 1) / P) * ((p->w + P - 1) / P);
+    int32_t items = p->nobase ? 0 : ((p->h + P - 1) / P) * ((p->w + P - 1) / P);
     for (int32_t m = 1; m <= L; ++m) items += 4 * (((p->h >> m) + P - 1) / P) * (((p->w >> m) + P - 1) / P);
     p->items = items;
     p->tab_off = off;
@@ -135,9 +138,11 @@ WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p)
 // requested number of units (images, or (image, tile) pairs) per workgroup.
 static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                         int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
-                                        int32_t elem_bytes, int32_t budget_floats, int32_t ih, int32_t iw)
+                                        int32_t elem_bytes, int32_t budget_floats, int32_t ih, int32_t iw,
+                                        int32_t nobase)
 {
     const int32_t r = k / 2;
+    p->nobase = nobase && levels >= 1;
     p->n = n;
     p->c = c;
     p->h = h;
@@ -201,12 +206,14 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     return p->lds_floats <= budget_floats ? 0 : -1;
 }
 
+// nobase: the base path is zero (L >= 1 only; the base weights, bias and
+// scale are then not read).
 static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                       int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
-                                      int32_t elem_bytes, int32_t budget_floats)
+                                      int32_t elem_bytes, int32_t budget_floats, int32_t nobase = 0)
 {
     return wtc_whole_plan_common(p, n, c, h, w, k, levels, rotate, nthreads, planes, elem_bytes, budget_floats, h,
-                                 w);
+                                 w, nobase);
 }
 
 // Tiled plan: th x tw tiles of ih x iw images, L = 1 (plus the added low-pass
@@ -214,11 +221,11 @@ static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int
 static inline int wtc_make_whole_tile_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
                                            int32_t th, int32_t tw, int32_t k, int32_t levels, int32_t rotate,
                                            int32_t nthreads, int32_t planes, int32_t elem_bytes,
-                                           int32_t budget_floats)
+                                           int32_t budget_floats, int32_t nobase = 0)
 {
     if (th == ih && tw == iw) return -1;
     return wtc_whole_plan_common(p, n, c, th, tw, k, levels, rotate, nthreads, planes, elem_bytes, budget_floats,
-                                 ih, iw);
+                                 ih, iw, nobase);
 }
 
 template <typename T>
@@ -276,7 +283,7 @@ WTC_HD WTC_INLINE void wtc_whole_setup(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     ctx.n0 = g * p.planes;
     ctx.nimg = wtc_min(p.planes, p.units - ctx.n0);
     float b = 0.0f;
-    if (!p.rotate && a.bias) b = a.s_base[ctx.c] * a.bias[ctx.c];
+    if (!p.rotate && !p.nobase && a.bias) b = a.s_base[ctx.c] * a.bias[ctx.c];
     ctx.bias = b;
     const int gpr = (p.w + 2 * p.lh) / p.vec;
     const int grp = wtc_min(ctx.tid, p.groups - 1);  // threads past the last group repeat it, unstored
@@ -338,7 +345,7 @@ WTC_HD WTC_INLINE void wtc_whole_fold(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
         const int se = p.rotate ? (kk - 1 - e) : e;
         float v;
         if (blk == 0) {
-            v = WTC_PAR(a.s_base, c, C) * WTC_PAR(a.w_base, c * kk + se, (int64_t)C * kk);
+            v = p.nobase ? 0.0f : WTC_PAR(a.s_base, c, C) * WTC_PAR(a.w_base, c * kk + se, (int64_t)C * kk);
         } else {
             const int m = (blk - 1) / 4 + 1, b = (blk - 1) % 4;
             const int ch = (m - 1) * 4 * C + 4 * c + b;
@@ -617,8 +624,10 @@ WTC_HD WTC_INLINE void wtc_whole_table(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
 {
     constexpr int P = WTC_WP;
     const WtcWholePlan &p = a.p;
+    // without the base path the pieces start at level 1's
+    const int skip = p.nobase ? ((p.h + P - 1) / P) * ((p.w + P - 1) / P) : 0;
     for (int it = ctx.tid; it < p.items; it += ctx.nth) {
-        int rem = it, g = 0, npc = 0, npr = 0, m = 0, b = 0;
+        int rem = it + skip, g = 0, npc = 0, npr = 0, m = 0, b = 0;
         for (;;) {
             m = g == 0 ? 0 : (g - 1) / 4 + 1;
             b = g == 0 ? 0 : (g - 1) % 4;
@@ -796,9 +805,14 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         const int bx = it == ctx.tid ? ctx.oblk & 0xffff : it - by * nbx;
         const int i1 = by;
         float acc[2][BW];
-        const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
-        wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
-        wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
+        if (p.nobase) {
+#pragma unroll
+            for (int e = 0; e < BW; ++e) acc[0][e] = acc[1][e] = 0.0f;
+        } else {
+            const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
+            wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
+            wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
+        }
         float band[4][Q];
         if (p.levels >= 1) {
             const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;

@@ -46,9 +46,9 @@ def _load():
         lib.emu_fused.restype = ci
         lib.emu_fused_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
         lib.emu_fused_plan.restype = ci
-        lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci]
+        lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci, ci]
         lib.emu_whole.restype = ci
-        lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci]
+        lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
         lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 12 + [ci, ci, ci]
@@ -103,8 +103,9 @@ def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f
 
 
 def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32", nthreads=256, planes=1,
-          budget_floats=40960):
-    """Run the whole-plane kernel on the CPU emulation."""
+          budget_floats=40960, nobase=False):
+    """Run the whole-plane kernel on the CPU emulation (nobase: without the
+    base path, as in the nested call for the deeper levels)."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -113,14 +114,14 @@ def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
     rc = lib.emu_whole(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, k, levels,
-                       rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats)
+                       rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats, int(nobase))
     if rc != 0:
         raise ValueError("emu_whole failed: %d" % rc)
     return out.astype(np.float64)
 
 
 def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0, dtype="f32", nthreads=256, planes=1,
-                budget_floats=40960):
+                budget_floats=40960, nobase=False):
     """Run the tiled whole-plane kernel (base and level-1 convolutions on th x tw
     tiles, plus the deeper levels' low-pass term `low`) on the CPU emulation.
     w_lvl / s_lvl: the level-1 weights and scales (1, 4C, k, k) / (1, 4C), or
@@ -135,7 +136,8 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
     ptr = lambda a: None if a is None else a.ctypes.data
     levels = 0 if w_lvl is None else 1
     rc = lib.emu_whole_tiled(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, ptr(lin), n, c, ih, iw,
-                             th, tw, k, levels, rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats)
+                             th, tw, k, levels, rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats,
+                             int(nobase))
     if rc != 0:
         raise ValueError("emu_whole_tiled failed: %d" % rc)
     return out.astype(np.float64)

@@ -428,11 +428,11 @@ int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, in
 
 int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, int k, int levels, int rotate,
               const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
-              int nthreads, int planes, int budget_floats)
+              int nthreads, int planes, int budget_floats, int nobase)
 {
     WtcWholePlan p;
     if (wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
-                            budget_floats))
+                            budget_floats, nobase))
         return -1;
     if (dtype == 0) {
         WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
@@ -443,14 +443,15 @@ int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, 
 }
 
 // The tiled whole-plane pass (L = 1 plus the deeper levels' low-pass term
-// `low`, (N, C, ih/2, iw/2), or null) on host arrays.
+// `low`, (N, C, ih/2, iw/2), or null) on host arrays.  nobase: without the
+// base path (both entry points; w_base, bias and s_base may then be null).
 int emu_whole_tiled(int dtype, const void *in, void *out, const void *low, int n, int c, int ih, int iw, int th,
                     int tw, int k, int levels, int rotate, const float *w_base, const float *bias, const float *s_base,
-                    const float *w_lvl, const float *s_lvl, int nthreads, int planes, int budget_floats)
+                    const float *w_lvl, const float *s_lvl, int nthreads, int planes, int budget_floats, int nobase)
 {
     WtcWholePlan p;
     if (wtc_make_whole_tile_plan(&p, n, c, ih, iw, th, tw, k, levels, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
-                                 budget_floats))
+                                 budget_floats, nobase))
         return -1;
     if (dtype == 0) {
         WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p,

@@ -240,6 +240,58 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
         assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
 
 
+NOBASE = [
+    # n, c, h, w, k, L, nthreads, dtype
+    (2, 3, 32, 32, 5, 1, 256, "f32"),
+    (1, 2, 64, 64, 5, 1, 512, "f32"),
+    (2, 2, 28, 28, 3, 2, 256, "f16"),
+    (1, 2, 32, 48, 7, 3, 256, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", NOBASE, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_whole_plane_without_the_base_path(orc, case, rotate):
+    """The nested call for the deeper levels of a larger layer runs without
+    the base path (its base scale is zero): no base pieces, no base output,
+    base weights, bias and scale never read (NaN here).  It must equal the
+    oracle's layer with a zero base scale and no bias."""
+    n, c, h, w, k, L, nth, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=7 * h + L + rotate)
+    nan_w, nan_c = np.full_like(inp.w_base, np.nan), np.full_like(inp.s_base, np.nan)
+    y = emu.whole(inp.x, nan_w, nan_c, nan_c, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate, dtype=dt, nthreads=nth,
+                  planes=2, budget_floats=1 << 15, nobase=True)
+    zero = np.zeros_like(inp.s_base)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, None, zero, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.x, inp.w_base, zero, inp.w_lvl, inp.s_lvl, k, L)
+    if dt == "f32":
+        _check(y, ref)
+    else:
+        assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
+
+
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_tiled_pass_without_the_base_path(orc, rotate):
+    """The same for the tiled pass of a nested call (levels 1..L of a layer
+    whose base path is zero), with the deeper levels' low-pass term added."""
+    n, c, h, w, k, L, th, tw = 2, 2, 64, 64, 5, 3, 32, 32
+    inp = make_inputs(n, c, h, w, k, L, seed=99 + rotate)
+    zero = np.zeros_like(inp.s_base)
+    ll = _lowpass(inp.x)
+    if rotate == 0:
+        low = orc.forward(ll, inp.w_base, None, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
+        ref = orc.forward(inp.x, inp.w_base, None, zero, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        low = orc.backward_data(ll, inp.w_base, zero, inp.w_lvl[1:], inp.s_lvl[1:], k, L - 1)
+        ref = orc.backward_data(inp.x, inp.w_base, zero, inp.w_lvl, inp.s_lvl, k, L)
+    nan_w, nan_c = np.full_like(inp.w_base, np.nan), np.full_like(inp.s_base, np.nan)
+    y = emu.whole_tiled(inp.x, low, nan_w, nan_c, nan_c, inp.w_lvl[:1], inp.s_lvl[:1], k, th, tw, rotate=rotate,
+                        planes=3, budget_floats=1 << 16, nobase=True)
+    _check(y, ref)
+
+
 def test_emulated_tiled_pass_with_two_output_blocks_per_thread(orc):
     """Tiles with more output blocks than threads (64 x 64 tiles, 384 threads):
     a thread's second output block, with its own deeper-levels term."""
