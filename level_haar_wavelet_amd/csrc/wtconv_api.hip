@@ -344,7 +344,11 @@ int wgrad_groups(const wtconv_desc_t *d)
     return g < 1 ? 1 : g;
 }
 
-wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
+wtconv_status_t wgrad_workspace(const wtconv_desc_t *d, int nobase, size_t *bytes);
+
+// nobase: the base gradients are not wanted (the nested call for the deeper
+// levels of a larger layer); its workspace is sized with the same choice.
+wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch, int nobase = 0)
 {
     const int kk = d->k * d->k;
     ch->plen = kk + 1 + 4 * d->levels * kk;
@@ -356,10 +360,10 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     int wth = forced_wth ? forced_wth : kFusedThreads;
     ch->whole = !env_int("WTCONV_NO_WHOLE", 0, 0, 1) &&
                 wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1,
-                                    eb, whole_budget_floats()) == 0;
+                                    eb, whole_budget_floats(), nobase) == 0;
     if (ch->whole && !forced_wth && ch->wp.npieces > 2 * kFusedThreads &&
         wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels,
-                            2 * kFusedThreads, 1, eb, whole_budget_floats()) == 0)
+                            2 * kFusedThreads, 1, eb, whole_budget_floats(), nobase) == 0)
         wth = 2 * kFusedThreads;
     ch->tiles = false;
     // levels carried by the tiles (base and level 1; L = 0: the base alone)
@@ -373,13 +377,13 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
             const int *sh = shapes.s[si];
             if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
             if (wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                         tl, tile_threads(), 1, eb, whole_budget_floats()))
+                                         tl, tile_threads(), 1, eb, whole_budget_floats(), nobase))
                 continue;
             const int resident = wtc_wgrad_resident(d->dtype, ch->wp);
             int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 1 << 20);
             if (!planes) planes = wtc_choose_planes(ch->wp.units, d->c, resident > 0 ? resident : 512, kWgradFixed);
             wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                     tl, tile_threads(), planes, eb, whole_budget_floats());
+                                     tl, tile_threads(), planes, eb, whole_budget_floats(), nobase);
             ch->tiles = true;
             break;
         }
@@ -393,7 +397,7 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
             const wtconv_desc_t sd = deeper_desc(d);
             ch->quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * eb);
             size_t sub = 0;
-            wtconv_status_t st = wtconv_workspace_size(&sd, WTCONV_OP_BWD_WEIGHT, &sub);
+            wtconv_status_t st = wgrad_workspace(&sd, 1, &sub);
             if (st != WTCONV_OK) return st;
             ch->sub_bytes = sub;
         }
@@ -404,11 +408,11 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     }
     if (ch->whole) {
         wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, 1, eb,
-                            whole_budget_floats());
+                            whole_budget_floats(), nobase);
         const int planes = pick_planes(d, wtc_wgrad_resident(d->dtype, ch->wp), kWgradFixed,
                                        "WTCONV_WGRAD_PLANES");
         wtc_make_wgrad_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, wth, planes, eb,
-                            whole_budget_floats());
+                            whole_budget_floats(), nobase);
         ch->groups = ch->wp.groups;
     } else {
         ch->groups = (int)wgrad_groups(d);
@@ -421,6 +425,19 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch)
     }
     wtc_wtile_carve(&ch->cv, d->n, d->c, d->h, d->w, ch->whole ? 0 : d->levels, ch->groups, ch->plen);
     ch->total_bytes = ch->cv.total;
+    return WTCONV_OK;
+}
+
+// Workspace of the weight backward (nobase: see choose_wgrad).
+wtconv_status_t wgrad_workspace(const wtconv_desc_t *d, int nobase, size_t *bytes)
+{
+    WgradChoice ch;
+    const wtconv_desc_t pd = padded_desc(d);
+    wtconv_status_t st = check_desc(&pd);
+    if (st != WTCONV_OK) return st;
+    if ((st = choose_wgrad(&pd, &ch, nobase)) != WTCONV_OK) return st;
+    // ragged sides: zero-padded copies of x and dy ahead of the padded call's workspace
+    *bytes = (ragged(d) ? 2 * align256(act_bytes(&pd)) : 0) + ch.total_bytes;
     return WTCONV_OK;
 }
 
@@ -470,24 +487,18 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     switch (op) {
     case WTCONV_OP_FWD: *bytes = pass_workspace(desc, 0); return WTCONV_OK;
     case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1); return WTCONV_OK;
-    case WTCONV_OP_BWD_WEIGHT: {
-        WgradChoice ch;
-        const wtconv_desc_t pd = padded_desc(desc);
-        if ((st = check_desc(&pd)) != WTCONV_OK) return st;
-        if ((st = choose_wgrad(&pd, &ch)) != WTCONV_OK) return st;
-        // ragged sides: zero-padded copies of x and dy ahead of the padded call's workspace
-        *bytes = (ragged(desc) ? 2 * align256(act_bytes(&pd)) : 0) + ch.total_bytes;
-        return WTCONV_OK;
-    }
+    case WTCONV_OP_BWD_WEIGHT: return wgrad_workspace(desc, 0, bytes);
     default: return WTCONV_ERR_UNSUPPORTED;
     }
 }
 
-wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
-                                       const float *w_base, const float *bias, const float *s_base,
-                                       const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
-                                       float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
-                                       size_t workspace_bytes, wtconv_stream_t stream)
+// The weight backward; nobase: the base gradients are not wanted (the nested
+// call for the deeper levels of a larger layer, which writes them to
+// scratch): the whole-plane and tiled kernels skip them and write 0.
+static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, const void *dy, const float *w_base,
+                                  const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+                                  float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                                  void *workspace, size_t workspace_bytes, wtconv_stream_t stream, int nobase)
 {
     wtconv_status_t st = check_desc(desc);
     if (st != WTCONV_OK) return st;
@@ -500,7 +511,7 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
         const wtconv_desc_t pd = padded_desc(desc);
         if ((st = check_desc(&pd)) != WTCONV_OK) return st;
         size_t need = 0;
-        if ((st = wtconv_workspace_size(desc, WTCONV_OP_BWD_WEIGHT, &need)) != WTCONV_OK) return st;
+        if ((st = wgrad_workspace(desc, nobase, &need)) != WTCONV_OK) return st;
         if (!workspace || workspace_bytes < need) return WTCONV_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
         const size_t a = align256(act_bytes(&pd));
@@ -512,11 +523,11 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
             wtc_launch_repack(desc->dtype, dy, ws + a, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w,
                               s) != hipSuccess)
             return WTCONV_ERR_HIP;
-        return wtconv_backward_weight(&pd, ws, ws + a, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
-                                      dw_lvl, ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream);
+        return wgrad_pass(&pd, ws, ws + a, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl,
+                          ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream, nobase);
     }
     WgradChoice ch;
-    if ((st = choose_wgrad(desc, &ch)) != WTCONV_OK) return st;
+    if ((st = choose_wgrad(desc, &ch, nobase)) != WTCONV_OK) return st;
     if (!workspace || workspace_bytes < ch.total_bytes) return WTCONV_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
@@ -539,9 +550,11 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
         float *scratch = (float *)(lld + ch.quarter);
         char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
         const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
-        return wtconv_backward_weight(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C,
-                                      scratch, scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk,
-                                      ds_lvl + 4 * C, sub, ch.sub_bytes, stream);
+        // levels 2..L: the layer with L - 1 levels on the low-pass maps, its
+        // base gradients not wanted (written to scratch)
+        return wgrad_pass(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C, scratch,
+                          scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk, ds_lvl + 4 * C, sub,
+                          ch.sub_bytes, stream, 1);
     }
     if (ch.whole) {
         e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
@@ -566,6 +579,16 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
         e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels, ch.groups, ch.plen, partial, w_base,
                                       bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
     return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+}
+
+wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                       const float *w_base, const float *bias, const float *s_base,
+                                       const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                       float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
+                                       size_t workspace_bytes, wtconv_stream_t stream)
+{
+    return wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl,
+                      workspace, workspace_bytes, stream, 0);
 }
 
 wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,

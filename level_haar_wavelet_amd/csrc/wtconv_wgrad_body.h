@@ -77,6 +77,9 @@ struct WtcWgradPlan {
     // one tile, lh = 0, origins (r, r).
     int32_t tiled, ih, iw, tiles_x, tiles_y, units;
     int32_t lh, xr, xc, u1r, u1c;
+    // the base gradients are not wanted (the deeper levels of a larger
+    // layer): the base map has no pieces and its partial-row entries are 0
+    int32_t nobase;
 };
 
 // stride of one thread's parked accumulators: k*k + 1 rounded up to odd
@@ -120,7 +123,7 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     for (int32_t g = 0; g < p->nmaps; ++g) {
         const int32_t m = g == 0 ? 0 : (g - 1) / 4 + 1;
         p->first[g] = np;
-        np += ((p->h >> m) + P - 1) / P * (((p->w >> m) + P - 1) / P);
+        if (g > 0 || !p->nobase) np += ((p->h >> m) + P - 1) / P * (((p->w >> m) + P - 1) / P);
     }
     p->first[p->nmaps] = np;
     p->npieces = np;
@@ -166,9 +169,10 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
 
 static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                         int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
-                                        int32_t budget_floats, int32_t ih, int32_t iw)
+                                        int32_t budget_floats, int32_t ih, int32_t iw, int32_t nobase)
 {
     const int32_t r = k / 2;
+    p->nobase = nobase && levels >= 1;
     p->n = n;
     p->c = c;
     p->h = h;
@@ -220,21 +224,25 @@ static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, i
     return p->lds_floats <= budget_floats ? 0 : -1;
 }
 
+// nobase: the base gradients are not wanted (L >= 1 only).
 static inline int wtc_make_wgrad_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                       int32_t levels, int32_t nthreads, int32_t planes, int32_t elem_bytes,
-                                      int32_t budget_floats)
+                                      int32_t budget_floats, int32_t nobase = 0)
 {
-    return wtc_wgrad_plan_common(p, n, c, h, w, k, levels, nthreads, planes, elem_bytes, budget_floats, h, w);
+    return wtc_wgrad_plan_common(p, n, c, h, w, k, levels, nthreads, planes, elem_bytes, budget_floats, h, w,
+                                 nobase);
 }
 
 // Tiled plan: th x tw tiles of ih x iw images, L = 1 (base and level-1
 // gradients) or L = 0.
 static inline int wtc_make_wgrad_tile_plan(WtcWgradPlan *p, int32_t n, int32_t c, int32_t ih, int32_t iw,
                                            int32_t th, int32_t tw, int32_t k, int32_t levels, int32_t nthreads,
-                                           int32_t planes, int32_t elem_bytes, int32_t budget_floats)
+                                           int32_t planes, int32_t elem_bytes, int32_t budget_floats,
+                                           int32_t nobase = 0)
 {
     if (th == ih && tw == iw) return -1;
-    return wtc_wgrad_plan_common(p, n, c, th, tw, k, levels, nthreads, planes, elem_bytes, budget_floats, ih, iw);
+    return wtc_wgrad_plan_common(p, n, c, th, tw, k, levels, nthreads, planes, elem_bytes, budget_floats, ih, iw,
+                                 nobase);
 }
 
 template <typename T>

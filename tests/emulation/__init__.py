@@ -51,10 +51,10 @@ def _load():
         lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
         lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
-        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 12 + [ci, ci, ci]
+        lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 12 + [ci, ci, ci, ci]
         lib.emu_wgrad_tiles.restype = ci
         lib.emu_whole_plan.restype = ci
-        lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_wgrad.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci, ci]
         lib.emu_wgrad.restype = ci
         lib.emu_wgrad_plan.argtypes = [ci] * 10 + [ctypes.POINTER(ci)]
         lib.emu_wgrad_plan.restype = ci
@@ -144,7 +144,7 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
 
 
 def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32", nthreads=256, planes=1,
-                budget_floats=40960, lowpass=False):
+                budget_floats=40960, lowpass=False, nobase=False):
     """Base and level-1 parameter gradients through the emulated tiled
     weight-gradient pass (w_lvl / s_lvl: level 1 only, or None for L = 0);
     with lowpass=True also the level-1 low-pass maps of x and dy it writes."""
@@ -163,7 +163,7 @@ def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32
     lls = [np.full((n, c, ih // 2, iw // 2), np.nan, npdt) for _ in range(2)] if lowpass else [None, None]
     rc = lib.emu_wgrad_tiles(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, ih, iw, th, tw, k,
                              levels, *[ptr(a) for a in keep], *optr, *[ptr(a) for a in lls], nthreads, planes,
-                             budget_floats)
+                             budget_floats, int(nobase))
     if rc != 0:
         raise ValueError("emu_wgrad_tiles failed: %d" % rc)
     res = [o.astype(np.float64) for o in outs]
@@ -187,8 +187,9 @@ def choose_planes(n, c, slots, fixed):
 
 
 def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nthreads=256, planes=1,
-          budget_floats=40960, tiled=False):
-    """Parameter gradients through the emulated fused weight-gradient kernel."""
+          budget_floats=40960, tiled=False, nobase=False):
+    """Parameter gradients through the emulated fused weight-gradient kernel
+    (nobase: the base gradients skipped and written as 0; whole-plane only)."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -202,7 +203,8 @@ def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nth
     ptr = lambda a: None if a is None else a.ctypes.data
     fn = lib.emu_wgrad_tiled if tiled else lib.emu_wgrad
     rc = fn(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, h, w, k, levels,
-            *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes, budget_floats)
+            *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes, budget_floats,
+            *(() if tiled else (int(nobase),)))
     if rc != 0:
         raise ValueError("emu_wgrad failed: %d" % rc)
     outs[3] = outs[3][:levels]

@@ -336,14 +336,15 @@ int emu_wgrad_tiled(int dtype, const void *x, const void *dy, int n, int c, int 
 }
 
 // Parameter gradients through the fused weight-gradient phases and the
-// fixed-order finalize.  Outputs overwritten, fp32.
+// fixed-order finalize.  Outputs overwritten, fp32.  nobase: the base
+// gradients are skipped (written as 0), as in the nested call for deeper levels.
 int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int w, int k, int levels,
               const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
               float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl, int nthreads, int planes,
-              int budget_floats)
+              int budget_floats, int nobase)
 {
     WtcWgradPlan p;
-    if (wtc_make_wgrad_plan(&p, n, c, h, w, k, levels, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats))
+    if (wtc_make_wgrad_plan(&p, n, c, h, w, k, levels, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats, nobase))
         return -1;
     std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
     int rc;
@@ -368,11 +369,11 @@ int emu_wgrad(int dtype, const void *x, const void *dy, int n, int c, int h, int
 int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int ih, int iw, int th, int tw, int k,
                     int levels, const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
                     const float *s_lvl, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
-                    void *llx, void *lld, int nthreads, int planes, int budget_floats)
+                    void *llx, void *lld, int nthreads, int planes, int budget_floats, int nobase)
 {
     WtcWgradPlan p;
     if (wtc_make_wgrad_tile_plan(&p, n, c, ih, iw, th, tw, k, levels, nthreads, planes, dtype == 0 ? 4 : 2,
-                                 budget_floats))
+                                 budget_floats, nobase))
         return -1;
     std::vector<float> partial((size_t)p.groups * p.c * p.plen, __builtin_nanf(""));
     int rc;

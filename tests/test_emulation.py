@@ -353,6 +353,50 @@ def test_emulated_tiled_weight_gradients_write_the_low_pass_maps(orc, case):
         assert np.abs(ll - ref).max() <= tol * (1 + np.abs(ref).max())
 
 
+WGRAD_NOBASE = [
+    # n, c, h, w, k, L, nthreads, dtype
+    (2, 3, 32, 32, 5, 1, 256, "f32"),
+    (3, 2, 28, 28, 3, 2, 256, "f16"),
+    (1, 2, 64, 64, 5, 1, 256, "f32"),
+    (2, 2, 32, 48, 7, 3, 512, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", WGRAD_NOBASE, ids=lambda c: "x".join(map(str, c)))
+def test_emulated_weight_gradients_without_the_base_path(orc, case):
+    """The nested call for the deeper levels wants only the level gradients:
+    the base map gets no pieces, its gradients come out as 0 (the scale
+    gradient of the base is then s0 . 0 = 0), and every level gradient equals
+    the oracle's."""
+    n, c, h, w, k, L, nth, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=11 * h + L)
+    got = emu.wgrad(inp.x, inp.dy, inp.w_base, None, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, dtype=dt,
+                    nthreads=nth, planes=2, budget_floats=1 << 15, nobase=True)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, None, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    tol = 2e-6 if dt == "f32" else 5e-3
+    for gg in got[:3]:
+        assert np.array_equal(gg, np.zeros_like(gg))
+    for gg, rr in zip(got[3:], ref[3:]):
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= tol
+
+
+def test_emulated_tiled_weight_gradients_without_the_base_path(orc):
+    """The same for the tiled pass (the nested call on 128 x 128 maps of a
+    256 x 256 layer): level-1 gradients equal the oracle's, base ones 0, and
+    the low-pass maps still written."""
+    n, c, h, w, k, th, tw = 2, 2, 64, 64, 5, 32, 16
+    inp = make_inputs(n, c, h, w, k, 1, seed=5)
+    got, (llx, lld) = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, None, inp.s_base, inp.w_lvl, inp.s_lvl, k, th, tw,
+                                      planes=3, budget_floats=1 << 16, lowpass=True, nobase=True)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, None, inp.s_base, inp.w_lvl, inp.s_lvl, k, 1)
+    for gg in got[:3]:
+        assert np.array_equal(gg, np.zeros_like(gg))
+    for gg, rr in zip(got[3:], ref[3:]):
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
+    assert np.abs(llx - _lowpass(inp.x.astype(np.float64))).max() <= 1e-6 * (1 + np.abs(llx).max())
+    assert np.abs(lld - _lowpass(inp.dy.astype(np.float64))).max() <= 1e-6 * (1 + np.abs(lld).max())
+
+
 @pytest.mark.parametrize("L", [2, 3, 4])
 def test_deeper_level_gradients_are_the_layer_on_the_low_pass_maps(orc, L):
     """The decomposition the large-plane weight gradient relies on, checked on
