@@ -86,10 +86,58 @@ def workload_name(wl) -> str:
                                            "fp32" if wl.dtype == "f32" else "fp16 storage")
 
 
+_BUILTIN = {"f": "float", "d": "double", "i": "int", "j": "unsigned int", "b": "bool", "DF16_": "_Float16"}
+
+
+def _demangle(name: str) -> str:
+    """Function name and template arguments of an Itanium-mangled kernel name
+    (the subset of the grammar kernel names here use: an optional nested name,
+    builtin types and integer literals as template arguments); other names are
+    returned unchanged."""
+    if not name.startswith("_Z"):
+        return name
+    i, parts = 2, []
+
+    def ident(i):
+        j = i
+        while j < len(name) and name[j].isdigit():
+            j += 1
+        n = int(name[i:j])
+        return name[j:j + n], j + n
+
+    try:
+        if name[i] == "N":
+            i += 1
+            while name[i].isdigit():
+                part, i = ident(i)
+                parts.append(part)
+        else:
+            part, i = ident(i)
+            parts.append(part)
+        base = [p for p in parts if not p.startswith("_GLOBAL__N")][-1]
+        if i >= len(name) or name[i] != "I":
+            return base
+        i += 1
+        args = []
+        while name[i] != "E":
+            if name[i] == "L":
+                j = name.index("E", i)
+                t, v = name[i + 1], name[i + 2:j]
+                args.append(("true" if v == "1" else "false") if t == "b" else v.replace("n", "-"))
+                i = j + 1
+            else:
+                key = next(k for k in sorted(_BUILTIN, key=len, reverse=True) if name.startswith(k, i))
+                args.append(_BUILTIN[key])
+                i += len(key)
+        return "%s<%s>" % (base, ", ".join(args))
+    except (ValueError, IndexError, StopIteration):
+        return name
+
+
 def _short_kernel(name: str) -> str:
     """Kernel name without the return type and the parameter list, as profilers
-    print it in either form."""
-    name = name.strip()
+    print it in any of its forms (plain, with its signature, or mangled)."""
+    name = _demangle(name.strip())
     if name.startswith("void "):
         name = name[5:]
     depth = 0

@@ -112,3 +112,15 @@ def test_traffic_summary_scales_counters_by_the_copy_calibration(tmp_path):
     saved = json.load(open(tmp_path / "hbm_traffic.json"))
     assert set(saved) == {out["workload"], out2["workload"]}
     assert (tmp_path / "stage1_hbm_traffic.md").read_text().count("rocprofv3 --pmc") == 4
+
+
+@pytest.mark.parametrize("raw, short", [
+    ("_Z19wtconv_whole_kernelIDF16_Li5ELi4ELb1EEv12WtcWholeArgsIT_E", "wtconv_whole_kernel<_Float16, 5, 4, true>"),
+    ("_Z19wtconv_wgrad_kernelIfLi5ELi4ELi3ELb0EEv12WtcWgradArgsIT_E", "wtconv_wgrad_kernel<float, 5, 4, 3, false>"),
+    ("_ZN12_GLOBAL__N_114lowpass_kernelIDF16_EEvPKT_PS1_lii", "lowpass_kernel<_Float16>"),
+    ("void wtconv_whole_kernel<float, 5, 4, false>(WtcWholeArgs<float>)", "wtconv_whole_kernel<float, 5, 4, false>"),
+    ("wtconv_wgrad_finalize_kernel(int, int, float const*)", "wtconv_wgrad_finalize_kernel"),
+    ("__amd_rocclr_copyBuffer", "__amd_rocclr_copyBuffer"),
+])
+def test_profiler_kernel_names_are_shortened(raw, short):
+    assert bench._short_kernel(raw) == short
