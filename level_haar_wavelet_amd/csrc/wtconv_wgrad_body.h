@@ -346,13 +346,13 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
 #else
             if constexpr (VEC * sizeof(T) == 16) {
                 typedef float v4 __attribute__((ext_vector_type(4)));
-                v4 d0 = __builtin_nontemporal_load((const v4 *)(a.x + e));
+                v4 d0 = wtc_stream_load<v4, !TL>((const v4 *)(a.x + e));
                 v4 d1 = __builtin_nontemporal_load((const v4 *)(a.dy + e));
                 __builtin_memcpy(&ctx.prex[q][0], &d0, 16);
                 __builtin_memcpy(&ctx.prey[q][0], &d1, 16);
             } else if constexpr (VEC * sizeof(T) == 8) {
                 typedef float v2 __attribute__((ext_vector_type(2)));
-                v2 d0 = __builtin_nontemporal_load((const v2 *)(a.x + e));
+                v2 d0 = wtc_stream_load<v2, !TL>((const v2 *)(a.x + e));
                 v2 d1 = __builtin_nontemporal_load((const v2 *)(a.dy + e));
                 __builtin_memcpy(&ctx.prex[q][0], &d0, 8);
                 __builtin_memcpy(&ctx.prey[q][0], &d1, 8);

@@ -356,6 +356,20 @@ WTC_HD WTC_INLINE void wtc_whole_fold(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     }
 }
 
+#ifndef WTC_EMULATE
+// Input loads: non-temporal where every element is read once (whole planes);
+// plain in tiled plans, whose halos are read again by the neighbouring tiles
+// (the same workgroup's next units), so the lines are worth keeping in L2.
+template <typename V, bool NT>
+static __device__ __forceinline__ V wtc_stream_load(const V *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+#endif
+
 // Elements per global chunk: 16 bytes, or the output block width if smaller
 // (the plan picks the same value from the image width).
 template <typename T, int BW>
@@ -412,14 +426,14 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 #else
             if constexpr (vec * sizeof(T) == 16) {
                 typedef float v4 __attribute__((ext_vector_type(4)));
-                v4 d = __builtin_nontemporal_load((const v4 *)(src + e));
+                v4 d = wtc_stream_load<v4, !TL>((const v4 *)(src + e));
                 __builtin_memcpy(&ctx.pre[q][0], &d, 16);
             } else if constexpr (vec * sizeof(T) == 8) {
                 typedef float v2 __attribute__((ext_vector_type(2)));
-                v2 d = __builtin_nontemporal_load((const v2 *)(src + e));
+                v2 d = wtc_stream_load<v2, !TL>((const v2 *)(src + e));
                 __builtin_memcpy(&ctx.pre[q][0], &d, 8);
             } else if constexpr (vec * sizeof(T) == 4) {
-                float d = __builtin_nontemporal_load((const float *)(src + e));
+                float d = wtc_stream_load<float, !TL>((const float *)(src + e));
                 __builtin_memcpy(&ctx.pre[q][0], &d, 4);
             } else {
 #pragma unroll
