@@ -54,7 +54,10 @@
  *              host synchronisation; outputs are ready when the stream reaches
  *              that point.  Inputs and outputs must not overlap (y != x,
  *              dx != dy).  Results are bitwise reproducible run to run (no
- *              floating-point atomics).
+ *              floating-point atomics).  Only kernels are enqueued (no memset,
+ *              copy or allocation), so calls may be captured into a HIP graph
+ *              on a capturing stream and replayed; the workspace and buffers
+ *              captured must then stay allocated.
  * Errors       Arguments are validated before any HIP call; a bad argument
  *              returns its status code and enqueues nothing.  A failed kernel
  *              launch returns WTCONV_ERR_HIP.  Asynchronous faults are reported
