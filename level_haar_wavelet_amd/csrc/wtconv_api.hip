@@ -20,6 +20,7 @@ namespace {
 constexpr int kFusedThreads = 256;
 constexpr int kWholeThreads = 256;     // whole-plane forward / data backward: 256 or 512 threads
 constexpr int kWholeWideItems = 384;  // convolution pieces per image from which 512 threads pay
+constexpr int kStackItems = 192;      // at most this many pieces per image: two images per pass
 constexpr int kMaxLdsFloats = 160 * 1024 / 4;
 
 // LDS budget of one fused workgroup.  The default keeps two workgroups per
@@ -129,13 +130,24 @@ bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp, int noba
         (!nobase || wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                         wth ? wth : kWholeThreads, 1, eb, whole_budget_floats(), nobase)))
         return false;
+    // small planes (few pieces per image): two images per pass, stacked down
+    // one plane with zero rows between them, so that a pass fills more of
+    // the workgroup's waves and its barriers are paid once for both
+    // (WTCONV_STACK=1 switches it off)
+    int stack = 1;
+    if (!nobase && d->levels >= 1 && wp->items <= kStackItems && env_int("WTCONV_STACK", 2, 1, 2) == 2 &&
+        wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                            wth ? wth : kWholeThreads, 1, eb, whole_budget_floats(), 0, 2) == 0)
+        stack = 2;
     if (!wth) wth = wp->items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
     if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1, eb,
-                            whole_budget_floats(), nobase))
+                            whole_budget_floats(), nobase, stack))
         return false;
-    const int planes = pick_planes(d, wtc_whole_resident(d->dtype, wp[0]), kWholeFixed, "WTCONV_PLANES");
+    wtconv_desc_t units = *d;  // the units of work: images, or stacks of two
+    units.n = wp->units;
+    const int planes = pick_planes(&units, wtc_whole_resident(d->dtype, wp[0]), kWholeFixed, "WTCONV_PLANES");
     wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, planes, eb,
-                        whole_budget_floats(), nobase);
+                        whole_budget_floats(), nobase, stack);
     return true;
 }
 

@@ -11,7 +11,9 @@
 // clobber keeps the compiler from moving LDS accesses across it.
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <typename T, int K, int BW, bool TL>
+// ST: stacked small planes (two images per pass); a kernel instance of its
+// own, so that the other plans carry none of its row checks
+template <typename T, int K, int BW, bool TL, bool ST>
 __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
@@ -20,7 +22,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     ctx.tid = threadIdx.x;
     ctx.nth = blockDim.x;
     wtc_whole_setup<T>(a, ctx, blockIdx.x);
-    wtc_whole_load<T, K, BW, TL>(a, ctx, 0);
+    wtc_whole_load<T, K, BW, TL, ST>(a, ctx, 0);
     wtc_whole_init<T, K>(a, ctx);
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(a, ctx);
@@ -31,9 +33,9 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     // so the wait for a prefetched input never waits for output stores issued
     // just before it (loads and stores share one counter) and the loads do
     // not queue behind the stores.
-    wtc_whole_stage<T, K, BW, TL>(a, ctx);
+    wtc_whole_stage<T, K, BW, TL, ST>(a, ctx);
     wtc_lds_barrier();
-    if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL>(a, ctx, 1);
+    if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL, ST>(a, ctx, 1);
     for (int img = 0; img < ctx.nimg; ++img) {
         for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
@@ -44,19 +46,19 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
         // the convolutions above have finished reading the input and analysis
         // maps, which the staging of the next image overwrites; the output
         // pass reads only the convolution outputs
-        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL>(a, ctx);
-        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL>(a, ctx, img + 2);
-        wtc_whole_select<T>(a, ctx, img);
-        wtc_whole_out<T, K, BW, TL>(a, ctx);
+        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx);
+        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL, ST>(a, ctx, img + 2);
+        wtc_whole_select<T, ST>(a, ctx, img);
+        wtc_whole_out<T, K, BW, TL, ST>(a, ctx);
         wtc_lds_barrier();
     }
 }
 
-template <typename T, int K, int BW, bool TL>
+template <typename T, int K, int BW, bool TL, bool ST>
 static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL>;
+    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -67,14 +69,16 @@ static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *r
     }
     const unsigned groups = (unsigned)((a.p.units + a.p.planes - 1) / a.p.planes);
     const unsigned blocks = groups * (unsigned)a.p.c;
-    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL, ST>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, int K, int BW>
 static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
-    return a.p.tiled ? launch_tl<T, K, BW, true>(a, stream, resident) : launch_tl<T, K, BW, false>(a, stream, resident);
+    if (a.p.tiled) return launch_tl<T, K, BW, true, false>(a, stream, resident);
+    return a.p.stack > 1 ? launch_tl<T, K, BW, false, true>(a, stream, resident)
+                         : launch_tl<T, K, BW, false, false>(a, stream, resident);
 }
 
 template <typename T, int K>

@@ -72,6 +72,12 @@ struct WtcWholePlan {
     // the base path is known to be zero (the deeper levels of a larger layer,
     // whose base scale is 0): no base convolution pieces, no base output read
     int32_t nobase;
+    // Small planes: `stack` images of sh rows stacked down one plane of h
+    // rows, separated by sgap zero rows (r rows at every level's resolution,
+    // so no convolution window reaches from one image into the next); a unit
+    // is then a stack of images.  1: one image per plane.  Stacked plans run
+    // a kernel instance of their own (ST), so the others carry no checks.
+    int32_t stack, sh, sgap;
 };
 
 #define WTC_WP 4  // piece side (outputs)
@@ -139,10 +145,20 @@ WTC_HD WTC_INLINE int wtc_whole_first_deep(const WtcWholePlan &p)
 static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                         int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
                                         int32_t elem_bytes, int32_t budget_floats, int32_t ih, int32_t iw,
-                                        int32_t nobase)
+                                        int32_t nobase, int32_t stack = 1)
 {
     const int32_t r = k / 2;
     p->nobase = nobase && levels >= 1;
+    p->stack = stack < 2 ? 1 : stack;
+    p->sh = h;
+    p->sgap = 0;
+    if (p->stack > 1) {
+        if (ih != h || iw != w || levels < 1 || levels > WTC_MAXL) return -1;
+        if (h % wtc_max(4, 1 << levels)) return -1;  // whole staging groups and level cells per image
+        p->sgap = wtc_roundup(r << levels, wtc_max(4, 1 << levels));
+        h = p->stack * h + (p->stack - 1) * p->sgap;
+        ih = h;
+    }
     p->n = n;
     p->c = c;
     p->h = h;
@@ -158,6 +174,7 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     p->tiles_y = ih / h;
     p->tiles_x = iw / w;
     p->units = n * p->tiles_y * p->tiles_x;
+    if (p->stack > 1) p->units = (n + p->stack - 1) / p->stack;
     p->planes = planes < 1 ? 1 : (planes > p->units ? p->units : planes);
     // L = 0 (a plain depthwise convolution) needs even sides: the staging and
     // output passes work on 2-row groups and blocks
@@ -208,12 +225,14 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
 
 // nobase: the base path is zero (L >= 1 only; the base weights, bias and
 // scale are then not read).
+// stack: images stacked per plane (small planes; L >= 1).
 static inline int wtc_make_whole_plan(WtcWholePlan *p, int32_t n, int32_t c, int32_t h, int32_t w, int32_t k,
                                       int32_t levels, int32_t rotate, int32_t nthreads, int32_t planes,
-                                      int32_t elem_bytes, int32_t budget_floats, int32_t nobase = 0)
+                                      int32_t elem_bytes, int32_t budget_floats, int32_t nobase = 0,
+                                      int32_t stack = 1)
 {
     return wtc_whole_plan_common(p, n, c, h, w, k, levels, rotate, nthreads, planes, elem_bytes, budget_floats, h,
-                                 w, nobase);
+                                 w, nobase, stack);
 }
 
 // Tiled plan: th x tw tiles of ih x iw images, L = 1 (plus the added low-pass
@@ -257,6 +276,7 @@ struct WtcWholeCtx {
     int64_t plane;  // current unit's plane index (n * C + c)
     int vmask;     // rows of the prefetched group that lie in the image (bit q)
     float u2;      // the group's level-2 low-pass sum (for level 3 across the lane quad)
+    int cur;       // unit of the output pass (stacked plans)
     T pre[4][16 / sizeof(T)];
 #ifdef WTC_EMULATE
     int64_t lds_n, img_n;
@@ -316,13 +336,20 @@ WTC_HD WTC_INLINE void wtc_whole_unit(const WtcWholeArgs<T> &a, const WtcWholeCt
     tx0 = (t - ty * p.tiles_x) * p.w;
 }
 
-template <typename T>
+template <typename T, bool ST = false>
 WTC_HD WTC_INLINE void wtc_whole_select(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
     const int64_t hw = (int64_t)a.p.ih * a.p.iw;
     wtc_whole_unit(a, ctx, img, ctx.plane, ctx.ty0, ctx.tx0);
-    ctx.in = a.in + ctx.plane * hw;
-    ctx.out = a.out + ctx.plane * hw;
+    if constexpr (ST) {
+        // stacked plans address every output row on its own, from the tensor base
+        ctx.cur = img;
+        ctx.in = a.in;
+        ctx.out = a.out;
+    } else {
+        ctx.in = a.in + ctx.plane * hw;
+        ctx.out = a.out + ctx.plane * hw;
+    }
 }
 
 // Phase: zero all of LDS (once per workgroup) and fold the channel's weights.
@@ -382,7 +409,7 @@ struct WtcVec {
 // group, so that no branch surrounds the loads).
 // TL: tiled plan (halo loads, bounds, shifted map origins, the added
 // low-pass term); untiled plans compile without any of it.
-template <typename T, int K, int BW, bool TL>
+template <typename T, int K, int BW, bool TL, bool ST = false>
 WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
     const WtcWholePlan &p = a.p;
@@ -397,16 +424,29 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 #endif
     int64_t plane;
     int ty0 = 0, tx0 = 0;
-    if constexpr (TL)
+    int grow0 = p.gr * ctx.grow;  // the group's first row in its image
+    bool sval = true;             // stacked plans: the group lies in an image
+    if constexpr (TL) {
         wtc_whole_unit(a, ctx, img, plane, ty0, tx0);
-    else
+    } else if constexpr (ST) {
+        // image `sub` of the stack, or the zero rows between images (or an
+        // image past the batch): those load image 0's first rows and are
+        // zeroed when staged
+        const int per = p.sh + p.sgap, sub = grow0 / per;
+        const int im = (ctx.n0 + img) * p.stack + sub;
+        grow0 -= sub * per;
+        sval = grow0 < p.sh && im < p.n;
+        plane = (int64_t)(sval ? im : 0) * p.c + ctx.c;
+        if (!sval) grow0 = 0;
+    } else {
         plane = (int64_t)(ctx.n0 + img) * p.c + ctx.c;
-    const T *src = a.in + plane * ((int64_t)p.ih * p.iw);
+    }
+    const T *src = a.in + plane * ((int64_t)(ST ? p.sh : p.ih) * p.iw);
     // image row / column of the group's first element; in tiled plans rows
     // and segments outside the image load a clamped address and are zeroed
     // when staged
     const int lh = TL ? p.lh : 0;
-    const int row0 = ty0 - lh + p.gr * ctx.grow, col = tx0 - lh + vec * ctx.gcol;
+    const int row0 = ty0 - lh + grow0, col = tx0 - lh + vec * ctx.gcol;
     const bool colok = !TL || (col >= 0 && col < p.iw);
     const int ccol = TL ? wtc_min(wtc_max(col, 0), p.iw - vec) : col;
     int vm = 0;
@@ -417,11 +457,11 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     for (int q = 0; q < 4; ++q) {
         if (q < p.gr) {
             const int row = row0 + q;
-            vm |= (!TL || (colok && row >= 0 && row < p.ih)) ? (1 << q) : 0;
+            vm |= (TL ? (colok && row >= 0 && row < p.ih) : (!ST || sval)) ? (1 << q) : 0;
             const int64_t e = TL ? (int64_t)wtc_min(wtc_max(row, 0), p.ih - 1) * p.iw + ccol
                                  : e0 + (int64_t)q * p.iw;
 #ifdef WTC_EMULATE
-            const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.ih * p.iw;
+            const int64_t base = src - a.in, all = (int64_t)p.n * p.c * (ST ? p.sh : p.ih) * p.iw;
             for (int t = 0; t < vec; ++t) ctx.pre[q][t] = wtc_chk(a.in, base + e + t, all, __LINE__);
 #else
             if constexpr (vec * sizeof(T) == 16) {
@@ -511,7 +551,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage_l3(const WtcWholeArgs<T> &a, WtcWholeCtx<
 // (and level 2 when the group has 4 rows) of it straight from registers:
 //   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
 //   U_2 and B_2^1..3 at its 1 x (vec/4) level-2 positions.
-template <typename T, int K, int BW, bool TL>
+template <typename T, int K, int BW, bool TL, bool ST = false>
 WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int R = K / 2;
@@ -525,7 +565,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < vec; ++t)
-            x[q][t] = (q < p.gr && (!TL || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+            x[q][t] = (q < p.gr && ((!TL && !ST) || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
     // r0, c0: the group's position in the loaded region (the tile plus lh);
     // map origins are the plan's in tiled plans, (r, r) otherwise
     const int lh = TL ? p.lh : 0, xr = TL ? p.xr : R, xc = TL ? p.xc : R;
@@ -805,7 +845,7 @@ WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 // the 2x2 butterfly, the deeper levels through the closed form with the
 // coordinate bits picking the signs, added to the low-pass input of the
 // butterfly; one rounding, one store.
-template <typename T, int K, int BW, bool TL>
+template <typename T, int K, int BW, bool TL, bool ST = false>
 WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int Q = BW / 2;
@@ -900,8 +940,16 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
             acc[1][2 * q] += d01 + d23;
             acc[1][2 * q + 1] += d01 - d23;
         }
-        const int64_t o0 = TL ? (int64_t)(ctx.ty0 + 2 * by) * p.iw + ctx.tx0 + BW * bx
-                              : (int64_t)wtc_mul24(2 * by, p.w) + BW * bx;
+        int64_t o0 = TL ? (int64_t)(ctx.ty0 + 2 * by) * p.iw + ctx.tx0 + BW * bx
+                        : (int64_t)wtc_mul24(2 * by, p.w) + BW * bx;
+        if constexpr (ST) {
+            // the block's image in the stack and its row there; blocks in the
+            // zero rows between images (or past the batch) store nothing
+            const int per = p.sh + p.sgap, sub = (2 * by) / per, rr = 2 * by - sub * per;
+            const int im = (ctx.n0 + ctx.cur) * p.stack + sub;
+            if (rr >= p.sh || im >= p.n) continue;
+            o0 = (((int64_t)im * p.c + ctx.c) * p.sh + rr) * p.iw + BW * bx;
+        }
 #ifdef WTC_EMULATE
         for (int dr = 0; dr < 2; ++dr)
             for (int e = 0; e < BW; ++e) WTC_WOUT(ctx, o0 + dr * p.iw + e) = wtc_from_float<T>(acc[dr][e]);

@@ -46,7 +46,7 @@ def _load():
         lib.emu_fused.restype = ci
         lib.emu_fused_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci)]
         lib.emu_fused_plan.restype = ci
-        lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci, ci]
+        lib.emu_whole.argtypes = [ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci]
         lib.emu_whole.restype = ci
         lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
@@ -103,9 +103,10 @@ def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f
 
 
 def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32", nthreads=256, planes=1,
-          budget_floats=40960, nobase=False):
+          budget_floats=40960, nobase=False, stack=1):
     """Run the whole-plane kernel on the CPU emulation (nobase: without the
-    base path, as in the nested call for the deeper levels)."""
+    base path, as in the nested call for the deeper levels; stack: images
+    stacked per plane)."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -114,7 +115,7 @@ def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
     rc = lib.emu_whole(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, k, levels,
-                       rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats, int(nobase))
+                       rotate, *[ptr(a) for a in keep], nthreads, planes, budget_floats, int(nobase), stack)
     if rc != 0:
         raise ValueError("emu_whole failed: %d" % rc)
     return out.astype(np.float64)

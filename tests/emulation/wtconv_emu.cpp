@@ -91,7 +91,7 @@ static void emu_stage_l3(const WtcWholeArgs<T> &a, std::vector<WtcWholeCtx<T>> &
     }
 }
 
-template <typename T, int K, int BW, bool TL>
+template <typename T, int K, int BW, bool TL, bool ST = false>
 static void run_whole(const WtcWholeArgs<T> &a)
 {
     const WtcWholePlan &p = a.p;
@@ -108,32 +108,33 @@ static void run_whole(const WtcWholeArgs<T> &a)
             ctx[t].tid = t;
             ctx[t].nth = nth;
             ctx[t].lds_n = p.lds_floats;
-            ctx[t].img_n = (int64_t)p.ih * p.iw;
+            // stacked plans address outputs from the tensor base
+            ctx[t].img_n = ST ? (int64_t)p.n * p.c * p.sh * p.iw : (int64_t)p.ih * p.iw;
             wtc_whole_setup<T>(a, ctx[t], bid);
         }
-        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, TL>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], 0);
         for (int t = 0; t < nth; ++t) wtc_whole_init<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_fold<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_table<T, K, BW>(a, ctx[t]);
         // the kernel's software pipeline: image i+1 is staged in the same
         // barrier interval as image i's output pass (here every staging runs
         // first, so a staging write that the output pass reads would show)
-        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx[t]);
         if (p.stage_l3) emu_stage_l3(a, ctx);
         for (int t = 0; t < nth; ++t)
-            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL>(a, ctx[t], 1);
+            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], 1);
         for (int img = 0; img < ctx[0].nimg; ++img) {
             for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
             for (int t = 0; t < nth; ++t) {
-                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL>(a, ctx[t]);
-                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL>(a, ctx[t], img + 2);
+                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx[t]);
+                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], img + 2);
             }
             if (p.stage_l3 && img + 1 < ctx[0].nimg) emu_stage_l3(a, ctx);
             for (int t = 0; t < nth; ++t) {
-                wtc_whole_select<T>(a, ctx[t], img);
-                wtc_whole_out<T, K, BW, TL>(a, ctx[t]);
+                wtc_whole_select<T, ST>(a, ctx[t], img);
+                wtc_whole_out<T, K, BW, TL, ST>(a, ctx[t]);
             }
         }
     }
@@ -147,6 +148,14 @@ static void run_whole_k(const WtcWholeArgs<T> &a)
         case 8: run_whole<T, K, 8, true>(a); break;
         case 4: run_whole<T, K, 4, true>(a); break;
         default: run_whole<T, K, 2, true>(a); break;
+        }
+        return;
+    }
+    if (a.p.stack > 1) {
+        switch (a.p.out_bw) {
+        case 8: run_whole<T, K, 8, false, true>(a); break;
+        case 4: run_whole<T, K, 4, false, true>(a); break;
+        default: run_whole<T, K, 2, false, true>(a); break;
         }
         return;
     }
@@ -429,11 +438,11 @@ int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, in
 
 int emu_whole(int dtype, const void *in, void *out, int n, int c, int h, int w, int k, int levels, int rotate,
               const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
-              int nthreads, int planes, int budget_floats, int nobase)
+              int nthreads, int planes, int budget_floats, int nobase, int stack)
 {
     WtcWholePlan p;
     if (wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, dtype == 0 ? 4 : 2,
-                            budget_floats, nobase))
+                            budget_floats, nobase, stack))
         return -1;
     if (dtype == 0) {
         WtcWholeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};

@@ -240,6 +240,41 @@ def test_emulated_tiled_pass_with_deeper_levels(orc, case, rotate):
         assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
 
 
+STACKED = [
+    # n, c, h, w, k, L, nthreads, planes, dtype: odd batches leave the last
+    # stack half empty
+    (4, 3, 28, 28, 5, 2, 256, 2, "f16"),
+    (3, 2, 28, 28, 5, 2, 256, 1, "f32"),
+    (5, 2, 16, 16, 5, 2, 256, 2, "f32"),
+    (2, 2, 16, 24, 3, 3, 512, 1, "f32"),
+    (3, 2, 12, 20, 7, 1, 256, 3, "f32"),
+    (2, 1, 8, 8, 1, 2, 256, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STACKED, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_stacked_small_planes(orc, case, rotate):
+    """Small planes run two images per workgroup pass, stacked down one plane
+    with zero rows between them (r rows at every level's resolution): the
+    result must be each image's own layer, and the rows between images never
+    stored (the output starts as NaN)."""
+    n, c, h, w, k, L, nth, planes, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=3 * h + w + L + rotate)
+    src = inp.x if rotate == 0 else inp.dy
+    y = emu.whole(src, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, rotate=rotate, dtype=dt,
+                  nthreads=nth, planes=planes, budget_floats=1 << 15, stack=2)
+    if rotate == 0:
+        ref = orc.forward(src, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(src, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert not np.isnan(y).any()
+    if dt == "f32":
+        _check(y, ref)
+    else:
+        assert np.linalg.norm(y - ref) / np.linalg.norm(ref) <= 5e-3
+
+
 NOBASE = [
     # n, c, h, w, k, L, nthreads, dtype
     (2, 3, 32, 32, 5, 1, 256, "f32"),
