@@ -135,10 +135,14 @@ bool whole_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *wp, int noba
     // the workgroup's waves and its barriers are paid once for both
     // (WTCONV_STACK=1 switches it off)
     int stack = 1;
-    if (!nobase && d->levels >= 1 && wp->items <= kStackItems && env_int("WTCONV_STACK", 2, 1, 2) == 2 &&
-        wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
-                            wth ? wth : kWholeThreads, 1, eb, whole_budget_floats(), 0, 2) == 0)
-        stack = 2;
+    if (!nobase && d->levels >= 1 && wp->items <= kStackItems && env_int("WTCONV_STACK", 2, 1, 2) == 2) {
+        if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                wth ? wth : kWholeThreads, 1, eb, whole_budget_floats(), 0, 2) == 0)
+            stack = 2;
+        else  // back to the one-image plan the thread count is chosen from
+            wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
+                                wth ? wth : kWholeThreads, 1, eb, whole_budget_floats());
+    }
     if (!wth) wth = wp->items >= kWholeWideItems ? 2 * kWholeThreads : kWholeThreads;
     if (wtc_make_whole_plan(wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate, wth, 1, eb,
                             whole_budget_floats(), nobase, stack))
