@@ -83,6 +83,38 @@ def test_whole_plane_thread_counts_and_image_groups(orc, case, monkeypatch):
     assert_close(dx, ref_dx, dt, "dx")
 
 
+STACKED = [
+    # n, c, h, w, k, L, dtype, images per workgroup: odd batches and odd image
+    # groups leave half-empty stacks
+    (5, 6, 28, 28, 5, 2, "f16", 0),
+    (3, 4, 16, 24, 3, 3, "f32", 0),
+    (7, 3, 28, 28, 5, 2, "f32", 3),
+    (4, 2, 12, 20, 7, 1, "f32", 1),
+]
+
+
+@pytest.mark.parametrize("case", STACKED, ids=lambda c: "x".join(map(str, c)))
+def test_stacked_small_planes_equal_one_image_per_pass(orc, case, monkeypatch):
+    """Small planes run two images per pass, stacked with zero rows between
+    them.  Every output is the same sum in the same order either way, so the
+    stacked result must equal the one-image-per-pass result bit for bit, and
+    the oracle's within the tolerance."""
+    n, c, h, w, k, L, dt, planes = case
+    _log("case %s" % (case,))
+    if planes:
+        monkeypatch.setenv("WTCONV_PLANES", str(planes))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=17 * h + w + L)
+    d = DevInputs(inp, dt)
+    y, dx = forward(d), backward_data(d)
+    monkeypatch.setenv("WTCONV_STACK", "1")
+    y1, dx1 = forward(d), backward_data(d)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y1), "stacked forward differs from one image per pass"
+    assert torch.equal(dx, dx1), "stacked data backward differs from one image per pass"
+    assert_close(y, orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "y")
+    assert_close(dx, orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "dx")
+
+
 TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
          (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32"),
          (2, 3, 64, 64, 7, 0, "f32"), (1, 4, 32, 64, 5, 0, "f16")]  # L = 0: a depthwise conv on tiles
