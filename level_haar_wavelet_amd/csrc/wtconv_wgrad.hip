@@ -39,8 +39,12 @@ __global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) 
             wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
             wtc_lds_barrier_wg();
         }
+        // low wave priority for the FMA-bound correlation, high for the
+        // latency-bound staging and analysis (as in the whole-plane kernel)
+        __builtin_amdgcn_s_setprio(0);
         wtc_wgrad_correlate<T, K, VEC, Q>(a, ctx, acc);
         wtc_lds_barrier_wg();
+        __builtin_amdgcn_s_setprio(2);
     }
 #pragma unroll
     for (int s = 0; s < Q; ++s) {
