@@ -13,7 +13,7 @@ from level_haar_wavelet_amd.synthetic import WORKLOADS, make_inputs, sweep_workl
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from tests.gpu_util import DevInputs, assert_close, backward_data, forward
+    from tests.gpu_util import DevInputs, assert_close, assert_grad_close, backward_data, backward_weight, forward
 
 
 def _log(msg):
@@ -81,6 +81,29 @@ def test_whole_plane_thread_counts_and_image_groups(orc, case, monkeypatch):
     ref_dx = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
     assert_close(y, ref_y, dt, "y")
     assert_close(dx, ref_dx, dt, "dx")
+
+
+@pytest.mark.parametrize("case", [(1, 2, 272, 272, 5, 2, "f32"), (1, 2, 272, 272, 3, 3, "f16")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_nested_call_on_the_strip_fallback(orc, case):
+    """272 x 272 planes tile only at 16 x 16, and their 136 x 136 level-1
+    low-pass map fits neither one workgroup nor any tile shape: the nested
+    call for the deeper levels then takes the strip kernel, which runs the
+    base path with a zero scale written to the workspace (the whole-plane and
+    tiled kernels skip it).  The weight backward's nested call takes the
+    level-by-level fallback the same way."""
+    n, c, h, w, k, L, dt = case
+    _log("case %s" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=272 + L)
+    d = DevInputs(inp, dt)
+    y, dx = forward(d), backward_data(d)
+    g = backward_weight(d)
+    torch.cuda.synchronize()
+    assert_close(y, orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "y")
+    assert_close(dx, orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "dx")
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    for gg, rr, name in zip(g, ref, ("dw_base", "dbias", "ds_base", "dw_lvl", "ds_lvl")):
+        assert_grad_close(gg, rr, dt, name)
 
 
 STACKED = [
