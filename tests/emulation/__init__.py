@@ -50,7 +50,7 @@ def _load():
         lib.emu_whole.restype = ci
         lib.emu_whole_tiled.argtypes = [ci, vp, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci, ci]
         lib.emu_whole_tiled.restype = ci
-        lib.emu_whole_plan.argtypes = [ci] * 11 + [ctypes.POINTER(ci)]
+        lib.emu_whole_plan.argtypes = [ci] * 12 + [ctypes.POINTER(ci)]
         lib.emu_wgrad_tiles.argtypes = [ci, vp, vp] + [ci] * 8 + [vp] * 12 + [ci, ci, ci, ci]
         lib.emu_wgrad_tiles.restype = ci
         lib.emu_whole_plan.restype = ci
@@ -94,12 +94,14 @@ def fused(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
     return out.astype(np.float64)
 
 
-def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f32", budget_floats=40960):
-    out = (ctypes.c_int * 8)()
+def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f32", budget_floats=40960, stack=1):
+    out = (ctypes.c_int * 11)()
     rc = _load().emu_whole_plan(n, c, h, w, k, levels, rotate, nthreads, planes, 4 if dtype == "f32" else 2,
-                                budget_floats, out)
-    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok", "stage_l3")
-    return dict(zip(keys, list(out)))
+                                budget_floats, stack, out)
+    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok", "stage_l3", "rows", "gap", "units")
+    d = dict(zip(keys, list(out)))
+    d["ok"] = rc == 0
+    return d
 
 
 def whole(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32", nthreads=256, planes=1,

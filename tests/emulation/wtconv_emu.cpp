@@ -419,12 +419,13 @@ int emu_wgrad_plan(int n, int c, int h, int w, int k, int levels, int nthreads, 
 // Images per workgroup chosen for a grid of c x ceil(n / planes) workgroups.
 int emu_choose_planes(int n, int c, int slots, double fixed) { return wtc_choose_planes(n, c, slots, fixed); }
 
-// Whole-plane plan: out[0..6] = planes, vec, out_bw, lds_floats, blocks, nthreads, ok.
+// Whole-plane plan: out[0..10] = planes, vec, out_bw, lds_floats, pieces, nthreads, ok, stage_l3, plane rows,
+// rows between stacked images, units.
 int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int planes, int ebytes,
-                   int budget_floats, int *out)
+                   int budget_floats, int stack, int *out)
 {
     WtcWholePlan p;
-    int rc = wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, ebytes, budget_floats);
+    int rc = wtc_make_whole_plan(&p, n, c, h, w, k, levels, rotate, nthreads, planes, ebytes, budget_floats, 0, stack);
     out[0] = p.planes;
     out[1] = p.vec;
     out[2] = p.out_bw;
@@ -433,6 +434,9 @@ int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, in
     out[5] = p.nthreads;
     out[6] = rc == 0;
     out[7] = p.stage_l3;
+    out[8] = p.h;
+    out[9] = p.sgap;
+    out[10] = p.units;
     return rc;
 }
 

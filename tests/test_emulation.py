@@ -252,6 +252,28 @@ STACKED = [
 ]
 
 
+@pytest.mark.parametrize("k, L, gap", [(5, 2, 8), (5, 3, 16), (3, 1, 4), (7, 1, 8), (1, 2, 0), (3, 4, 16),
+                                        (7, 2, 12)])
+def test_stacked_plan_gap_and_units(k, L, gap):
+    """The rows between stacked images: r rows at every level's resolution
+    (r 2^L at full resolution), rounded up to whole 4-row staging groups and
+    level-L cells; two images per unit, the last one half empty for odd
+    batches."""
+    r = k // 2
+    assert gap == -(-(r << L) // max(4, 1 << L)) * max(4, 1 << L)
+    p = emu.whole_plan(5, 2, 16, 16, k, L, nthreads=256, planes=1, stack=2, budget_floats=1 << 15)
+    assert p["ok"] and p["gap"] == gap and p["rows"] == 2 * 16 + gap and p["units"] == 3
+
+
+def test_stacked_plan_refused_where_it_would_not_be_exact():
+    """No stacking for L = 0 (the caller's depthwise path) or when an image's
+    rows are not whole staging groups and level-L cells."""
+    assert not emu.whole_plan(2, 1, 16, 16, 5, 0, stack=2)["ok"]
+    assert not emu.whole_plan(2, 1, 12, 16, 5, 3, stack=2)["ok"]  # 12 rows, 8-row level-3 cells
+    assert not emu.whole_plan(2, 1, 18, 16, 3, 1, stack=2)["ok"]  # 18 rows, 4-row groups
+    assert emu.whole_plan(2, 1, 16, 16, 5, 3, stack=2)["ok"]
+
+
 @pytest.mark.parametrize("case", STACKED, ids=lambda c: "x".join(map(str, c)))
 @pytest.mark.parametrize("rotate", [0, 1])
 def test_emulated_stacked_small_planes(orc, case, rotate):
