@@ -858,15 +858,12 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         const int by = it == ctx.tid ? ctx.oblk >> 16 : it / nbx;
         const int bx = it == ctx.tid ? ctx.oblk & 0xffff : it - by * nbx;
         const int i1 = by;
+        // the base output (without the base path the map is never written
+        // and reads as the zeros LDS was cleared to, so no branch here)
         float acc[2][BW];
-        if (p.nobase) {
-#pragma unroll
-            for (int e = 0; e < BW; ++e) acc[0][e] = acc[1][e] = 0.0f;
-        } else {
-            const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
-            wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
-            wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
-        }
+        const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
+        wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
+        wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
         float band[4][Q];
         if (p.levels >= 1) {
             const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
