@@ -96,11 +96,21 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     p->x.off = off;
     p->x.rows = wtc_max(p->lh + p->h + p->xr, wtc_roundup(p->h, P) - P - r + p->xr + P + 2 * r);
     p->x.pitch = wtc_roundup(wtc_max(p->lh + p->w + p->xc, wtc_roundup(p->w, P) - P - r + p->xc + NR), 4);
-    off += p->x.rows * p->x.pitch;
-    p->dy.off = off;
     p->dy.rows = wtc_roundup(p->h, P);
     p->dy.pitch = wtc_roundup(p->w, P);
-    off += p->dy.rows * p->dy.pitch;
+    if (p->nobase) {
+        // without the base correlation nothing reads the full-resolution maps:
+        // one row each with a zero pitch takes the staging's stores
+        off += p->x.pitch;
+        p->dy.off = off;
+        off += p->dy.pitch;
+        p->x.rows = p->dy.rows = 1;
+        p->x.pitch = p->dy.pitch = 0;
+    } else {
+        off += p->x.rows * p->x.pitch;
+        p->dy.off = off;
+        off += p->dy.rows * p->dy.pitch;
+    }
     for (int32_t m = 0; m <= WTC_MAXL; ++m) {
         p->u[m].off = p->u[m].pitch = p->u[m].rows = 0;
         p->d[m] = p->u[m];

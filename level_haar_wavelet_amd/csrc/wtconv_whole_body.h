@@ -104,7 +104,15 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
     p->x.off = off;
     p->x.rows = wtc_max(p->lh + p->h + p->xr, wtc_roundup(p->h, P) - P - r + p->xr + P + 2 * r);
     p->x.pitch = wtc_pitch16(wtc_max(p->lh + p->w + p->xc, wtc_roundup(p->w, P) - P - r + p->xc + NR));
-    off += p->x.rows * p->x.pitch;
+    if (p->nobase) {
+        // without the base path nothing reads the input map: one row with a
+        // zero pitch takes the staging's stores (every row lands on it)
+        off += p->x.pitch;
+        p->x.rows = 1;
+        p->x.pitch = 0;
+    } else {
+        off += p->x.rows * p->x.pitch;
+    }
     for (int32_t m = 1; m <= L; ++m) {
         const int32_t Hm = p->h >> m, Wm = p->w >> m;
         const int32_t orow = m == 1 ? p->u1r : r, ocol = m == 1 ? p->u1c : r, lm = m == 1 ? p->lh / 2 : 0;
@@ -118,6 +126,13 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
         p->z[m].off = off;
         p->z[m].rows = wtc_roundup(Hm, P);
         p->z[m].pitch = wtc_pitch16(wtc_roundup(Wm, P));
+        if (m == 0 && p->nobase) {
+            // no base output: the output pass reads one zero row for every row
+            off += p->z[0].pitch;
+            p->z[0].rows = 1;
+            p->z[0].pitch = 0;
+            continue;
+        }
         off += (m == 0 ? 1 : 4) * p->z[m].rows * p->z[m].pitch;
     }
     int32_t items = p->nobase ? 0 : ((p->h + P - 1) / P) * ((p->w + P - 1) / P);
