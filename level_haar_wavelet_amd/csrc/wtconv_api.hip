@@ -36,6 +36,10 @@ int env_int(const char *name, int dflt, int lo, int hi)
 
 int lds_budget_floats() { return env_int("WTCONV_LDS_KB", 64, 16, 160) * 1024 / 4; }
 
+// WTCONV_NO_STRIPS=1 takes the strip and level-step fallbacks away (tests: a
+// call whose plan needs them is refused with WTCONV_ERR_UNSUPPORTED).
+bool no_strips() { return env_int("WTCONV_NO_STRIPS", 0, 0, 1) != 0; }
+
 // LDS budget of the whole-plane kernel: all of a compute unit's 160 KB.  Planes
 // up to 80 KB still run two workgroups per compute unit (the images per
 // workgroup follow the occupancy); larger ones run one rather than being
@@ -224,39 +228,48 @@ bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp, int nobas
 
 // The deeper levels (L >= 2) of a tiled pass are the layer with L - 1 levels
 // on the level-1 low-pass map, with the level weights and scales from level 2
-// on and a zero base scale.
+// on and a zero base scale.  That map and the nested call's output are fp32
+// whatever the activation type (intermediates; the layer's outputs are rounded
+// once, at their store).
 wtconv_desc_t deeper_desc(const wtconv_desc_t *d)
 {
     wtconv_desc_t s = *d;
     s.h = d->h / 2;
     s.w = d->w / 2;
     s.levels = d->levels - 1;
+    s.dtype = WTCONV_F32;
     return s;
 }
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
-size_t pass_workspace(const wtconv_desc_t *d, int rotate)
+// Workspace of a forward / data-backward pass; nobase: the pass runs without
+// the base path (the nested call for the deeper levels of a larger layer), so
+// that the plans sized here are the ones fused_pass launches.
+size_t pass_workspace(const wtconv_desc_t *d, int rotate, int nobase)
 {
     if (ragged(d)) {
         const wtconv_desc_t pd = padded_desc(d);
-        return 2 * align256(act_bytes(&pd)) + pass_workspace(&pd, rotate);
+        return 2 * align256(act_bytes(&pd)) + pass_workspace(&pd, rotate, nobase);
     }
     WtcWholePlan wp;
-    if (whole_choice(d, rotate, &wp) || d->levels < 2 || !tile_choice(d, rotate, &wp)) return 0;
+    if (whole_choice(d, rotate, &wp, nobase) || d->levels < 2 || !tile_choice(d, rotate, &wp, nobase)) return 0;
     const wtconv_desc_t sd = deeper_desc(d);
-    const size_t quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * (d->dtype == WTCONV_F32 ? 4 : 2));
-    return 2 * quarter + align256((size_t)d->c * 4) + pass_workspace(&sd, rotate);
+    const size_t quarter = align256(act_bytes(&sd));
+    return 2 * quarter + align256((size_t)d->c * 4) + pass_workspace(&sd, rotate, 1);
 }
 
 // zero_base (C floats of scratch, or null): the base path is zero, as in the
 // nested call for the deeper levels of a larger layer (w_base, bias and
 // s_base are then not read); the whole-plane and tiled kernels skip it, the
 // other paths run with a zero base scale written there.
+// launch = false: a dry run that takes every decision and check of the pass,
+// nested and ragged calls included, and enqueues nothing; the entry points run
+// it first, so that a call that fails enqueues no work at all.
 wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *w_base, const float *bias,
                            const float *s_base, const float *w_lvl, const float *s_lvl, void *out, int rotate,
-                           void *workspace, size_t workspace_bytes, wtconv_stream_t stream,
-                           float *zero_base = nullptr)
+                           void *workspace, size_t workspace_bytes, wtconv_stream_t stream, float *zero_base,
+                           bool launch)
 {
     wtconv_status_t st = check_desc(d);
     if (st != WTCONV_OK) return st;
@@ -264,22 +277,22 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     if ((st = check_params(d, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
     if (!aligned16(in) || !aligned16(out)) return WTCONV_ERR_UNSUPPORTED;
     if (overlaps(in, out, act_bytes(d))) return WTCONV_ERR_ALIAS;
+    const int nobase = zero_base != nullptr && d->levels >= 1;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
     if (ragged(d)) {
         // zero-padded copy in, the padded layer, crop out
         const wtconv_desc_t pd = padded_desc(d);
         if ((st = check_desc(&pd)) != WTCONV_OK) return st;
-        const size_t a = align256(act_bytes(&pd)), inner = pass_workspace(&pd, rotate);
+        const size_t a = align256(act_bytes(&pd)), inner = pass_workspace(&pd, rotate, nobase);
         if (!workspace || workspace_bytes < 2 * a + inner) return WTCONV_ERR_WORKSPACE;
         if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
         char *ws = (char *)workspace;
-        if (wtc_launch_repack(d->dtype, in, ws, d->n * d->c, (int)d->h, (int)d->w, (int)pd.h, (int)pd.w, s) !=
-            hipSuccess)
+        if (launch && wtc_launch_repack(d->dtype, in, ws, d->n * d->c, (int)d->h, (int)d->w, (int)pd.h, (int)pd.w,
+                                        s) != hipSuccess)
             return WTCONV_ERR_HIP;
         st = fused_pass(&pd, ws, w_base, bias, s_base, w_lvl, s_lvl, ws + a, rotate, ws + 2 * a, inner, stream,
-                        zero_base);
-        if (st != WTCONV_OK) return st;
+                        zero_base, launch);
+        if (st != WTCONV_OK || !launch) return st;
         return wtc_launch_repack(d->dtype, ws + a, out, d->n * d->c, (int)pd.h, (int)pd.w, (int)d->h, (int)d->w,
                                  s) == hipSuccess
                    ? WTCONV_OK
@@ -288,51 +301,68 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     // the whole-plane kernel when a plane fits one workgroup (any L, even
     // sides for L = 0); else tiles where a tile shape divides the plane; else
     // the row-band kernel for L = 0 and the strip kernel for L >= 1
-    const int nobase = zero_base != nullptr && d->levels >= 1;
+    hipError_t e = hipSuccess;
     WtcWholePlan wp;
     if (whole_choice(d, rotate, &wp, nobase)) {
-        e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
+        if (launch) e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
     } else if (tile_choice(d, rotate, &wp, nobase)) {
         const void *low = nullptr;
         if (d->levels >= 2) {
-            const size_t need = pass_workspace(d, rotate);
+            const size_t need = pass_workspace(d, rotate, nobase);
             if (!workspace || workspace_bytes < need) return WTCONV_ERR_WORKSPACE;
             if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
             const wtconv_desc_t sd = deeper_desc(d);
-            const size_t quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * (d->dtype == WTCONV_F32 ? 4 : 2));
+            const size_t quarter = align256(act_bytes(&sd));
             char *ws = (char *)workspace;
-            void *ll = ws, *deep = ws + quarter;
+            float *ll = (float *)ws;
+            void *deep = ws + quarter;
             float *zeros = (float *)(ws + 2 * quarter);
             char *sub = ws + 2 * quarter + align256((size_t)d->c * 4);
             const int64_t kk = (int64_t)d->k * d->k;
-            if ((e = wtc_launch_lowpass(d->dtype, in, ll, d->n * d->c, (int)d->h, (int)d->w, s)) != hipSuccess)
+            if (launch && wtc_launch_lowpass(d->dtype, in, ll, d->n * d->c, (int)d->h, (int)d->w, s) != hipSuccess)
                 return WTCONV_ERR_HIP;
-            // the deeper levels: the layer with L - 1 levels and no base path
+            // the deeper levels: the layer with L - 1 levels and no base path,
+            // in fp32
             const float *wl2 = w_lvl + 4 * d->c * kk, *sl2 = s_lvl + 4 * d->c;
             st = fused_pass(&sd, ll, w_base, nullptr, zeros, wl2, sl2, deep, rotate, sub, need - (sub - ws), stream,
-                            zeros);
+                            zeros, launch);
             if (st != WTCONV_OK) return st;
             low = deep;
         }
-        e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s, low);
+        if (launch) e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s, low);
     } else if (d->levels == 0) {
-        e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
-                              (int)d->w, rotate, s);
+        if (launch)
+            e = wtc_launch_dwconv(d->dtype, d->k, in, out, w_base, bias, s_base, (int)d->n, (int)d->c, (int)d->h,
+                                  (int)d->w, rotate, s);
     } else {
-        if (nobase) {
-            if (wtc_launch_fill(zero_base, d->c, 0.0f, s) != hipSuccess) return WTCONV_ERR_HIP;
-            s_base = zero_base;
-            bias = nullptr;
-        }
         WtcFusedPlan p;
+        if (no_strips()) return WTCONV_ERR_UNSUPPORTED;
         if (wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                 kFusedThreads, lds_budget_floats()) &&
             wtc_make_fused_plan(&p, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, rotate,
                                 kFusedThreads, kMaxLdsFloats))
             return WTCONV_ERR_UNSUPPORTED;
+        if (!launch) return WTCONV_OK;
+        if (nobase) {
+            if (wtc_launch_fill(zero_base, d->c, 0.0f, s) != hipSuccess) return WTCONV_ERR_HIP;
+            s_base = zero_base;
+            bias = nullptr;
+        }
         e = wtc_launch_fused(d->dtype, p, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
     }
     return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+}
+
+// A forward / data-backward entry point: the dry run, then the launches.
+wtconv_status_t run_pass(const wtconv_desc_t *d, const void *in, const float *w_base, const float *bias,
+                         const float *s_base, const float *w_lvl, const float *s_lvl, void *out, int rotate,
+                         void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
+{
+    wtconv_status_t st = fused_pass(d, in, w_base, bias, s_base, w_lvl, s_lvl, out, rotate, workspace,
+                                    workspace_bytes, stream, nullptr, false);
+    if (st != WTCONV_OK) return st;
+    return fused_pass(d, in, w_base, bias, s_base, w_lvl, s_lvl, out, rotate, workspace, workspace_bytes, stream,
+                      nullptr, true);
 }
 
 // Weight-gradient plan: the whole-plane kernel when the plane fits in LDS,
@@ -410,8 +440,8 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch, int nobase
         ch->part_bytes = align256((size_t)ch->groups * d->c * ch->plen * 4);
         ch->quarter = ch->sub_bytes = 0;
         if (d->levels >= 2) {
-            const wtconv_desc_t sd = deeper_desc(d);
-            ch->quarter = align256((size_t)(sd.n * sd.c * sd.h * sd.w) * eb);
+            const wtconv_desc_t sd = deeper_desc(d);  // fp32 low-pass maps
+            ch->quarter = align256(act_bytes(&sd));
             size_t sub = 0;
             wtconv_status_t st = wgrad_workspace(&sd, 1, &sub);
             if (st != WTCONV_OK) return st;
@@ -431,6 +461,7 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch, int nobase
                             whole_budget_floats(), nobase);
         ch->groups = ch->wp.groups;
     } else {
+        if (no_strips()) return WTCONV_ERR_UNSUPPORTED;
         ch->groups = (int)wgrad_groups(d);
         for (int j = 0; j <= d->levels; ++j) {
             WtcWtilePlan tp;
@@ -501,8 +532,8 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     if (st != WTCONV_OK) return st;
     if (!bytes) return WTCONV_ERR_NULL;
     switch (op) {
-    case WTCONV_OP_FWD: *bytes = pass_workspace(desc, 0); return WTCONV_OK;
-    case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1); return WTCONV_OK;
+    case WTCONV_OP_FWD: *bytes = pass_workspace(desc, 0, 0); return WTCONV_OK;
+    case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1, 0); return WTCONV_OK;
     case WTCONV_OP_BWD_WEIGHT: return wgrad_workspace(desc, 0, bytes);
     default: return WTCONV_ERR_UNSUPPORTED;
     }
@@ -511,10 +542,12 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
 // The weight backward; nobase: the base gradients are not wanted (the nested
 // call for the deeper levels of a larger layer, which writes them to
 // scratch): the whole-plane and tiled kernels skip them and write 0.
+// launch = false: the dry run (see fused_pass).
 static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, const void *dy, const float *w_base,
                                   const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                                   float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
-                                  void *workspace, size_t workspace_bytes, wtconv_stream_t stream, int nobase)
+                                  void *workspace, size_t workspace_bytes, wtconv_stream_t stream, int nobase,
+                                  bool launch)
 {
     wtconv_status_t st = check_desc(desc);
     if (st != WTCONV_OK) return st;
@@ -522,6 +555,7 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
     if ((st = check_params(desc, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
     if (desc->levels > 0 && (!dw_lvl || !ds_lvl)) return WTCONV_ERR_NULL;
     if (!aligned16(x) || !aligned16(dy)) return WTCONV_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
     if (ragged(desc)) {
         // the gradients of the layer on zero-padded copies of x and dy
         const wtconv_desc_t pd = padded_desc(desc);
@@ -532,46 +566,56 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
         if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
         const size_t a = align256(act_bytes(&pd));
         char *ws = (char *)workspace;
-        hipStream_t s = (hipStream_t)stream;
         const int64_t planes = desc->n * desc->c;
-        if (wtc_launch_repack(desc->dtype, x, ws, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w, s) !=
-                hipSuccess ||
-            wtc_launch_repack(desc->dtype, dy, ws + a, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w,
-                              s) != hipSuccess)
+        if (launch &&
+            (wtc_launch_repack(desc->dtype, x, ws, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w, s) !=
+                 hipSuccess ||
+             wtc_launch_repack(desc->dtype, dy, ws + a, planes, (int)desc->h, (int)desc->w, (int)pd.h, (int)pd.w,
+                               s) != hipSuccess))
             return WTCONV_ERR_HIP;
         return wgrad_pass(&pd, ws, ws + a, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl,
-                          ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream, nobase);
+                          ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream, nobase, launch);
     }
     WgradChoice ch;
     if ((st = choose_wgrad(desc, &ch, nobase)) != WTCONV_OK) return st;
     if (!workspace || workspace_bytes < ch.total_bytes) return WTCONV_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
-    hipStream_t s = (hipStream_t)stream;
     char *ws = (char *)workspace;
     float *partial = (float *)ws;
     hipError_t e = hipSuccess;
     if (ch.tiles) {
         // with L >= 2 the tiles also write the level-1 low-pass maps of x and
-        // dy (every tile its interior), the inputs of the nested call
+        // dy (every tile its interior, fp32), the inputs of the nested call
         char *llx = desc->levels >= 2 ? ws + ch.part_bytes : nullptr;
         char *lld = desc->levels >= 2 ? llx + ch.quarter : nullptr;
-        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s, llx, lld);
+        if (desc->levels >= 2) {
+            // levels 2..L: the layer with L - 1 levels on the low-pass maps,
+            // its base gradients not wanted (written to scratch); checked here,
+            // launched after the tiles
+            const wtconv_desc_t sd = deeper_desc(desc);
+            float *scratch = (float *)(lld + ch.quarter);
+            char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
+            const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
+            if (launch) {
+                e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s, llx, lld);
+                if (e == hipSuccess)
+                    e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, 1, ch.groups, ch.plen, partial, w_base, bias,
+                                                  s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
+                if (e != hipSuccess) return WTCONV_ERR_HIP;
+            }
+            return wgrad_pass(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C, scratch,
+                              scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk, ds_lvl + 4 * C, sub,
+                              ch.sub_bytes, stream, 1, launch);
+        }
+        if (!launch) return WTCONV_OK;
+        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
         if (e == hipSuccess)
             e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels >= 1 ? 1 : 0, ch.groups, ch.plen,
                                           partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
                                           dw_lvl, ds_lvl, s);
-        if (e != hipSuccess) return WTCONV_ERR_HIP;
-        if (desc->levels < 2) return WTCONV_OK;
-        const wtconv_desc_t sd = deeper_desc(desc);
-        float *scratch = (float *)(lld + ch.quarter);
-        char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
-        const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
-        // levels 2..L: the layer with L - 1 levels on the low-pass maps, its
-        // base gradients not wanted (written to scratch)
-        return wgrad_pass(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C, scratch,
-                          scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk, ds_lvl + 4 * C, sub,
-                          ch.sub_bytes, stream, 1);
+        return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
     }
+    if (!launch) return WTCONV_OK;
     if (ch.whole) {
         e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
     } else {
@@ -603,22 +647,25 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
                                        float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
                                        size_t workspace_bytes, wtconv_stream_t stream)
 {
+    wtconv_status_t st = wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
+                                    dw_lvl, ds_lvl, workspace, workspace_bytes, stream, 0, false);
+    if (st != WTCONV_OK) return st;
     return wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl,
-                      workspace, workspace_bytes, stream, 0);
+                      workspace, workspace_bytes, stream, 0, true);
 }
 
 wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,
                                const float *s_base, const float *w_lvl, const float *s_lvl, void *y,
                                void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
 {
-    return fused_pass(desc, x, w_base, bias, s_base, w_lvl, s_lvl, y, 0, workspace, workspace_bytes, stream);
+    return run_pass(desc, x, w_base, bias, s_base, w_lvl, s_lvl, y, 0, workspace, workspace_bytes, stream);
 }
 
 wtconv_status_t wtconv_backward_data(const wtconv_desc_t *desc, const void *dy, const float *w_base,
                                      const float *s_base, const float *w_lvl, const float *s_lvl, void *dx,
                                      void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
 {
-    return fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, workspace, workspace_bytes, stream);
+    return run_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, workspace, workspace_bytes, stream);
 }
 
 const char *wtconv_status_string(wtconv_status_t status)

@@ -16,14 +16,16 @@ hipError_t wtc_launch_fused(int dtype, const WtcFusedPlan &p, const void *in, vo
                             hipStream_t stream);
 
 // Whole-plane fused forward / data backward, per plan p; for a tiled plan,
-// `low` is the deeper levels' low-pass term at level-1 resolution (or null).
+// `low` is the deeper levels' low-pass term at level-1 resolution, fp32 (or
+// null).
 hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, void *out, const float *w_base,
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                             hipStream_t stream, const void *low = nullptr);
 
 // Level-1 low-pass band (orthonormal, (a + b + c + d) / 2 of every 2x2 block)
-// of `planes` planes of h x w (even), into planes of (h/2) x (w/2).
-hipError_t wtc_launch_lowpass(int dtype, const void *in, void *out, int64_t planes, int h, int w,
+// of `planes` planes of h x w (multiples of 4) of the input dtype, into fp32
+// planes of (h/2) x (w/2).
+hipError_t wtc_launch_lowpass(int dtype, const void *in, float *out, int64_t planes, int h, int w,
                               hipStream_t stream);
 
 // n floats set to v (a kernel, so that callers may capture it in a graph).
@@ -36,7 +38,7 @@ hipError_t wtc_launch_repack(int dtype, const void *in, void *out, int64_t plane
 
 // Fused parameter-gradient correlations (partials per workgroup) and the
 // fixed-order reduction with the chain rule.  Tiled plans may also write the
-// level-1 low-pass maps of x and dy (llx, lld: (N, C, ih/2, iw/2), both or
+// level-1 low-pass maps of x and dy (llx, lld: (N, C, ih/2, iw/2) fp32, both or
 // neither).
 hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, const void *dy, float *partial,
                             hipStream_t stream, void *llx = nullptr, void *lld = nullptr);

@@ -13,9 +13,11 @@ namespace {
 constexpr int kThreads = 256;
 
 // One thread per 2 x 2 output block: reads a 4 x 4 input block as four
-// 16-byte (fp32) rows, writes two 8-byte rows.
+// 16-byte (fp32) rows, writes two 8-byte rows.  The output is fp32 whatever
+// the input type: it is an intermediate of the layer, and the layer's outputs
+// are rounded once, at their own store.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void lowpass_kernel(const T *__restrict__ in, T *__restrict__ out,
+__global__ __launch_bounds__(kThreads) void lowpass_kernel(const T *__restrict__ in, float *__restrict__ out,
                                                            int64_t planes, int h, int w)
 {
     const int h2 = h / 2, w2 = w / 2, bw = w2 / 2, bh = h2 / 2;
@@ -31,13 +33,13 @@ __global__ __launch_bounds__(kThreads) void lowpass_kernel(const T *__restrict__
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[q][e] = (float)src[(int64_t)q * w + e];
-        T *dst = out + p * ((int64_t)h2 * w2) + (int64_t)(2 * bi) * w2 + 2 * bj;
+        float *dst = out + p * ((int64_t)h2 * w2) + (int64_t)(2 * bi) * w2 + 2 * bj;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int b = 0; b < 2; ++b)
                 dst[(int64_t)a * w2 + b] =
-                    (T)(0.5f * (v[2 * a][2 * b] + v[2 * a][2 * b + 1] + v[2 * a + 1][2 * b] + v[2 * a + 1][2 * b + 1]));
+                    0.5f * (v[2 * a][2 * b] + v[2 * a][2 * b + 1] + v[2 * a + 1][2 * b] + v[2 * a + 1][2 * b + 1]);
     }
 }
 
@@ -55,17 +57,17 @@ unsigned grid_for(int64_t n)
 
 }  // namespace
 
-hipError_t wtc_launch_lowpass(int dtype, const void *in, void *out, int64_t planes, int h, int w,
+hipError_t wtc_launch_lowpass(int dtype, const void *in, float *out, int64_t planes, int h, int w,
                               hipStream_t stream)
 {
     if (h % 4 || w % 4) return hipErrorInvalidValue;  // whole 2 x 2 output blocks
     const unsigned g = grid_for(planes * (h / 4) * (w / 4));
     if (dtype == 0)
-        hipLaunchKernelGGL(lowpass_kernel<float>, dim3(g), dim3(kThreads), 0, stream, (const float *)in, (float *)out,
-                           planes, h, w);
+        hipLaunchKernelGGL(lowpass_kernel<float>, dim3(g), dim3(kThreads), 0, stream, (const float *)in, out, planes,
+                           h, w);
     else
-        hipLaunchKernelGGL(lowpass_kernel<_Float16>, dim3(g), dim3(kThreads), 0, stream, (const _Float16 *)in,
-                           (_Float16 *)out, planes, h, w);
+        hipLaunchKernelGGL(lowpass_kernel<_Float16>, dim3(g), dim3(kThreads), 0, stream, (const _Float16 *)in, out,
+                           planes, h, w);
     return hipGetLastError();
 }
 

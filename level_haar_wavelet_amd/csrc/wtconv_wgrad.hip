@@ -162,8 +162,8 @@ hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, con
         WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial, p, (float *)llx, (float *)lld};
         return launch_wgrad_t<float>(a, stream);
     }
-    WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial, p, (_Float16 *)llx,
-                             (_Float16 *)lld};
+    WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial, p, (float *)llx,
+                             (float *)lld};
     return launch_wgrad_t<_Float16>(a, stream);
 }
 

@@ -262,10 +262,10 @@ struct WtcWgradArgs {
     float *partial;  // [groups][C][plen]
     WtcWgradPlan p;
     // tiled plans: the level-1 low-pass maps of x and dy, (N, C, ih/2, iw/2)
-    // orthonormal, written for every tile's interior (the input of the deeper
-    // levels' gradients), or null
-    T *llx = nullptr;
-    T *lld = nullptr;
+    // orthonormal, fp32 whatever T is, written for every tile's interior (the
+    // input of the deeper levels' gradients), or null
+    float *llx = nullptr;
+    float *lld = nullptr;
 };
 
 template <typename T, int VEC>
@@ -489,14 +489,14 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
 #ifdef WTC_EMULATE
                         const int64_t all = (int64_t)p.n * p.c * (p.ih / 2) * (p.iw / 2);
                         for (int j = 0; j < H1; ++j) {
-                            wtc_chk(a.llx, o + j, all, __LINE__) = wtc_from_float<T>(0.5f * bx[0][j]);
-                            wtc_chk(a.lld, o + j, all, __LINE__) = wtc_from_float<T>(0.5f * bd[0][j]);
+                            wtc_chk(a.llx, o + j, all, __LINE__) = 0.5f * bx[0][j];
+                            wtc_chk(a.lld, o + j, all, __LINE__) = 0.5f * bd[0][j];
                         }
 #else
 #pragma unroll
                         for (int j = 0; j < H1; ++j) {
-                            a.llx[o + j] = wtc_from_float<T>(0.5f * bx[0][j]);
-                            a.lld[o + j] = wtc_from_float<T>(0.5f * bd[0][j]);
+                            a.llx[o + j] = 0.5f * bx[0][j];
+                            a.lld[o + j] = 0.5f * bd[0][j];
                         }
 #endif
                     }

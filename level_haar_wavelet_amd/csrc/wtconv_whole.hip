@@ -120,7 +120,7 @@ hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, vo
         return launch_t<float>(a, stream);
     }
     WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
-                             (const _Float16 *)low};
+                             (const float *)low};
     return launch_t<_Float16>(a, stream);
 }
 

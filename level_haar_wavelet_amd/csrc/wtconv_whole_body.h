@@ -269,8 +269,9 @@ struct WtcWholeArgs {
     const float *w_base, *bias, *s_base, *w_lvl, *s_lvl;
     WtcWholePlan p;
     // tiled plans: the deeper levels' low-pass contribution at level-1
-    // resolution, (N, C, ih/2, iw/2) orthonormal, or null
-    const T *low = nullptr;
+    // resolution, (N, C, ih/2, iw/2) orthonormal, fp32 whatever T is (the
+    // outputs are rounded once, at the store), or null
+    const float *low = nullptr;
 };
 
 // Per-thread state of the whole-plane kernel.
@@ -935,10 +936,9 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
 #ifdef WTC_EMULATE
-                const float v = wtc_to_float(
-                    wtc_chk(a.low, lo + q, (int64_t)p.n * p.c * (p.ih / 2) * (p.iw / 2), __LINE__));
+                const float v = wtc_chk(a.low, lo + q, (int64_t)p.n * p.c * (p.ih / 2) * (p.iw / 2), __LINE__);
 #else
-                const float v = wtc_to_float(a.low[lo + q]);
+                const float v = a.low[lo + q];
 #endif
                 band[0][q] = wtc_fma(0.5f, v, band[0][q]);
             }

@@ -133,7 +133,7 @@ def whole_tiled(x, low, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, rotate=0,
     n, c, ih, iw = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
     xin = np.ascontiguousarray(x, dtype=npdt)
-    lin = None if low is None else np.ascontiguousarray(low, dtype=npdt)
+    lin = None if low is None else np.ascontiguousarray(low, dtype=np.float32)  # fp32 intermediate
     out = np.full_like(xin, np.nan)
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
@@ -163,7 +163,7 @@ def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32
             np.full((1, 4 * c), np.nan, np.float32)][:3 + 2 * levels]
     ptr = lambda a: None if a is None else a.ctypes.data
     optr = [o.ctypes.data for o in outs] + [None] * (5 - len(outs))
-    lls = [np.full((n, c, ih // 2, iw // 2), np.nan, npdt) for _ in range(2)] if lowpass else [None, None]
+    lls = [np.full((n, c, ih // 2, iw // 2), np.nan, np.float32) for _ in range(2)] if lowpass else [None, None]
     rc = lib.emu_wgrad_tiles(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, n, c, ih, iw, th, tw, k,
                              levels, *[ptr(a) for a in keep], *optr, *[ptr(a) for a in lls], nthreads, planes,
                              budget_floats, int(nobase))

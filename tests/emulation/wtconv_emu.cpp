@@ -390,8 +390,8 @@ int emu_wgrad_tiles(int dtype, const void *x, const void *dy, int n, int c, int 
         WtcWgradArgs<float> a{(const float *)x, (const float *)dy, partial.data(), p, (float *)llx, (float *)lld};
         rc = run_wgrad_t<float>(a);
     } else {
-        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p, (_Float16 *)llx,
-                                 (_Float16 *)lld};
+        WtcWgradArgs<_Float16> a{(const _Float16 *)x, (const _Float16 *)dy, partial.data(), p, (float *)llx,
+                                 (float *)lld};
         rc = run_wgrad_t<_Float16>(a);
     }
     if (rc) return rc;
@@ -473,7 +473,7 @@ int emu_whole_tiled(int dtype, const void *in, void *out, const void *low, int n
         return run_whole_t<float>(a);
     }
     WtcWholeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p,
-                             (const _Float16 *)low};
+                             (const float *)low};
     return run_whole_t<_Float16>(a);
 }
 

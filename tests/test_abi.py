@@ -144,3 +144,70 @@ def test_unfused_validation_before_any_launch(lib):
                                       None) == 1
     one = ctypes.c_void_p(16)
     assert lib.wtconv_unfused_forward(ctypes.byref(good), one, one, None, one, one, one, one, one, 8, None) == 4
+
+
+def _no_device():
+    import torch
+
+    return torch.cuda.device_count() == 0
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+@pytest.mark.skipif(not _no_device(), reason="calls the ops with fake pointers: only where no GPU is visible")
+def test_nested_plan_is_checked_before_anything_is_enqueued(lib, monkeypatch):
+    """A 272 x 272 plane tiles (16 x 16), but its 136 x 136 level-1 low-pass
+    map fits neither one workgroup nor a tile shape; with the strip fallbacks
+    taken away (WTCONV_NO_STRIPS) the nested call for the deeper levels has no
+    plan.  The whole recursion is planned before the first launch, so the call
+    returns WTCONV_ERR_UNSUPPORTED; were the level-1 low-pass pass launched
+    first, the GPU-less runtime would report WTCONV_ERR_HIP instead."""
+    monkeypatch.setenv("WTCONV_NO_STRIPS", "1")
+    d = _native.desc(1, 2, 272, 272, 5, 2, _native.F32)
+    st, need = _ws(lib, d, 0)
+    assert st == 0 and need > 0
+    p = _fake(0x10000000)
+    out = _fake(0x20000000)
+    ws = _fake(0x40000000)
+    assert lib.wtconv_forward(ctypes.byref(d), p, p, None, p, p, p, out, ws, need, None) == 3
+    assert lib.wtconv_backward_data(ctypes.byref(d), p, p, p, p, p, out, ws, need, None) == 3
+    st, _ = _ws(lib, d, 2)
+    assert st == 3
+    assert lib.wtconv_backward_weight(ctypes.byref(d), p, out, p, None, p, p, p, p, p, p, p, p, ws, 1 << 40,
+                                      None) == 3
+
+
+@pytest.mark.skipif(not _no_device(), reason="calls the ops with fake pointers: only where no GPU is visible")
+@pytest.mark.parametrize("shape", [(1, 2, 128, 128, 5, 3, 0), (2, 1, 256, 256, 5, 4, 1), (1, 1, 128, 256, 3, 5, 1)])
+def test_workspace_size_is_what_the_launch_plan_needs(lib, monkeypatch, shape):
+    """For every LDS budget of the whole-plane and tiled plans
+    (WTCONV_WHOLE_LDS_KB, which moves the choice between whole planes, tiles
+    and the nested calls with and without their base path), the size that
+    wtconv_workspace_size reports is exactly what the call checks: 256 bytes
+    less is refused with WTCONV_ERR_WORKSPACE before anything is enqueued,
+    the reported size passes every check (the GPU-less runtime then fails the
+    first launch: WTCONV_ERR_HIP)."""
+    d = _native.desc(*shape)
+    p, out, ws = _fake(0x10000000), _fake(0x80000000), _fake(0x100000000)
+    seen = 0
+    for kb in range(8, 161, 2):
+        monkeypatch.setenv("WTCONV_WHOLE_LDS_KB", str(kb))
+        for op in (0, 1):
+            st, need = _ws(lib, d, op)
+            if st != 0:
+                continue
+            call = (lambda n: lib.wtconv_forward(ctypes.byref(d), p, p, None, p, p, p, out, ws, n, None)) if op == 0 \
+                else (lambda n: lib.wtconv_backward_data(ctypes.byref(d), p, p, p, p, p, out, ws, n, None))
+            if need > 0:
+                seen += 1
+                assert call(need - 256) == 4, (kb, op, need)
+            assert call(need) == 5, (kb, op, need)
+        st, need = _ws(lib, d, 2)
+        if st == 0:
+            assert lib.wtconv_backward_weight(ctypes.byref(d), p, out, p, None, p, p, p, p, p, p, p, p, ws,
+                                              need - 256, None) == 4
+            assert lib.wtconv_backward_weight(ctypes.byref(d), p, out, p, None, p, p, p, p, p, p, p, p, ws, need,
+                                              None) == 5
+    assert seen > 0
