@@ -1,29 +1,41 @@
 """Benchmark of the WTConv layer on one MI355X: forward + backward (data and
-parameter gradients) per step, on synthetic WTConvNeXt-shaped tensors.
+parameter gradients) on synthetic WTConvNeXt-shaped tensors.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stage1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sweep]
 
-Prints ONE JSON line.  A step is one pass of the whole layer: wtconv_forward,
-wtconv_backward_data and wtconv_backward_weight on one batch already resident
-in device memory.  `value` is the achieved rate on the modeled minimum bytes
-of a step (forward reads x and writes y, the data backward reads dy and
-writes dx, the weight backward reads x and dy: 6 E e bytes for E elements of
-e bytes).  Kernel durations are measured with HIP events on the stream the
-library launches on.  The `roofline` object is for the dominant kernel of the
-step; the `cpu_baseline` object times the CPU oracle on a bounded sample of
-the same workload.  Other options:
-    --cpu-sample N   images of the CPU-oracle sample (default: the whole batch; 0 disables it)
-    --mall-flush     write a 512 MiB buffer between timed steps
-    --all            also print one line per workload (stderr)
-    --copy-calibration BYTES   only run a plain device copy (for counter scaling)
+Prints ONE JSON line.  The default workload is the level sweep the metric is
+quoted on: N=32, C=128, H=W=128, k=5, L = 1..5, each in fp32 and in fp16
+storage (fp32 arithmetic), ten points.  A step is one pass of the whole layer
+(wtconv_forward, wtconv_backward_data, wtconv_backward_weight) at every point,
+on batches already resident in device memory.  `value` is the achieved rate on
+the modeled minimum bytes: the ten points' 6 E e bytes each (forward reads x
+and writes y, the data backward reads dy and writes dx, the weight backward
+reads x and dy; E elements of e bytes), summed, over the step time.  Per point
+the line gives the median microseconds of every op, the step, its GB/s and its
+fraction of the 8 TB/s HBM peak.  Op durations are HIP events recorded around
+each call on the stream the library launches on.  The `roofline` object is
+for the dominant op (the longest mean op duration of any point); `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+
+Other modes:
+    --workload stage1|stage2|large|tiny   one workload (with --levels/--dtype for one sweep point)
+    --counter-op fwd|bwd_data|bwd_weight|unfused_fwd  only that op, --reps times after one warm call
+                    (the program profiled by the counter runs)
+    --traffic-summary OUT   HBM bytes per op from counter runs under OUT (see traffic_summary)
+    --valu-summary OUT      VALU / LDS counter summary from counter runs under OUT
+    --trace-summary OUT     kernel-duration summary from a kernel-trace run under OUT
+    --copy-calibration BYTES   only a plain device copy of BYTES (counter scaling)
+    --mall-flush            write a 512 MiB buffer between timed steps
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
-import re
 import json
 import os
+import platform
+import re
 import sys
 import time
 
@@ -32,13 +44,20 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "WTConv fwd+bwd µs/layer and achieved HBM GB/s (% of peak), fp32/fp16, L=1–5"
+# MI355X published peaks: HBM3E 8 TB/s; fp32 vector 157.3 TFLOP/s, i.e. 256 CUs x
+# 2.4 GHz x 256 FLOP per clock per CU, which counts packed fp32 FMAs.  The
+# library is built with packed fp32 switched off, so its reachable fp32 vector
+# rate is half of that (256 x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6
+# TFLOP/s), reported next to the published roof.
 HBM_PEAK_GBS = 8000.0
-# fp32 FMA on the vector ALUs without packed instructions (the library is built
-# with packed fp32 switched off): 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz
-VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-PACKED_FP32_PUBLISHED_TFLOPS = 157.3
+FP32_PEAK_TFLOPS = 157.3
+FP32_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+RIDGE_FLOP_PER_BYTE = FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 CSRC = os.path.join(ROOT, "level_haar_wavelet_amd", "csrc")
+OPS = ("wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight")
+OP_KEYS = {"fwd": "wtconv_forward", "bwd_data": "wtconv_backward_data", "bwd_weight": "wtconv_backward_weight",
+           "unfused_fwd": "wtconv_unfused_forward"}
 
 
 def _code_only(text: str) -> str:
@@ -59,16 +78,40 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def level_sum(levels: int) -> float:
+    """S(L) = sum over l = 1..L of 4^(1-l): the level maps' share of the pixels."""
+    return sum(4.0 ** (1 - l) for l in range(1, levels + 1))
+
+
 def conv_flops(wl) -> float:
-    """Algorithmic FLOPs of one op: 2 k^2 (1 + S(L)) per element, S(L) = sum 4^(1-l)."""
-    s = sum(4.0 ** (1 - l) for l in range(1, wl.levels + 1))
-    return 2.0 * wl.k * wl.k * (1.0 + s) * wl.elems
+    """Algorithmic FLOPs of one op: 2 k^2 (1 + S(L)) per element."""
+    return 2.0 * wl.k * wl.k * (1.0 + level_sum(wl.levels)) * wl.elems
 
 
-def measured_traffic(kernel: str, digest: str, workload: str):
-    """HBM bytes per launch of `kernel` (an op) on `workload` from the
-    committed counter summary, if it was taken on the current kernel sources
-    (else None)."""
+def op_bytes(wl) -> float:
+    """Algorithmic bytes of one op: two activation tensors (read x and write y,
+    read dy and write dx, or read x and dy)."""
+    return 2.0 * wl.elems * wl.ebytes
+
+
+def unfused_forward_elements(wl) -> float:
+    """Element moves of the unfused forward: (7 + 10.75 S(L)) E (per level a
+    Haar analysis, a convolution and a scale pass, the low-pass add, the band
+    concatenation and the synthesis at 4^(1-l) of the size, plus the base
+    convolution, its scale and the final add); 17.75 E at L = 1 and 21.32 E at
+    L = 5, the two ends of the count the pages give for the reference layer."""
+    return (7.0 + 10.75 * level_sum(wl.levels)) * wl.elems
+
+
+def workload_name(wl) -> str:
+    return "%s %dx%dx%dx%d k=%d L=%d %s" % (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels,
+                                           "fp32" if wl.dtype == "f32" else "fp16 storage")
+
+
+def measured_traffic(op: str, digest: str, workload: str):
+    """HBM bytes per call of `op` (all its kernel launches) on `workload` from
+    the committed counter summary, if it was taken on the current kernel
+    sources (else None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         with open(path) as fh:
@@ -77,13 +120,35 @@ def measured_traffic(kernel: str, digest: str, workload: str):
         return None
     if d.get("source_digest") != digest:
         return None
-    k = d.get("kernels", {}).get(kernel)
+    k = d.get("ops", {}).get(op)
     return None if k is None else k.get("bytes_per_launch")
 
 
-def workload_name(wl) -> str:
-    return "%s %dx%dx%dx%d k=%d L=%d %s" % (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels,
-                                           "fp32" if wl.dtype == "f32" else "fp16 storage")
+def roofline(wl, op: str, mean_us: float, digest: str) -> dict:
+    """Roofline of one op at one workload: the bound is the published roof its
+    arithmetic intensity meets first (HBM below the ridge of 157.3 TFLOP/s over
+    8 TB/s = 19.7 FLOP/B, the fp32 vector ALUs above it); `achieved` is the
+    algorithmic bytes (or FLOPs) of one call over its mean duration."""
+    flops, nbytes = conv_flops(wl), op_bytes(wl)
+    t = mean_us * 1e-6
+    intensity = flops / nbytes
+    tflops, gbs = flops / t / 1e12, nbytes / t / 1e9
+    if intensity < RIDGE_FLOP_PER_BYTE:
+        out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        out = {"bound": "alu", "achieved": round(tflops, 3), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(tflops / FP32_PEAK_TFLOPS, 4)}
+    out.update({
+        "traffic": measured_traffic(op, digest, workload_name(wl)),
+        "kernel": op, "workload": workload_name(wl), "mean_us": round(mean_us, 2),
+        "bytes_per_launch": nbytes, "flops_per_launch": flops, "intensity_flop_per_byte": round(intensity, 2),
+        "achieved_GBs": round(gbs, 1), "achieved_TFLOPs": round(tflops, 3),
+        "nonpacked_fp32_peak_TFLOPs": round(FP32_NONPACKED_TFLOPS, 1),
+        "nonpacked_fp32_frac": round(tflops / FP32_NONPACKED_TFLOPS, 4),
+        "source_digest": digest,
+    })
+    return out
 
 
 _BUILTIN = {"f": "float", "d": "double", "i": "int", "j": "unsigned int", "b": "bool", "DF16_": "_Float16"}
@@ -151,54 +216,67 @@ def _short_kernel(name: str) -> str:
     return name
 
 
-def _counter_means(folder: str) -> dict:
-    """Mean counter value per dispatch for each kernel, from the
-    *counter_collection.csv files that `rocprofv3 --pmc` wrote under folder."""
+def _counter_rows(folder: str):
+    """(dispatch id, kernel, counter, value) of every *counter_collection.csv
+    that `rocprofv3 --pmc` wrote under folder (values of one dispatch summed
+    over the rows it spans)."""
     import csv
     import glob
 
-    sums = {}
+    acc = {}
     for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         with open(path, newline="") as fh:
             for row in csv.DictReader(fh):
-                key = (_short_kernel(row["Kernel_Name"]), row["Counter_Name"])
-                acc = sums.setdefault(key, {})
-                acc[row["Dispatch_Id"]] = acc.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
-    return {key: sum(v.values()) / len(v) for key, v in sums.items()}
+                key = (int(row["Dispatch_Id"]), _short_kernel(row["Kernel_Name"]), row["Counter_Name"])
+                acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    return [(d, k, c, v) for (d, k, c), v in sorted(acc.items())]
 
 
-def traffic_summary(folder: str, workload: str, copy_bytes: int, outdir: str = None) -> dict:
-    """Writes profiles/hbm_traffic.json and profiles/<workload>_hbm_traffic.md
-    from four counter runs under folder: fetch/ and write/ (FETCH_SIZE and
-    WRITE_SIZE of the bench), cfetch/ and cwrite/ (the same counters over a
-    plain device copy of copy_bytes bytes, which scales KiB to bytes)."""
-    from level_haar_wavelet_amd.synthetic import WORKLOADS
+def _library_kernel(k: str) -> bool:
+    return k.startswith(("wtconv_", "lowpass_", "repack_", "fill_", "unfused_", "dwconv_"))
 
+
+def traffic_summary(folder: str, wl, reps: int, copy_bytes: int, outdir: str = None) -> dict:
+    """HBM bytes per op from counter runs of `bench.py --counter-op OP --reps
+    reps` (reps + 1 calls of the op and nothing else): OUT/<op>_fetch and
+    OUT/<op>_write (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) for each op
+    run, and OUT/cfetch, OUT/cwrite (the same counters over a plain device copy
+    of copy_bytes bytes, which scale KiB to bytes).  An op's bytes are its
+    kernels' scaled counters summed over all dispatches, divided by the calls.
+    Writes profiles/hbm_traffic.json (one entry per workload, merged) and a
+    markdown summary named for the workload."""
     outdir = outdir or os.path.join(ROOT, "profiles")
-    wl = WORKLOADS[workload]
-    fetch, write = _counter_means(os.path.join(folder, "fetch")), _counter_means(os.path.join(folder, "write"))
-    cf, cw = _counter_means(os.path.join(folder, "cfetch")), _counter_means(os.path.join(folder, "cwrite"))
-    copy_f = max(v for (k, c), v in cf.items() if c == "FETCH_SIZE")
-    copy_w = max(v for (k, c), v in cw.items() if c == "WRITE_SIZE")
+    cf = [v for _, _, c, v in _counter_rows(os.path.join(folder, "cfetch")) if c == "FETCH_SIZE"]
+    cw = [v for _, _, c, v in _counter_rows(os.path.join(folder, "cwrite")) if c == "WRITE_SIZE"]
+    copy_f, copy_w = max(cf), max(cw)
     ff, fw = copy_bytes / 1024.0 / copy_f, copy_bytes / 1024.0 / copy_w
-    kernels = {}
-    for (k, c), v in sorted(fetch.items()):
-        if c == "FETCH_SIZE" and k.startswith(("wtconv_", "lowpass_")):
-            kernels[k] = {"fetch_kib": v, "write_kib": write.get((k, "WRITE_SIZE"), 0.0),
-                          "fetch_bytes": v * 1024.0 * ff, "write_bytes": write.get((k, "WRITE_SIZE"), 0.0) * 1024.0 * fw}
-    whole = [k for k in kernels if k.startswith("wtconv_whole_kernel")]
-    wgrad = [k for k in kernels if k.startswith("wtconv_wgrad_kernel")]
-    fin = [k for k in kernels if k.startswith("wtconv_wgrad_finalize")]
-    out = {"source_digest": source_digest(), "workload": workload_name(wl), "fetch_factor": ff, "write_factor": fw,
-           "kernels": {k: {"fetch_bytes": v["fetch_bytes"], "write_bytes": v["write_bytes"]} for k, v in kernels.items()}}
-    # per-op bytes where each op is one kernel launch (plus the reduction pass)
-    if len(whole) == 1 and len(wgrad) == 1 and not any(k.startswith("lowpass_") for k in kernels):
-        wb = kernels[whole[0]]["fetch_bytes"] + kernels[whole[0]]["write_bytes"]
-        gb = sum(kernels[k]["fetch_bytes"] + kernels[k]["write_bytes"] for k in wgrad + fin)
-        out["kernels"]["wtconv_forward"] = {"bytes_per_launch": wb}
-        out["kernels"]["wtconv_backward_data"] = {"bytes_per_launch": wb}
-        out["kernels"]["wtconv_backward_weight"] = {"bytes_per_launch": gb}
-    # one entry per workload, merged into what the file already holds
+    calls = reps + 1
+    name = workload_name(wl)
+    ops = {}
+    for key, op in OP_KEYS.items():
+        fr = _counter_rows(os.path.join(folder, key + "_fetch"))
+        wr = _counter_rows(os.path.join(folder, key + "_write"))
+        if not fr or not wr:
+            continue
+        kern = {}
+        for _, k, c, v in fr:
+            if c == "FETCH_SIZE" and _library_kernel(k):
+                e = kern.setdefault(k, {"dispatches": 0, "fetch_bytes": 0.0, "write_bytes": 0.0})
+                e["dispatches"] += 1
+                e["fetch_bytes"] += v * 1024.0 * ff / calls
+        for _, k, c, v in wr:
+            if c == "WRITE_SIZE" and _library_kernel(k):
+                e = kern.setdefault(k, {"dispatches": 0, "fetch_bytes": 0.0, "write_bytes": 0.0})
+                e["write_bytes"] += v * 1024.0 * fw / calls
+        for e in kern.values():
+            e["dispatches"] = e["dispatches"] / calls
+        f = sum(e["fetch_bytes"] for e in kern.values())
+        w = sum(e["write_bytes"] for e in kern.values())
+        model = unfused_forward_elements(wl) * wl.ebytes if key == "unfused_fwd" else op_bytes(wl)
+        ops[op] = {"fetch_bytes": f, "write_bytes": w, "bytes_per_launch": f + w, "modeled_bytes": model,
+                   "ratio_to_model": (f + w) / model, "kernels": kern}
+    out = {"source_digest": source_digest(), "workload": name, "fetch_factor": ff, "write_factor": fw,
+           "calls_per_run": calls, "ops": ops}
     jpath = os.path.join(outdir, "hbm_traffic.json")
     try:
         with open(jpath) as fh:
@@ -207,198 +285,278 @@ def traffic_summary(folder: str, workload: str, copy_bytes: int, outdir: str = N
             allw = {}
     except (OSError, ValueError):
         allw = {}
-    allw[out["workload"]] = out
+    allw[name] = out
     with open(jpath, "w") as fh:
         json.dump(allw, fh, indent=1)
-    E, e = wl.elems, wl.ebytes
-    bench = ("python3 bench.py --workload %s --steps 2 --warmup 1 --cpu-sample 0 --no-unfused --no-comparator"
-             % workload)
-    lines = ["# HBM traffic per launch: %s" % out["workload"], "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 counter runs, each scaled by what "
-             "the same counter reads for a plain %d-byte device copy (`bench.py --copy-calibration %d`): "
-             "FETCH_SIZE reads %.0f KiB for the copy's %.0f KiB (factor %.4f), WRITE_SIZE %.0f KiB (factor %.4f)."
-             % (copy_bytes, copy_bytes, copy_f, copy_bytes / 1024.0, ff, copy_w, fw), "",
-             "Commands (from the repository root; OUT is any output folder):", "",
-             "    rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o fetch --output-format csv -- " + bench,
-             "    rocprofv3 --pmc WRITE_SIZE -d OUT/write -o write --output-format csv -- " + bench,
-             "    rocprofv3 --pmc FETCH_SIZE -d OUT/cfetch -o cfetch --output-format csv -- "
+    sel = "--workload %s%s" % (wl.name, point_args(wl))
+    lines = ["# HBM traffic per op: %s" % name, "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 counter runs per op, each scaled by "
+             "what the same counter reads for a plain %d-byte device copy (`bench.py --copy-calibration %d`): "
+             "FETCH_SIZE reads %.0f KiB for the copy's %.0f KiB (factor %.4f), WRITE_SIZE %.0f KiB (factor %.4f). "
+             "Each run calls the op %d times and nothing else; an op's bytes are the sum over its kernels' "
+             "dispatches divided by the calls." % (copy_bytes, copy_bytes, copy_f, copy_bytes / 1024.0, ff, copy_w,
+                                                   fw, calls), "",
+             "Commands (from the repository root; OUT is any output folder; OP is fwd, bwd_data, bwd_weight "
+             "or unfused_fwd):", "",
+             "    rocprofv3 --pmc FETCH_SIZE -d OUT/OP_fetch -o f --output-format csv -- "
+             "python3 bench.py %s --counter-op OP --reps %d" % (sel, reps),
+             "    rocprofv3 --pmc WRITE_SIZE -d OUT/OP_write -o w --output-format csv -- "
+             "python3 bench.py %s --counter-op OP --reps %d" % (sel, reps),
+             "    rocprofv3 --pmc FETCH_SIZE -d OUT/cfetch -o f --output-format csv -- "
              "python3 bench.py --copy-calibration %d" % copy_bytes,
-             "    rocprofv3 --pmc WRITE_SIZE -d OUT/cwrite -o cwrite --output-format csv -- "
+             "    rocprofv3 --pmc WRITE_SIZE -d OUT/cwrite -o w --output-format csv -- "
              "python3 bench.py --copy-calibration %d" % copy_bytes,
-             "    python3 bench.py --traffic-summary OUT --workload %s --copy-calibration %d" % (workload, copy_bytes),
-             "", "| kernel | FETCH KiB | WRITE KiB | fetch bytes (scaled) | write bytes (scaled) |",
-             "|---|---|---|---|---|"]
-    for k, v in kernels.items():
-        lines.append("| `%s` | %.0f | %.0f | %.4g | %.4g |" % (k, v["fetch_kib"], v["write_kib"], v["fetch_bytes"],
-                                                               v["write_bytes"]))
-    lines += ["", "Counters per dispatch, averaged over all launches of a kernel (sizes mixed where one op "
-              "launches it at several sizes).", "",
-              "Modeled minimum per launch: forward or data backward %.4g bytes (read E e, write E e), weight "
-              "backward %.4g bytes (read 2 E e)." % (2.0 * E * e, 2.0 * E * e), "",
+             "    python3 bench.py --traffic-summary OUT %s --reps %d --copy-calibration %d" % (sel, reps, copy_bytes),
+             "", "| op | kernel | launches per call | fetch bytes | write bytes |", "|---|---|---|---|---|"]
+    for op, d in ops.items():
+        for k, e in d["kernels"].items():
+            lines.append("| %s | `%s` | %.2f | %.4g | %.4g |" % (op, k, e["dispatches"], e["fetch_bytes"],
+                                                                  e["write_bytes"]))
+    lines += ["", "| op | fetch bytes | write bytes | total | modeled | ratio |", "|---|---|---|---|---|---|"]
+    for op, d in ops.items():
+        lines.append("| %s | %.4g | %.4g | %.4g | %.4g | %.3f |" % (op, d["fetch_bytes"], d["write_bytes"],
+                                                                      d["bytes_per_launch"], d["modeled_bytes"],
+                                                                      d["ratio_to_model"]))
+    lines += ["", "Modeled bytes: 2 E e per fused op (E = %d elements of %d bytes); for the unfused forward "
+              "(7 + 10.75 S(L)) E e, S(L) = sum 4^(1-l)." % (wl.elems, wl.ebytes), "",
               "Source digest of the kernels counted: `%s` (bench.py reports `traffic` only while the library "
               "sources still hash to it)." % out["source_digest"]]
-    with open(os.path.join(outdir, "%s_hbm_traffic.md" % workload), "w") as fh:
+    with open(os.path.join(outdir, "%s_hbm_traffic.md" % file_stem(wl)), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return out
 
 
-def trace_summary(folder: str, workload: str, outdir: str = None) -> str:
+VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def valu_summary(folder: str, wl, reps: int, outdir: str = None) -> str:
+    """VALU and LDS counters per op from `rocprofv3 --pmc <VALU_COUNTERS>` runs
+    of `bench.py --counter-op OP` under OUT/<op>_valu.  Per kernel: counters per
+    dispatch (summed over the GPU), and VALU busy = SQ_ACTIVE_INST_VALU x 4 /
+    (SIMDs x GRBM_GUI_ACTIVE) with 1024 SIMDs (the fraction of the SIMDs' cycles
+    spent issuing VALU instructions), instructions per wave, and LDS bank-
+    conflict cycles per LDS-active cycle."""
+    outdir = outdir or os.path.join(ROOT, "profiles")
+    sel = "--workload %s%s" % (wl.name, point_args(wl))
+    lines = ["# VALU and LDS counters per op: %s" % workload_name(wl), "",
+             "Commands (from the repository root; OUT is any output folder; OP is fwd, bwd_data or bwd_weight):", "",
+             "    rocprofv3 --pmc %s -d OUT/OP_valu -o v --output-format csv -- python3 bench.py %s "
+             "--counter-op OP --reps %d" % (" ".join(VALU_COUNTERS), sel, reps),
+             "    python3 bench.py --valu-summary OUT %s --reps %d" % (sel, reps), "",
+             "VALU busy = SQ_ACTIVE_INST_VALU x 4 / (1024 SIMDs x GRBM_GUI_ACTIVE); counters are per dispatch, "
+             "averaged over the dispatches of a kernel.", "",
+             "| op | kernel | dispatches | waves | VALU instr / wave | LDS instr / wave | VALU busy | "
+             "LDS bank-conflict cycles / LDS-active cycle |", "|---|---|---|---|---|---|---|---|"]
+    for key in ("fwd", "bwd_data", "bwd_weight"):
+        rows = _counter_rows(os.path.join(folder, key + "_valu"))
+        per = {}
+        for d, k, c, v in rows:
+            if _library_kernel(k):
+                per.setdefault(k, {}).setdefault(d, {})[c] = v
+        for k, disp in per.items():
+            n = len(disp)
+            mean = {c: sum(x.get(c, 0.0) for x in disp.values()) / n for c in VALU_COUNTERS}
+            waves = max(mean["SQ_WAVES"], 1.0)
+            busy = mean["SQ_ACTIVE_INST_VALU"] * 4.0 / (1024.0 * max(mean["GRBM_GUI_ACTIVE"], 1.0))
+            conf = mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_ACTIVE_INST_LDS"], 1.0)
+            lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %.3f | %.3f |" % (
+                OP_KEYS[key], k, n, waves, mean["SQ_INSTS_VALU"] / waves, mean["SQ_INSTS_LDS"] / waves, busy, conf))
+    lines += ["", "Source digest of the kernels counted: `%s`." % source_digest()]
+    path = os.path.join(outdir, "%s_valu_lds.md" % file_stem(wl))
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
+def point_args(wl) -> str:
+    from level_haar_wavelet_amd.synthetic import WORKLOADS
+
+    base = WORKLOADS[wl.name]
+    return "" if (base.levels, base.dtype) == (wl.levels, wl.dtype) else " --levels %d --dtype %s" % (wl.levels,
+                                                                                                     wl.dtype)
+
+
+def file_stem(wl) -> str:
+    """File name stem of a workload's summaries: its name, and for the level
+    sweep the level and storage type."""
+    return wl.name if wl.name != "sweep" else "sweep_L%d_%s" % (wl.levels, wl.dtype)
+
+
+def trace_summary(folder: str, wl, outdir: str = None) -> str:
     """Writes profiles/<workload>_kernel_trace.md from the *kernel_stats.csv of
     a `rocprofv3 --kernel-trace --stats` run under folder, with the bench line
     folder/bench.json (a plain run of the same build) if present."""
     import csv
     import glob
 
-    from level_haar_wavelet_amd.synthetic import WORKLOADS
-
     outdir = outdir or os.path.join(ROOT, "profiles")
-    wl = WORKLOADS[workload]
-    name = workload_name(wl)
     rows = []
     for path in glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True):
         with open(path, newline="") as fh:
             rows += list(csv.DictReader(fh))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    cmd = ("rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- python3 bench.py --workload %s "
-           "--steps 5 --warmup 2 --cpu-sample 0 --no-unfused --no-comparator" % workload)
-    lines = ["# Kernel durations: %s (MI355X)" % name, "", "Commands (from the repository root; OUT is any output "
-             "folder):", "", "    " + cmd,
-             "    python3 bench.py --workload %s > OUT/kt/bench.json" % workload,
-             "    python3 bench.py --trace-summary OUT/kt --workload %s" % workload, "",
+    sel = "--workload %s%s" % (wl.name, point_args(wl))
+    cmd = ("rocprofv3 --kernel-trace --stats -d OUT/kt -o kt --output-format csv -- python3 bench.py %s "
+           "--steps 5 --warmup 2 --cpu-sample 0 --no-unfused --no-comparator" % sel)
+    lines = ["# Kernel durations: %s (MI355X)" % workload_name(wl), "",
+             "Commands (from the repository root; OUT is any output folder):", "", "    " + cmd,
+             "    python3 bench.py %s --cpu-sample 0 --no-unfused --no-comparator > OUT/kt/bench.json" % sel,
+             "    python3 bench.py --trace-summary OUT/kt %s" % sel, "",
              "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows:
         lines.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f %% |" % (
-            _short_kernel(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            float(r["Percentage"])))
+            _short_kernel(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     lines += ["", "Before the 2 warm-up and 5 timed steps, bench.py runs the step for 0.5 s untimed (clock ramp), "
               "so the call counts are those of about half a second of steps.  A kernel launched at several sizes "
-              "within one op (a tiled pass and the nested call on its level-1 low-pass map) is averaged over all "
-              "its launches."]
+              "within one op is averaged over all its launches."]
     bj = os.path.join(folder, "bench.json")
     if os.path.exists(bj):
         with open(bj) as fh:
             line = [ln for ln in fh.read().splitlines() if ln.startswith("{")][-1]
-        lines += ["", "bench.py line of the same build (`python3 bench.py --workload %s`):" % workload, "", "```",
-                  line, "```"]
-    path = os.path.join(outdir, "%s_kernel_trace.md" % workload)
+        lines += ["", "bench.py line of the same build:", "", "```", line, "```"]
+    path = os.path.join(outdir, "%s_kernel_trace.md" % file_stem(wl))
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     return path
 
 
-def run_gpu(args, wl):
+# ---- GPU runs ----------------------------------------------------------------
+
+
+class Point:
+    """One workload point resident on the GPU: inputs, outputs, parameters,
+    gradient buffers and the three ops' workspaces."""
+
+    def __init__(self, wl, x, dy, params):
+        import torch
+
+        import level_haar_wavelet_amd as wt
+        from level_haar_wavelet_amd import _native
+
+        self.wl = wl
+        dev = x.device
+        self.x, self.dy = x, dy
+        self.y, self.dx = torch.empty_like(x), torch.empty_like(dy)
+        self.w0, self.b0, self.s0, self.wl_, self.sl_ = params
+        dt = 0 if wl.dtype == "f32" else 1
+        shape = (wl.n, wl.c, wl.h, wl.w)
+        self.ws = [torch.empty(max(wt.wtconv_workspace_size(shape, wl.k, wl.levels, dt, op), 1), dtype=torch.uint8,
+                               device=dev) for op in (_native.OP_FWD, _native.OP_BWD_DATA, _native.OP_BWD_WEIGHT)]
+        self.grads = tuple(torch.empty_like(t) if t is not None else None for t in params)
+
+    def ops(self, stream):
+        import level_haar_wavelet_amd as wt
+
+        return (lambda: wt.wtconv_forward(self.x, self.w0, self.b0, self.s0, self.wl_, self.sl_, y=self.y,
+                                          stream=stream, workspace=self.ws[0]),
+                lambda: wt.wtconv_backward_data(self.dy, self.w0, self.s0, self.wl_, self.sl_, dx=self.dx,
+                                                stream=stream, workspace=self.ws[1]),
+                lambda: wt.wtconv_backward_weight(self.x, self.dy, self.w0, self.b0, self.s0, self.wl_, self.sl_,
+                                                  workspace=self.ws[2], grads=self.grads, stream=stream))
+
+
+def make_points(wls):
+    """Device-resident points for a list of workloads.  Sweep points share
+    their activations: the inputs are drawn in the order x, dy, base
+    parameters, then level by level, so every level count of one seed has the
+    same x and dy and its parameters are a prefix of the deepest one's."""
+    import numpy as np
     import torch
 
-    import level_haar_wavelet_amd as wt
-    from level_haar_wavelet_amd import _native
     from level_haar_wavelet_amd.synthetic import make_inputs
 
-    _native.load()
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
-    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
-    T = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev, dtype=dt)
-    x, dy = T(inp.x, tdt), T(inp.dy, tdt)
-    w0, b0, s0, wl_, sl_ = T(inp.w_base), T(inp.bias), T(inp.s_base), T(inp.w_lvl), T(inp.s_lvl)
-    y, dx = torch.empty_like(x), torch.empty_like(dy)
-    ws_bytes = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, 0 if wl.dtype == "f32" else 1,
-                                        _native.OP_BWD_WEIGHT)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    # forward / data-backward workspaces (planes too large for one workgroup keep
-    # their level-1 low-pass map and deeper levels' term there), allocated once
-    wsf = [torch.empty(max(wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels,
-                                                    0 if wl.dtype == "f32" else 1, op), 1),
-                       dtype=torch.uint8, device=dev) for op in (_native.OP_FWD, _native.OP_BWD_DATA)]
-    grads = (torch.empty_like(w0), torch.empty_like(b0), torch.empty_like(s0), torch.empty_like(wl_),
-             torch.empty_like(sl_))
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.mall_flush else None
-    stream = torch.cuda.current_stream()
+    T = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dtype=dt)
+    cache, points = {}, []
+    for wl in wls:
+        key = (wl.name, wl.n, wl.c, wl.h, wl.w, wl.k, wl.seed)
+        if key not in cache:
+            deepest = max(w.levels for w in wls if (w.name, w.n, w.c, w.h, w.w, w.k, w.seed) == key)
+            inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, deepest, dtype="f32", seed=wl.seed)
+            cache[key] = {"inp": inp, "act": {}}
+        ent = cache[key]
+        inp = ent["inp"]
+        if wl.dtype not in ent["act"]:
+            tdt = torch.float32 if wl.dtype == "f32" else torch.float16
+            # fp16 storage: the fp32 draws rounded to fp16, as the recipe does
+            ent["act"][wl.dtype] = (T(inp.x, tdt), T(inp.dy, tdt))
+        x, dy = ent["act"][wl.dtype]
+        L = wl.levels
+        params = (T(inp.w_base), T(inp.bias), T(inp.s_base), T(inp.w_lvl[:L]) if L else None,
+                  T(inp.s_lvl[:L]) if L else None)
+        points.append(Point(wl, x, dy, params))
+    for ent in cache.values():
+        ent["inp"].x = ent["inp"].dy = None
+    return points
 
-    def step(ev=None, s=None):
-        s = s or stream
-        if ev:
-            ev[0].record(s)
-        wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=s, workspace=wsf[0])
-        if ev:
-            ev[1].record(s)
-        wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=s, workspace=wsf[1])
-        if ev:
-            ev[2].record(s)
-        wt.wtconv_backward_weight(x, dy, w0, b0, s0, wl_, sl_, workspace=ws, grads=grads, stream=s)
-        if ev:
-            ev[3].record(s)
+
+def time_points(args, points):
+    """Times the step -- the three ops at every point -- K times after the
+    clock ramp and W warm-up steps.  Returns the step time and, per point and
+    op, the median and mean of the event-timed durations."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ops = [p.ops(stream) for p in points]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0") if args.mall_flush else None
+
+    def step(ev=None):
+        for i, po in enumerate(ops):
+            if ev:
+                ev[i][0].record(stream)
+            for j, op in enumerate(po):
+                op()
+                if ev:
+                    ev[i][j + 1].record(stream)
 
     # the GPU raises its clocks only under sustained load: run the step for
     # about half a second (untimed) before the warm-up steps proper
     t_ramp = time.perf_counter()
     while time.perf_counter() - t_ramp < args.ramp_s:
-        for _ in range(5):
+        for _ in range(3):
             step()
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in points] for _ in range(args.steps)]
     if flush is None:
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         start.record(stream)
-        for i in range(args.steps):
-            step(evs[i])
+        for s in range(args.steps):
+            step(evs[s])
         end.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         ms_total = start.elapsed_time(end)
     else:
         ms_total = 0.0
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            flush.fill_(i & 255)
+        for s in range(args.steps):
+            flush.fill_(s & 255)
             torch.cuda.synchronize()
-            step(evs[i])
+            step(evs[s])
             torch.cuda.synchronize()
-            ms_total += evs[i][0].elapsed_time(evs[i][3])
-        wall = time.perf_counter() - t0
-    per = [[e[j].elapsed_time(e[j + 1]) * 1000.0 for j in range(3)] for e in evs]  # us per op and step
-    med = [sorted(p[j] for p in per)[len(per) // 2] for j in range(3)]
-    mean = [sum(p[j] for p in per) / len(per) for j in range(3)]
-    out = {"ms_per_step": ms_total / args.steps, "us_ops": med, "us_ops_mean": mean, "wall_s": wall}
-    if flush is None and args.graph:
-        out["graph"] = graph_step_ms(torch, step, args.warmup, args.steps)
-    return out
+            ms_total += evs[s][0][0].elapsed_time(evs[s][-1][3])
+    res = []
+    for i in range(len(points)):
+        per = [[evs[s][i][j].elapsed_time(evs[s][i][j + 1]) * 1000.0 for j in range(3)] for s in range(args.steps)]
+        med = [sorted(p[j] for p in per)[len(per) // 2] for j in range(3)]
+        mean = [sum(p[j] for p in per) / len(per) for j in range(3)]
+        step_us = sorted(sum(p) for p in per)[len(per) // 2]
+        res.append({"us_ops": med, "us_ops_mean": mean, "us_step": step_us})
+    return ms_total / args.steps, res
 
 
-def graph_step_ms(torch, step, warmup, steps):
-    """The same step captured once in a HIP graph (the library allocates
-    nothing and only launches kernels on the stream it is given, so the three
-    calls capture as they are) and replayed: K replays timed between two
-    events, after W untimed ones.  Returns ms per step, or the error text if
-    capture fails."""
-    try:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(s=side)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(s=torch.cuda.current_stream())
-        for _ in range(warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cur = torch.cuda.current_stream()
-        a.record(cur)
-        for _ in range(steps):
-            g.replay()
-        b.record(cur)
-        torch.cuda.synchronize()
-        return {"ms_per_step": a.elapsed_time(b) / steps}
-    except RuntimeError as e:  # report, keep the eager measurement
-        return {"error": str(e)[:200]}
+def point_record(wl, r) -> dict:
+    f, b, w = r["us_ops"]
+    gbs = 6.0 * wl.elems * wl.ebytes / (r["us_step"] * 1e-6) / 1e9
+    return {"levels": wl.levels, "dtype": wl.dtype, "us_fwd": round(f, 2), "us_bwd_data": round(b, 2),
+            "us_bwd_weight": round(w, 2), "us_fwd_bwd": round(r["us_step"], 2), "GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "fwd_GBs": round(op_bytes(wl) / (f * 1e-6) / 1e9, 1),
+            "fwd_hbm_frac": round(op_bytes(wl) / (f * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def stream_copy_gbs(nbytes=1 << 30, reps=10):
@@ -435,21 +593,16 @@ def run_unfused(args, wl):
     import level_haar_wavelet_amd as wt
     from level_haar_wavelet_amd import _native
     from level_haar_wavelet_amd import unfused as uf
-    from level_haar_wavelet_amd.synthetic import make_inputs
 
-    dev = torch.device("cuda:0")
-    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
-    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
-    T = lambda a, dt=torch.float32: torch.from_numpy(a).to(dev, dtype=dt)
-    x, dy = T(inp.x, tdt), T(inp.dy, tdt)
-    w0, b0, s0, wl_, sl_ = T(inp.w_base), T(inp.bias), T(inp.s_base), T(inp.w_lvl), T(inp.s_lvl)
-    y, dx = torch.empty_like(x), torch.empty_like(dy)
-    grads = (torch.empty_like(w0), torch.empty_like(b0), torch.empty_like(s0), torch.empty_like(wl_),
-             torch.empty_like(sl_))
-    if wl.levels == 0:
-        wl_ = sl_ = None
-        grads = grads[:3] + (None, None)
+    p = make_points([wl])[0]
+    x, dy, y, dx = p.x, p.dy, p.y, p.dx
+    w0, b0, s0, wl_, sl_ = p.w0, p.b0, p.s0, p.wl_, p.sl_
+    grads = p.grads
+    del p
+    torch.cuda.empty_cache()
     stream = torch.cuda.current_stream()
+    dt = 0 if wl.dtype == "f32" else 1
+    shape = (wl.n, wl.c, wl.h, wl.w)
 
     def peak(fn):
         torch.cuda.synchronize()
@@ -460,11 +613,10 @@ def run_unfused(args, wl):
         return torch.cuda.max_memory_allocated() - base
 
     def fused_step():
-        n = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, 0 if wl.dtype == "f32" else 1,
-                                     _native.OP_BWD_WEIGHT)
-        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         wt.wtconv_forward(x, w0, b0, s0, wl_, sl_, y=y, stream=stream)
         wt.wtconv_backward_data(dy, w0, s0, wl_, sl_, dx=dx, stream=stream)
+        n = wt.wtconv_workspace_size(shape, wl.k, wl.levels, dt, _native.OP_BWD_WEIGHT)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
         wt.wtconv_backward_weight(x, dy, w0, b0, s0, wl_, sl_, workspace=ws, grads=grads, stream=stream)
 
     def unfused_step(ws=None):
@@ -479,7 +631,8 @@ def run_unfused(args, wl):
            lambda: uf.wtconv_unfused_backward_data(dy, w0, s0, wl_, sl_, ws, dx=dx, stream=stream),
            lambda: uf.wtconv_unfused_backward_weight(x, dy, w0, b0, s0, wl_, sl_, ws, grads=grads, stream=stream))
     for _ in range(max(2, args.warmup // 2)):
-        unfused_step(ws)
+        for op in ops:
+            op()
     steps = max(5, args.steps // 5)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -491,84 +644,185 @@ def run_unfused(args, wl):
     torch.cuda.synchronize()
     per = [[e[j].elapsed_time(e[j + 1]) * 1000.0 for j in range(3)] for e in evs]
     med = [sorted(p[j] for p in per)[len(per) // 2] for j in range(3)]
+    del ws
+    torch.cuda.empty_cache()
     return {"us_ops": med, "steps": steps, "peak_mem_fused_bytes": int(mem_fused),
             "peak_mem_unfused_bytes": int(mem_unfused)}
 
 
-def cpu_baseline(wl, images, min_seconds=2.0):
-    """The CPU oracle (as it stands) on `images` images of the workload: one
-    forward, data backward and weight backward, repeated until at least
-    `min_seconds` have passed; the rate is the sample's own modeled bytes
-    (6 E e per pass) over the mean time of a pass."""
+def counter_op(args, wl):
+    """Only one op, reps + 1 times (the first one warm), on one workload: the
+    program the counter runs profile."""
+    import torch
+
+    import level_haar_wavelet_amd as wt
+    from level_haar_wavelet_amd import _native
+    from level_haar_wavelet_amd import unfused as uf
+
+    _native.load()
+    p = make_points([wl])[0]
+    stream = torch.cuda.current_stream()
+    if args.counter_op == "unfused_fwd":
+        ws = uf.workspace(p.x, wl.k, wl.levels)
+        op = lambda: uf.wtconv_unfused_forward(p.x, p.w0, p.b0, p.s0, p.wl_, p.sl_, ws, y=p.y, stream=stream)
+    else:
+        op = p.ops(stream)[("fwd", "bwd_data", "bwd_weight").index(args.counter_op)]
+    for _ in range(args.reps + 1):
+        op()
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_op": args.counter_op, "workload": workload_name(wl), "calls": args.reps + 1}))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _oracle_pass(oracle, inp, wl, threads):
+    args = (inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+    oracle.forward(inp.x, *args, nthreads=threads)
+    oracle.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels, nthreads=threads)
+    oracle.backward_weight(inp.x, inp.dy, *args, nthreads=threads)
+
+
+def cpu_baseline(wls, images, single_thread=(), min_seconds=0.0):
+    """The CPU oracle (as it stands) on a bounded sample: `images` images of
+    every workload point in `wls`, one forward, data backward and weight
+    backward each (repeated until `min_seconds` have passed); the rate is the
+    sample's own modeled bytes (6 E e per pass) over the time.  Also a
+    one-thread time of one pass for each workload in `single_thread`."""
     import oracle
     from level_haar_wavelet_amd.synthetic import make_inputs
 
-    images = max(1, min(images, wl.n))
-    inp = make_inputs(images, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
     threads = oracle.default_threads()
     try:
         threads = min(threads, len(os.sched_getaffinity(0)))
     except AttributeError:
         pass
-    args = (inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
-    oracle.forward(inp.x[:1], *args, nthreads=1)  # load the library outside the timing
-    passes, t0 = 0, time.perf_counter()
+    samples = []
+    for wl in wls:
+        n = max(1, min(images, wl.n))
+        samples.append((wl, n, make_inputs(n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)))
+    wl0, _, inp0 = samples[0]
+    one = make_inputs(1, 1, 8, 8, wl0.k, wl0.levels, seed=0)
+    _oracle_pass(oracle, one, dataclasses.replace(wl0, n=1, c=1, h=8, w=8), 1)  # load outside the timing
+    passes, nbytes, t0 = 0, 0.0, time.perf_counter()
     while True:
-        oracle.forward(inp.x, *args, nthreads=threads)
-        oracle.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels,
-                             nthreads=threads)
-        oracle.backward_weight(inp.x, inp.dy, *args, nthreads=threads)
+        for wl, n, inp in samples:
+            _oracle_pass(oracle, inp, wl, threads)
+            nbytes += 6.0 * n * wl.c * wl.h * wl.w * wl.ebytes
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= 50:
             break
-    per = dt / passes
-    e = images * wl.c * wl.h * wl.w
-    return {"value": round(6.0 * e * wl.ebytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d images (%dx%dx%dx%d), fwd + bwd_data + bwd_weight in fp64, %d passes, %.3f s/pass"
-                      % (images, wl.n, images, wl.c, wl.h, wl.w, passes, per),
-            "seconds_per_pass": round(per, 4)}
+    names = sorted({"%s L=%s" % (wl.name, ",".join(str(w.levels) for w in wls if w.name == wl.name)) for wl in wls})
+    out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": "%d image(s) of each of %d point(s) (%s, %s), fwd + bwd_data + bwd_weight in fp64, %d pass(es), "
+                     "%.2f s wall" % (samples[0][1], len(samples), "; ".join(names),
+                                      "/".join(sorted({w.dtype for w in wls})), passes, dt),
+           "seconds": round(dt, 3)}
+    one_thread = {}
+    for wl in single_thread:
+        inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+        t1 = time.perf_counter()
+        _oracle_pass(oracle, inp, wl, 1)
+        dt1 = time.perf_counter() - t1
+        one_thread[wl.name] = {"seconds_per_pass": round(dt1, 4),
+                               "GBs": round(6.0 * wl.elems * wl.ebytes / dt1 / 1e9, 4)}
+    if one_thread:
+        out["one_thread"] = one_thread
+    return out
+
+
+def graph_step_ms(torch, step, warmup, steps):
+    """The same step captured once in a HIP graph and replayed: K replays timed
+    between two events, after W untimed ones.  Returns ms per step, or the
+    error text if capture fails."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        a.record(cur)
+        for _ in range(steps):
+            g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        return {"ms_per_step": a.elapsed_time(b) / steps}
+    except RuntimeError as e:  # report, keep the eager measurement
+        return {"error": str(e)[:200]}
+
+
+def selected_workloads(args):
+    from level_haar_wavelet_amd.synthetic import WORKLOADS, sweep_workloads
+
+    if args.workload == "sweep" and args.levels is None and args.dtype is None:
+        return sweep_workloads()
+    wl = WORKLOADS[args.workload]
+    if args.levels is not None or args.dtype is not None:
+        wl = wl.with_levels(args.levels if args.levels is not None else wl.levels, args.dtype)
+    return [wl]
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ramp-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warm-up steps (clock ramp)")
-    ap.add_argument("--workload", default="stage1")
+    ap.add_argument("--workload", default="sweep")
     ap.add_argument("--levels", type=int, default=None)
     ap.add_argument("--dtype", default=None)
-    ap.add_argument("--cpu-sample", type=int, default=64)
+    ap.add_argument("--cpu-sample", type=int, default=4, help="images per point of the CPU-oracle sample (0: none)")
     ap.add_argument("--mall-flush", action="store_true")
-    ap.add_argument("--all", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
-    ap.add_argument("--trace-summary", default=None,
-                    help="folder of a kernel-trace run: write the kernel-duration summary under profiles/ and exit")
-    ap.add_argument("--traffic-summary", default=None,
-                    help="folder of the four counter runs: write the HBM-traffic summaries under profiles/ and exit")
+    ap.add_argument("--counter-op", default=None, choices=sorted(OP_KEYS))
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--trace-summary", default=None)
+    ap.add_argument("--traffic-summary", default=None)
+    ap.add_argument("--valu-summary", default=None)
     ap.add_argument("--no-unfused", action="store_true", help="skip the unfused-baseline comparison")
     ap.add_argument("--no-comparator", action="store_true", help="skip the 7x7 depthwise comparator")
+    ap.add_argument("--no-extra", action="store_true", help="skip the stage1 and large-workload lines")
     ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured in a HIP graph and replayed (reported as graph_ms_per_step)")
+                    help="also time the step captured in a HIP graph and replayed (graph_ms_per_step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU layer; more than one GPU is not supported in this build "
-              "(the layer needs no collective for forward or data backward; see the design notes).",
-              file=sys.stderr)
+              "(every workload fits one GPU, and the layer needs no collective for its forward or data "
+              "backward; the design notes describe how it would shard).", file=sys.stderr)
         sys.exit(2)
 
+    wls = selected_workloads(args)
     if args.trace_summary:
-        print(trace_summary(args.trace_summary, args.workload))
+        print(trace_summary(args.trace_summary, wls[0]))
         return
-
     if args.traffic_summary:
-        print(json.dumps(traffic_summary(args.traffic_summary, args.workload, args.copy_calibration or (1 << 30)),
+        print(json.dumps(traffic_summary(args.traffic_summary, wls[0], args.reps, args.copy_calibration or (1 << 30)),
                          indent=1))
         return
-
+    if args.valu_summary:
+        print(valu_summary(args.valu_summary, wls[0], args.reps))
+        return
     if args.copy_calibration:
         import torch
 
@@ -579,31 +833,34 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_calibration}))
         return
+    if args.counter_op:
+        counter_op(args, wls[0])
+        return
 
+    import torch
+
+    from level_haar_wavelet_amd import _native
     from level_haar_wavelet_amd.synthetic import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
-    if args.levels is not None or args.dtype is not None:
-        wl = wl.with_levels(args.levels if args.levels is not None else wl.levels, args.dtype)
-
-    res = run_gpu(args, wl)
-    E, e = wl.elems, wl.ebytes
-    step_bytes = 6.0 * E * e
-    # eager launches; with --graph the same step captured in a HIP graph and
-    # replayed is reported next to it (it measured slower on MI355X, 223
-    # against 205 us per step at stage1, so it does not set the value)
-    graph = res.get("graph", {})
-    ms = res["ms_per_step"]
+    _native.load()
+    torch.cuda.set_device(0)
+    points = make_points(wls)
+    ms, res = time_points(args, points)
+    graph = None
+    if args.graph and not args.mall_flush:
+        stream = torch.cuda.current_stream()
+        allops = [op for p in points for op in p.ops(stream)]
+        graph = graph_step_ms(torch, lambda: [op() for op in allops], args.warmup, args.steps)
+    del points
+    torch.cuda.empty_cache()
+    step_bytes = sum(6.0 * wl.elems * wl.ebytes for wl in wls)
     value = step_bytes / (ms * 1e-3) / 1e9
-    us_f, us_b, us_w = res["us_ops"]
-    flops = conv_flops(wl)
-    # the roofline uses each op's average duration over the timed steps (the
-    # statistic a kernel-trace summary reports)
-    ops = dict(zip(("wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight"), res["us_ops_mean"]))
-    dominant = max(ops, key=ops.get)
-    achieved = flops / (ops[dominant] * 1e-6) / 1e12
     digest = source_digest()
-    traffic = measured_traffic(dominant, digest, workload_name(wl))
+    # the dominant op: the longest mean duration of any op at any point
+    dom = max(((i, j) for i in range(len(wls)) for j in range(3)), key=lambda ij: res[ij[0]]["us_ops_mean"][ij[1]])
+    rl = roofline(wls[dom[0]], OPS[dom[1]], res[dom[0]]["us_ops_mean"][dom[1]], digest)
+    wl0 = wls[0]
+    sweep = len(wls) > 1
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -617,41 +874,49 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": workload_name(wl),
-                   "n": wl.n, "c": wl.c, "h": wl.h, "w": wl.w, "k": wl.k, "levels": wl.levels,
-                   "parallelism": "single GPU"},
-        "us_fwd": round(us_f, 2),
-        "us_bwd_data": round(us_b, 2),
-        "us_bwd_weight": round(us_w, 2),
-        "us_fwd_bwd": round(us_f + us_b + us_w, 2),
-        "us_per_op": "median over the timed steps (events around each call); means %s" % (
-            ", ".join("%.2f" % v for v in res["us_ops_mean"])),
+        "config": {"workload": ("level sweep 32x128x128x128 k=5, L=1..5, fp32 and fp16 storage (ten points, "
+                                "one step = fwd + bwd_data + bwd_weight at every point)") if sweep
+                   else workload_name(wl0),
+                   "n": wl0.n, "c": wl0.c, "h": wl0.h, "w": wl0.w, "k": wl0.k,
+                   "levels": sorted({w.levels for w in wls}), "storage": sorted({w.dtype for w in wls}),
+                   "arithmetic": "fp32", "parallelism": "single GPU"},
+        "value_is": "sum over the points of the modeled minimum bytes 6 E e (fwd 2 E e, bwd_data 2 E e, "
+                    "bwd_weight 2 E e) / the step time",
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "points": [point_record(w, r) for w, r in zip(wls, res)],
+        "us_per_op": "medians over the timed steps of HIP events around each call",
         "stream_copy_GBs": round(stream_copy_gbs(), 1),
         "modeled_bytes_per_step": step_bytes,
         "mall_flush": bool(args.mall_flush),
-        "graph_ms_per_step": round(graph["ms_per_step"], 4) if "ms_per_step" in graph else graph.get("error"),
-        "roofline": {
-            "bound": "alu",
-            "kernel": dominant,
-            "achieved": round(achieved, 3),
-            "peak": round(VALU_FP32_PEAK_TFLOPS, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / VALU_FP32_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "flops_per_launch": flops,
-            "peak_published_packed_fp32": PACKED_FP32_PUBLISHED_TFLOPS,
-            "source_digest": digest,
-        },
+        "roofline": rl,
     }
+    if graph is not None:
+        line["graph_ms_per_step"] = round(graph["ms_per_step"], 4) if "ms_per_step" in graph else graph.get("error")
+    if not args.no_extra and sweep:
+        # the other workloads, one step each, timed the same way
+        extra = {}
+        for name in ("stage1", "stage2", "large"):
+            wl = WORKLOADS[name]
+            ms2, r2 = time_points(args, make_points([wl]))
+            torch.cuda.empty_cache()
+            rec = point_record(wl, r2[0])
+            rec["workload"] = workload_name(wl)
+            rec["roofline_frac_dominant"] = roofline(wl, OPS[max(range(3), key=lambda j: r2[0]["us_ops_mean"][j])],
+                                                     max(r2[0]["us_ops_mean"]), digest)["frac"]
+            extra[name] = rec
+        line["other_workloads"] = extra
+    ref = wls[min(2, len(wls) - 1)] if sweep else wl0  # the L = 3 fp32 point of the sweep
     if not args.no_unfused:
-        u = run_unfused(args, wl)
+        u = run_unfused(args, ref)
+        r = next(rr for w, rr in zip(wls, res) if w == ref)
         uf, ub, uw = u["us_ops"]
+        us_f, us_b, us_w = r["us_ops"]
         line["unfused_baseline"] = {
             "what": "the same layer as separate kernels with every intermediate in HBM (wtconv_unfused_*), "
                     "timed the same way (medians over %d steps)" % u["steps"],
+            "workload": workload_name(ref),
             "us_fwd": round(uf, 2), "us_bwd_data": round(ub, 2), "us_bwd_weight": round(uw, 2),
             "us_fwd_bwd": round(uf + ub + uw, 2),
             "speedup_fwd": round(uf / us_f, 3), "speedup_fwd_bwd": round((uf + ub + uw) / (us_f + us_b + us_w), 3),
@@ -662,35 +927,27 @@ def main():
         # the same shape through a plain 7 x 7 depthwise convolution with bias
         # and scale (the library at L = 0, k = 7): the layer the method's
         # accuracy and cost are compared with
-        import dataclasses
-
-        dw = dataclasses.replace(wl, name=wl.name + "-dw7x7", k=7, levels=0)
-        r7 = run_gpu(args, dw)
-        f7, b7, w7 = r7["us_ops"]
-        line["dw7x7_comparator"] = {
-            "what": "7x7 depthwise conv (+bias, scale) on the same tensors, same timing",
-            "us_fwd": round(f7, 2), "us_bwd_data": round(b7, 2), "us_bwd_weight": round(w7, 2),
-            "us_fwd_bwd": round(f7 + b7 + w7, 2),
-            "flops_per_element": 2 * 49, "wtconv_flops_per_element": round(conv_flops(wl) / wl.elems, 2),
-            "wtconv_over_dw7x7_fwd": round(us_f / f7, 3),
-            "wtconv_over_dw7x7_fwd_bwd": round((us_f + us_b + us_w) / (f7 + b7 + w7), 3),
-        }
+        cmp_ = {}
+        for w in ([ref, next((w for w in wls if w.dtype == "f16" and w.levels == ref.levels), None)]
+                  if sweep else [ref]):
+            if w is None:
+                continue
+            dw = dataclasses.replace(w, name=w.name, k=7, levels=0)
+            _, r7 = time_points(args, make_points([dw]))
+            torch.cuda.empty_cache()
+            f7, b7, w7 = r7[0]["us_ops"]
+            r = next(rr for ww, rr in zip(wls, res) if ww == w)
+            us_f, us_b, us_w = r["us_ops"]
+            cmp_[w.dtype] = {"workload": workload_name(w), "us_fwd": round(f7, 2), "us_bwd_data": round(b7, 2),
+                             "us_bwd_weight": round(w7, 2), "us_fwd_bwd": round(f7 + b7 + w7, 2),
+                             "wtconv_over_dw7x7_fwd": round(us_f / f7, 3),
+                             "wtconv_over_dw7x7_fwd_bwd": round((us_f + us_b + us_w) / (f7 + b7 + w7), 3)}
+        line["dw7x7_comparator"] = {"what": "7x7 depthwise conv (+bias, scale) on the same tensors, same timing; "
+                                            "98 FLOP per element against WTConv's 2 k^2 (1 + S(L))", **cmp_}
     if args.cpu_sample > 0:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        single = [WORKLOADS[n] for n in ("tiny", "stage1", "stage2")] if sweep else []
+        line["cpu_baseline"] = cpu_baseline(wls, args.cpu_sample, single_thread=single)
     print(json.dumps(line), flush=True)
-
-    if args.all:
-        from level_haar_wavelet_amd.synthetic import sweep_workloads
-
-        for w2 in [WORKLOADS["stage2"]] + sweep_workloads() + [WORKLOADS["large"]]:
-            r2 = run_gpu(args, w2)
-            ms2 = r2["ms_per_step"]
-            v2 = 6.0 * w2.elems * w2.ebytes / (ms2 * 1e-3) / 1e9
-            print(json.dumps({"workload": w2.name, "levels": w2.levels, "dtype": w2.dtype,
-                              "us_fwd": round(r2["us_ops"][0], 2), "us_bwd_data": round(r2["us_ops"][1], 2),
-                              "us_bwd_weight": round(r2["us_ops"][2], 2), "ms_per_step": round(ms2, 4),
-                              "GB/s": round(v2, 1), "hbm_frac": round(v2 / HBM_PEAK_GBS, 4)}), file=sys.stderr,
-                  flush=True)
 
 
 if __name__ == "__main__":

@@ -44,7 +44,7 @@ def test_counter_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_pa
     digest = bench.source_digest()
     wname = bench.workload_name(WORKLOADS["stage1"])
     (prof / "hbm_traffic.json").write_text(json.dumps(
-        {wname: {"source_digest": digest, "kernels": {"wtconv_forward": {"bytes_per_launch": 123.0}}}}))
+        {wname: {"source_digest": digest, "ops": {"wtconv_forward": {"bytes_per_launch": 123.0}}}}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("wtconv_forward", digest, wname) == 123.0
     assert bench.measured_traffic("wtconv_forward", "0" * 16, wname) is None
@@ -55,9 +55,38 @@ def test_counter_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_pa
 
 def test_cpu_baseline_times_the_oracle_on_a_bounded_sample():
     wl = WORKLOADS["tiny"]
-    out = bench.cpu_baseline(wl, images=1, min_seconds=0.05)
+    out = bench.cpu_baseline([wl, wl.with_levels(1)], images=1, single_thread=[wl])
     assert out["kind"] == "oracle" and out["cores"] >= 1 and out["value"] > 0
-    assert "1 of %d images" % wl.n in out["sample"]
+    assert out["sample"].startswith("1 image(s) of each of 2 point(s)")
+    assert out["cpu_model"] and out["one_thread"]["tiny"]["seconds_per_pass"] > 0
+
+
+@pytest.mark.parametrize("name,levels,dtype,bound", [("stage1", 3, "f32", "hbm"), ("sweep", 5, "f32", "hbm"),
+                                                     ("sweep", 1, "f16", "alu"), ("large", 4, "f16", "alu")])
+def test_roofline_bound_follows_the_intensity_against_the_published_ridge(name, levels, dtype, bound):
+    """fp32 storage: 100-117 FLOP per 8 bytes (12.5-14.6 FLOP/B) is below the
+    ridge of 157.3 TFLOP/s over 8 TB/s (19.7 FLOP/B), so HBM bounds it; fp16
+    storage halves the bytes (25-29 FLOP/B) and the fp32 vector ALUs bound it."""
+    wl = WORKLOADS[name].with_levels(levels, dtype)
+    r = bench.roofline(wl, "wtconv_forward", 100.0, "0" * 16)
+    assert r["bound"] == bound
+    if bound == "hbm":
+        assert r["unit"] == "GB/s" and r["peak"] == 8000.0
+        assert r["achieved"] == pytest.approx(2 * wl.elems * wl.ebytes / 1e-4 / 1e9, rel=1e-3)
+    else:
+        assert r["unit"] == "TFLOP/s" and r["peak"] == 157.3
+        assert r["achieved"] == pytest.approx(bench.conv_flops(wl) / 1e-4 / 1e12, rel=1e-3)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-3)
+    assert r["nonpacked_fp32_frac"] == pytest.approx(r["achieved_TFLOPs"] / 78.6432, rel=1e-3)
+
+
+def test_unfused_byte_model_matches_the_pages_endpoints():
+    """The unfused forward moves (7 + 10.75 S(L)) E elements: 17.75 E at L = 1
+    and 21.32 E at L = 5, the two ends the pages give for the reference."""
+    wl1 = WORKLOADS["sweep"].with_levels(1, "f32")
+    wl5 = WORKLOADS["sweep"].with_levels(5, "f32")
+    assert bench.unfused_forward_elements(wl1) / wl1.elems == pytest.approx(17.75)
+    assert bench.unfused_forward_elements(wl5) / wl5.elems == pytest.approx(21.32, abs=0.01)
 
 
 def test_source_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
@@ -83,32 +112,32 @@ def _write_counters(folder, rows):
         w.writerows(rows)
 
 
-def test_traffic_summary_scales_counters_by_the_copy_calibration(tmp_path):
+def test_traffic_summary_sums_an_ops_launches_and_scales_by_the_copy(tmp_path):
     # a 1 MiB copy whose FETCH_SIZE reads half its bytes (factor 2) and whose
-    # WRITE_SIZE reads them exactly (factor 1); two dispatches per kernel
+    # WRITE_SIZE reads them exactly (factor 1); the op runs twice (reps = 1),
+    # two kernels per call
     copy = 1 << 20
-    whole, wgrad, fin = ("wtconv_whole_kernel<float, 5, 4, false>", "wtconv_wgrad_kernel<float, 5, 4, 3, false>",
-                         "wtconv_wgrad_finalize_kernel")
-    _write_counters(tmp_path / "fetch", [(1, "void %s(WtcWholeArgs<float>)" % whole, "FETCH_SIZE", 100), (2, whole, "FETCH_SIZE", 300),
-                                         (3, wgrad, "FETCH_SIZE", 50), (4, fin, "FETCH_SIZE", 2),
-                                         (5, "copyBuffer", "FETCH_SIZE", 7)])
-    _write_counters(tmp_path / "write", [(1, whole, "WRITE_SIZE", 10), (2, whole, "WRITE_SIZE", 30),
-                                         (3, wgrad, "WRITE_SIZE", 4), (4, fin, "WRITE_SIZE", 1)])
+    whole, low = "wtconv_whole_kernel<float, 5, 4, true, false>", "lowpass_kernel<float>"
+    _write_counters(tmp_path / "fwd_fetch", [(1, "void %s(WtcWholeArgs<float>)" % low, "FETCH_SIZE", 100),
+                                             (2, whole, "FETCH_SIZE", 300), (3, low, "FETCH_SIZE", 100),
+                                             (4, whole, "FETCH_SIZE", 300), (5, "copyBuffer", "FETCH_SIZE", 7)])
+    _write_counters(tmp_path / "fwd_write", [(1, low, "WRITE_SIZE", 10), (2, whole, "WRITE_SIZE", 30),
+                                             (3, low, "WRITE_SIZE", 10), (4, whole, "WRITE_SIZE", 30)])
     _write_counters(tmp_path / "cfetch", [(1, "copyBuffer", "FETCH_SIZE", 512)])
     _write_counters(tmp_path / "cwrite", [(1, "copyBuffer", "WRITE_SIZE", 1024)])
-    out = bench.traffic_summary(str(tmp_path), "stage1", copy, outdir=str(tmp_path))
+    wl = WORKLOADS["stage1"]
+    out = bench.traffic_summary(str(tmp_path), wl, 1, copy, outdir=str(tmp_path))
     assert out["fetch_factor"] == pytest.approx(2.0) and out["write_factor"] == pytest.approx(1.0)
-    k = out["kernels"]
-    assert k[whole]["fetch_bytes"] == pytest.approx(200 * 1024 * 2.0)
-    assert k[whole]["write_bytes"] == pytest.approx(20 * 1024)
-    assert k["wtconv_forward"]["bytes_per_launch"] == pytest.approx((400 + 20) * 1024)
-    assert k["wtconv_backward_weight"]["bytes_per_launch"] == pytest.approx((100 + 4 + 4 + 1) * 1024)
-    assert "copyBuffer" not in k
+    op = out["ops"]["wtconv_forward"]
+    assert op["fetch_bytes"] == pytest.approx(400 * 1024 * 2.0)
+    assert op["write_bytes"] == pytest.approx(40 * 1024)
+    assert op["bytes_per_launch"] == pytest.approx((800 + 40) * 1024)
+    assert op["kernels"][low]["dispatches"] == pytest.approx(1.0)
+    assert "copyBuffer" not in op["kernels"]
     assert out["source_digest"] == bench.source_digest()
     saved = json.load(open(tmp_path / "hbm_traffic.json"))
     assert saved == {out["workload"]: json.loads(json.dumps(out))}
-    # a second workload is merged in, the first kept
-    out2 = bench.traffic_summary(str(tmp_path), "stage2", copy, outdir=str(tmp_path))
+    out2 = bench.traffic_summary(str(tmp_path), WORKLOADS["stage2"], 1, copy, outdir=str(tmp_path))
     saved = json.load(open(tmp_path / "hbm_traffic.json"))
     assert set(saved) == {out["workload"], out2["workload"]}
     assert (tmp_path / "stage1_hbm_traffic.md").read_text().count("rocprofv3 --pmc") == 4

@@ -222,12 +222,31 @@ def test_workload_stage2_full(orc):
     _workload_case(orc, WORKLOADS["stage2"])
 
 
+def _workload_chunked(orc, wl, chunk):
+    """Every image of the workload against the oracle, the oracle run on
+    `chunk` images at a time (bounded host memory); the library runs the whole
+    batch in one launch, as bench.py times it."""
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    d = DevInputs(inp, wl.dtype)
+    y = forward(d)
+    dx = backward_data(d)
+    torch.cuda.synchronize()
+    for n0 in range(0, wl.n, chunk):
+        sel = slice(n0, n0 + chunk)
+        _log("  images %d..%d" % (n0, min(n0 + chunk, wl.n) - 1))
+        ref = orc.forward(inp.x[sel], inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+        assert_close(y[sel], ref, wl.dtype, "%s L=%d y images %d+" % (wl.name, wl.levels, n0))
+        ref = orc.backward_data(inp.dy[sel], inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, wl.k, wl.levels)
+        assert_close(dx[sel], ref, wl.dtype, "%s L=%d dx images %d+" % (wl.name, wl.levels, n0))
+        del ref
+
+
 @pytest.mark.parametrize("wl", sweep_workloads(), ids=lambda w: "L%d_%s" % (w.levels, w.dtype))
-def test_workload_sweep_sampled(orc, wl):
-    _log("sweep 32x128x128x128 L=%d %s, samples n=0 and n=31" % (wl.levels, wl.dtype))
-    _workload_case(orc, wl, planes=np.array([0, 31]))
+def test_workload_sweep_full(orc, wl):
+    _log("sweep 32x128x128x128 L=%d %s, every image" % (wl.levels, wl.dtype))
+    _workload_chunked(orc, wl, chunk=8)
 
 
-def test_workload_large_sampled(orc):
-    _log("large 16x256x256x256 L=4 fp16, sample n=5")
-    _workload_case(orc, WORKLOADS["large"], planes=np.array([5]))
+def test_workload_large_full(orc):
+    _log("large 16x256x256x256 L=4 fp16, every image")
+    _workload_chunked(orc, WORKLOADS["large"], chunk=4)

@@ -1,9 +1,10 @@
 """GPU parity of the parameter gradients (wtconv_backward_weight) against the
 CPU oracle, through the C ABI: relative L2 per gradient tensor <= 1e-4 for
-fp32 activations, <= 5e-3 for fp16 storage.  Shapes cover the whole-plane
+fp32 activations, <= 5e-3 for fp16 storage, per tensor and per channel.  Shapes cover the whole-plane
 kernel and the level-by-level tiled path; at the large workloads the
-full-batch launch is checked as the sum of batch chunks, each chunk against
-the oracle where it is cheap enough."""
+full-batch launch is compared with the oracle's gradients summed over image
+chunks (the gradients are sums over images, so the chunks add up exactly in
+fp64)."""
 import sys
 
 import numpy as np
@@ -112,37 +113,24 @@ def test_workload_full(orc, name):
     assert_grads_close(got, _oracle(orc, inp, wl.k, wl.levels), wl.dtype, name)
 
 
-def _chunked(orc, wl, chunk, check_chunks):
+def _full_batch(orc, wl, chunk):
     inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
-    d = DevInputs(inp, wl.dtype)
-    full = [None if t is None else t.double().cpu().numpy() for t in backward_weight(d)]
+    got = backward_weight(DevInputs(inp, wl.dtype))
     torch.cuda.synchronize()
     total = None
-    for i, n0 in enumerate(range(0, wl.n, chunk)):
-        sub = make_inputs(1, 1, 2, 2, wl.k, wl.levels, seed=0)  # shape holder only
-        sub.x, sub.dy = inp.x[n0:n0 + chunk], inp.dy[n0:n0 + chunk]
-        sub.w_base, sub.bias, sub.s_base, sub.w_lvl, sub.s_lvl = inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl
-        part = [None if t is None else t.double().cpu().numpy() for t in backward_weight(DevInputs(sub, wl.dtype))]
-        torch.cuda.synchronize()
-        if i in check_chunks:
-            assert_grads_close(part, _oracle(orc, inp, wl.k, wl.levels, slice(n0, n0 + chunk)), wl.dtype,
-                               "%s chunk %d" % (wl.name, i))
-        if total is None:
-            total = part
-        else:
-            # ds and dw are linear in the (x, dy) pairs, so chunks add up
-            total = [t + p for t, p in zip(total, part)]
-    for name, f, t in zip(("dw_base", "dbias", "ds_base", "dw_lvl", "ds_lvl"), full, total):
-        rel = np.linalg.norm(f - t) / max(np.linalg.norm(t), 1e-30)
-        assert rel <= 1e-5, (wl.name, name, rel)
+    for n0 in range(0, wl.n, chunk):
+        _log("  oracle images %d..%d" % (n0, min(n0 + chunk, wl.n) - 1))
+        part = _oracle(orc, inp, wl.k, wl.levels, slice(n0, n0 + chunk))
+        total = list(part) if total is None else [t + p for t, p in zip(total, part)]
+    assert_grads_close(got, total, wl.dtype, "%s L=%d %s" % (wl.name, wl.levels, wl.dtype))
 
 
 @pytest.mark.parametrize("wl", sweep_workloads(), ids=lambda w: "L%d_%s" % (w.levels, w.dtype))
-def test_workload_sweep_chunked(orc, wl):
-    _log("wgrad sweep L=%d %s" % (wl.levels, wl.dtype))
-    _chunked(orc, wl, chunk=8, check_chunks=(0,))
+def test_workload_sweep_full(orc, wl):
+    _log("wgrad sweep L=%d %s, full batch" % (wl.levels, wl.dtype))
+    _full_batch(orc, wl, chunk=8)
 
 
-def test_workload_large_chunked(orc):
-    _log("wgrad large")
-    _chunked(orc, WORKLOADS["large"], chunk=4, check_chunks=(1,))
+def test_workload_large_full(orc):
+    _log("wgrad large, full batch")
+    _full_batch(orc, WORKLOADS["large"], chunk=4)
