@@ -226,6 +226,31 @@ bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp, int nobas
     return false;
 }
 
+// Fused large-plane plan (planes too large for one workgroup whose level-1
+// low-pass map fits one, L >= 2, no base-less call): the deeper levels staged
+// from x and kept on chip, the base and level 1 on tiles, in one kernel with
+// no workspace.  Tile shapes in the order of tile_shapes(); WTCONV_NO_LARGE=1
+// takes it away (the tiles plus a nested call on a stored low-pass map).
+bool large_choice(const wtconv_desc_t *d, int rotate, WtcLargePlan *lp, int nobase)
+{
+    if (nobase || d->levels < 2 || env_int("WTCONV_NO_LARGE", 0, 0, 1) || env_int("WTCONV_NO_TILES", 0, 0, 1))
+        return false;
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    const TileShapes shapes = tile_shapes(false);
+    for (int si = 0; si < shapes.n; ++si) {
+        const int *sh = shapes.s[si];
+        if (wtc_make_large_plan(lp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, d->levels,
+                                rotate, kFusedThreads, 1, eb, whole_budget_floats()))
+            continue;
+        const int resident = wtc_large_resident(d->dtype, *lp);
+        int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
+        if (!planes) planes = wtc_choose_planes(d->n, d->c, resident > 0 ? resident : 512, kWholeFixed);
+        return wtc_make_large_plan(lp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, d->levels,
+                                   rotate, kFusedThreads, planes, eb, whole_budget_floats()) == 0;
+    }
+    return false;
+}
+
 // The deeper levels (L >= 2) of a tiled pass are the layer with L - 1 levels
 // on the level-1 low-pass map, with the level weights and scales from level 2
 // on and a zero base scale.  That map and the nested call's output are fp32
@@ -254,6 +279,8 @@ size_t pass_workspace(const wtconv_desc_t *d, int rotate, int nobase)
     }
     WtcWholePlan wp;
     if (whole_choice(d, rotate, &wp, nobase) || d->levels < 2 || !tile_choice(d, rotate, &wp, nobase)) return 0;
+    WtcLargePlan lp;
+    if (large_choice(d, rotate, &lp, nobase)) return 0;
     const wtconv_desc_t sd = deeper_desc(d);
     const size_t quarter = align256(act_bytes(&sd));
     return 2 * quarter + align256((size_t)d->c * 4) + pass_workspace(&sd, rotate, 1);
@@ -305,6 +332,8 @@ wtconv_status_t fused_pass(const wtconv_desc_t *d, const void *in, const float *
     WtcWholePlan wp;
     if (whole_choice(d, rotate, &wp, nobase)) {
         if (launch) e = wtc_launch_whole(d->dtype, wp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
+    } else if (WtcLargePlan lp; tile_choice(d, rotate, &wp, nobase) && large_choice(d, rotate, &lp, nobase)) {
+        if (launch) e = wtc_launch_large(d->dtype, lp, in, out, w_base, bias, s_base, w_lvl, s_lvl, s);
     } else if (tile_choice(d, rotate, &wp, nobase)) {
         const void *low = nullptr;
         if (d->levels >= 2) {

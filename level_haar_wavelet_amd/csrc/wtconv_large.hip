@@ -1,0 +1,135 @@
+// wtconv_large.hip -- the fused large-plane forward / data-backward kernel for
+// gfx950 (plans and phases in wtconv_large_body.h and wtconv_whole_body.h).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "wtconv_large_body.h"
+#include "wtconv_launch.h"
+
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads issued before it (the next tile's input) stay in flight.
+static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int K, int BW>
+__global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
+{
+    extern __shared__ float wtc_lds[];
+    const WtcWholeArgs<T> ad = A.dview(), at = A.tview();
+    WtcWholeCtx<T> cd, ct;
+    cd.lds = ct.lds = wtc_lds;
+    cd.tid = ct.tid = threadIdx.x;
+    cd.nth = ct.nth = blockDim.x;
+    wtc_whole_setup<T>(ad, cd, blockIdx.x);
+    wtc_whole_setup<T>(at, ct, blockIdx.x);
+    const int tiles = at.p.tiles_x * at.p.tiles_y;
+    for (int i = ct.tid; i < A.p.lds_floats; i += ct.nth) wtc_lds[i] = 0.0f;
+    wtc_lds_barrier();
+    wtc_whole_fold<T, K>(ad, cd);
+    wtc_whole_fold<T, K>(at, ct);
+    wtc_whole_table<T, K, BW>(ad, cd);
+    wtc_whole_table<T, K, BW>(at, ct);
+    for (int img = 0; img < cd.nimg; ++img) {
+        // deeper levels, staged from x through registers
+        float ll[4][4];
+        wtc_large_load_d<T>(A, cd, img, ll);
+        if (img > 0) {
+            wtc_large_zero_d<T>(A.p, cd);
+            wtc_lds_barrier();
+        }
+        wtc_whole_stage_vals<T, K, BW, false, false>(ad, cd, ll);
+        // the first tile's input is requested now and lands while the deeper
+        // levels are computed
+        const int u0 = img * tiles;
+        wtc_whole_load<T, K, BW, true, false>(at, ct, u0);
+        wtc_lds_barrier();
+        for (int m = wtc_whole_first_deep(ad.p); m <= ad.p.levels; ++m) {
+            wtc_whole_analysis<T, K>(ad, cd, m);
+            wtc_lds_barrier();
+        }
+        __builtin_amdgcn_s_setprio(0);
+        wtc_whole_conv<T, K, BW>(ad, cd);
+        wtc_lds_barrier();
+        __builtin_amdgcn_s_setprio(2);
+        wtc_whole_out<T, K, BW, false, false, 2>(ad, cd);
+        wtc_lds_barrier();
+        // base and level 1 on the tiles of the image, the deeper levels' term
+        // from LDS; the same software pipeline as the tiled whole-plane kernel
+        wtc_whole_stage<T, K, BW, true, false>(at, ct);
+        wtc_lds_barrier();
+        if (tiles > 1) wtc_whole_load<T, K, BW, true, false>(at, ct, u0 + 1);
+        for (int t = 0; t < tiles; ++t) {
+            __builtin_amdgcn_s_setprio(0);
+            wtc_whole_conv<T, K, BW>(at, ct);
+            wtc_lds_barrier();
+            __builtin_amdgcn_s_setprio(2);
+            if (t + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct);
+            if (t + 2 < tiles) wtc_whole_load<T, K, BW, true, false>(at, ct, u0 + t + 2);
+            wtc_whole_select<T, false>(at, ct, u0 + t);
+            wtc_whole_out<T, K, BW, true, false, 1>(at, ct);
+            wtc_lds_barrier();
+        }
+    }
+}
+
+template <typename T, int K>
+static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
+{
+    if (a.p.d.out_bw != 4 || a.p.t.out_bw != 4) return hipErrorInvalidValue;
+    const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
+    const void *fn = (const void *)&wtconv_large_kernel<T, K, 4>;
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    if (resident) {
+        *resident = wtc_resident_blocks(fn, a.p.nthreads, lds);
+        return hipSuccess;
+    }
+    const unsigned groups = (unsigned)((a.p.n + a.p.planes - 1) / a.p.planes);
+    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4>), dim3(groups * (unsigned)a.p.c), dim3(a.p.nthreads), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_t(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident = nullptr)
+{
+    if (a.p.nthreads != 256) return hipErrorInvalidValue;
+    switch (a.p.k) {
+    case 1: return launch_k<T, 1>(a, stream, resident);
+    case 3: return launch_k<T, 3>(a, stream, resident);
+    case 5: return launch_k<T, 5>(a, stream, resident);
+    case 7: return launch_k<T, 7>(a, stream, resident);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t wtc_launch_large(int dtype, const WtcLargePlan &p, const void *in, void *out, const float *w_base,
+                            const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+                            hipStream_t stream)
+{
+    if (dtype == 0) {
+        WtcLargeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        return launch_t<float>(a, stream);
+    }
+    WtcLargeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return launch_t<_Float16>(a, stream);
+}
+
+int wtc_large_resident(int dtype, const WtcLargePlan &p)
+{
+    int r = 0;
+    hipError_t e;
+    if (dtype == 0) {
+        WtcLargeArgs<float> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
+        e = launch_t<float>(a, nullptr, &r);
+    } else {
+        WtcLargeArgs<_Float16> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
+        e = launch_t<_Float16>(a, nullptr, &r);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return r;
+}

@@ -78,6 +78,11 @@ struct WtcWholePlan {
     // is then a stack of images.  1: one image per plane.  Stacked plans run
     // a kernel instance of their own (ST), so the others carry no checks.
     int32_t stack, sh, sgap;
+    // The deeper levels' term in LDS (the fused large-plane kernel): an fp32
+    // map of (ih/2) x (iw/2) at deep_off with row pitch deep_pitch, written by
+    // the output pass of the deeper-levels plan and read by the tiled plan's
+    // output pass in place of the global `low`.
+    int32_t deep_off, deep_pitch;
 };
 
 #define WTC_WP 4  // piece side (outputs)
@@ -182,6 +187,7 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     p->levels = levels;
     p->rotate = rotate;
     p->nthreads = nthreads;
+    p->deep_off = p->deep_pitch = 0;
     p->tiled = ih != h || iw != w;
     p->ih = ih;
     p->iw = iw;
@@ -568,7 +574,30 @@ WTC_HD WTC_INLINE void wtc_whole_stage_l3(const WtcWholeArgs<T> &a, WtcWholeCtx<
 //   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
 //   U_2 and B_2^1..3 at its 1 x (vec/4) level-2 positions.
 template <typename T, int K, int BW, bool TL, bool ST = false>
+WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
+                                            const float (&x)[4][WtcVec<T, BW>::v]);
+
+template <typename T, int K, int BW, bool TL, bool ST = false>
 WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
+{
+    constexpr int vec = WtcVec<T, BW>::v;
+    const WtcWholePlan &p = a.p;
+    if (!ctx.gvalid) return;
+    float x[4][vec];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < vec; ++t)
+            x[q][t] = (q < p.gr && ((!TL && !ST) || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+    wtc_whole_stage_vals<T, K, BW, TL, ST>(a, ctx, x);
+}
+
+// The staging of a group from its values (gr rows of vec fp32 values): the
+// input map, Haar level 1 and (4-row groups) level 2, and with L >= 3 the
+// lane-quad exchange for level 3.
+template <typename T, int K, int BW, bool TL, bool ST>
+WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
+                                            const float (&x)[4][WtcVec<T, BW>::v])
 {
     constexpr int R = K / 2;
     constexpr int vec = WtcVec<T, BW>::v, h1 = vec / 2, h2 = vec / 4 > 0 ? vec / 4 : 1;
@@ -576,12 +605,6 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     if (!ctx.gvalid) return;
     const WtcMap xm = p.x, u1 = p.u[1];
     const int st1 = u1.rows * u1.pitch;
-    float x[4][vec];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int t = 0; t < vec; ++t)
-            x[q][t] = (q < p.gr && ((!TL && !ST) || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
     // r0, c0: the group's position in the loaded region (the tile plus lh);
     // map origins are the plan's in tiled plans, (r, r) otherwise
     const int lh = TL ? p.lh : 0, xr = TL ? p.xr : R, xc = TL ? p.xc : R;
@@ -861,7 +884,11 @@ WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 // the 2x2 butterfly, the deeper levels through the closed form with the
 // coordinate bits picking the signs, added to the low-pass input of the
 // butterfly; one rounding, one store.
-template <typename T, int K, int BW, bool TL, bool ST = false>
+// DEEP = 1: a tiled plan adds the deeper levels' term from the LDS map at
+// p.deep_off instead of the global `low`; DEEP = 2: an untiled plan writes its
+// result to that LDS map (the deeper levels of a larger plane) instead of
+// storing it.
+template <typename T, int K, int BW, bool TL, bool ST = false, int DEEP = 0>
 WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int Q = BW / 2;
@@ -928,7 +955,15 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
                 band[0][q] += wtc_fma(sq, t1, t0);
             }
         }
-        if (TL && a.low) {
+        if constexpr (DEEP == 1) {
+            // the deeper levels' term (orthonormal, at level-1 resolution of
+            // the image), half of it in these unnormalised sums
+            float v[Q];
+            wtc_lds_vec<T, Q>(ctx, p.deep_off + wtc_mul24(ctx.ty0 / 2 + i1, p.deep_pitch) + ctx.tx0 / 2 + Q * bx, v);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) band[0][q] = wtc_fma(0.5f, v[q], band[0][q]);
+        }
+        if (TL && DEEP == 0 && a.low) {
             // the deeper levels' low-pass term (orthonormal) enters level 1's
             // synthesis as half its value in these unnormalised sums
             const int64_t lo = ctx.plane * ((int64_t)(p.ih / 2) * (p.iw / 2)) +
@@ -951,6 +986,12 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
             acc[0][2 * q + 1] += s01 - s23;
             acc[1][2 * q] += d01 + d23;
             acc[1][2 * q + 1] += d01 - d23;
+        }
+        if constexpr (DEEP == 2) {
+            const int od = p.deep_off + wtc_mul24(2 * by, p.deep_pitch) + BW * bx;
+            wtc_lds_put<BW, wtc_align_of(BW, 0)>(ctx, od, acc[0]);
+            wtc_lds_put<BW, wtc_align_of(BW, 0)>(ctx, od + p.deep_pitch, acc[1]);
+            continue;
         }
         int64_t o0 = TL ? (int64_t)(ctx.ty0 + 2 * by) * p.iw + ctx.tx0 + BW * bx
                         : (int64_t)wtc_mul24(2 * by, p.w) + BW * bx;

@@ -10,7 +10,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(os.path.dirname(_HERE))
 _SRC = os.path.join(_HERE, "wtconv_emu.cpp")
 _DEPS = [_SRC] + [os.path.join(_ROOT, "level_haar_wavelet_amd", "csrc", f)
-                  for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h", "wtconv_wgrad_body.h", "wtconv_wgrad_tile_body.h")]
+                  for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h", "wtconv_wgrad_body.h",
+                            "wtconv_wgrad_tile_body.h", "wtconv_large_body.h")]
 _LIB = os.path.join(_ROOT, "_build", "libwtconv_emu.so")
 _lib = None
 
@@ -60,6 +61,8 @@ def _load():
         lib.emu_wgrad_plan.restype = ci
         lib.emu_wgrad_tiled.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
         lib.emu_wgrad_tiled.restype = ci
+        lib.emu_large.argtypes = [ci, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ctypes.POINTER(ci)]
+        lib.emu_large.restype = ci
         _lib = lib
     return _lib
 
@@ -213,3 +216,31 @@ def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nth
     outs[3] = outs[3][:levels]
     outs[4] = outs[4][:levels]
     return [o.astype(np.float64) for o in outs]
+
+
+def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dtype="f32", planes=1,
+          budget_floats=40960):
+    """Run the fused large-plane kernel (deeper levels staged from x and kept
+    on chip, base and level 1 on th x tw tiles) on the CPU emulation.  Returns
+    (output, info) with info = images per workgroup, LDS floats, deeper-levels
+    map floats, tiles per image."""
+    lib = _load()
+    n, c, h, w = x.shape
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    out = np.full_like(xin, np.nan)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    info = (ctypes.c_int * 4)()
+    rc = lib.emu_large(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, th, tw, k, levels,
+                       rotate, *[ptr(a) for a in keep], planes, budget_floats, info)
+    if rc != 0:
+        raise ValueError("emu_large failed: %d" % rc)
+    return out.astype(np.float64), list(info)
+
+
+def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floats=40960):
+    info = (ctypes.c_int * 4)()
+    rc = _load().emu_large(0 if dtype == "f32" else 1, None, None, n, c, h, w, th, tw, k, levels, 0, None, None, None,
+                           None, None, planes, budget_floats, info)
+    return None if rc != 0 else list(info)

@@ -11,9 +11,11 @@
 #include <cstdint>
 #include <cstring>
 #include <algorithm>
+#include <array>
 #include <vector>
 
 #include "../../level_haar_wavelet_amd/csrc/wtconv_fused_body.h"
+#include "../../level_haar_wavelet_amd/csrc/wtconv_large_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_whole_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_wgrad_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_wgrad_tile_body.h"
@@ -174,6 +176,99 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
     case 3: run_whole_k<T, 3>(a); return 0;
     case 5: run_whole_k<T, 5>(a); return 0;
     case 7: run_whole_k<T, 7>(a); return 0;
+    default: return -1;
+    }
+}
+
+// The fused large-plane kernel, phase by phase.  After the deeper levels'
+// output pass and after every image's tiles, the aliased map region is
+// poisoned with NaN: the tiles must write every element they read (their
+// staging covers the halos), and the deeper levels must zero their own maps.
+template <typename T, int K, int BW>
+static void run_large(const WtcLargeArgs<T> &A)
+{
+    const WtcLargePlan &lp = A.p;
+    const WtcWholeArgs<T> ad = A.dview(), at = A.tview();
+    const int groups = (lp.n + lp.planes - 1) / lp.planes;
+    const int nblocks = groups * lp.c;
+    std::vector<float> lds((size_t)lp.lds_floats);
+    const int nth = lp.nthreads;
+    const int tiles = at.p.tiles_x * at.p.tiles_y;
+    auto poison_maps = [&]() {
+        for (int i = lp.maps_off; i < lp.maps_off + lp.maps_floats; ++i) lds[(size_t)i] = __builtin_nanf("");
+    };
+    for (int bid = 0; bid < nblocks; ++bid) {
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcWholeCtx<T>> cd((size_t)nth), ct((size_t)nth);
+        for (int t = 0; t < nth; ++t) {
+            for (auto *c : {&cd[t], &ct[t]}) {
+                c->lds = lds.data();
+                c->tid = t;
+                c->nth = nth;
+                c->lds_n = lp.lds_floats;
+                c->img_n = (int64_t)lp.h * lp.w;
+            }
+            wtc_whole_setup<T>(ad, cd[t], bid);
+            wtc_whole_setup<T>(at, ct[t], bid);
+        }
+        for (int i = 0; i < lp.lds_floats; ++i) lds[(size_t)i] = 0.0f;
+        for (int t = 0; t < nth; ++t) {
+            wtc_whole_fold<T, K>(ad, cd[t]);
+            wtc_whole_fold<T, K>(at, ct[t]);
+            wtc_whole_table<T, K, BW>(ad, cd[t]);
+            wtc_whole_table<T, K, BW>(at, ct[t]);
+        }
+        for (int img = 0; img < cd[0].nimg; ++img) {
+            std::vector<std::array<std::array<float, 4>, 4>> ll((size_t)nth);
+            for (int t = 0; t < nth; ++t) {
+                float v[4][4];
+                wtc_large_load_d<T>(A, cd[t], img, v);
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 4; ++j) ll[(size_t)t][(size_t)i][(size_t)j] = v[i][j];
+            }
+            if (img > 0)
+                for (int t = 0; t < nth; ++t) wtc_large_zero_d<T>(lp, cd[t]);
+            for (int t = 0; t < nth; ++t) {
+                float v[4][4];
+                for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < 4; ++j) v[i][j] = ll[(size_t)t][(size_t)i][(size_t)j];
+                wtc_whole_stage_vals<T, K, BW, false, false>(ad, cd[t], v);
+            }
+            if (ad.p.stage_l3) emu_stage_l3(ad, cd);
+            const int u0 = img * tiles;
+            for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0);
+            for (int m = wtc_whole_first_deep(ad.p); m <= ad.p.levels; ++m)
+                for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(ad, cd[t], m);
+            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(ad, cd[t]);
+            for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW, false, false, 2>(ad, cd[t]);
+            poison_maps();
+            for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
+            for (int t = 0; t < nth; ++t)
+                if (tiles > 1) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + 1);
+            for (int tt = 0; tt < tiles; ++tt) {
+                for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(at, ct[t]);
+                for (int t = 0; t < nth; ++t) {
+                    if (tt + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
+                    if (tt + 2 < tiles) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + tt + 2);
+                }
+                for (int t = 0; t < nth; ++t) {
+                    wtc_whole_select<T, false>(at, ct[t], u0 + tt);
+                    wtc_whole_out<T, K, BW, true, false, 1>(at, ct[t]);
+                }
+            }
+            poison_maps();
+        }
+    }
+}
+
+template <typename T>
+static int run_large_t(const WtcLargeArgs<T> &a)
+{
+    switch (a.p.k) {
+    case 1: run_large<T, 1, 4>(a); return 0;
+    case 3: run_large<T, 3, 4>(a); return 0;
+    case 5: run_large<T, 5, 4>(a); return 0;
+    case 7: run_large<T, 7, 4>(a); return 0;
     default: return -1;
     }
 }
@@ -508,6 +603,32 @@ int emu_fused(int dtype, const void *in, void *out, int n, int c, int h, int w, 
     }
     WtcFusedArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
     return run_t<_Float16>(a);
+}
+
+// The fused large-plane pass (every level on chip) on host arrays: th x tw
+// tiles; out[0..3] of `info` = images per workgroup, LDS floats, deeper-levels
+// plan's LDS-map floats, tiles per image (info may be null).
+int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, int th, int tw, int k, int levels,
+              int rotate, const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
+              const float *s_lvl, int planes, int budget_floats, int *info)
+{
+    WtcLargePlan p;
+    if (wtc_make_large_plan(&p, n, c, h, w, th, tw, k, levels, rotate, 256, planes, dtype == 0 ? 4 : 2,
+                            budget_floats))
+        return -1;
+    if (info) {
+        info[0] = p.planes;
+        info[1] = p.lds_floats;
+        info[2] = p.dmaps_floats;
+        info[3] = p.t.tiles_x * p.t.tiles_y;
+    }
+    if (!in) return 0;
+    if (dtype == 0) {
+        WtcLargeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+        return run_large_t<float>(a);
+    }
+    WtcLargeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
+    return run_large_t<_Float16>(a);
 }
 
 }  // extern "C"

@@ -62,7 +62,7 @@ def assert_close(got, ref, act_dtype, what=""):
         assert rel <= TOL_F16_L2, "%s: rel L2 %.3e" % (what, rel)
 
 
-def assert_grad_close(got, ref, act_dtype, what=""):
+def assert_grad_close(got, ref, act_dtype, what="", per_channel=True):
     got = _np64(got)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -70,6 +70,8 @@ def assert_grad_close(got, ref, act_dtype, what=""):
     tol = TOL_F32_GRAD_L2 if act_dtype == "f32" else TOL_F16_L2
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     assert rel <= tol, "%s: rel L2 %.3e > %.1e" % (what, rel, tol)
+    if not per_channel:
+        return
     # per channel: one row per channel (and band) -- the k*k taps of dw_base
     # (C, k, k) and dw_lvl (L, 4C, k, k), one entry of dbias, ds_base (C) and
     # ds_lvl (L, 4C)
@@ -91,8 +93,8 @@ def backward_weight(d, **kw):
 GRAD_NAMES = ("dw_base", "dbias", "ds_base", "dw_lvl", "ds_lvl")
 
 
-def assert_grads_close(got, ref, act_dtype, what=""):
+def assert_grads_close(got, ref, act_dtype, what="", per_channel=True):
     for name, g, r in zip(GRAD_NAMES, got, ref):
         if r is None or np.asarray(r).size == 0:
             continue
-        assert_grad_close(g, np.asarray(r), act_dtype, "%s %s" % (what, name))
+        assert_grad_close(g, np.asarray(r), act_dtype, "%s %s" % (what, name), per_channel)

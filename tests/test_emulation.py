@@ -468,3 +468,52 @@ def test_deeper_level_gradients_are_the_layer_on_the_low_pass_maps(orc, L):
                               inp.s_lvl[1:], k, L - 1)
     assert np.abs(full[3][1:] - sub[3]).max() <= 1e-12 * (1 + np.abs(full[3]).max())
     assert np.abs(full[4][1:] - sub[4]).max() <= 1e-12 * (1 + np.abs(full[4]).max())
+
+
+LARGE = [
+    # n, c, h, w, k, L, dtype, tile rows, tile cols, images per workgroup
+    (2, 2, 32, 32, 5, 2, "f32", 16, 16, 1),
+    (3, 1, 64, 64, 5, 3, "f32", 32, 64, 2),   # odd batch: a last workgroup with one image
+    (2, 1, 64, 64, 3, 4, "f16", 32, 32, 2),
+    (1, 2, 64, 128, 7, 5, "f32", 32, 64, 1),
+    (2, 1, 32, 64, 1, 2, "f16", 16, 32, 2),
+    (1, 1, 128, 128, 5, 3, "f32", 32, 64, 1),  # the level sweep's plane
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_large_plane_kernel_keeps_every_level_on_chip(orc, case, rotate):
+    """The fused large-plane kernel: the deeper levels staged straight from x
+    (8 x 8 blocks reduced to the level-1 low-pass map in registers), their
+    output kept in an LDS map that the tiles' output pass reads, both plans'
+    maps aliasing one LDS region.  The emulation poisons that region with NaN
+    after the deeper levels and after every image, so the result also shows
+    that the tiles' staging writes every element they read and that the
+    deeper levels zero their own maps."""
+    n, c, h, w, k, L, dt, th, tw, planes = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + k + L)
+    src = inp.x if rotate == 0 else inp.dy
+    bias = inp.bias if rotate == 0 else None
+    y, info = emu.large(src, inp.w_base, bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, th, tw, rotate=rotate,
+                        dtype=dt, planes=planes, budget_floats=160 * 256)
+    assert info[0] == planes and info[3] == (h // th) * (w // tw)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    _check(y, ref, tol=1e-4 if dt == "f32" else 4 * 2.0 ** -11)
+
+
+def test_large_plane_plan_sizes():
+    """At the level sweep's 128 x 128 planes the fused plan (32 x 64 tiles, 256
+    threads) fits two workgroups per compute unit for every L = 2..5 (at most
+    80 KB of LDS each); it does not apply at L = 1 (no deeper levels) nor to a
+    256 x 256 plane (its 128 x 128 level-1 map needs more staging groups than
+    threads)."""
+    for L in range(2, 6):
+        for dt in ("f32", "f16"):
+            info = emu.large_plan(32, 128, 128, 128, 32, 64, 5, L, dtype=dt, budget_floats=160 * 256)
+            assert info is not None and info[1] * 4 <= 80 * 1024, (L, dt, info)
+    assert emu.large_plan(32, 128, 128, 128, 32, 64, 5, 1) is None
+    assert emu.large_plan(16, 256, 256, 256, 32, 64, 5, 4, budget_floats=160 * 256) is None

@@ -139,18 +139,23 @@ def test_stacked_small_planes_equal_one_image_per_pass(orc, case, monkeypatch):
 
 
 TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
-         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32"),
+         (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32"), (3, 2, 128, 128, 1, 3, "f16"),
          (2, 3, 64, 64, 7, 0, "f32"), (1, 4, 32, 64, 5, 0, "f16")]  # L = 0: a depthwise conv on tiles
 
 
 @pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
-def test_tiled_planes(orc, case, monkeypatch):
-    """The path for planes too large for one workgroup, forced on small planes:
-    base and level-1 convolutions on tiles with halos, the deeper levels from
-    the level-1 low-pass map through a nested call (itself tiled)."""
+@pytest.mark.parametrize("nested", [False, True], ids=["fused", "nested"])
+def test_tiled_planes(orc, case, nested, monkeypatch):
+    """The paths for planes too large for one workgroup, forced on small
+    planes: base and level-1 convolutions on tiles with halos, and the deeper
+    levels either in the same kernel, staged from x and kept on chip (fused),
+    or from a stored level-1 low-pass map through a nested call (nested, the
+    path of planes whose level-1 map is itself too large)."""
     n, c, h, w, k, L, dt = case
-    _log("case %s" % (case,))
+    _log("case %s %s" % (case, "nested" if nested else "fused"))
     monkeypatch.setenv("WTCONV_NO_WHOLE", "1")
+    if nested:
+        monkeypatch.setenv("WTCONV_NO_LARGE", "1")
     inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h * w + L)
     d = DevInputs(inp, dt)
     y = forward(d)

@@ -29,4 +29,8 @@ def test_unfused_matches_oracle(orc, case):
     assert_close(y, orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "y")
     assert_close(dx, orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L), dt, "dx")
     ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
-    assert_grads_close(g, ref, dt, "unfused")
+    # the baseline stores every intermediate in the activation type (fp16
+    # here), so its gradients carry those roundings: the per-tensor bound
+    # applies, the per-channel one (sized for the fused path's fp32
+    # intermediates) does not
+    assert_grads_close(g, ref, dt, "unfused", per_channel=dt == "f32")
