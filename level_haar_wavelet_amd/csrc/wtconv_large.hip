@@ -14,7 +14,7 @@ template <typename T, int K, int BW>
 __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
 {
     extern __shared__ float wtc_lds[];
-    const WtcWholeArgs<T> ad = A.dview(), at = A.tview();
+    const WtcWholeArgs<T> &ad = A.d, &at = A.t;
     WtcWholeCtx<T> cd, ct;
     cd.lds = ct.lds = wtc_lds;
     cd.tid = ct.tid = threadIdx.x;
@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
     wtc_whole_setup<T>(ad, cd, blockIdx.x);
     wtc_whole_setup<T>(at, ct, blockIdx.x);
     const int tiles = at.p.tiles_x * at.p.tiles_y;
-    for (int i = ct.tid; i < A.p.lds_floats; i += ct.nth) wtc_lds[i] = 0.0f;
+    for (int i = ct.tid; i < A.lds_floats; i += ct.nth) wtc_lds[i] = 0.0f;
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(ad, cd);
     wtc_whole_fold<T, K>(at, ct);
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
         float ll[4][4];
         wtc_large_load_d<T>(A, cd, img, ll);
         if (img > 0) {
-            wtc_large_zero_d<T>(A.p, cd);
+            wtc_large_zero_d<T>(A, cd);
             wtc_lds_barrier();
         }
         wtc_whole_stage_vals<T, K, BW, false, false>(ad, cd, ll);
@@ -74,19 +74,19 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
 template <typename T, int K>
 static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
 {
-    if (a.p.d.out_bw != 4 || a.p.t.out_bw != 4) return hipErrorInvalidValue;
-    const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
+    if (a.d.p.out_bw != 4 || a.t.p.out_bw != 4) return hipErrorInvalidValue;
+    const size_t lds = (size_t)a.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_large_kernel<T, K, 4>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     if (resident) {
-        *resident = wtc_resident_blocks(fn, a.p.nthreads, lds);
+        *resident = wtc_resident_blocks(fn, a.t.p.nthreads, lds);
         return hipSuccess;
     }
-    const unsigned groups = (unsigned)((a.p.n + a.p.planes - 1) / a.p.planes);
-    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4>), dim3(groups * (unsigned)a.p.c), dim3(a.p.nthreads), lds,
+    const unsigned groups = (unsigned)((a.n + a.planes - 1) / a.planes);
+    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4>), dim3(groups * (unsigned)a.c), dim3(a.t.p.nthreads), lds,
                        stream, a);
     return hipGetLastError();
 }
@@ -94,8 +94,8 @@ static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *re
 template <typename T>
 static hipError_t launch_t(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident = nullptr)
 {
-    if (a.p.nthreads != 256) return hipErrorInvalidValue;
-    switch (a.p.k) {
+    if (a.t.p.nthreads != 256 || a.d.p.nthreads != 256) return hipErrorInvalidValue;
+    switch (a.t.p.k) {
     case 1: return launch_k<T, 1>(a, stream, resident);
     case 3: return launch_k<T, 3>(a, stream, resident);
     case 5: return launch_k<T, 5>(a, stream, resident);
@@ -108,25 +108,25 @@ hipError_t wtc_launch_large(int dtype, const WtcLargePlan &p, const void *in, vo
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                             hipStream_t stream)
 {
-    if (dtype == 0) {
-        WtcLargeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
-        return launch_t<float>(a, stream);
-    }
-    WtcLargeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
-    return launch_t<_Float16>(a, stream);
+    if (dtype == 0)
+        return launch_t<float>(wtc_large_args<float>(p, (const float *)in, (float *)out, w_base, bias, s_base, w_lvl,
+                                                     s_lvl),
+                               stream);
+    return launch_t<_Float16>(wtc_large_args<_Float16>(p, (const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base,
+                                                       w_lvl, s_lvl),
+                              stream);
 }
 
 int wtc_large_resident(int dtype, const WtcLargePlan &p)
 {
     int r = 0;
     hipError_t e;
-    if (dtype == 0) {
-        WtcLargeArgs<float> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
-        e = launch_t<float>(a, nullptr, &r);
-    } else {
-        WtcLargeArgs<_Float16> a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, p};
-        e = launch_t<_Float16>(a, nullptr, &r);
-    }
+    if (dtype == 0)
+        e = launch_t<float>(wtc_large_args<float>(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr),
+                            nullptr, &r);
+    else
+        e = launch_t<_Float16>(
+            wtc_large_args<_Float16>(p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr), nullptr, &r);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return 0;

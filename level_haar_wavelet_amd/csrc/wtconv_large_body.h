@@ -115,37 +115,48 @@ static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, in
     return lp->lds_floats <= budget_floats ? 0 : -1;
 }
 
+// Kernel arguments: the two plans' views of the layer's arguments, built on
+// the host and passed whole, so that the kernel reads plan fields (indexed by
+// level at run time) from the argument segment rather than from a private
+// copy.  The deeper levels take the level weights and scales from level 2 on
+// (no base path, no output), the tiles the base and level 1.
 template <typename T>
 struct WtcLargeArgs {
-    const T *in;
-    T *out;
-    const float *w_base, *bias, *s_base, *w_lvl, *s_lvl;
-    WtcLargePlan p;
-
-    // The two plans' views of the arguments: the deeper levels take the level
-    // weights and scales from level 2 on (no base path, no output), the tiles
-    // the base and level 1.
-    WTC_HD WtcWholeArgs<T> dview() const
-    {
-        const int64_t kk = (int64_t)p.k * p.k;
-        WtcWholeArgs<T> a{in, nullptr, nullptr, nullptr, nullptr, w_lvl + 4 * p.c * kk, s_lvl + 4 * p.c, p.d};
-        return a;
-    }
-    WTC_HD WtcWholeArgs<T> tview() const
-    {
-        WtcWholeArgs<T> a{in, out, w_base, bias, s_base, w_lvl, s_lvl, p.t};
-        return a;
-    }
+    WtcWholeArgs<T> d, t;
+    int32_t n, c, h, w;
+    int32_t planes, maps_off, dmaps_floats, maps_floats, lds_floats;
 };
+
+template <typename T>
+static inline WtcLargeArgs<T> wtc_large_args(const WtcLargePlan &lp, const T *in, T *out, const float *w_base,
+                                            const float *bias, const float *s_base, const float *w_lvl,
+                                            const float *s_lvl)
+{
+    const int64_t kk = (int64_t)lp.k * lp.k;
+    WtcLargeArgs<T> a;
+    a.d = WtcWholeArgs<T>{in, nullptr, nullptr, nullptr, nullptr, w_lvl ? w_lvl + 4 * lp.c * kk : nullptr,
+                          s_lvl ? s_lvl + 4 * lp.c : nullptr, lp.d};
+    a.t = WtcWholeArgs<T>{in, out, w_base, bias, s_base, w_lvl, s_lvl, lp.t};
+    a.n = lp.n;
+    a.c = lp.c;
+    a.h = lp.h;
+    a.w = lp.w;
+    a.planes = lp.planes;
+    a.maps_off = lp.maps_off;
+    a.dmaps_floats = lp.dmaps_floats;
+    a.maps_floats = lp.maps_floats;
+    a.lds_floats = lp.lds_floats;
+    return a;
+}
 
 // Zero the deeper-levels plan's maps (their zero borders are the
 // convolutions' padding; the tiles wrote over them).
 template <typename T>
-WTC_HD WTC_INLINE void wtc_large_zero_d(const WtcLargePlan &lp, WtcWholeCtx<T> &ctx)
+WTC_HD WTC_INLINE void wtc_large_zero_d(const WtcLargeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
-    for (int i = 4 * ctx.tid; i < lp.dmaps_floats; i += 4 * ctx.nth) {
+    for (int i = 4 * ctx.tid; i < a.dmaps_floats; i += 4 * ctx.nth) {
         const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        wtc_lds_put<4, 4>(ctx, lp.maps_off + i, z);
+        wtc_lds_put<4, 4>(ctx, a.maps_off + i, z);
     }
 }
 
@@ -156,19 +167,18 @@ template <typename T>
 WTC_HD WTC_INLINE void wtc_large_load_d(const WtcLargeArgs<T> &a, const WtcWholeCtx<T> &ctx, int img,
                                         float (&ll)[4][4])
 {
-    const WtcLargePlan &lp = a.p;
-    const int64_t plane = (int64_t)(ctx.n0 + img) * lp.c + ctx.c;
-    const T *src = a.in + plane * ((int64_t)lp.h * lp.w);
+    const int64_t plane = (int64_t)(ctx.n0 + img) * a.c + ctx.c;
+    const T *src = a.d.in + plane * ((int64_t)a.h * a.w);
     const int row0 = 8 * ctx.grow, col0 = 8 * ctx.gcol;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float v[2][8];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int64_t e = (int64_t)(row0 + 2 * i + q) * lp.w + col0;
+            const int64_t e = (int64_t)(row0 + 2 * i + q) * a.w + col0;
 #ifdef WTC_EMULATE
-            const int64_t base = src - a.in, all = (int64_t)lp.n * lp.c * lp.h * lp.w;
-            for (int t = 0; t < 8; ++t) v[q][t] = wtc_to_float(wtc_chk(a.in, base + e + t, all, __LINE__));
+            const int64_t base = src - a.d.in, all = (int64_t)a.n * a.c * a.h * a.w;
+            for (int t = 0; t < 8; ++t) v[q][t] = wtc_to_float(wtc_chk(a.d.in, base + e + t, all, __LINE__));
 #else
             constexpr int PER = 16 / sizeof(T);  // elements per 16-byte load
 #pragma unroll

@@ -187,12 +187,12 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
 template <typename T, int K, int BW>
 static void run_large(const WtcLargeArgs<T> &A)
 {
-    const WtcLargePlan &lp = A.p;
-    const WtcWholeArgs<T> ad = A.dview(), at = A.tview();
+    const WtcLargeArgs<T> &lp = A;
+    const WtcWholeArgs<T> &ad = A.d, &at = A.t;
     const int groups = (lp.n + lp.planes - 1) / lp.planes;
     const int nblocks = groups * lp.c;
     std::vector<float> lds((size_t)lp.lds_floats);
-    const int nth = lp.nthreads;
+    const int nth = at.p.nthreads;
     const int tiles = at.p.tiles_x * at.p.tiles_y;
     auto poison_maps = [&]() {
         for (int i = lp.maps_off; i < lp.maps_off + lp.maps_floats; ++i) lds[(size_t)i] = __builtin_nanf("");
@@ -227,7 +227,7 @@ static void run_large(const WtcLargeArgs<T> &A)
                     for (int j = 0; j < 4; ++j) ll[(size_t)t][(size_t)i][(size_t)j] = v[i][j];
             }
             if (img > 0)
-                for (int t = 0; t < nth; ++t) wtc_large_zero_d<T>(lp, cd[t]);
+                for (int t = 0; t < nth; ++t) wtc_large_zero_d<T>(A, cd[t]);
             for (int t = 0; t < nth; ++t) {
                 float v[4][4];
                 for (int i = 0; i < 4; ++i)
@@ -264,7 +264,7 @@ static void run_large(const WtcLargeArgs<T> &A)
 template <typename T>
 static int run_large_t(const WtcLargeArgs<T> &a)
 {
-    switch (a.p.k) {
+    switch (a.t.p.k) {
     case 1: run_large<T, 1, 4>(a); return 0;
     case 3: run_large<T, 3, 4>(a); return 0;
     case 5: run_large<T, 5, 4>(a); return 0;
@@ -623,12 +623,11 @@ int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, 
         info[3] = p.t.tiles_x * p.t.tiles_y;
     }
     if (!in) return 0;
-    if (dtype == 0) {
-        WtcLargeArgs<float> a{(const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
-        return run_large_t<float>(a);
-    }
-    WtcLargeArgs<_Float16> a{(const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl, p};
-    return run_large_t<_Float16>(a);
+    if (dtype == 0)
+        return run_large_t<float>(
+            wtc_large_args<float>(p, (const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl));
+    return run_large_t<_Float16>(
+        wtc_large_args<_Float16>(p, (const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl));
 }
 
 }  // extern "C"
