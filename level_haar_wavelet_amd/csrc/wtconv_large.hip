@@ -22,6 +22,9 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
     wtc_whole_setup<T>(ad, cd, blockIdx.x);
     wtc_whole_setup<T>(at, ct, blockIdx.x);
     const int tiles = at.p.tiles_x * at.p.tiles_y;
+    // the first image's deeper-levels input is requested before the set-up
+    WtcLargeRaw<T> raw;
+    wtc_large_fetch_d<T>(A, cd, 0, raw);
     for (int i = ct.tid; i < A.lds_floats; i += ct.nth) wtc_lds[i] = 0.0f;
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(ad, cd);
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
     for (int img = 0; img < cd.nimg; ++img) {
         // deeper levels, staged from x through registers
         float ll[4][4];
-        wtc_large_load_d<T>(A, cd, img, ll);
+        wtc_large_reduce_d<T>(raw, ll);
         if (img > 0) {
             wtc_large_zero_d<T>(A, cd);
             wtc_lds_barrier();
@@ -58,6 +61,8 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
         wtc_lds_barrier();
         if (tiles > 1) wtc_whole_load<T, K, BW, true, false>(at, ct, u0 + 1);
         for (int t = 0; t < tiles; ++t) {
+            // the next image's deeper-levels input lands during the last tile
+            if (t == tiles - 1 && img + 1 < cd.nimg) wtc_large_fetch_d<T>(A, cd, img + 1, raw);
             __builtin_amdgcn_s_setprio(0);
             wtc_whole_conv<T, K, BW>(at, ct);
             wtc_lds_barrier();

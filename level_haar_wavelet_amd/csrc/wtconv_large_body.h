@@ -160,42 +160,50 @@ WTC_HD WTC_INLINE void wtc_large_zero_d(const WtcLargeArgs<T> &a, WtcWholeCtx<T>
     }
 }
 
-// The deeper levels' staging input of image `img` of the workgroup: this
-// thread's 8 x 8 block of x (the 4 x 4 group of the level-1 map it stages)
-// reduced to the orthonormal low-pass values (a + b + c + d) / 2.
+// The deeper levels' staging input of image `img` of the workgroup, in two
+// steps so that the loads can be issued a phase ahead: wtc_large_fetch_d loads
+// this thread's 8 x 8 block of x (the 4 x 4 group of the level-1 map it
+// stages) as it is stored, wtc_large_reduce_d turns it into the orthonormal
+// low-pass values (a + b + c + d) / 2.
 template <typename T>
-WTC_HD WTC_INLINE void wtc_large_load_d(const WtcLargeArgs<T> &a, const WtcWholeCtx<T> &ctx, int img,
-                                        float (&ll)[4][4])
+struct WtcLargeRaw {
+    T v[8][8];
+};
+
+template <typename T>
+WTC_HD WTC_INLINE void wtc_large_fetch_d(const WtcLargeArgs<T> &a, const WtcWholeCtx<T> &ctx, int img,
+                                         WtcLargeRaw<T> &raw)
 {
     const int64_t plane = (int64_t)(ctx.n0 + img) * a.c + ctx.c;
     const T *src = a.d.in + plane * ((int64_t)a.h * a.w);
     const int row0 = 8 * ctx.grow, col0 = 8 * ctx.gcol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float v[2][8];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int64_t e = (int64_t)(row0 + 2 * i + q) * a.w + col0;
+    for (int r = 0; r < 8; ++r) {
+        const int64_t e = (int64_t)(row0 + r) * a.w + col0;
 #ifdef WTC_EMULATE
-            const int64_t base = src - a.d.in, all = (int64_t)a.n * a.c * a.h * a.w;
-            for (int t = 0; t < 8; ++t) v[q][t] = wtc_to_float(wtc_chk(a.d.in, base + e + t, all, __LINE__));
+        const int64_t base = src - a.d.in, all = (int64_t)a.n * a.c * a.h * a.w;
+        for (int t = 0; t < 8; ++t) raw.v[r][t] = wtc_chk(a.d.in, base + e + t, all, __LINE__);
 #else
-            constexpr int PER = 16 / sizeof(T);  // elements per 16-byte load
+        constexpr int PER = 16 / sizeof(T);  // elements per 16-byte load
 #pragma unroll
-            for (int s = 0; s < 8 / PER; ++s) {
-                typedef float v4 __attribute__((ext_vector_type(4)));
-                const v4 d = *(const v4 *)(src + e + s * PER);
-                T tmp[PER];
-                __builtin_memcpy(tmp, &d, 16);
-#pragma unroll
-                for (int t = 0; t < PER; ++t) v[q][s * PER + t] = wtc_to_float(tmp[t]);
-            }
-#endif
+        for (int s = 0; s < 8 / PER; ++s) {
+            typedef float v4 __attribute__((ext_vector_type(4)));
+            const v4 d = *(const v4 *)(src + e + s * PER);
+            __builtin_memcpy(&raw.v[r][s * PER], &d, 16);
         }
+#endif
+    }
+}
+
+template <typename T>
+WTC_HD WTC_INLINE void wtc_large_reduce_d(const WtcLargeRaw<T> &raw, float (&ll)[4][4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            ll[i][j] = 0.5f * ((v[0][2 * j] + v[0][2 * j + 1]) + (v[1][2 * j] + v[1][2 * j + 1]));
-    }
+            ll[i][j] = 0.5f * ((wtc_to_float(raw.v[2 * i][2 * j]) + wtc_to_float(raw.v[2 * i][2 * j + 1])) +
+                               (wtc_to_float(raw.v[2 * i + 1][2 * j]) + wtc_to_float(raw.v[2 * i + 1][2 * j + 1])));
 }
 
 #endif  // WTCONV_LARGE_BODY_H

@@ -221,8 +221,10 @@ static void run_large(const WtcLargeArgs<T> &A)
         for (int img = 0; img < cd[0].nimg; ++img) {
             std::vector<std::array<std::array<float, 4>, 4>> ll((size_t)nth);
             for (int t = 0; t < nth; ++t) {
+                WtcLargeRaw<T> raw;
+                wtc_large_fetch_d<T>(A, cd[t], img, raw);
                 float v[4][4];
-                wtc_large_load_d<T>(A, cd[t], img, v);
+                wtc_large_reduce_d<T>(raw, v);
                 for (int i = 0; i < 4; ++i)
                     for (int j = 0; j < 4; ++j) ll[(size_t)t][(size_t)i][(size_t)j] = v[i][j];
             }
