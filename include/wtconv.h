@@ -47,9 +47,11 @@
  *              even).
  * Ownership    The caller allocates every buffer, including the workspace
  *              (size from wtconv_workspace_size, 256-byte aligned; its contents
- *              need no initialisation and are scratch after the call).  The library allocates no
- *              device memory and holds no state between calls; calls are
- *              reentrant.
+ *              need no initialisation and are scratch after the call).  The
+ *              library allocates no device memory and holds no state between
+ *              calls; calls are reentrant.  The one exception is
+ *              wtconv_backward_weight_noalloc, whose partial results live in a
+ *              static device array of the library (see there).
  * Execution    All work is enqueued on `stream` (0 = the null stream) with no
  *              host synchronisation; outputs are ready when the stream reaches
  *              that point.  Inputs and outputs must not overlap (y != x,
@@ -139,6 +141,26 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
                                        const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
                                        float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
                                        size_t workspace_bytes, wtconv_stream_t stream);
+
+/* ---- The weight backward without a workspace argument --------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * gradients as wtconv_backward_weight, with the partial results kept in a
+ * static device array of WTCONV_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends.  Nothing is allocated
+ * by the call.  Calls whose workspace (wtconv_workspace_size(desc,
+ * WTCONV_OP_BWD_WEIGHT)) exceeds the array return WTCONV_ERR_WORKSPACE before
+ * anything is enqueued (planes that fit one workgroup need a few MB; the
+ * large-plane paths with L >= 2 keep low-pass maps there and are refused).
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams, or from several threads) race and give wrong gradients;
+ * calls in stream order do not.  Other errors as for wtconv_backward_weight;
+ * WTCONV_ERR_HIP if the array's device address cannot be obtained. */
+#define WTCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+wtconv_status_t wtconv_backward_weight_noalloc(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                               const float *w_base, const float *bias, const float *s_base,
+                                               const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                               float *ds_base, float *dw_lvl, float *ds_lvl, wtconv_stream_t stream);
 
 /* ---- Unfused baseline (test and benchmark use only) ----------------------
  * The same layer composed of separate kernels with every intermediate in HBM:

@@ -13,8 +13,8 @@ import ctypes
 
 from . import _native
 
-__all__ = ["wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight", "wtconv_workspace_size",
-           "library_path"]
+__all__ = ["wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight", "wtconv_backward_weight_noalloc",
+           "wtconv_workspace_size", "library_path"]
 
 
 def library_path() -> str:
@@ -147,4 +147,30 @@ def wtconv_backward_weight(x, dy, w_base, bias, s_base, w_lvl, s_lvl, workspace=
                                     _ptr(dsl), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream))
     _native.check(st, "wtconv_backward_weight")
+    return dw0, db0, ds0, dwl, dsl
+
+
+def wtconv_backward_weight_noalloc(x, dy, w_base, bias, s_base, w_lvl, s_lvl, grads=None, stream=None):
+    """wtconv_backward_weight without a workspace argument: the library keeps
+    the partial results in its own static device array (no allocation by the
+    call; calls that overlap on one GPU race).  `grads` optionally supplies the
+    five output tensors (overwritten); they are allocated here if None."""
+    torch = _torch()
+    lib = _native.load()
+    for t, name in ((w_base, "w_base"), (bias, "bias"), (s_base, "s_base"), (w_lvl, "w_lvl"), (s_lvl, "s_lvl")):
+        _check_param(t, name)
+    levels = _levels_of(w_lvl)
+    d = _desc_for(x, w_base, levels)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise TypeError("dy must match x in shape, dtype and layout")
+    if grads is None:
+        c = x.shape[1]
+        grads = (torch.empty_like(w_base), torch.empty((c,), dtype=torch.float32, device=x.device),
+                 torch.empty_like(s_base),
+                 torch.empty_like(w_lvl) if levels else None, torch.empty_like(s_lvl) if levels else None)
+    dw0, db0, ds0, dwl, dsl = grads
+    st = lib.wtconv_backward_weight_noalloc(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(bias),
+                                            _ptr(s_base), _ptr(w_lvl), _ptr(s_lvl), _ptr(dw0), _ptr(db0), _ptr(ds0),
+                                            _ptr(dwl), _ptr(dsl), _stream(stream))
+    _native.check(st, "wtconv_backward_weight_noalloc")
     return dw0, db0, ds0, dwl, dsl

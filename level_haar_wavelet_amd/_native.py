@@ -40,6 +40,7 @@ SIGNATURES = {
     "wtconv_forward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_data": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_weight": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "wtconv_backward_weight_noalloc": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "wtconv_unfused_workspace_size": [_dp, ctypes.POINTER(ctypes.c_size_t)],
     "wtconv_unfused_forward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_unfused_backward_data": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],

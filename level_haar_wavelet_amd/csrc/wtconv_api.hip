@@ -555,6 +555,38 @@ int wtc_resident_blocks(const void *fn, int nthreads, size_t lds)
     return resident;
 }
 
+// ---- The weight backward without a caller's workspace ---------------------
+// Its partial rows live in this file-scope device array, one copy per GPU; in
+// host code `scratch` only names the symbol, so the kernels get the per-device
+// address that hipGetSymbolAddress returns (looked up once per device, with
+// that device current).
+static __device__ __align__(256) unsigned char scratch[WTCONV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+void *scratch_address(int dev)
+{
+    static std::mutex mu;
+    static void *ptr[kMaxDevices];
+    static bool done[kMaxDevices];
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptr[dev] = p;
+        done[dev] = true;
+    }
+    return ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op, size_t *bytes)
@@ -670,6 +702,32 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
         e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels, ch.groups, ch.plen, partial, w_base,
                                       bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
     return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+}
+
+wtconv_status_t wtconv_backward_weight_noalloc(const wtconv_desc_t *desc, const void *x, const void *dy,
+                                               const float *w_base, const float *bias, const float *s_base,
+                                               const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
+                                               float *ds_base, float *dw_lvl, float *ds_lvl, wtconv_stream_t stream)
+{
+    size_t need = 0;
+    wtconv_status_t st = check_desc(desc);
+    if (st != WTCONV_OK) return st;
+    if ((st = wgrad_workspace(desc, 0, &need)) != WTCONV_OK) return st;
+    if (need > (size_t)WTCONV_NOALLOC_SCRATCH_BYTES) return WTCONV_ERR_WORKSPACE;
+    // the whole call checked with a stand-in address before anything else
+    void *const probe = (void *)(uintptr_t)256;
+    st = wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, probe,
+                    WTCONV_NOALLOC_SCRATCH_BYTES, stream, 0, false);
+    if (st != WTCONV_OK) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return WTCONV_ERR_HIP;
+    }
+    void *ws = scratch_address(dev);
+    if (!ws) return WTCONV_ERR_HIP;
+    return wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, ws,
+                      WTCONV_NOALLOC_SCRATCH_BYTES, stream, 0, true);
 }
 
 wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x, const void *dy,
