@@ -549,6 +549,116 @@ def time_points(args, points):
     return ms_total / args.steps, res
 
 
+def time_backward(args, wl, reps=None, fused=True):
+    """Median microseconds of wtconv_backward (dx and every gradient in one
+    call; fused: the single pass over x and dy, WTCONV_FUSED_BWD=1) at one
+    workload, timed like the step's ops, after the same clock ramp."""
+    old = os.environ.get("WTCONV_FUSED_BWD")
+    os.environ["WTCONV_FUSED_BWD"] = "1" if fused else "0"
+    try:
+        return _time_backward(args, wl, reps)
+    finally:
+        if old is None:
+            os.environ.pop("WTCONV_FUSED_BWD", None)
+        else:
+            os.environ["WTCONV_FUSED_BWD"] = old
+
+
+def _time_backward(args, wl, reps):
+    import torch
+
+    import level_haar_wavelet_amd as wt
+    from level_haar_wavelet_amd import _native
+
+    p = make_points([wl])[0]
+    stream = torch.cuda.current_stream()
+    dt = 0 if wl.dtype == "f32" else 1
+    n = wt.wtconv_workspace_size((wl.n, wl.c, wl.h, wl.w), wl.k, wl.levels, dt, _native.OP_BWD)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda:0")
+    op = lambda: wt.wtconv_backward(p.x, p.dy, p.w0, p.b0, p.s0, p.wl_, p.sl_, dx=p.dx, grads=p.grads,
+                                    workspace=ws, stream=stream)
+    t_ramp = time.perf_counter()
+    while time.perf_counter() - t_ramp < args.ramp_s:
+        for _ in range(3):
+            op()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        op()
+    reps = reps or args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        op()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1000.0 for a, b in evs)
+    return ts[len(ts) // 2]
+
+
+def make_block(c, dtype):
+    """A synthetic WTConvNeXt-style block around the layer: LayerNorm over the
+    channels, then a pointwise MLP (C -> 4C, GELU, 4C -> C), added back to the
+    block's input (random init, seed 0)."""
+    import torch
+
+    torch.manual_seed(0)
+    mods = torch.nn.ModuleDict({"norm": torch.nn.LayerNorm(c), "fc1": torch.nn.Linear(c, 4 * c),
+                                "fc2": torch.nn.Linear(4 * c, c)}).cuda()
+    return mods.to(dtype)
+
+
+def block_step(mods, layer, x, params):
+    """One training step of the block (forward, loss, backward)."""
+    import torch
+
+    h = layer(x, *params)
+    t = h.permute(0, 2, 3, 1)
+    t = mods["fc2"](torch.nn.functional.gelu(mods["fc1"](mods["norm"](t))))
+    out = x + t.permute(0, 3, 1, 2)
+    out.float().square().mean().backward()
+
+
+def block_memory(wl) -> dict:
+    """Peak device memory of one training step of the synthetic block with the
+    fused layer (it saves only its input) and with the unfused baseline (it
+    keeps its intermediates for the backward): torch.cuda.max_memory_allocated
+    above what the block's input and parameters already hold."""
+    import torch
+
+    from level_haar_wavelet_amd.module import WTConvFunction
+    from level_haar_wavelet_amd.synthetic import make_inputs
+    from level_haar_wavelet_amd.unfused import UnfusedWTConvFunction
+
+    tdt = torch.float32 if wl.dtype == "f32" else torch.float16
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(inp.x).to(dev, dtype=tdt).requires_grad_(True)
+    params = [torch.from_numpy(a).to(dev).requires_grad_(True)
+              for a in (inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl)]
+    mods = make_block(wl.c, tdt)
+    out = {}
+    for name, layer in (("fused", WTConvFunction.apply), ("unfused", UnfusedWTConvFunction.apply)):
+        block_step(mods, layer, x, params)  # warm (library plans, cuBLAS-like handles)
+        for t in [x] + params + list(mods.parameters()):
+            t.grad = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        block_step(mods, layer, x, params)
+        torch.cuda.synchronize()
+        out[name] = torch.cuda.max_memory_allocated() - base
+        for t in [x] + params + list(mods.parameters()):
+            t.grad = None
+    return {"what": "one training step (forward, loss, backward) of a synthetic WTConvNeXt-style block: the layer, "
+                    "LayerNorm over the channels, a pointwise MLP C -> 4C -> C with GELU, residual add; peak "
+                    "device memory above the input and parameters",
+            "workload": workload_name(wl), "peak_MB_fused": round(out["fused"] / 2 ** 20, 1),
+            "peak_MB_unfused": round(out["unfused"] / 2 ** 20, 1),
+            "unfused_over_fused": round(out["unfused"] / max(out["fused"], 1), 3)}
+
+
 def point_record(wl, r) -> dict:
     f, b, w = r["us_ops"]
     gbs = 6.0 * wl.elems * wl.ebytes / (r["us_step"] * 1e-6) / 1e9
@@ -907,6 +1017,25 @@ def main():
                                                      max(r2[0]["us_ops_mean"]), digest)["frac"]
             extra[name] = rec
         line["other_workloads"] = extra
+    if not args.no_extra and sweep:
+        # dx and every gradient in one call: fused where a plane fits one
+        # workgroup (stage1, stage2), the two calls elsewhere (the sweep)
+        fb = {}
+        for name in ("stage1", "stage2"):
+            rec = extra[name]
+            us = time_backward(args, WORKLOADS[name])
+            torch.cuda.empty_cache()
+            two = rec["us_bwd_data"] + rec["us_bwd_weight"]
+            fb[name] = {"us_backward": round(us, 2), "us_bwd_data_plus_bwd_weight": round(two, 2),
+                        "speedup": round(two / us, 3),
+                        "GBs_modeled_5Ee": round(5.0 * WORKLOADS[name].elems * WORKLOADS[name].ebytes / (us * 1e-6)
+                                                 / 1e9, 1)}
+        line["fused_backward"] = {"what": "the single fused backward pass (wtconv_backward with WTCONV_FUSED_BWD=1: "
+                                          "x and dy read once, dx and all gradients written) against "
+                                          "wtconv_backward_data + wtconv_backward_weight (the default)", **fb}
+    if not args.no_unfused and sweep:
+        line["block_peak_memory"] = {name: block_memory(WORKLOADS[name]) for name in ("stage1", "stage2")}
+        torch.cuda.empty_cache()
     ref = wls[min(2, len(wls) - 1)] if sweep else wl0  # the L = 3 fp32 point of the sweep
     if not args.no_unfused:
         u = run_unfused(args, ref)

@@ -90,7 +90,12 @@ typedef enum {
 
 typedef enum { WTCONV_F32 = 0, WTCONV_F16 = 1 } wtconv_dtype_t;
 
-typedef enum { WTCONV_OP_FWD = 0, WTCONV_OP_BWD_DATA = 1, WTCONV_OP_BWD_WEIGHT = 2 } wtconv_op_t;
+typedef enum {
+    WTCONV_OP_FWD = 0,
+    WTCONV_OP_BWD_DATA = 1,
+    WTCONV_OP_BWD_WEIGHT = 2,
+    WTCONV_OP_BWD = 3  /* wtconv_backward: dx and all parameter gradients */
+} wtconv_op_t;
 
 typedef struct {
     int64_t n, c, h, w;   /* activation shape, NCHW */
@@ -141,6 +146,24 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
                                        const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
                                        float *ds_base, float *dw_lvl, float *ds_lvl, void *workspace,
                                        size_t workspace_bytes, wtconv_stream_t stream);
+
+/* dx and all parameter gradients in one call (technical summary, Key
+ * Contributions: forward outputs and all parameter gradients).  By default it
+ * runs wtconv_backward_data and then wtconv_backward_weight.  With
+ * WTCONV_FUSED_BWD=1 in the environment, planes that fit one workgroup run as
+ * one fused pass instead: x and dy are read once, dy's Haar pyramid is built
+ * once on chip and serves both the data backward's convolution (kernels turned
+ * by 180 degrees) and the correlation with x's pyramid, and dx is written once
+ * (5 E e bytes of activation traffic instead of 6 E e).  On MI355X the fused
+ * pass measured slower than the two calls (it holds both pyramids and the
+ * accumulators, so fewer waves stay in flight), hence the default.  The
+ * results are those of the two calls (to rounding).  Arguments as theirs; dx
+ * must not overlap x or dy; the workspace is wtconv_workspace_size(desc,
+ * WTCONV_OP_BWD) under the same environment. */
+wtconv_status_t wtconv_backward(const wtconv_desc_t *desc, const void *x, const void *dy, const float *w_base,
+                                const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+                                void *dx, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                                void *workspace, size_t workspace_bytes, wtconv_stream_t stream);
 
 /* ---- The weight backward without a workspace argument --------------------
  * For callers that cannot allocate device memory (code under HIP graph

@@ -13,8 +13,8 @@ import ctypes
 
 from . import _native
 
-__all__ = ["wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight", "wtconv_backward_weight_noalloc",
-           "wtconv_workspace_size", "library_path"]
+__all__ = ["wtconv_forward", "wtconv_backward_data", "wtconv_backward_weight", "wtconv_backward",
+           "wtconv_backward_weight_noalloc", "wtconv_workspace_size", "library_path"]
 
 
 def library_path() -> str:
@@ -148,6 +148,41 @@ def wtconv_backward_weight(x, dy, w_base, bias, s_base, w_lvl, s_lvl, workspace=
                                     _stream(stream))
     _native.check(st, "wtconv_backward_weight")
     return dw0, db0, ds0, dwl, dsl
+
+
+def wtconv_backward(x, dy, w_base, bias, s_base, w_lvl, s_lvl, dx=None, grads=None, workspace=None, stream=None):
+    """dx and the parameter gradients in one call: (dx, (dw_base, dbias,
+    ds_base, dw_lvl, ds_lvl)).  One fused pass over x and dy where a plane fits
+    one workgroup, else the data and weight backward one after the other.
+    `workspace` is a uint8 GPU tensor of at least wtconv_workspace_size(...,
+    OP_BWD) bytes (allocated here if None)."""
+    torch = _torch()
+    lib = _native.load()
+    for t, name in ((w_base, "w_base"), (bias, "bias"), (s_base, "s_base"), (w_lvl, "w_lvl"), (s_lvl, "s_lvl")):
+        _check_param(t, name)
+    levels = _levels_of(w_lvl)
+    d = _desc_for(x, w_base, levels)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise TypeError("dy must match x in shape, dtype and layout")
+    if dx is None:
+        dx = torch.empty_like(dy)
+    need = ctypes.c_size_t(0)
+    _native.check(lib.wtconv_workspace_size(ctypes.byref(d), _native.OP_BWD, ctypes.byref(need)),
+                  "wtconv_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=x.device)
+    if grads is None:
+        c = x.shape[1]
+        grads = (torch.empty_like(w_base), torch.empty((c,), dtype=torch.float32, device=x.device),
+                 torch.empty_like(s_base),
+                 torch.empty_like(w_lvl) if levels else None, torch.empty_like(s_lvl) if levels else None)
+    dw0, db0, ds0, dwl, dsl = grads
+    st = lib.wtconv_backward(ctypes.byref(d), _ptr(x), _ptr(dy), _ptr(w_base), _ptr(bias), _ptr(s_base),
+                             _ptr(w_lvl), _ptr(s_lvl), _ptr(dx), _ptr(dw0), _ptr(db0), _ptr(ds0), _ptr(dwl),
+                             _ptr(dsl), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _native.check(st, "wtconv_backward")
+    return dx, (dw0, db0, ds0, dwl, dsl)
 
 
 def wtconv_backward_weight_noalloc(x, dy, w_base, bias, s_base, w_lvl, s_lvl, grads=None, stream=None):

@@ -17,7 +17,7 @@ WTCONV_OK = 0
 STATUS = {0: "WTCONV_OK", 1: "WTCONV_ERR_NULL", 2: "WTCONV_ERR_SHAPE", 3: "WTCONV_ERR_UNSUPPORTED",
           4: "WTCONV_ERR_WORKSPACE", 5: "WTCONV_ERR_HIP", 6: "WTCONV_ERR_ALIAS"}
 F32, F16 = 0, 1
-OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT = 0, 1, 2
+OP_FWD, OP_BWD_DATA, OP_BWD_WEIGHT, OP_BWD = 0, 1, 2, 3
 
 
 class WtconvDesc(ctypes.Structure):
@@ -40,6 +40,7 @@ SIGNATURES = {
     "wtconv_forward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_data": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_weight": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "wtconv_backward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "wtconv_backward_weight_noalloc": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "wtconv_unfused_workspace_size": [_dp, ctypes.POINTER(ctypes.c_size_t)],
     "wtconv_unfused_forward": [_dp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],

@@ -519,6 +519,49 @@ wtconv_status_t wgrad_workspace(const wtconv_desc_t *d, int nobase, size_t *byte
     return WTCONV_OK;
 }
 
+// Fused single-pass backward plan (512 threads; WTCONV_BWD_THREADS=256
+// overrides), with its images per workgroup; false where it does not apply or
+// is not selected.  It is correct but measured slower than the two calls on
+// MI355X (stage1 151.5 against 126.3 us, stage2 125.6 against 83.1 us: with
+// both pyramids, the convolution outputs and the accumulators a compute unit
+// holds one 512-thread workgroup, where the two calls keep 16 and 8 waves in
+// flight), so the two calls are the default and WTCONV_FUSED_BWD=1 selects it.
+bool bwd_choice(const wtconv_desc_t *d, WtcBwdPlan *bp)
+{
+    if (!env_int("WTCONV_FUSED_BWD", 0, 0, 1) || d->levels < 1 || ragged(d) || env_int("WTCONV_NO_WHOLE", 0, 0, 1))
+        return false;
+    const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
+    const int nth = env_int("WTCONV_BWD_THREADS", 512, 256, 512) >= 512 ? 512 : 256;
+    if (wtc_make_bwd_plan(bp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, nth, 1, eb,
+                          whole_budget_floats()))
+        return false;
+    const int planes = pick_planes(d, wtc_bwd_resident(d->dtype, *bp), kWgradFixed, "WTCONV_BWD_PLANES");
+    return wtc_make_bwd_plan(bp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, d->k, d->levels, nth, planes, eb,
+                             whole_budget_floats()) == 0;
+}
+
+size_t bwd_partial_bytes(const wtconv_desc_t *d, const WtcBwdPlan &bp)
+{
+    return align256((size_t)bp.g.groups * d->c * bp.g.plen * 4);
+}
+
+// Workspace of wtconv_backward: the fused pass's partial rows, else the larger
+// of the two calls' workspaces (they run one after the other).
+wtconv_status_t bwd_workspace(const wtconv_desc_t *d, size_t *bytes)
+{
+    WtcBwdPlan bp;
+    if (bwd_choice(d, &bp)) {
+        *bytes = bwd_partial_bytes(d, bp);
+        return WTCONV_OK;
+    }
+    size_t wb = 0;
+    wtconv_status_t st = wgrad_workspace(d, 0, &wb);
+    if (st != WTCONV_OK) return st;
+    const size_t pb = pass_workspace(d, 1, 0);
+    *bytes = wb > pb ? wb : pb;
+    return WTCONV_OK;
+}
+
 }  // namespace
 
 int wtc_resident_blocks(const void *fn, int nthreads, size_t lds)
@@ -598,6 +641,7 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
     case WTCONV_OP_FWD: *bytes = pass_workspace(desc, 0, 0); return WTCONV_OK;
     case WTCONV_OP_BWD_DATA: *bytes = pass_workspace(desc, 1, 0); return WTCONV_OK;
     case WTCONV_OP_BWD_WEIGHT: return wgrad_workspace(desc, 0, bytes);
+    case WTCONV_OP_BWD: return bwd_workspace(desc, bytes);
     default: return WTCONV_ERR_UNSUPPORTED;
     }
 }
@@ -741,6 +785,44 @@ wtconv_status_t wtconv_backward_weight(const wtconv_desc_t *desc, const void *x,
     if (st != WTCONV_OK) return st;
     return wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl,
                       workspace, workspace_bytes, stream, 0, true);
+}
+
+wtconv_status_t wtconv_backward(const wtconv_desc_t *desc, const void *x, const void *dy, const float *w_base,
+                                const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+                                void *dx, float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
+                                void *workspace, size_t workspace_bytes, wtconv_stream_t stream)
+{
+    wtconv_status_t st = check_desc(desc);
+    if (st != WTCONV_OK) return st;
+    if (!x || !dy || !dx || !dw_base || !dbias || !ds_base) return WTCONV_ERR_NULL;
+    if ((st = check_params(desc, w_base, s_base, w_lvl, s_lvl)) != WTCONV_OK) return st;
+    if (desc->levels > 0 && (!dw_lvl || !ds_lvl)) return WTCONV_ERR_NULL;
+    if (!aligned16(x) || !aligned16(dy) || !aligned16(dx)) return WTCONV_ERR_UNSUPPORTED;
+    if (overlaps(dx, dy, act_bytes(desc)) || overlaps(dx, x, act_bytes(desc))) return WTCONV_ERR_ALIAS;
+    WtcBwdPlan bp;
+    if (!bwd_choice(desc, &bp)) {
+        // the two calls, each checked in full before anything is enqueued
+        st = fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, workspace, workspace_bytes, stream,
+                        nullptr, false);
+        if (st == WTCONV_OK)
+            st = wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl,
+                            workspace, workspace_bytes, stream, 0, false);
+        if (st != WTCONV_OK) return st;
+        st = fused_pass(desc, dy, w_base, nullptr, s_base, w_lvl, s_lvl, dx, 1, workspace, workspace_bytes, stream,
+                        nullptr, true);
+        if (st != WTCONV_OK) return st;
+        return wgrad_pass(desc, x, dy, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl,
+                          workspace, workspace_bytes, stream, 0, true);
+    }
+    if (!workspace || workspace_bytes < bwd_partial_bytes(desc, bp)) return WTCONV_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return WTCONV_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    float *partial = (float *)workspace;
+    hipError_t e = wtc_launch_bwd(desc->dtype, bp, x, dy, dx, w_base, s_base, w_lvl, s_lvl, partial, s);
+    if (e == hipSuccess)
+        e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels, bp.g.groups, bp.g.plen, partial, w_base,
+                                      bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
+    return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
 }
 
 wtconv_status_t wtconv_forward(const wtconv_desc_t *desc, const void *x, const float *w_base, const float *bias,

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "wtconv_bwd_body.h"
 #include "wtconv_large_body.h"
 #include "wtconv_plan.h"
 #include "wtconv_whole_body.h"
@@ -27,6 +28,12 @@ hipError_t wtc_launch_whole(int dtype, const WtcWholePlan &p, const void *in, vo
 hipError_t wtc_launch_large(int dtype, const WtcLargePlan &p, const void *in, void *out, const float *w_base,
                             const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                             hipStream_t stream);
+
+// Fused single-pass backward (dx and the weight-gradient partial rows), per
+// plan p; the weight backward's finalize pass reduces the partials.
+hipError_t wtc_launch_bwd(int dtype, const WtcBwdPlan &p, const void *x, const void *dy, void *dx,
+                          const float *w_base, const float *s_base, const float *w_lvl, const float *s_lvl,
+                          float *partial, hipStream_t stream);
 
 // Level-1 low-pass band (orthonormal, (a + b + c + d) / 2 of every 2x2 block)
 // of `planes` planes of h x w (multiples of 4) of the input dtype, into fp32
@@ -66,6 +73,7 @@ int wtc_resident_blocks(const void *fn, int nthreads, size_t lds);
 // Resident workgroups of the whole-plane and weight-gradient kernels for a plan.
 int wtc_whole_resident(int dtype, const WtcWholePlan &p);
 int wtc_large_resident(int dtype, const WtcLargePlan &p);
+int wtc_bwd_resident(int dtype, const WtcBwdPlan &p);
 int wtc_wgrad_resident(int dtype, const WtcWgradPlan &p);
 
 #endif  // WTCONV_LAUNCH_H

@@ -78,3 +78,37 @@ def wtconv_unfused_backward_weight(x, dy, w_base, bias, s_base, w_lvl, s_lvl, ws
                                             _ptr(dwl), _ptr(dsl), _ptr(ws), _nbytes(ws), _stream(stream))
     _native.check(st, "wtconv_unfused_backward_weight")
     return grads
+
+
+class UnfusedWTConvFunction:
+    """The unfused baseline as a PyTorch autograd function (benchmark use): the
+    forward keeps its intermediates (subbands, convolution outputs, partial
+    reconstructions) in a workspace saved for the backward, as autograd keeps
+    the tensors of a layer composed of separate operations."""
+
+    @staticmethod
+    def apply(x, w_base, bias, s_base, w_lvl, s_lvl):
+        import torch
+
+        class _Fn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x, w_base, bias, s_base, w_lvl, s_lvl):
+                x = x.contiguous()
+                k = int(w_base.shape[-1])
+                levels = 0 if w_lvl is None else int(w_lvl.shape[0])
+                ws = workspace(x, k, levels)
+                y = wtconv_unfused_forward(x, w_base, bias, s_base, w_lvl, s_lvl, ws)
+                ctx.save_for_backward(x, w_base, bias, s_base, w_lvl, s_lvl, ws)
+                ctx.has_bias = bias is not None
+                return y
+
+            @staticmethod
+            def backward(ctx, dy):
+                x, w_base, bias, s_base, w_lvl, s_lvl, ws = ctx.saved_tensors
+                dy = dy.contiguous().to(x.dtype)
+                dx = wtconv_unfused_backward_data(dy, w_base, s_base, w_lvl, s_lvl, ws)
+                dw0, db0, ds0, dwl, dsl = wtconv_unfused_backward_weight(x, dy, w_base, bias, s_base, w_lvl, s_lvl,
+                                                                         ws)
+                return dx, dw0, db0 if ctx.has_bias else None, ds0, dwl, dsl
+
+        return _Fn.apply(x, w_base, bias, s_base, w_lvl, s_lvl)

@@ -11,7 +11,7 @@ _ROOT = os.path.dirname(os.path.dirname(_HERE))
 _SRC = os.path.join(_HERE, "wtconv_emu.cpp")
 _DEPS = [_SRC] + [os.path.join(_ROOT, "level_haar_wavelet_amd", "csrc", f)
                   for f in ("wtconv_fused_body.h", "wtconv_plan.h", "wtconv_whole_body.h", "wtconv_wgrad_body.h",
-                            "wtconv_wgrad_tile_body.h", "wtconv_large_body.h")]
+                            "wtconv_wgrad_tile_body.h", "wtconv_large_body.h", "wtconv_bwd_body.h")]
 _LIB = os.path.join(_ROOT, "_build", "libwtconv_emu.so")
 _lib = None
 
@@ -63,6 +63,8 @@ def _load():
         lib.emu_wgrad_tiled.restype = ci
         lib.emu_large.argtypes = [ci, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ctypes.POINTER(ci)]
         lib.emu_large.restype = ci
+        lib.emu_bwd.argtypes = [ci, vp, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
+        lib.emu_bwd.restype = ci
         _lib = lib
     return _lib
 
@@ -244,3 +246,27 @@ def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floa
     rc = _load().emu_large(0 if dtype == "f32" else 1, None, None, n, c, h, w, th, tw, k, levels, 0, None, None, None,
                            None, None, planes, budget_floats, info)
     return None if rc != 0 else list(info)
+
+
+def bwd(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, dtype="f32", nthreads=512, planes=1,
+        budget_floats=40960):
+    """The fused single-pass backward on the CPU emulation: (dx, [dw_base,
+    dbias, ds_base, dw_lvl, ds_lvl])."""
+    lib = _load()
+    n, c, h, w = x.shape
+    levels = w_lvl.shape[0]
+    npdt = np.float32 if dtype == "f32" else np.float16
+    xin = np.ascontiguousarray(x, dtype=npdt)
+    dyin = np.ascontiguousarray(dy, dtype=npdt)
+    dx = np.full_like(xin, np.nan)
+    keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
+    outs = [np.full((c, k, k), np.nan, np.float32), np.full((c,), np.nan, np.float32),
+            np.full((c,), np.nan, np.float32), np.full((levels, 4 * c, k, k), np.nan, np.float32),
+            np.full((levels, 4 * c), np.nan, np.float32)]
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.emu_bwd(0 if dtype == "f32" else 1, xin.ctypes.data, dyin.ctypes.data, dx.ctypes.data, n, c, h, w, k,
+                     levels, *[ptr(a) for a in keep], *[o.ctypes.data for o in outs], nthreads, planes,
+                     budget_floats)
+    if rc != 0:
+        raise ValueError("emu_bwd failed: %d" % rc)
+    return dx.astype(np.float64), [o.astype(np.float64) for o in outs]

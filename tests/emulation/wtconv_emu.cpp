@@ -14,6 +14,7 @@
 #include <array>
 #include <vector>
 
+#include "../../level_haar_wavelet_amd/csrc/wtconv_bwd_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_fused_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_large_body.h"
 #include "../../level_haar_wavelet_amd/csrc/wtconv_whole_body.h"
@@ -273,6 +274,98 @@ static int run_large_t(const WtcLargeArgs<T> &a)
     case 7: run_large<T, 7, 4>(a); return 0;
     default: return -1;
     }
+}
+
+// The fused single-pass backward, phase by phase (the data plan's lane-quad
+// exchange for Haar level 3 after every thread has staged).
+template <typename T, int K, int Q>
+static void run_bwd(const WtcBwdArgs<T> &A, float *partial)
+{
+    const WtcWholeArgs<T> &ad = A.d;
+    WtcWgradArgs<T> ag = A.g;
+    ag.partial = partial;
+    const int nblocks = ag.p.groups * ag.p.c;
+    std::vector<float> lds((size_t)A.lds_floats);
+    const int nth = ad.p.nthreads;
+    for (int bid = 0; bid < nblocks; ++bid) {
+        for (auto &v : lds) v = __builtin_nanf("");
+        std::vector<WtcWholeCtx<T>> cw((size_t)nth);
+        std::vector<WtcWgradCtx<T, 4>> cg((size_t)nth);
+        std::vector<std::array<std::array<float, K * K + 1>, Q>> acc((size_t)nth);
+        for (int t = 0; t < nth; ++t) {
+            cw[t].lds = cg[t].lds = lds.data();
+            cw[t].tid = cg[t].tid = t;
+            cw[t].nth = cg[t].nth = nth;
+            cw[t].lds_n = cg[t].lds_n = A.lds_floats;
+            cw[t].img_n = (int64_t)ad.p.h * ad.p.w;
+            wtc_whole_setup<T>(ad, cw[t], bid);
+            wtc_wgrad_setup<T, 4>(ag, cg[t], bid);
+            cg[t].grow = cw[t].grow;
+            cg[t].gcol = cw[t].gcol;
+            cg[t].gvalid = cw[t].gvalid;
+            for (auto &a1 : acc[(size_t)t])
+                for (auto &v : a1) v = 0.0f;
+        }
+        for (int t = 0; t < nth; ++t) wtc_wgrad_load<T, 4, false>(ag, cg[t], 0);
+        for (int i = 0; i < A.lds_floats; ++i) lds[(size_t)i] = 0.0f;
+        for (int t = 0; t < nth; ++t) {
+            wtc_whole_fold<T, K>(ad, cw[t]);
+            wtc_whole_table<T, K, 4>(ad, cw[t]);
+            wtc_wgrad_table<T, K, 4>(ag, cg[t]);
+        }
+        auto stage = [&]() {
+            for (int t = 0; t < nth; ++t) {
+                wtc_wgrad_stage<T, K, 4, false>(ag, cg[t]);
+                wtc_bwd_stage_dy<T, K, 4>(ad, cw[t], cg[t]);
+            }
+            if (ad.p.stage_l3) emu_stage_l3(ad, cw);
+        };
+        stage();
+        for (int t = 0; t < nth; ++t)
+            if (cw[t].nimg > 1) wtc_wgrad_load<T, 4, false>(ag, cg[t], 1);
+        for (int img = 0; img < cw[0].nimg; ++img) {
+            for (int m = ag.p.first_deep; m <= ag.p.levels; ++m)
+                for (int t = 0; t < nth; ++t) wtc_wgrad_analysis<T, K, 4>(ag, cg[t], m);
+            for (int m = wtc_whole_first_deep(ad.p); m <= ad.p.levels; ++m)
+                for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(ad, cw[t], m);
+            for (int t = 0; t < nth; ++t) {
+                float a2[Q][K * K + 1];
+                for (int q = 0; q < Q; ++q)
+                    for (int e = 0; e < K * K + 1; ++e) a2[q][e] = acc[(size_t)t][(size_t)q][(size_t)e];
+                wtc_wgrad_correlate<T, K, 4, Q>(ag, cg[t], a2);
+                for (int q = 0; q < Q; ++q)
+                    for (int e = 0; e < K * K + 1; ++e) acc[(size_t)t][(size_t)q][(size_t)e] = a2[q][e];
+            }
+            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, 4>(ad, cw[t]);
+            if (img + 1 < cw[0].nimg) stage();
+            for (int t = 0; t < nth; ++t)
+                if (img + 2 < cw[t].nimg) wtc_wgrad_load<T, 4, false>(ag, cg[t], img + 2);
+            for (int t = 0; t < nth; ++t) {
+                wtc_whole_select<T, false>(ad, cw[t], img);
+                wtc_whole_out<T, K, 4, false, false>(ad, cw[t]);
+            }
+        }
+        for (int q = 0; q < Q; ++q) {
+            if (q >= ag.p.q) continue;
+            for (int t = 0; t < nth; ++t) {
+                float a1[K * K + 1];
+                for (int e = 0; e < K * K + 1; ++e) a1[e] = acc[(size_t)t][(size_t)q][(size_t)e];
+                wtc_wgrad_park<T, K, 4>(ag, cg[t], a1);
+            }
+            for (int t = 0; t < nth; ++t) wtc_wgrad_chunks<T, K, 4>(ag, cg[t], q);
+            for (int t = 0; t < nth; ++t) wtc_wgrad_combine<T, K, 4>(ag, cg[t], q);
+        }
+        for (int t = 0; t < nth; ++t) wtc_wgrad_write<T, K, 4>(ag, cg[t]);
+    }
+}
+
+template <typename T, int K>
+static void run_bwd_k(const WtcBwdArgs<T> &a, float *partial)
+{
+    if (a.g.p.q == 1)
+        run_bwd<T, K, 1>(a, partial);
+    else
+        run_bwd<T, K, WTC_WG_QMAX>(a, partial);
 }
 
 template <typename T, int K, int VEC, bool TL = false>
@@ -630,6 +723,39 @@ int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, 
             wtc_large_args<float>(p, (const float *)in, (float *)out, w_base, bias, s_base, w_lvl, s_lvl));
     return run_large_t<_Float16>(
         wtc_large_args<_Float16>(p, (const _Float16 *)in, (_Float16 *)out, w_base, bias, s_base, w_lvl, s_lvl));
+}
+
+// The fused single-pass backward on host arrays: dx and the five gradients
+// (through the weight backward's finalize).  Returns -1 where the plan does
+// not apply.
+int emu_bwd(int dtype, const void *x, const void *dy, void *dx, int n, int c, int h, int w, int k, int levels,
+            const float *w_base, const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
+            float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl, int nthreads, int planes,
+            int budget_floats)
+{
+    WtcBwdPlan p;
+    if (wtc_make_bwd_plan(&p, n, c, h, w, k, levels, nthreads, planes, dtype == 0 ? 4 : 2, budget_floats)) return -1;
+    std::vector<float> partial((size_t)p.g.groups * c * p.g.plen, __builtin_nanf(""));
+    auto run = [&](auto tag) {
+        using T = decltype(tag);
+        const WtcBwdArgs<T> a = wtc_bwd_args<T>(p, (const T *)x, (const T *)dy, (T *)dx, w_base, s_base, w_lvl,
+                                                s_lvl, partial.data());
+        switch (k) {
+        case 1: run_bwd_k<T, 1>(a, partial.data()); break;
+        case 3: run_bwd_k<T, 3>(a, partial.data()); break;
+        case 5: run_bwd_k<T, 5>(a, partial.data()); break;
+        default: run_bwd_k<T, 7>(a, partial.data()); break;
+        }
+    };
+    if (dtype == 0)
+        run(float{});
+    else
+        run(_Float16{});
+    for (int cc = 0; cc < c; ++cc)
+        for (int g = 0; g < 1 + 4 * levels; ++g)
+            wtc_wgrad_finalize_one(cc, g, c, k, levels, p.g.groups, p.g.plen, partial.data(), w_base, bias, s_base,
+                                   w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl);
+    return 0;
 }
 
 }  // extern "C"

@@ -517,3 +517,30 @@ def test_large_plane_plan_sizes():
             assert info is not None and info[1] * 4 <= 80 * 1024, (L, dt, info)
     assert emu.large_plan(32, 128, 128, 128, 32, 64, 5, 1) is None
     assert emu.large_plan(16, 256, 256, 256, 32, 64, 5, 4, budget_floats=160 * 256) is None
+
+
+BWD = [
+    # n, c, h, w, k, L, dtype, threads, images per workgroup
+    (2, 2, 16, 16, 5, 2, "f32", 256, 2),
+    (3, 2, 56, 56, 5, 3, "f32", 512, 2),   # odd batch: a last workgroup with one image
+    (3, 2, 28, 28, 5, 2, "f16", 512, 2),
+    (2, 1, 32, 32, 3, 5, "f32", 256, 1),
+    (2, 2, 24, 40, 7, 1, "f32", 512, 2),
+    (2, 2, 12, 20, 1, 2, "f16", 256, 2),
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=lambda c: "x".join(map(str, c)))
+def test_emulated_fused_backward(orc, case):
+    """The fused single-pass backward: one staging of x and dy serving the
+    data backward's convolution and the weight backward's correlation; dx and
+    every gradient against the oracle."""
+    n, c, h, w, k, L, dt, nth, planes = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + w + L)
+    dx, g = emu.bwd(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, dtype=dt,
+                    nthreads=nth, planes=planes, budget_floats=160 * 256)
+    ref = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    _check(dx, ref, tol=1e-4 if dt == "f32" else 4 * 2.0 ** -11)
+    rg = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    for a, b in zip(g, rg):
+        assert np.linalg.norm(a - b) <= 1e-5 * np.linalg.norm(b)

@@ -1,0 +1,101 @@
+"""GPU parity of the single-call backward (wtconv_backward: dx and every
+parameter gradient) against the oracle, through the C ABI: the fused pass
+(WTCONV_FUSED_BWD=1) on planes that fit one workgroup (x and dy read once),
+the two-call path elsewhere and by default, and the two paths against each
+other."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import level_haar_wavelet_amd as wt
+from level_haar_wavelet_amd.synthetic import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests.gpu_util import DevInputs, assert_close, assert_grads_close
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _backward(d):
+    return wt.wtconv_backward(d.x, d.dy, d.w_base, d.bias, d.s_base, d.w_lvl, d.s_lvl)
+
+
+def _check(orc, inp, d, k, L, dt, what, sel=slice(None)):
+    dx, g = _backward(d)
+    torch.cuda.synchronize()
+    ref_dx = orc.backward_data(inp.dy[sel], inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(dx[sel], ref_dx, dt, what + " dx")
+    ref_g = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_grads_close(g, ref_g, dt, what)
+    return dx, g
+
+
+CASES = [
+    # n, c, h, w, k, L, dtype
+    (2, 8, 16, 16, 5, 2, "f32"),
+    (3, 3, 16, 24, 3, 3, "f32"),
+    (5, 2, 56, 56, 5, 3, "f32"),
+    (3, 4, 28, 28, 5, 2, "f16"),
+    (2, 2, 32, 32, 5, 5, "f32"),
+    (3, 2, 24, 40, 7, 1, "f32"),
+    (2, 3, 12, 20, 1, 2, "f16"),
+    (1, 2, 96, 160, 5, 4, "f32"),   # too large for one workgroup: the two calls
+    (2, 3, 15, 13, 5, 2, "f32"),    # sides 2^L does not divide: the two calls
+]
+
+
+@pytest.fixture
+def fused(monkeypatch):
+    monkeypatch.setenv("WTCONV_FUSED_BWD", "1")
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_backward_matches_oracle(orc, case, fused):
+    n, c, h, w, k, L, dt = case
+    _log("case %s" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=n + c + h + w + k + L)
+    _check(orc, inp, DevInputs(inp, dt), k, L, dt, str(case))
+
+
+@pytest.mark.parametrize("case", [(5, 2, 56, 56, 5, 3, "f32"), (3, 4, 28, 28, 5, 2, "f16")],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_fused_and_two_call_paths_agree(orc, case, monkeypatch, fused):
+    """The fused pass and the two calls compute the same sums in different
+    orders: equal within the tolerance, and each equal to the oracle."""
+    n, c, h, w, k, L, dt = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=7 * h + L)
+    d = DevInputs(inp, dt)
+    dx1, g1 = _check(orc, inp, d, k, L, dt, "fused")
+    monkeypatch.setenv("WTCONV_FUSED_BWD", "0")
+    dx2, g2 = _check(orc, inp, d, k, L, dt, "two calls")
+    assert_close(dx1, dx2.double().cpu().numpy(), dt, "fused vs two calls")
+
+
+@pytest.mark.parametrize("name", ["stage1", "stage2"])
+def test_workload_full(orc, name, fused):
+    wl = WORKLOADS[name]
+    _log("backward %s, every image" % name)
+    inp = make_inputs(wl.n, wl.c, wl.h, wl.w, wl.k, wl.levels, dtype=wl.dtype, seed=wl.seed)
+    _check(orc, inp, DevInputs(inp, wl.dtype), wl.k, wl.levels, wl.dtype, name)
+
+
+def test_default_is_the_two_calls(orc):
+    """Without WTCONV_FUSED_BWD the call runs the data and the weight backward:
+    bit for bit what the two calls give."""
+    n, c, h, w, k, L, dt = 3, 4, 28, 28, 5, 2, "f16"
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=9)
+    d = DevInputs(inp, dt)
+    dx, g = _backward(d)
+    dx2 = wt.wtconv_backward_data(d.dy, d.w_base, d.s_base, d.w_lvl, d.s_lvl)
+    g2 = wt.wtconv_backward_weight(d.x, d.dy, d.w_base, d.bias, d.s_base, d.w_lvl, d.s_lvl)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx2)
+    for a, b in zip(g, g2):
+        assert torch.equal(a, b)

@@ -80,3 +80,31 @@ def test_saved_activation_memory_is_the_input_only():
     torch.cuda.synchronize()
     held = torch.cuda.memory_allocated() - before
     assert held <= y.numel() * y.element_size() + (1 << 20), held
+
+
+def test_block_with_fused_and_unfused_layer_gives_the_same_gradients():
+    """The synthetic WTConvNeXt-style block that bench.py measures peak memory
+    on: with the fused layer and with the unfused baseline as autograd
+    functions, every gradient (input, layer parameters, block parameters)
+    agrees."""
+    import bench
+    from level_haar_wavelet_amd.module import WTConvFunction
+    from level_haar_wavelet_amd.synthetic import make_inputs
+    from level_haar_wavelet_amd.unfused import UnfusedWTConvFunction
+
+    n, c, h, w, k, L = 2, 16, 32, 32, 5, 3
+    inp = make_inputs(n, c, h, w, k, L, seed=5)
+    dev = torch.device("cuda:0")
+    mods = bench.make_block(c, torch.float32)
+    grads = []
+    for layer in (WTConvFunction.apply, UnfusedWTConvFunction.apply):
+        x = torch.from_numpy(inp.x).to(dev).requires_grad_(True)
+        params = [torch.from_numpy(a).to(dev).requires_grad_(True)
+                  for a in (inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl)]
+        for p in mods.parameters():
+            p.grad = None
+        bench.block_step(mods, layer, x, params)
+        grads.append([x.grad.clone()] + [p.grad.clone() for p in params] + [p.grad.clone() for p in mods.parameters()])
+    for a, b in zip(*grads):
+        rel = float((a - b).norm() / b.norm().clamp_min(1e-30))
+        assert rel <= 1e-4, rel
