@@ -326,28 +326,32 @@ def traffic_summary(folder: str, wl, reps: int, copy_bytes: int, outdir: str = N
     return out
 
 
-VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS",
-                 "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VALU_FMA_F32", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_LDS",
+                 "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+XCDS = 8        # MI355X: GRBM_GUI_ACTIVE is summed over its eight XCDs
+SIMDS = 1024    # 256 compute units x 4 SIMDs
 
 
 def valu_summary(folder: str, wl, reps: int, outdir: str = None) -> str:
     """VALU and LDS counters per op from `rocprofv3 --pmc <VALU_COUNTERS>` runs
-    of `bench.py --counter-op OP` under OUT/<op>_valu.  Per kernel: counters per
-    dispatch (summed over the GPU), and VALU busy = SQ_ACTIVE_INST_VALU x 4 /
-    (SIMDs x GRBM_GUI_ACTIVE) with 1024 SIMDs (the fraction of the SIMDs' cycles
-    spent issuing VALU instructions), instructions per wave, and LDS bank-
-    conflict cycles per LDS-active cycle."""
+    of `bench.py --counter-op OP` under OUT/<op>_valu, per kernel and dispatch
+    averaged over its dispatches: instructions per wave, the FMA share of the
+    VALU instructions, VALU busy = SQ_ACTIVE_INST_VALU x 4 / (1024 SIMDs x
+    GRBM_GUI_ACTIVE per XCD) (the fraction of the SIMDs' cycles spent issuing
+    VALU instructions), and LDS bank-conflict cycles per LDS-active cycle."""
     outdir = outdir or os.path.join(ROOT, "profiles")
     sel = "--workload %s%s" % (wl.name, point_args(wl))
-    lines = ["# VALU and LDS counters per op: %s" % workload_name(wl), "",
+    lines = ["# VALU and LDS counters per op: %s (MI355X)" % workload_name(wl), "",
              "Commands (from the repository root; OUT is any output folder; OP is fwd, bwd_data or bwd_weight):", "",
              "    rocprofv3 --pmc %s -d OUT/OP_valu -o v --output-format csv -- python3 bench.py %s "
              "--counter-op OP --reps %d" % (" ".join(VALU_COUNTERS), sel, reps),
              "    python3 bench.py --valu-summary OUT %s --reps %d" % (sel, reps), "",
-             "VALU busy = SQ_ACTIVE_INST_VALU x 4 / (1024 SIMDs x GRBM_GUI_ACTIVE); counters are per dispatch, "
-             "averaged over the dispatches of a kernel.", "",
-             "| op | kernel | dispatches | waves | VALU instr / wave | LDS instr / wave | VALU busy | "
-             "LDS bank-conflict cycles / LDS-active cycle |", "|---|---|---|---|---|---|---|---|"]
+             "Per dispatch, averaged over the dispatches of a kernel.  VALU busy = SQ_ACTIVE_INST_VALU x 4 / "
+             "(1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); FMA share = SQ_INSTS_VALU_FMA_F32 / SQ_INSTS_VALU; "
+             "conflict = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS; us = GRBM_GUI_ACTIVE / 8 / 2.4 GHz (the "
+             "busy time at the published clock, for orientation).", "",
+             "| op | kernel | dispatches | waves | VALU instr / wave | FMA share | LDS instr / wave | VALU busy | "
+             "LDS conflict | us |", "|---|---|---|---|---|---|---|---|---|---|"]
     for key in ("fwd", "bwd_data", "bwd_weight"):
         rows = _counter_rows(os.path.join(folder, key + "_valu"))
         per = {}
@@ -358,11 +362,15 @@ def valu_summary(folder: str, wl, reps: int, outdir: str = None) -> str:
             n = len(disp)
             mean = {c: sum(x.get(c, 0.0) for x in disp.values()) / n for c in VALU_COUNTERS}
             waves = max(mean["SQ_WAVES"], 1.0)
-            busy = mean["SQ_ACTIVE_INST_VALU"] * 4.0 / (1024.0 * max(mean["GRBM_GUI_ACTIVE"], 1.0))
+            gui = max(mean["GRBM_GUI_ACTIVE"] / XCDS, 1.0)
+            busy = mean["SQ_ACTIVE_INST_VALU"] * 4.0 / (SIMDS * gui)
+            fma = mean["SQ_INSTS_VALU_FMA_F32"] / max(mean["SQ_INSTS_VALU"], 1.0)
             conf = mean["SQ_LDS_BANK_CONFLICT"] / max(mean["SQ_ACTIVE_INST_LDS"], 1.0)
-            lines.append("| %s | `%s` | %d | %.0f | %.0f | %.0f | %.3f | %.3f |" % (
-                OP_KEYS[key], k, n, waves, mean["SQ_INSTS_VALU"] / waves, mean["SQ_INSTS_LDS"] / waves, busy, conf))
-    lines += ["", "Source digest of the kernels counted: `%s`." % source_digest()]
+            lines.append("| %s | `%s` | %.2f | %.0f | %.0f | %.3f | %.0f | %.3f | %.3f | %.1f |" % (
+                OP_KEYS[key], k, n / (reps + 1), waves, mean["SQ_INSTS_VALU"] / waves, fma,
+                mean["SQ_INSTS_LDS"] / waves, busy, conf, gui / 2.4e3))
+    lines += ["", "dispatches: launches of the kernel per call of the op.", "",
+              "Source digest of the kernels counted: `%s`." % source_digest()]
     path = os.path.join(outdir, "%s_valu_lds.md" % file_stem(wl))
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
