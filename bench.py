@@ -233,7 +233,7 @@ def _counter_rows(folder: str):
 
 
 def _library_kernel(k: str) -> bool:
-    return k.startswith(("wtconv_", "lowpass_", "repack_", "fill_", "unfused_", "dwconv_"))
+    return not k.startswith("__amd_")  # every kernel but the runtime's own copies
 
 
 def traffic_summary(folder: str, wl, reps: int, copy_bytes: int, outdir: str = None) -> dict:

@@ -11,10 +11,18 @@
 static __device__ __forceinline__ void wtc_lds_barrier_wg() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Q: accumulator sets per thread the kernel holds (1, or WTC_WG_QMAX for q = 2..3).
-// With one set (fp32, k <= 5) the kernel is held to 128 VGPRs: two 512-thread workgroups
-// (four waves per SIMD) share a compute unit.
+// With one set (fp32, k <= 5) the whole-plane kernel is held to 128 VGPRs: two
+// 512-thread workgroups (four waves per SIMD) share a compute unit.  The tiled
+// instance is held to three waves per SIMD (168 VGPRs), the occupancy its LDS
+// allows anyway (three 256-thread workgroups of 42-45 KB per compute unit): at
+// 128 VGPRs its fp32 variant spilled 11 VGPRs to scratch memory.
+template <int Q, int TB, int K, bool TL>
+struct WtcWgradWaves {
+    static constexpr int v = (Q == 1 && TB == 4 && K <= 5) ? (TL ? 3 : 4) : 1;
+};
+
 template <typename T, int K, int VEC, int Q, bool TL>
-__global__ __launch_bounds__(512, (Q == 1 && sizeof(T) == 4 && K <= 5 ? 4 : 1)) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
+__global__ __launch_bounds__(512, (WtcWgradWaves<Q, (int)sizeof(T), K, TL>::v)) void wtconv_wgrad_kernel(WtcWgradArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
     WtcWgradCtx<T, VEC> ctx;
