@@ -321,32 +321,75 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
     int64_t plane, e0;
     int row0 = 0, col = 0;
     if constexpr (TL) {
+        // Tiled plans load through buffer resources over the x and dy planes:
+        // the hardware returns zeros for every offset past a plane, which is
+        // what the rows above and below the image get (a negative offset reads
+        // as a large unsigned one); segments left or right of the image, and
+        // the dy side of groups in the halo (the correlation reads dy inside
+        // the tile only), are sent past the plane and fetch nothing.
         const int tiles = p.tiles_x * p.tiles_y, unit = ctx.n0 + img;
         const int im = unit / tiles, t = unit - im * tiles, ty = t / p.tiles_x;
-        plane = ((int64_t)im * p.c + ctx.c) * ((int64_t)p.ih * p.iw);
-        row0 = ty * p.h - p.lh + p.gr * ctx.grow;
-        col = (t - ty * p.tiles_x) * p.w - p.lh + VEC * ctx.gcol;
-        e0 = plane;
+        const int tx = t - ty * p.tiles_x;
+        const int64_t pl = ((int64_t)im * p.c + ctx.c) * ((int64_t)p.ih * p.iw);
+        const int r0 = p.gr * ctx.grow - p.lh, c0 = VEC * ctx.gcol - p.lh;  // in the tile
+        row0 = ty * p.h + r0;
+        col = tx * p.w + c0;
         ctx.llo = ((int64_t)im * p.c + ctx.c) * ((int64_t)(p.ih / 2) * (p.iw / 2)) +
-                  (int64_t)(ty * p.h / 2) * (p.iw / 2) + (t - ty * p.tiles_x) * p.w / 2;
-    } else {
-        plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
-        e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
+                  (int64_t)(ty * p.h / 2) * (p.iw / 2) + tx * p.w / 2;
+        const bool colok = col >= 0 && col < p.iw;
+        const bool dyin = r0 >= 0 && r0 < p.h && c0 >= 0 && c0 < p.w;
+        // columns past any plane (sides <= 4096: offsets stay below 2^31);
+        // two selects, so that the loads below need no branch
+        const int colx = colok ? col : (1 << 27), cold = dyin ? col : (1 << 27);
+        const int plane_bytes = p.ih * p.iw * (int)sizeof(T);
+#ifndef WTC_EMULATE
+        const __amdgpu_buffer_rsrc_t rx =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(a.x + pl), (short)0, plane_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(a.dy + pl), (short)0, plane_bytes, 0x00020000);
+#endif
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q < p.gr) {
+                const int row = row0 + q;
+                const int ox = (row * p.iw + colx) * (int)sizeof(T), od = (row * p.iw + cold) * (int)sizeof(T);
+#ifdef WTC_EMULATE
+                const bool ok = colok && row >= 0 && row < p.ih;
+                const int64_t all = (int64_t)p.n * p.c * p.ih * p.iw, e = pl + (int64_t)row * p.iw + col;
+                for (int t2 = 0; t2 < VEC; ++t2) {
+                    ctx.prex[q][t2] = ok ? wtc_chk(a.x, e + t2, all, __LINE__) : (T)0.0f;
+                    ctx.prey[q][t2] = (ok && dyin) ? wtc_chk(a.dy, e + t2, all, __LINE__) : (T)0.0f;
+                }
+                (void)ox;
+                (void)od;
+#else
+                static_assert(VEC * sizeof(T) == 16 || VEC * sizeof(T) == 8, "tiled plans stage 4-element segments");
+                if constexpr (VEC * sizeof(T) == 16) {
+                    const auto dx4 = __builtin_amdgcn_raw_buffer_load_b128(rx, (unsigned)ox, 0, 0);
+                    const auto dd4 = __builtin_amdgcn_raw_buffer_load_b128(rd, (unsigned)od, 0, 0);
+                    __builtin_memcpy(&ctx.prex[q][0], &dx4, 16);
+                    __builtin_memcpy(&ctx.prey[q][0], &dd4, 16);
+                } else {
+                    const auto dx2 = __builtin_amdgcn_raw_buffer_load_b64(rx, (unsigned)ox, 0, 0);
+                    const auto dd2 = __builtin_amdgcn_raw_buffer_load_b64(rd, (unsigned)od, 0, 0);
+                    __builtin_memcpy(&ctx.prex[q][0], &dx2, 8);
+                    __builtin_memcpy(&ctx.prey[q][0], &dd2, 8);
+                }
+#endif
+            }
+        }
+        ctx.vmask = 0xF;
+        return;
     }
-    const bool colok = col >= 0 && col < p.iw;
-    int vm = 0;
+    // untiled: whole planes, every group in the image
+    plane = ((int64_t)(ctx.n0 + img) * p.c + ctx.c) * ((int64_t)p.h * p.w);
+    e0 = plane + (int64_t)(p.gr * ctx.grow) * p.w + VEC * ctx.gcol;
+    (void)row0;
+    (void)col;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (q < p.gr) {
-            int64_t e;
-            if constexpr (TL) {
-                const int row = row0 + q;
-                vm |= (colok && row >= 0 && row < p.ih) ? (1 << q) : 0;
-                e = e0 + (int64_t)wtc_min(wtc_max(row, 0), p.ih - 1) * p.iw + wtc_min(wtc_max(col, 0), p.iw - VEC);
-            } else {
-                vm |= 1 << q;
-                e = e0 + (int64_t)q * p.w;
-            }
+            const int64_t e = e0 + (int64_t)q * p.w;
 #ifdef WTC_EMULATE
             const int64_t all = (int64_t)p.n * p.c * p.ih * p.iw;
             for (int t = 0; t < VEC; ++t) {
@@ -356,13 +399,13 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
 #else
             if constexpr (VEC * sizeof(T) == 16) {
                 typedef float v4 __attribute__((ext_vector_type(4)));
-                v4 d0 = wtc_stream_load<v4, !TL>((const v4 *)(a.x + e));
+                v4 d0 = __builtin_nontemporal_load((const v4 *)(a.x + e));
                 v4 d1 = __builtin_nontemporal_load((const v4 *)(a.dy + e));
                 __builtin_memcpy(&ctx.prex[q][0], &d0, 16);
                 __builtin_memcpy(&ctx.prey[q][0], &d1, 16);
             } else if constexpr (VEC * sizeof(T) == 8) {
                 typedef float v2 __attribute__((ext_vector_type(2)));
-                v2 d0 = wtc_stream_load<v2, !TL>((const v2 *)(a.x + e));
+                v2 d0 = __builtin_nontemporal_load((const v2 *)(a.x + e));
                 v2 d1 = __builtin_nontemporal_load((const v2 *)(a.dy + e));
                 __builtin_memcpy(&ctx.prex[q][0], &d0, 8);
                 __builtin_memcpy(&ctx.prey[q][0], &d1, 8);
@@ -376,7 +419,7 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
 #endif
         }
     }
-    ctx.vmask = vm;
+    ctx.vmask = 0xF;
 }
 
 // One 2x2 Haar step on four pairs of rows held in registers: out[b][j] for
@@ -421,7 +464,7 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < VEC; ++t) {
-            const bool ok = q < p.gr && (!TL || ((ctx.vmask >> q) & 1));
+            const bool ok = q < p.gr;  // tiled loads return zeros outside the image
             xv[q][t] = ok ? wtc_to_float(ctx.prex[q][t]) : 0.0f;
             dv[q][t] = ok ? wtc_to_float(ctx.prey[q][t]) : 0.0f;
         }

@@ -464,9 +464,52 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
         plane = (int64_t)(ctx.n0 + img) * p.c + ctx.c;
     }
     const T *src = a.in + plane * ((int64_t)(ST ? p.sh : p.ih) * p.iw);
-    // image row / column of the group's first element; in tiled plans rows
-    // and segments outside the image load a clamped address and are zeroed
-    // when staged
+    if constexpr (TL) {
+        // Tiled plans load through a buffer resource over the image plane:
+        // the hardware returns zeros for every offset past the plane, which
+        // is what the rows above and below the image get (a negative offset
+        // reads as a large unsigned one); segments left or right of the image
+        // are sent past the plane.  No clamp, no mask, no select.
+        const int row0 = ty0 - p.lh + grow0, col = tx0 - p.lh + vec * ctx.gcol;
+        const bool colok = col >= 0 && col < p.iw;
+        // a column past any plane (sides <= 4096: offsets stay below 2^31);
+        // one select, so that the loads below need no branch
+        const int colx = colok ? col : (1 << 27);
+        const int plane_bytes = p.ih * p.iw * (int)sizeof(T);
+#ifndef WTC_EMULATE
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, plane_bytes, 0x00020000);
+#endif
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = row0 + q;
+            const int off = (row * p.iw + colx) * (int)sizeof(T);
+#ifdef WTC_EMULATE
+            const bool ok = colok && row >= 0 && row < p.ih;
+            const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.ih * p.iw;
+            for (int t = 0; t < vec; ++t)
+                ctx.pre[q][t] = ok ? wtc_chk(a.in, base + (int64_t)row * p.iw + col + t, all, __LINE__) : (T)0.0f;
+            (void)off;
+#else
+            if constexpr (vec * sizeof(T) == 16) {
+                const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)off, 0, 0);
+                __builtin_memcpy(&ctx.pre[q][0], &d, 16);
+            } else if constexpr (vec * sizeof(T) == 8) {
+                const auto d = __builtin_amdgcn_raw_buffer_load_b64(rs, (unsigned)off, 0, 0);
+                __builtin_memcpy(&ctx.pre[q][0], &d, 8);
+            } else if constexpr (vec * sizeof(T) == 4) {
+                const auto d = __builtin_amdgcn_raw_buffer_load_b32(rs, (unsigned)off, 0, 0);
+                __builtin_memcpy(&ctx.pre[q][0], &d, 4);
+            } else {
+                const auto d = __builtin_amdgcn_raw_buffer_load_b16(rs, (unsigned)off, 0, 0);
+                __builtin_memcpy(&ctx.pre[q][0], &d, 2);
+            }
+#endif
+        }
+        ctx.vmask = 0xF;
+        return;
+    }
+    // image row / column of the group's first element
     const int lh = TL ? p.lh : 0;
     const int row0 = ty0 - lh + grow0, col = tx0 - lh + vec * ctx.gcol;
     const bool colok = !TL || (col >= 0 && col < p.iw);
@@ -588,7 +631,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < vec; ++t)
-            x[q][t] = (q < p.gr && ((!TL && !ST) || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+            x[q][t] = (q < p.gr && (!ST || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
     wtc_whole_stage_vals<T, K, BW, TL, ST>(a, ctx, x);
 }
 
@@ -614,9 +657,13 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
     // the x map's origin column is r (mod 4) and c0 a multiple of vec: 8-byte
     // stores for even r (two per 4-element row: half the bank conflicts of
     // 4-byte stores from lanes 16 bytes apart)
+    // without the base path nothing reads the input map (a scalar branch:
+    // its one zero-pitch row would take every thread's stores)
+    if (!p.nobase) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
+        for (int q = 0; q < 4; ++q)
+            if (q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
+    }
     if (p.levels < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
@@ -904,9 +951,15 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         // the base output (without the base path the map is never written
         // and reads as the zeros LDS was cleared to, so no branch here)
         float acc[2][BW];
-        const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
-        wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
-        wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
+        if (DEEP == 2) {
+            // the deeper levels of a larger plane have no base path
+#pragma unroll
+            for (int e = 0; e < BW; ++e) acc[0][e] = acc[1][e] = 0.0f;
+        } else {
+            const int oz0 = z0.off + wtc_mul24(2 * by, z0.pitch) + BW * bx;
+            wtc_lds_vec<T, BW>(ctx, oz0, acc[0]);
+            wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
+        }
         float band[4][Q];
         if (p.levels >= 1) {
             const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
