@@ -120,7 +120,7 @@ def test_traffic_summary_sums_an_ops_launches_and_scales_by_the_copy(tmp_path):
     whole, low = "wtconv_whole_kernel<float, 5, 4, true, false>", "lowpass_kernel<float>"
     _write_counters(tmp_path / "fwd_fetch", [(1, "void %s(WtcWholeArgs<float>)" % low, "FETCH_SIZE", 100),
                                              (2, whole, "FETCH_SIZE", 300), (3, low, "FETCH_SIZE", 100),
-                                             (4, whole, "FETCH_SIZE", 300), (5, "copyBuffer", "FETCH_SIZE", 7)])
+                                             (4, whole, "FETCH_SIZE", 300), (5, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 7)])
     _write_counters(tmp_path / "fwd_write", [(1, low, "WRITE_SIZE", 10), (2, whole, "WRITE_SIZE", 30),
                                              (3, low, "WRITE_SIZE", 10), (4, whole, "WRITE_SIZE", 30)])
     _write_counters(tmp_path / "cfetch", [(1, "copyBuffer", "FETCH_SIZE", 512)])
@@ -133,7 +133,7 @@ def test_traffic_summary_sums_an_ops_launches_and_scales_by_the_copy(tmp_path):
     assert op["write_bytes"] == pytest.approx(40 * 1024)
     assert op["bytes_per_launch"] == pytest.approx((800 + 40) * 1024)
     assert op["kernels"][low]["dispatches"] == pytest.approx(1.0)
-    assert "copyBuffer" not in op["kernels"]
+    assert "__amd_rocclr_copyBuffer" not in op["kernels"]
     assert out["source_digest"] == bench.source_digest()
     saved = json.load(open(tmp_path / "hbm_traffic.json"))
     assert saved == {out["workload"]: json.loads(json.dumps(out))}
