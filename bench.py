@@ -205,6 +205,7 @@ def _short_kernel(name: str) -> str:
     name = _demangle(name.strip())
     if name.startswith("void "):
         name = name[5:]
+    name = name.replace("(anonymous namespace)::", "")
     depth = 0
     for i, ch in enumerate(name):
         if ch == "<":
@@ -910,6 +911,8 @@ def main():
     ap.add_argument("--levels", type=int, default=None)
     ap.add_argument("--dtype", default=None)
     ap.add_argument("--cpu-sample", type=int, default=4, help="images per point of the CPU-oracle sample (0: none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU-oracle sample until this much wall time has passed")
     ap.add_argument("--mall-flush", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--counter-op", default=None, choices=sorted(OP_KEYS))
@@ -1083,7 +1086,7 @@ def main():
                                             "98 FLOP per element against WTConv's 2 k^2 (1 + S(L))", **cmp_}
     if args.cpu_sample > 0:
         single = [WORKLOADS[n] for n in ("tiny", "stage1", "stage2")] if sweep else []
-        line["cpu_baseline"] = cpu_baseline(wls, args.cpu_sample, single_thread=single)
+        line["cpu_baseline"] = cpu_baseline(wls, args.cpu_sample, single_thread=single, min_seconds=args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

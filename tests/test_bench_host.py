@@ -150,6 +150,8 @@ def test_traffic_summary_sums_an_ops_launches_and_scales_by_the_copy(tmp_path):
     ("void wtconv_whole_kernel<float, 5, 4, false>(WtcWholeArgs<float>)", "wtconv_whole_kernel<float, 5, 4, false>"),
     ("wtconv_wgrad_finalize_kernel(int, int, float const*)", "wtconv_wgrad_finalize_kernel"),
     ("__amd_rocclr_copyBuffer", "__amd_rocclr_copyBuffer"),
+    ("void (anonymous namespace)::lowpass_kernel<float>(float const*, float*, long, int, int)",
+     "lowpass_kernel<float>"),
 ])
 def test_profiler_kernel_names_are_shortened(raw, short):
     assert bench._short_kernel(raw) == short
