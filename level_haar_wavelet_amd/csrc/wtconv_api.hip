@@ -227,13 +227,14 @@ bool tile_choice(const wtconv_desc_t *d, int rotate, WtcWholePlan *tp, int nobas
 }
 
 // Fused large-plane plan (planes too large for one workgroup whose level-1
-// low-pass map fits one, L >= 2, no base-less call): the deeper levels staged
-// from x and kept on chip, the base and level 1 on tiles, in one kernel with
-// no workspace.  Tile shapes in the order of tile_shapes(); WTCONV_NO_LARGE=1
-// takes it away (the tiles plus a nested call on a stored low-pass map).
+// low-pass map fits one, L >= 2): the deeper levels staged from x and kept on
+// chip, the base and level 1 on tiles, in one kernel with no workspace; also
+// without the base path (the nested deeper-levels call of a larger plane).
+// Tile shapes in the order of tile_shapes(); WTCONV_NO_LARGE=1 takes it away
+// (the tiles plus a nested call on a stored low-pass map).
 bool large_choice(const wtconv_desc_t *d, int rotate, WtcLargePlan *lp, int nobase)
 {
-    if (nobase || d->levels < 2 || env_int("WTCONV_NO_LARGE", 0, 0, 1) || env_int("WTCONV_NO_TILES", 0, 0, 1))
+    if (d->levels < 2 || env_int("WTCONV_NO_LARGE", 0, 0, 1) || env_int("WTCONV_NO_TILES", 0, 0, 1))
         return false;
     const int eb = d->dtype == WTCONV_F32 ? 4 : 2;
     // full-width 16 x 128 tiles first (fewer halo columns than 32 x 64: 128 x
@@ -242,13 +243,13 @@ bool large_choice(const wtconv_desc_t *d, int rotate, WtcLargePlan *lp, int noba
     for (int si = 0; si < shapes.n; ++si) {
         const int *sh = shapes.s[si];
         if (wtc_make_large_plan(lp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, d->levels,
-                                rotate, kFusedThreads, 1, eb, whole_budget_floats()))
+                                rotate, kFusedThreads, 1, eb, whole_budget_floats(), nobase))
             continue;
         const int resident = wtc_large_resident(d->dtype, *lp);
         int planes = env_int("WTCONV_PLANES", 0, 1, 1 << 20);
         if (!planes) planes = wtc_choose_planes(d->n, d->c, resident > 0 ? resident : 512, kWholeFixed);
         return wtc_make_large_plan(lp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k, d->levels,
-                                   rotate, kFusedThreads, planes, eb, whole_budget_floats()) == 0;
+                                   rotate, kFusedThreads, planes, eb, whole_budget_floats(), nobase) == 0;
     }
     return false;
 }

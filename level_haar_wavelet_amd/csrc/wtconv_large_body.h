@@ -25,6 +25,10 @@
 // The two plans' maps alias one LDS region (D's are zeroed again before every
 // image; T's staging writes every element T reads); the folded weights and
 // piece tables of both plans and the term map live outside it.
+// Without the base path (nobase: the nested deeper-levels call of a plane too
+// large even for this kernel) T has no base pieces and its output pass reads
+// the base output from one zero row, which lives outside the aliased region
+// too (D's maps overwrite that region every image).
 #ifndef WTCONV_LARGE_BODY_H
 #define WTCONV_LARGE_BODY_H
 
@@ -35,6 +39,7 @@ struct WtcLargePlan {
     WtcWholePlan t;     // base and level 1 on th x tw tiles of h x w
     int32_t n, c, h, w, k, levels, rotate, nthreads;
     int32_t planes;     // images per workgroup
+    int32_t nobase;     // no base path (w_base, bias, s_base not read)
     int32_t maps_off;   // the aliased map region [maps_off, maps_off + maps_floats)
     int32_t dmaps_floats, maps_floats;
     int32_t lds_floats;
@@ -64,7 +69,8 @@ static inline int32_t wtc_maps_floats(const WtcWholePlan *p) { return p->tab_off
 // plans' tables and weights, the term map and the larger plan's maps.
 static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, int32_t h, int32_t w, int32_t th,
                                       int32_t tw, int32_t k, int32_t levels, int32_t rotate, int32_t nthreads,
-                                      int32_t planes, int32_t elem_bytes, int32_t budget_floats)
+                                      int32_t planes, int32_t elem_bytes, int32_t budget_floats,
+                                      int32_t nobase = 0)
 {
     if (levels < 2 || h % 8 || w % 8 || (th >= h && tw >= w)) return -1;
     if (h % th || w % tw) return -1;
@@ -78,6 +84,7 @@ static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, in
     lp->rotate = rotate;
     lp->nthreads = nthreads;
     lp->planes = planes < 1 ? 1 : (planes > n ? n : planes);
+    lp->nobase = nobase ? 1 : 0;
     WtcWholePlan &d = lp->d, &t = lp->t;
     // the deeper levels: staged from registers in 4 x 4 groups of the
     // level-1 map (fp32 values, whatever the activation type)
@@ -85,7 +92,7 @@ static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, in
         return -1;
     if (d.gr != 4 || d.vec != 4 || d.groups != (h / 8) * (w / 8) || d.out_bw != 4) return -1;
     if (wtc_make_whole_tile_plan(&t, n, c, h, w, th, tw, k, 1, rotate, nthreads, lp->planes * tiles, elem_bytes,
-                                 1 << 30, 0))
+                                 1 << 30, lp->nobase))
         return -1;
     if (t.out_bw != 4 || t.planes != lp->planes * tiles) return -1;
     // persistent: D weights, T weights, D table, T table, the term map; then
@@ -103,11 +110,16 @@ static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, in
     const int32_t deep = off, dpitch = w / 2;
     off += (h / 2) * dpitch;
     off = wtc_roundup(off, 4);
+    // without the base path: the zero row T's output pass reads as its base
+    // output (as wide as the row the tile plan reserved for it)
+    const int32_t zrow = off;
+    if (lp->nobase) off += wtc_roundup(wtc_pitch16(wtc_roundup(tw, WTC_WP)), 4);
     lp->maps_off = off;
     lp->dmaps_floats = wtc_roundup(wtc_maps_floats(&d), 4);
     lp->maps_floats = wtc_max(lp->dmaps_floats, wtc_roundup(wtc_maps_floats(&t), 4));
     wtc_relocate(&d, off, dwf, dtab);
     wtc_relocate(&t, off, twf, ttab);
+    if (lp->nobase) t.z[0].off = zrow;
     d.deep_off = t.deep_off = deep;
     d.deep_pitch = t.deep_pitch = dpitch;
     lp->lds_floats = wtc_roundup(off + lp->maps_floats, 4);

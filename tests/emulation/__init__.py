@@ -61,7 +61,7 @@ def _load():
         lib.emu_wgrad_plan.restype = ci
         lib.emu_wgrad_tiled.argtypes = [ci, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
         lib.emu_wgrad_tiled.restype = ci
-        lib.emu_large.argtypes = [ci, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ctypes.POINTER(ci)]
+        lib.emu_large.argtypes = [ci, vp, vp] + [ci] * 9 + [vp] * 5 + [ci, ci, ci, ctypes.POINTER(ci)]
         lib.emu_large.restype = ci
         lib.emu_bwd.argtypes = [ci, vp, vp, vp] + [ci] * 6 + [vp] * 10 + [ci, ci, ci]
         lib.emu_bwd.restype = ci
@@ -221,11 +221,11 @@ def wgrad(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, levels, dtype="f32", nth
 
 
 def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dtype="f32", planes=1,
-          budget_floats=40960):
+          budget_floats=40960, nobase=False):
     """Run the fused large-plane kernel (deeper levels staged from x and kept
-    on chip, base and level 1 on th x tw tiles) on the CPU emulation.  Returns
-    (output, info) with info = images per workgroup, LDS floats, deeper-levels
-    map floats, tiles per image."""
+    on chip, base and level 1 on th x tw tiles; nobase: without the base path)
+    on the CPU emulation.  Returns (output, info) with info = images per
+    workgroup, LDS floats, deeper-levels map floats, tiles per image."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -235,16 +235,16 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
     ptr = lambda a: None if a is None else a.ctypes.data
     info = (ctypes.c_int * 4)()
     rc = lib.emu_large(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, th, tw, k, levels,
-                       rotate, *[ptr(a) for a in keep], planes, budget_floats, info)
+                       rotate, *[ptr(a) for a in keep], planes, budget_floats, int(bool(nobase)), info)
     if rc != 0:
         raise ValueError("emu_large failed: %d" % rc)
     return out.astype(np.float64), list(info)
 
 
-def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floats=40960):
+def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floats=40960, nobase=False):
     info = (ctypes.c_int * 4)()
     rc = _load().emu_large(0 if dtype == "f32" else 1, None, None, n, c, h, w, th, tw, k, levels, 0, None, None, None,
-                           None, None, planes, budget_floats, info)
+                           None, None, planes, budget_floats, int(bool(nobase)), info)
     return None if rc != 0 else list(info)
 
 

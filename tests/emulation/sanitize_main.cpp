@@ -168,7 +168,7 @@ int main()
         Case t(3, 1, 64, 64, 5, 3, 4);
         std::vector<float> y(t.elems());
         emu_large(0, t.x.data(), y.data(), t.n, t.c, t.h, t.w, 32, 64, t.k, t.L, 0, t.w0.data(), t.b0.data(),
-                  t.s0.data(), t.wl.data(), t.sl.data(), 2, 40960, nullptr);
+                  t.s0.data(), t.wl.data(), t.sl.data(), 2, 40960, 0, nullptr);
         check_elem("large-plane forward fp32 3x1x64x64 L=3", widen(y), ref_forward(t), 1e-4);
     }
     {  // weight gradients

@@ -701,15 +701,16 @@ int emu_fused(int dtype, const void *in, void *out, int n, int c, int h, int w, 
 }
 
 // The fused large-plane pass (every level on chip) on host arrays: th x tw
-// tiles; out[0..3] of `info` = images per workgroup, LDS floats, deeper-levels
-// plan's LDS-map floats, tiles per image (info may be null).
+// tiles, nobase: without the base path; out[0..3] of `info` = images per
+// workgroup, LDS floats, deeper-levels plan's LDS-map floats, tiles per image
+// (info may be null).
 int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, int th, int tw, int k, int levels,
               int rotate, const float *w_base, const float *bias, const float *s_base, const float *w_lvl,
-              const float *s_lvl, int planes, int budget_floats, int *info)
+              const float *s_lvl, int planes, int budget_floats, int nobase, int *info)
 {
     WtcLargePlan p;
     if (wtc_make_large_plan(&p, n, c, h, w, th, tw, k, levels, rotate, 256, planes, dtype == 0 ? 4 : 2,
-                            budget_floats))
+                            budget_floats, nobase))
         return -1;
     if (info) {
         info[0] = p.planes;

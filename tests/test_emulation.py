@@ -505,6 +505,29 @@ def test_emulated_large_plane_kernel_keeps_every_level_on_chip(orc, case, rotate
     _check(y, ref, tol=1e-4 if dt == "f32" else 4 * 2.0 ** -11)
 
 
+@pytest.mark.parametrize("case", [LARGE[0], LARGE[2], LARGE[5]], ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("rotate", [0, 1])
+def test_emulated_large_plane_kernel_without_base_path(orc, case, rotate):
+    """The fused large-plane kernel without the base path, as the nested
+    deeper-levels call of a larger plane runs it: the base weights, bias and
+    scale are NaN (never read), the tiles' output pass reads its base output
+    from a zero row outside the aliased map region (which the emulation
+    poisons), and the result is the layer with a zero base scale."""
+    n, c, h, w, k, L, dt, th, tw, planes = case
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=3 * h + w + k + L)
+    src = inp.x if rotate == 0 else inp.dy
+    nan_c = np.full(c, np.nan, np.float32)
+    nan_w = np.full_like(inp.w_base, np.nan)
+    y, _ = emu.large(src, nan_w, nan_c if rotate == 0 else None, nan_c, inp.w_lvl, inp.s_lvl, k, L, th, tw,
+                     rotate=rotate, dtype=dt, planes=planes, budget_floats=160 * 256, nobase=True)
+    zero_c = np.zeros(c, np.float32)
+    if rotate == 0:
+        ref = orc.forward(inp.x, inp.w_base, zero_c, zero_c, inp.w_lvl, inp.s_lvl, k, L)
+    else:
+        ref = orc.backward_data(inp.dy, inp.w_base, zero_c, inp.w_lvl, inp.s_lvl, k, L)
+    _check(y, ref, tol=1e-4 if dt == "f32" else 4 * 2.0 ** -11)
+
+
 def test_large_plane_plan_sizes():
     """At the level sweep's 128 x 128 planes the fused plan (32 x 64 tiles, 256
     threads) fits two workgroups per compute unit for every L = 2..5 (at most
@@ -517,6 +540,10 @@ def test_large_plane_plan_sizes():
             assert info is not None and info[1] * 4 <= 80 * 1024, (L, dt, info)
     assert emu.large_plan(32, 128, 128, 128, 32, 64, 5, 1) is None
     assert emu.large_plan(16, 256, 256, 256, 32, 64, 5, 4, budget_floats=160 * 256) is None
+    # the nested deeper-levels call of the 256 x 256 layer: its fp32 level-1
+    # map (128 x 128, L = 3) without the base path, 16 x 128 tiles
+    info = emu.large_plan(16, 256, 128, 128, 16, 128, 5, 3, dtype="f32", budget_floats=160 * 256, nobase=True)
+    assert info is not None and info[1] * 4 <= 80 * 1024, info
 
 
 BWD = [
