@@ -354,14 +354,21 @@ WTC_HD WTC_INLINE void wtc_wgrad_load(const WtcWgradArgs<T> &a, WtcWgradCtx<T, V
                 const int row = row0 + q;
                 const int ox = (row * p.iw + colx) * (int)sizeof(T), od = (row * p.iw + cold) * (int)sizeof(T);
 #ifdef WTC_EMULATE
-                const bool ok = colok && row >= 0 && row < p.ih;
+                // the hardware's rule: a load whose bytes lie past the range
+                // (the offset read as unsigned) returns zeros; it must agree
+                // with the segment lying in the image (and, for dy, in the tile)
+                const uint64_t seg = VEC * sizeof(T);
+                const bool ok = (uint64_t)(uint32_t)ox + seg <= (uint64_t)plane_bytes;
+                const bool okd = (uint64_t)(uint32_t)od + seg <= (uint64_t)plane_bytes;
+                if (ok != (colok && row >= 0 && row < p.ih) || okd != (ok && dyin)) {
+                    fprintf(stderr, "wtconv emulation: buffer range check disagrees at row %d col %d\n", row, col);
+                    abort();
+                }
                 const int64_t all = (int64_t)p.n * p.c * p.ih * p.iw, e = pl + (int64_t)row * p.iw + col;
                 for (int t2 = 0; t2 < VEC; ++t2) {
                     ctx.prex[q][t2] = ok ? wtc_chk(a.x, e + t2, all, __LINE__) : (T)0.0f;
-                    ctx.prey[q][t2] = (ok && dyin) ? wtc_chk(a.dy, e + t2, all, __LINE__) : (T)0.0f;
+                    ctx.prey[q][t2] = okd ? wtc_chk(a.dy, e + t2, all, __LINE__) : (T)0.0f;
                 }
-                (void)ox;
-                (void)od;
 #else
                 static_assert(VEC * sizeof(T) == 16 || VEC * sizeof(T) == 8, "tiled plans stage 4-element segments");
                 if constexpr (VEC * sizeof(T) == 16) {

@@ -485,11 +485,17 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
             const int row = row0 + q;
             const int off = (row * p.iw + colx) * (int)sizeof(T);
 #ifdef WTC_EMULATE
-            const bool ok = colok && row >= 0 && row < p.ih;
+            // the hardware's rule: a load whose bytes lie past the range
+            // (the offset read as unsigned) returns zeros; it must agree with
+            // the segment lying in the image
+            const bool ok = (uint64_t)(uint32_t)off + vec * sizeof(T) <= (uint64_t)plane_bytes;
+            if (ok != (colok && row >= 0 && row < p.ih)) {
+                fprintf(stderr, "wtconv emulation: buffer range check disagrees at row %d col %d\n", row, col);
+                abort();
+            }
             const int64_t base = src - a.in, all = (int64_t)p.n * p.c * p.ih * p.iw;
             for (int t = 0; t < vec; ++t)
                 ctx.pre[q][t] = ok ? wtc_chk(a.in, base + (int64_t)row * p.iw + col + t, all, __LINE__) : (T)0.0f;
-            (void)off;
 #else
             if constexpr (vec * sizeof(T) == 16) {
                 const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)off, 0, 0);
