@@ -140,7 +140,10 @@ def test_stacked_small_planes_equal_one_image_per_pass(orc, case, monkeypatch):
 
 TILED = [(2, 3, 64, 64, 5, 3, "f32"), (1, 4, 64, 96, 5, 2, "f16"), (2, 2, 48, 64, 3, 1, "f32"),
          (1, 2, 64, 64, 7, 4, "f32"), (2, 2, 128, 64, 5, 5, "f32"), (3, 2, 128, 128, 1, 3, "f16"),
-         (2, 3, 64, 64, 7, 0, "f32"), (1, 4, 32, 64, 5, 0, "f16")]  # L = 0: a depthwise conv on tiles
+         (2, 3, 64, 64, 7, 0, "f32"), (1, 4, 32, 64, 5, 0, "f16"),  # L = 0: a depthwise conv on tiles
+         # level-1 maps too large for the fused kernel: tiles plus a nested
+         # call, which itself runs fused without its base path
+         (1, 2, 256, 256, 5, 3, "f32"), (2, 1, 256, 128, 3, 4, "f16")]
 
 
 @pytest.mark.parametrize("case", TILED, ids=lambda c: "x".join(map(str, c)))
