@@ -101,7 +101,7 @@ WTC_HD WTC_INLINE void wtc_bwd_stage_dy(const WtcWholeArgs<T> &a, WtcWholeCtx<T>
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[q][t] = wtc_to_float(cg.prey[q][t]);
-    wtc_whole_stage_vals<T, K, BW, false, false>(a, cw, v);
+    wtc_whole_stage_vals<T, K, BW, false, false, true>(a, cw, v);  // the plan has 4-row groups
 }
 
 #endif  // WTCONV_BWD_BODY_H

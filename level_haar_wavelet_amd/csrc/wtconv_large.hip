@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
             wtc_large_zero_d<T>(A, cd);
             wtc_lds_barrier();
         }
-        wtc_whole_stage_vals<T, K, BW, false, false>(ad, cd, ll);
+        wtc_whole_stage_vals<T, K, BW, false, false, true>(ad, cd, ll);  // the plan has 4-row groups
         // the first tile's input is requested now and lands while the deeper
         // levels are computed
         const int u0 = img * tiles;

@@ -12,8 +12,10 @@
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ST: stacked small planes (two images per pass); a kernel instance of its
-// own, so that the other plans carry none of its row checks
-template <typename T, int K, int BW, bool TL, bool ST>
+// own, so that the other plans carry none of its row checks.  G4: 4-row
+// staging groups, which tiled and stacked plans always have (an instance of
+// its own for whole planes whose height 4 divides measured no faster).
+template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST>
 __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
@@ -22,7 +24,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     ctx.tid = threadIdx.x;
     ctx.nth = blockDim.x;
     wtc_whole_setup<T>(a, ctx, blockIdx.x);
-    wtc_whole_load<T, K, BW, TL, ST>(a, ctx, 0);
+    wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx, 0);
     wtc_whole_init<T, K>(a, ctx);
     wtc_lds_barrier();
     wtc_whole_fold<T, K>(a, ctx);
@@ -33,9 +35,9 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     // so the wait for a prefetched input never waits for output stores issued
     // just before it (loads and stores share one counter) and the loads do
     // not queue behind the stores.
-    wtc_whole_stage<T, K, BW, TL, ST>(a, ctx);
+    wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx);
     wtc_lds_barrier();
-    if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL, ST>(a, ctx, 1);
+    if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx, 1);
     for (int img = 0; img < ctx.nimg; ++img) {
         for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
@@ -53,19 +55,19 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
         // the convolutions above have finished reading the input and analysis
         // maps, which the staging of the next image overwrites; the output
         // pass reads only the convolution outputs
-        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx);
-        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL, ST>(a, ctx, img + 2);
+        if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx);
+        if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx, img + 2);
         wtc_whole_select<T, ST>(a, ctx, img);
         wtc_whole_out<T, K, BW, TL, ST>(a, ctx);
         wtc_lds_barrier();
     }
 }
 
-template <typename T, int K, int BW, bool TL, bool ST>
+template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST>
 static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST>;
+    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST, G4>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -76,7 +78,7 @@ static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *r
     }
     const unsigned groups = (unsigned)((a.p.units + a.p.planes - 1) / a.p.planes);
     const unsigned blocks = groups * (unsigned)a.p.c;
-    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL, ST>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL, ST, G4>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -220,6 +220,8 @@ static inline int wtc_whole_plan_common(WtcWholePlan *p, int32_t n, int32_t c, i
     // staging groups of 4 rows where the height allows (their threads also
     // compute Haar level 2 when L >= 2 and vec >= 4), else 2
     p->gr = (h % 4 == 0 && vec >= 2) ? 4 : 2;
+    // tiled and stacked instances assume 4-row groups
+    if (p->stack > 1 && p->gr != 4) return -1;
     if (p->tiled) {
         // the tile plus 2r input pixels (level 1's convolution needs r level-1
         // pixels around the tile), rounded to whole staging segments and groups
@@ -431,7 +433,7 @@ struct WtcVec {
 // group, so that no branch surrounds the loads).
 // TL: tiled plan (halo loads, bounds, shifted map origins, the added
 // low-pass term); untiled plans compile without any of it.
-template <typename T, int K, int BW, bool TL, bool ST = false>
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
 WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx, int img)
 {
     const WtcWholePlan &p = a.p;
@@ -526,7 +528,7 @@ WTC_HD WTC_INLINE void wtc_whole_load(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
     const int64_t e0 = (int64_t)row0 * p.iw + col;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (q < p.gr) {
+        if (G4 || q < p.gr) {
             const int row = row0 + q;
             vm |= (TL ? (colok && row >= 0 && row < p.ih) : (!ST || sval)) ? (1 << q) : 0;
             const int64_t e = TL ? (int64_t)wtc_min(wtc_max(row, 0), p.ih - 1) * p.iw + ccol
@@ -622,11 +624,14 @@ WTC_HD WTC_INLINE void wtc_whole_stage_l3(const WtcWholeArgs<T> &a, WtcWholeCtx<
 // (and level 2 when the group has 4 rows) of it straight from registers:
 //   U_1 and B_1^1..3 at the group's (gr/2) x (vec/2) level-1 positions,
 //   U_2 and B_2^1..3 at its 1 x (vec/4) level-2 positions.
-template <typename T, int K, int BW, bool TL, bool ST = false>
+// G4: the plan's staging groups are known to have 4 rows (tiled and stacked
+// plans always; whole-plane plans where the launch checked it), so no row of a
+// group needs a test.
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
 WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
                                             const float (&x)[4][WtcVec<T, BW>::v]);
 
-template <typename T, int K, int BW, bool TL, bool ST = false>
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
 WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int vec = WtcVec<T, BW>::v;
@@ -637,14 +642,14 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int t = 0; t < vec; ++t)
-            x[q][t] = (q < p.gr && (!ST || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
-    wtc_whole_stage_vals<T, K, BW, TL, ST>(a, ctx, x);
+            x[q][t] = ((G4 || q < p.gr) && (!ST || ((ctx.vmask >> q) & 1))) ? wtc_to_float(ctx.pre[q][t]) : 0.0f;
+    wtc_whole_stage_vals<T, K, BW, TL, ST, G4>(a, ctx, x);
 }
 
 // The staging of a group from its values (gr rows of vec fp32 values): the
 // input map, Haar level 1 and (4-row groups) level 2, and with L >= 3 the
 // lane-quad exchange for level 3.
-template <typename T, int K, int BW, bool TL, bool ST>
+template <typename T, int K, int BW, bool TL, bool ST, bool G4>
 WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
                                             const float (&x)[4][WtcVec<T, BW>::v])
 {
@@ -668,14 +673,14 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
     if (!p.nobase) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
+            if (G4 || q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
     }
     if (p.levels < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
-        if (2 * aa < p.gr) {
+        if (G4 || 2 * aa < p.gr) {
             const int i = (r0 - lh) / 2 + aa;
             float bnd[4][h1];
 #pragma unroll

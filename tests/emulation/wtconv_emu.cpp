@@ -94,7 +94,7 @@ static void emu_stage_l3(const WtcWholeArgs<T> &a, std::vector<WtcWholeCtx<T>> &
     }
 }
 
-template <typename T, int K, int BW, bool TL, bool ST = false>
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
 static void run_whole(const WtcWholeArgs<T> &a)
 {
     const WtcWholePlan &p = a.p;
@@ -115,24 +115,24 @@ static void run_whole(const WtcWholeArgs<T> &a)
             ctx[t].img_n = ST ? (int64_t)p.n * p.c * p.sh * p.iw : (int64_t)p.ih * p.iw;
             wtc_whole_setup<T>(a, ctx[t], bid);
         }
-        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], 0);
+        for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx[t], 0);
         for (int t = 0; t < nth; ++t) wtc_whole_init<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_fold<T, K>(a, ctx[t]);
         for (int t = 0; t < nth; ++t) wtc_whole_table<T, K, BW>(a, ctx[t]);
         // the kernel's software pipeline: image i+1 is staged in the same
         // barrier interval as image i's output pass (here every staging runs
         // first, so a staging write that the output pass reads would show)
-        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx[t]);
+        for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx[t]);
         if (p.stage_l3) emu_stage_l3(a, ctx);
         for (int t = 0; t < nth; ++t)
-            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], 1);
+            if (ctx[t].nimg > 1) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx[t], 1);
         for (int img = 0; img < ctx[0].nimg; ++img) {
             for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
             for (int t = 0; t < nth; ++t) {
-                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL, ST>(a, ctx[t]);
-                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL, ST>(a, ctx[t], img + 2);
+                if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx[t]);
+                if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx[t], img + 2);
             }
             if (p.stage_l3 && img + 1 < ctx[0].nimg) emu_stage_l3(a, ctx);
             for (int t = 0; t < nth; ++t) {
@@ -235,7 +235,7 @@ static void run_large(const WtcLargeArgs<T> &A)
                 float v[4][4];
                 for (int i = 0; i < 4; ++i)
                     for (int j = 0; j < 4; ++j) v[i][j] = ll[(size_t)t][(size_t)i][(size_t)j];
-                wtc_whole_stage_vals<T, K, BW, false, false>(ad, cd[t], v);
+                wtc_whole_stage_vals<T, K, BW, false, false, true>(ad, cd[t], v);
             }
             if (ad.p.stage_l3) emu_stage_l3(ad, cd);
             const int u0 = img * tiles;

@@ -30,6 +30,8 @@ CASES = [
     (1, 1, 64, 96, 3, 3, 4000),    # tiles and strips
     (1, 1, 64, 64, 5, 2, 3500),    # small tiles, short strips
     (1, 2, 48, 80, 5, 4, 5000),
+    (1, 2, 10, 14, 5, 1, None),    # 2-row staging groups (4 does not divide the height)
+    (2, 1, 6, 20, 3, 1, None),
 ]
 
 
