@@ -10,8 +10,10 @@
 // loads issued before it (the next tile's input) stay in flight.
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Two workgroups per compute unit (their LDS allows no more): at most 256
+// registers per lane.
 template <typename T, int K, int BW>
-__global__ __launch_bounds__(256) void wtconv_large_kernel(WtcLargeArgs<T> A)
+__global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
 {
     extern __shared__ float wtc_lds[];
     const WtcWholeArgs<T> &ad = A.d, &at = A.t;

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
     wtc_lds_barrier();
     if (ctx.nimg > 1) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx, 1);
     for (int img = 0; img < ctx.nimg; ++img) {
-        for (int m = wtc_whole_first_deep(a.p); m <= a.p.levels; ++m) {
+        for (int m = wtc_whole_first_deep(a.p); !TL && m <= a.p.levels; ++m) {
             wtc_whole_analysis<T, K>(a, ctx, m);
             wtc_lds_barrier();
         }

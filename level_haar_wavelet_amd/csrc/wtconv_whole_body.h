@@ -700,7 +700,9 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
             for (int b = 0; b < 4; ++b) wtc_lds_put<h1, wtc_align_of(h1, R)>(ctx, o + b * st1, bnd[b]);
         }
     }
-    if (vec >= 4 && wtc_whole_stage_l2(p)) {
+    // tiled plans carry levels 0 and 1 only (their deeper levels come from
+    // another pass or plan)
+    if (!TL && vec >= 4 && wtc_whole_stage_l2(p)) {
         const WtcMap u2 = p.u[2];
         const int st2 = u2.rows * u2.pitch;
 #pragma unroll
@@ -717,7 +719,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
         }
     }
 #ifndef WTC_EMULATE
-    if (p.stage_l3) {
+    if (!TL && p.stage_l3) {
         // the quad's four level-2 sums (lanes: top-left, top-right,
         // bottom-left, bottom-right), broadcast within the quad by DPP
         float v[4];
@@ -989,7 +991,7 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         // multiple of Q) span Q/2 cells of level 2 and one cell of every
         // deeper level, and each is read once.
         static_assert(Q <= 4, "one cell of level 3 and deeper per block");
-        if (p.levels >= 2) {
+        if (!TL && p.levels >= 2) {
             constexpr int C2 = Q >= 2 ? Q / 2 : 1;
             const WtcMap z2 = p.z[2];
             const int sz = z2.rows * z2.pitch;
@@ -1006,7 +1008,7 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
                 band[0][q] += wtc_fma(sq, t1, t0);
             }
         }
-        for (int m = 3; m <= p.levels; ++m) {
+        for (int m = 3; !TL && m <= p.levels; ++m) {
             const WtcMap zm = p.z[m];
             const int sz = zm.rows * zm.pitch;
             const float sp = ((i1 >> (m - 2)) & 1) ? -1.0f : 1.0f;
