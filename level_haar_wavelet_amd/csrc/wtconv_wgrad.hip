@@ -43,7 +43,7 @@ __global__ __launch_bounds__(512, (WtcWgradWaves<Q, (int)sizeof(T), K, TL>::v)) 
         wtc_wgrad_stage<T, K, VEC, TL>(a, ctx);
         wtc_lds_barrier_wg();
         if (img + 1 < ctx.nimg) wtc_wgrad_load<T, VEC, TL>(a, ctx, img + 1);
-        for (int m = a.p.first_deep; m <= a.p.levels; ++m) {
+        for (int m = a.p.first_deep; !TL && m <= a.p.levels; ++m) {
             wtc_wgrad_analysis<T, K, VEC>(a, ctx, m);
             wtc_lds_barrier_wg();
         }

@@ -553,7 +553,7 @@ WTC_HD WTC_INLINE void wtc_wgrad_stage(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
                 }
             }
         }
-        if constexpr (VEC >= 4) {
+        if constexpr (VEC >= 4 && !TL) {  // tiled plans carry levels 0 and 1 only
             if (p.first_deep != 3) return;
             constexpr int H2 = VEC / 4;
             const WtcMap u2 = p.u[2], d2 = p.d[2];
