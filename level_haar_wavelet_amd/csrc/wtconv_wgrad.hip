@@ -10,15 +10,18 @@
 
 static __device__ __forceinline__ void wtc_lds_barrier_wg() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Q: accumulator sets per thread the kernel holds (1, or WTC_WG_QMAX for q = 2..3).
+// Q: accumulator sets per thread the kernel holds (1, 2 for whole planes, or
+// WTC_WG_QMAX for q = 2..3 on tiles and q = 3).
 // With one set (fp32, k <= 5) the whole-plane kernel is held to 128 VGPRs: two
 // 512-thread workgroups (four waves per SIMD) share a compute unit.  The tiled
 // instance is held to three waves per SIMD (168 VGPRs), the occupancy its LDS
-// allows anyway (three 256-thread workgroups of 42-45 KB per compute unit): at
-// 128 VGPRs its fp32 variant spilled 11 VGPRs to scratch memory.
+// allows anyway (three 256-thread workgroups of 42-45 KB per compute unit), and
+// so is the two-set whole-plane instance (160 VGPRs at k = 5 fp32: three
+// workgroups fit where its LDS allows, e.g. the 64 x 64 maps of the nested
+// weight backward at L = 3; the three-set instance holds 188).
 template <int Q, int TB, int K, bool TL>
 struct WtcWgradWaves {
-    static constexpr int v = (Q == 1 && TB == 4 && K <= 5) ? (TL ? 3 : 4) : 1;
+    static constexpr int v = (Q == 1 && TB == 4 && K <= 5) ? (TL ? 3 : 4) : (Q == 2 && TB == 4 && K <= 5) ? 3 : 1;
 };
 
 template <typename T, int K, int VEC, int Q, bool TL>
@@ -116,8 +119,9 @@ static hipError_t launch_wgrad_q(const WtcWgradArgs<T> &a, hipStream_t stream, i
 template <typename T, int K, int VEC, bool TL = false>
 static hipError_t launch_wgrad(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
-    return a.p.q == 1 ? launch_wgrad_q<T, K, VEC, 1, TL>(a, stream, resident)
-                      : launch_wgrad_q<T, K, VEC, WTC_WG_QMAX, TL>(a, stream, resident);
+    if (a.p.q == 1) return launch_wgrad_q<T, K, VEC, 1, TL>(a, stream, resident);
+    if (a.p.q == 2 && !TL) return launch_wgrad_q<T, K, VEC, 2, false>(a, stream, resident);
+    return launch_wgrad_q<T, K, VEC, WTC_WG_QMAX, TL>(a, stream, resident);
 }
 
 template <typename T, int K>
