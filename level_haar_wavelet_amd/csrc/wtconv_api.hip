@@ -651,12 +651,35 @@ wtconv_status_t wtconv_workspace_size(const wtconv_desc_t *desc, wtconv_op_t op,
 // call for the deeper levels of a larger layer, which writes them to
 // scratch): the whole-plane and tiled kernels skip them and write 0.
 // launch = false: the dry run (see fused_pass).
+// fin: the partial-row sets of the calls above this one (null for the
+// outermost call).  Every call adds its own; the outermost call finalizes all
+// of them with one launch after the last correlation kernel.
 static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, const void *dy, const float *w_base,
                                   const float *bias, const float *s_base, const float *w_lvl, const float *s_lvl,
                                   float *dw_base, float *dbias, float *ds_base, float *dw_lvl, float *ds_lvl,
                                   void *workspace, size_t workspace_bytes, wtconv_stream_t stream, int nobase,
-                                  bool launch)
+                                  bool launch, WtcFinalizeSets *fin = nullptr)
 {
+    WtcFinalizeSets own;
+    const bool outer = fin == nullptr;
+    if (outer) {
+        own.C = (int)desc->c;
+        own.k = desc->k;
+        own.n = 0;
+        fin = &own;
+    }
+    // this call's set (levels of its partial rows, their layout), and the
+    // outermost call's single finalize launch
+    auto add_set = [&](int levels, int groups, int plen, const float *partial) -> bool {
+        if (fin->n >= WTC_FIN_MAX) return false;
+        fin->s[fin->n++] = WtcFinalizeSet{levels, groups, plen, partial, w_base, bias, s_base, w_lvl, s_lvl,
+                                          dw_base, dbias, ds_base, dw_lvl, ds_lvl};
+        return true;
+    };
+    auto finish = [&](hipStream_t hs) -> wtconv_status_t {
+        if (!outer || !launch) return WTCONV_OK;
+        return wtc_launch_wgrad_finalize_sets(*fin, hs) == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+    };
     wtconv_status_t st = check_desc(desc);
     if (st != WTCONV_OK) return st;
     if (!x || !dy || !dw_base || !dbias || !ds_base) return WTCONV_ERR_NULL;
@@ -682,7 +705,8 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
                                s) != hipSuccess))
             return WTCONV_ERR_HIP;
         return wgrad_pass(&pd, ws, ws + a, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl,
-                          ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream, nobase, launch);
+                          ds_lvl, ws + 2 * a, workspace_bytes - 2 * a, stream, nobase, launch,
+                          outer ? nullptr : fin);
     }
     WgradChoice ch;
     if ((st = choose_wgrad(desc, &ch, nobase)) != WTCONV_OK) return st;
@@ -704,25 +728,19 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
             float *scratch = (float *)(lld + ch.quarter);
             char *sub = (char *)scratch + align256((size_t)desc->c * (desc->k * desc->k + 2) * 4);
             const int64_t kk = (int64_t)desc->k * desc->k, C = desc->c;
-            if (launch) {
-                e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s, llx, lld);
-                if (e == hipSuccess)
-                    e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, 1, ch.groups, ch.plen, partial, w_base, bias,
-                                                  s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
-                if (e != hipSuccess) return WTCONV_ERR_HIP;
-            }
-            return wgrad_pass(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C, scratch,
-                              scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk, ds_lvl + 4 * C, sub,
-                              ch.sub_bytes, stream, 1, launch);
+            if (launch && wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s, llx, lld) != hipSuccess)
+                return WTCONV_ERR_HIP;
+            if (!add_set(1, ch.groups, ch.plen, partial)) return WTCONV_ERR_UNSUPPORTED;
+            st = wgrad_pass(&sd, llx, lld, w_base, nullptr, s_base, w_lvl + 4 * C * kk, s_lvl + 4 * C, scratch,
+                            scratch + C * kk, scratch + C * kk + C, dw_lvl + 4 * C * kk, ds_lvl + 4 * C, sub,
+                            ch.sub_bytes, stream, 1, launch, fin);
+            return st != WTCONV_OK ? st : finish(s);
         }
-        if (!launch) return WTCONV_OK;
-        e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
-        if (e == hipSuccess)
-            e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels >= 1 ? 1 : 0, ch.groups, ch.plen,
-                                          partial, w_base, bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base,
-                                          dw_lvl, ds_lvl, s);
-        return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+        if (!add_set(desc->levels >= 1 ? 1 : 0, ch.groups, ch.plen, partial)) return WTCONV_ERR_UNSUPPORTED;
+        if (launch && wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s) != hipSuccess) return WTCONV_ERR_HIP;
+        return finish(s);
     }
+    if (!add_set(desc->levels, ch.groups, ch.plen, partial)) return WTCONV_ERR_UNSUPPORTED;
     if (!launch) return WTCONV_OK;
     if (ch.whole) {
         e = wtc_launch_wgrad(desc->dtype, ch.wp, x, dy, partial, s);
@@ -743,10 +761,8 @@ static wtconv_status_t wgrad_pass(const wtconv_desc_t *desc, const void *x, cons
             dt = WTCONV_F32;
         }
     }
-    if (e == hipSuccess)
-        e = wtc_launch_wgrad_finalize((int)desc->c, desc->k, desc->levels, ch.groups, ch.plen, partial, w_base,
-                                      bias, s_base, w_lvl, s_lvl, dw_base, dbias, ds_base, dw_lvl, ds_lvl, s);
-    return e == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+    if (e != hipSuccess) return WTCONV_ERR_HIP;
+    return finish(s);
 }
 
 wtconv_status_t wtconv_backward_weight_noalloc(const wtconv_desc_t *desc, const void *x, const void *dy,

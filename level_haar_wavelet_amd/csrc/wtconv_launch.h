@@ -60,6 +60,21 @@ hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int p
                                      const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
                                      float *ds_base, float *dw_lvl, float *ds_lvl, hipStream_t stream);
 
+// Several partial-row sets finalized by one launch (a tiled weight backward
+// and its nested calls: every set is the chain rule of its own levels into its
+// own outputs).
+#define WTC_FIN_MAX 8
+struct WtcFinalizeSet {
+    int levels, groups, plen;
+    const float *partial, *w_base, *bias, *s_base, *w_lvl, *s_lvl;
+    float *dw_base, *dbias, *ds_base, *dw_lvl, *ds_lvl;
+};
+struct WtcFinalizeSets {
+    int C, k, n;
+    WtcFinalizeSet s[WTC_FIN_MAX];
+};
+hipError_t wtc_launch_wgrad_finalize_sets(const WtcFinalizeSets &f, hipStream_t stream);
+
 // Step `p.step` of the level-by-level tiled parameter gradient (input dtype:
 // 0 fp32, 1 fp16; steps after the first read the fp32 maps of the previous).
 hipError_t wtc_launch_wgrad_tile(int in_dtype, const WtcWtilePlan &p, const void *x, const void *dy, float *ux,

@@ -179,6 +179,38 @@ hipError_t wtc_launch_wgrad(int dtype, const WtcWgradPlan &p, const void *x, con
     return launch_wgrad_t<_Float16>(a, stream);
 }
 
+// The same over several partial-row sets: waves are numbered across the sets
+// (set i holds C (1 + 4 L_i) of them, in set order).
+__global__ __launch_bounds__(256) void wtconv_wgrad_finalize_sets_kernel(WtcFinalizeSets F)
+{
+    const int lane = threadIdx.x & 63;
+    int pair = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    int i = 0;
+    for (; i < F.n; ++i) {
+        const int n = F.C * (1 + 4 * F.s[i].levels);
+        if (pair < n) break;
+        pair -= n;
+    }
+    if (i >= F.n) return;  // whole waves leave together
+    const WtcFinalizeSet &f = F.s[i];
+    const int nmaps = 1 + 4 * f.levels;
+    const int c = pair / nmaps, g = pair - c * nmaps;
+    float term = wtc_wgrad_finalize_lane(lane, c, g, F.C, F.k, f.groups, f.plen, f.partial, f.w_base, f.bias,
+                                         f.s_base, f.w_lvl, f.s_lvl, f.dw_base, f.dbias, f.dw_lvl);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) term += __shfl_xor(term, d, 64);
+    if (lane == 0) wtc_wgrad_finalize_store(c, g, F.C, term, f.ds_base, f.ds_lvl);
+}
+
+hipError_t wtc_launch_wgrad_finalize_sets(const WtcFinalizeSets &f, hipStream_t stream)
+{
+    if (f.n < 1 || f.n > WTC_FIN_MAX) return hipErrorInvalidValue;
+    int pairs = 0;
+    for (int i = 0; i < f.n; ++i) pairs += f.C * (1 + 4 * f.s[i].levels);  // one wave each, four per workgroup
+    hipLaunchKernelGGL(wtconv_wgrad_finalize_sets_kernel, dim3((pairs + 3) / 4), dim3(256), 0, stream, f);
+    return hipGetLastError();
+}
+
 hipError_t wtc_launch_wgrad_finalize(int C, int k, int levels, int groups, int plen, const float *partial,
                                      const float *w_base, const float *bias, const float *s_base,
                                      const float *w_lvl, const float *s_lvl, float *dw_base, float *dbias,
