@@ -11,8 +11,11 @@
 static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Two workgroups per compute unit (their LDS allows no more): at most 256
-// registers per lane.
-template <typename T, int K, int BW>
+// registers per lane.  DL: the deeper-levels plan's level count (L - 1) for
+// DL = 1..3, a kernel instance each, so that its staging, analysis and output
+// passes take no branch on it; DL = 0: read from the plan (L >= 5, where the
+// unrolled instances measured no faster).
+template <typename T, int K, int BW, int DL>
 __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
 {
     extern __shared__ float wtc_lds[];
@@ -41,13 +44,16 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
             wtc_large_zero_d<T>(A, cd);
             wtc_lds_barrier();
         }
-        wtc_whole_stage_vals<T, K, BW, false, false, true>(ad, cd, ll);  // the plan has 4-row groups
+        wtc_whole_stage_vals<T, K, BW, false, false, true, DL>(ad, cd, ll);  // the plan has 4-row groups
         // the first tile's input is requested now and lands while the deeper
         // levels are computed
         const int u0 = img * tiles;
         wtc_whole_load<T, K, BW, true, false>(at, ct, u0);
         wtc_lds_barrier();
-        for (int m = wtc_whole_first_deep(ad.p); m <= ad.p.levels; ++m) {
+        // the staging computed levels 1, 2 (two or more) and 3 (three or more)
+#pragma unroll
+        for (int m = DL ? (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)) : wtc_whole_first_deep(ad.p); m <= (DL ? DL : ad.p.levels);
+             ++m) {
             wtc_whole_analysis<T, K>(ad, cd, m);
             wtc_lds_barrier();
         }
@@ -55,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
         wtc_whole_conv<T, K, BW>(ad, cd);
         wtc_lds_barrier();
         __builtin_amdgcn_s_setprio(2);
-        wtc_whole_out<T, K, BW, false, false, 2>(ad, cd);
+        wtc_whole_out<T, K, BW, false, false, 2, DL>(ad, cd);
         wtc_lds_barrier();
         // base and level 1 on the tiles of the image, the deeper levels' term
         // from LDS; the same software pipeline as the tiled whole-plane kernel
@@ -78,12 +84,15 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
     }
 }
 
-template <typename T, int K>
-static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
+template <typename T, int K, int DL>
+static hipError_t launch_dl(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
 {
-    if (a.d.p.out_bw != 4 || a.t.p.out_bw != 4) return hipErrorInvalidValue;
+    // the instance's analysis starts where the plan's staging stops
+    const WtcWholePlan &d = a.d.p;
+    const int first = d.stage_l3 ? 4 : (d.gr == 4 && d.vec >= 4 && d.levels >= 2 ? 3 : 2);
+    if (DL && (d.levels != DL || first != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)))) return hipErrorInvalidValue;
     const size_t lds = (size_t)a.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_large_kernel<T, K, 4>;
+    const void *fn = (const void *)&wtconv_large_kernel<T, K, 4, DL>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -93,9 +102,21 @@ static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *re
         return hipSuccess;
     }
     const unsigned groups = (unsigned)((a.n + a.planes - 1) / a.planes);
-    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4>), dim3(groups * (unsigned)a.c), dim3(a.t.p.nthreads), lds,
+    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4, DL>), dim3(groups * (unsigned)a.c), dim3(a.t.p.nthreads), lds,
                        stream, a);
     return hipGetLastError();
+}
+
+template <typename T, int K>
+static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
+{
+    if (a.d.p.out_bw != 4 || a.t.p.out_bw != 4 || a.d.p.gr != 4) return hipErrorInvalidValue;
+    switch (a.d.p.levels) {
+    case 1: return launch_dl<T, K, 1>(a, stream, resident);
+    case 2: return launch_dl<T, K, 2>(a, stream, resident);
+    case 3: return launch_dl<T, K, 3>(a, stream, resident);
+    default: return launch_dl<T, K, 0>(a, stream, resident);
+    }
 }
 
 template <typename T>

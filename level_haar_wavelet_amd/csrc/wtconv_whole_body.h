@@ -627,7 +627,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage_l3(const WtcWholeArgs<T> &a, WtcWholeCtx<
 // G4: the plan's staging groups are known to have 4 rows (tiled and stacked
 // plans always; whole-plane plans where the launch checked it), so no row of a
 // group needs a test.
-template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST, int LV = 0>
 WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
                                             const float (&x)[4][WtcVec<T, BW>::v]);
 
@@ -649,7 +649,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage(const WtcWholeArgs<T> &a, WtcWholeCtx<T> 
 // The staging of a group from its values (gr rows of vec fp32 values): the
 // input map, Haar level 1 and (4-row groups) level 2, and with L >= 3 the
 // lane-quad exchange for level 3.
-template <typename T, int K, int BW, bool TL, bool ST, bool G4>
+template <typename T, int K, int BW, bool TL, bool ST, bool G4, int LV>
 WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx,
                                             const float (&x)[4][WtcVec<T, BW>::v])
 {
@@ -675,7 +675,8 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
         for (int q = 0; q < 4; ++q)
             if (G4 || q < p.gr) wtc_lds_put<vec, wtc_align_of(vec, R)>(ctx, xo + wtc_mul24(q, xm.pitch), x[q]);
     }
-    if (p.levels < 1) return;
+    const int lv = LV ? LV : p.levels;  // LV: the plan's levels, known at compile time (0: not)
+    if (lv < 1) return;
     // level 1: 2x2 blocks (rows 2a, 2a+1; columns 2b, 2b+1) of the group
     float ll[2][h1];
 #pragma unroll
@@ -702,7 +703,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
     }
     // tiled plans carry levels 0 and 1 only (their deeper levels come from
     // another pass or plan)
-    if (!TL && vec >= 4 && wtc_whole_stage_l2(p)) {
+    if (!TL && vec >= 4 && (LV ? G4 && LV >= 2 : wtc_whole_stage_l2(p))) {
         const WtcMap u2 = p.u[2];
         const int st2 = u2.rows * u2.pitch;
 #pragma unroll
@@ -719,7 +720,7 @@ WTC_HD WTC_INLINE void wtc_whole_stage_vals(const WtcWholeArgs<T> &a, WtcWholeCt
         }
     }
 #ifndef WTC_EMULATE
-    if (!TL && p.stage_l3) {
+    if (!TL && (LV ? G4 && vec == 4 && LV >= 3 : p.stage_l3)) {
         // the quad's four level-2 sums (lanes: top-left, top-right,
         // bottom-left, bottom-right), broadcast within the quad by DPP
         float v[4];
@@ -948,7 +949,7 @@ WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
 // p.deep_off instead of the global `low`; DEEP = 2: an untiled plan writes its
 // result to that LDS map (the deeper levels of a larger plane) instead of
 // storing it.
-template <typename T, int K, int BW, bool TL, bool ST = false, int DEEP = 0>
+template <typename T, int K, int BW, bool TL, bool ST = false, int DEEP = 0, int LV = 0>
 WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int Q = BW / 2;
@@ -974,7 +975,8 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
             wtc_lds_vec<T, BW>(ctx, oz0 + z0.pitch, acc[1]);
         }
         float band[4][Q];
-        if (p.levels >= 1) {
+        const int lv = LV ? LV : p.levels;  // LV: the plan's levels, known at compile time (0: not)
+        if (lv >= 1) {
             const int o1 = z1.off + wtc_mul24(i1, z1.pitch) + Q * bx;
 #pragma unroll
             for (int b = 0; b < 4; ++b) wtc_lds_vec<T, Q>(ctx, o1 + b * st1, band[b]);
@@ -991,7 +993,7 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
         // multiple of Q) span Q/2 cells of level 2 and one cell of every
         // deeper level, and each is read once.
         static_assert(Q <= 4, "one cell of level 3 and deeper per block");
-        if (!TL && p.levels >= 2) {
+        if (!TL && lv >= 2) {
             constexpr int C2 = Q >= 2 ? Q / 2 : 1;
             const WtcMap z2 = p.z[2];
             const int sz = z2.rows * z2.pitch;
@@ -1008,7 +1010,7 @@ WTC_HD WTC_INLINE void wtc_whole_out(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &c
                 band[0][q] += wtc_fma(sq, t1, t0);
             }
         }
-        for (int m = 3; !TL && m <= p.levels; ++m) {
+        for (int m = 3; !TL && m <= lv; ++m) {
             const WtcMap zm = p.z[m];
             const int sz = zm.rows * zm.pitch;
             const float sp = ((i1 >> (m - 2)) & 1) ? -1.0f : 1.0f;

@@ -185,9 +185,15 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
 // output pass and after every image's tiles, the aliased map region is
 // poisoned with NaN: the tiles must write every element they read (their
 // staging covers the halos), and the deeper levels must zero their own maps.
-template <typename T, int K, int BW>
+// DL: the deeper-levels plan's level count, as the kernel instance has it
+// (0: read from the plan)
+template <typename T, int K, int BW, int DL>
 static void run_large(const WtcLargeArgs<T> &A)
 {
+    if (DL && (wtc_whole_first_deep(A.d.p) != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)) || A.d.p.levels != DL)) {
+        fprintf(stderr, "wtconv emulation: deeper-levels plan does not match its instance\n");
+        abort();
+    }
     const WtcLargeArgs<T> &lp = A;
     const WtcWholeArgs<T> &ad = A.d, &at = A.t;
     const int groups = (lp.n + lp.planes - 1) / lp.planes;
@@ -235,15 +241,16 @@ static void run_large(const WtcLargeArgs<T> &A)
                 float v[4][4];
                 for (int i = 0; i < 4; ++i)
                     for (int j = 0; j < 4; ++j) v[i][j] = ll[(size_t)t][(size_t)i][(size_t)j];
-                wtc_whole_stage_vals<T, K, BW, false, false, true>(ad, cd[t], v);
+                wtc_whole_stage_vals<T, K, BW, false, false, true, DL>(ad, cd[t], v);
             }
             if (ad.p.stage_l3) emu_stage_l3(ad, cd);
             const int u0 = img * tiles;
             for (int t = 0; t < nth; ++t) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0);
-            for (int m = wtc_whole_first_deep(ad.p); m <= ad.p.levels; ++m)
+            for (int m = DL ? (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)) : wtc_whole_first_deep(ad.p);
+                 m <= (DL ? DL : ad.p.levels); ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(ad, cd[t], m);
             for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(ad, cd[t]);
-            for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW, false, false, 2>(ad, cd[t]);
+            for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW, false, false, 2, DL>(ad, cd[t]);
             poison_maps();
             for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
             for (int t = 0; t < nth; ++t)
@@ -264,14 +271,25 @@ static void run_large(const WtcLargeArgs<T> &A)
     }
 }
 
+template <typename T, int K>
+static int run_large_k(const WtcLargeArgs<T> &a)
+{
+    switch (a.d.p.levels) {
+    case 1: run_large<T, K, 4, 1>(a); return 0;
+    case 2: run_large<T, K, 4, 2>(a); return 0;
+    case 3: run_large<T, K, 4, 3>(a); return 0;
+    default: run_large<T, K, 4, 0>(a); return 0;
+    }
+}
+
 template <typename T>
 static int run_large_t(const WtcLargeArgs<T> &a)
 {
     switch (a.t.p.k) {
-    case 1: run_large<T, 1, 4>(a); return 0;
-    case 3: run_large<T, 3, 4>(a); return 0;
-    case 5: run_large<T, 5, 4>(a); return 0;
-    case 7: run_large<T, 7, 4>(a); return 0;
+    case 1: return run_large_k<T, 1>(a);
+    case 3: return run_large_k<T, 3>(a);
+    case 5: return run_large_k<T, 5>(a);
+    case 7: return run_large_k<T, 7>(a);
     default: return -1;
     }
 }
