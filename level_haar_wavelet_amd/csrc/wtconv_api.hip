@@ -451,20 +451,35 @@ wtconv_status_t choose_wgrad(const wtconv_desc_t *d, WgradChoice *ch, int nobase
         // planes too large for one workgroup: base and level-1 correlations on
         // tiles (L = 1 partial rows); levels 2..L are the layer with L - 1
         // levels on the level-1 low-pass maps of x and dy, a nested call
-        // fp32: 16 x 128 tiles first; fp16: 32 x 64 (128 x 128 fp16 weight
-        // backward 3.5 % faster, fp32 within 1 %)
+        // 64 x 64 tiles on 512 threads first (128 x 128 weight backward: fp16
+        // L = 1 145.7 -> 141.3 us, L = 3 189.7 -> 186.9 us, fp32 L = 1 1-4 %
+        // faster, the other points within 1 %), unless the tile knobs are
+        // set; then fp32: 16 x 128 tiles first; fp16: 32 x 64 (128 x 128 fp16
+        // weight backward 3.5 % faster, fp32 within 1 %), on tile_threads()
+        // threads
         const TileShapes shapes = tile_shapes(d->dtype == WTCONV_F32);
-        for (int si = 0; si < shapes.n; ++si) {
-            const int *sh = shapes.s[si];
+        int cand[12][3], nc = 0;
+        if (!std::getenv("WTCONV_TILE") && !std::getenv("WTCONV_TILE_THREADS")) {
+            cand[nc][0] = 64;
+            cand[nc][1] = 64;
+            cand[nc++][2] = 2 * kFusedThreads;
+        }
+        for (int si = 0; si < shapes.n && nc < 12; ++si, ++nc) {
+            cand[nc][0] = shapes.s[si][0];
+            cand[nc][1] = shapes.s[si][1];
+            cand[nc][2] = tile_threads();
+        }
+        for (int ci = 0; ci < nc; ++ci) {
+            const int *sh = cand[ci];
             if (d->h % sh[0] || d->w % sh[1] || (sh[0] == d->h && sh[1] == d->w)) continue;
             if (wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                         tl, tile_threads(), 1, eb, whole_budget_floats(), nobase))
+                                         tl, sh[2], 1, eb, whole_budget_floats(), nobase))
                 continue;
             const int resident = wtc_wgrad_resident(d->dtype, ch->wp);
             int planes = env_int("WTCONV_WGRAD_PLANES", 0, 1, 1 << 20);
             if (!planes) planes = wtc_choose_planes(ch->wp.units, d->c, resident > 0 ? resident : 512, kWgradFixed);
             wtc_make_wgrad_tile_plan(&ch->wp, (int)d->n, (int)d->c, (int)d->h, (int)d->w, sh[0], sh[1], d->k,
-                                     tl, tile_threads(), planes, eb, whole_budget_floats(), nobase);
+                                     tl, sh[2], planes, eb, whole_budget_floats(), nobase);
             ch->tiles = true;
             break;
         }
