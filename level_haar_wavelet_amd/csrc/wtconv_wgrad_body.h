@@ -651,9 +651,11 @@ WTC_HD WTC_INLINE void wtc_wgrad_table(const WtcWgradArgs<T> &a, WtcWgradCtx<T, 
 }
 
 // Correlation of one 4x4 dy-side piece with its x-side window, added to acc
-// (k*k taps, then the sum of the dy-side values).
+// (k*k taps, then, for a piece of the base map, the sum of the dy-side values:
+// the bias gradient's; the level maps' partial rows have no such entry, so
+// their pieces skip it).
 template <typename T, int K, int VEC>
-WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1, int xp, int dp,
+WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1, int xp, int dp, bool base,
                                       float (&acc)[K * K + 1])
 {
     constexpr int P = WTC_WG_P;
@@ -661,10 +663,12 @@ WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1,
     float av[P][P];
 #pragma unroll
     for (int r = 0; r < P; ++r) wtc_lds_row<T, P>(ctx, d1 + r * dp, av[r]);
+    if (base) {
 #pragma unroll
-    for (int r = 0; r < P; ++r)
+        for (int r = 0; r < P; ++r)
 #pragma unroll
-        for (int c = 0; c < P; ++c) acc[K * K] += av[r][c];
+            for (int c = 0; c < P; ++c) acc[K * K] += av[r][c];
+    }
     float row[NR];
     wtc_lds_row<T, NR>(ctx, d0, row);
 #pragma unroll
@@ -709,7 +713,7 @@ WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx
             t1 = tv.y;
 #endif
             wtc_wgrad_piece<T, K, VEC>(ctx, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
-                                      (int)((t1 >> 8) & 0xffu), acc[s]);
+                                      (int)((t1 >> 8) & 0xffu), (t1 >> 16) == 0, acc[s]);
         }
     }
 }

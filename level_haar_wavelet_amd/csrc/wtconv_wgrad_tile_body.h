@@ -349,7 +349,7 @@ WTC_HD WTC_INLINE void wtc_wtile_correlate(const WtcWtileArgs<TI> &a, WtcWtileCt
             const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
             const unsigned t0 = (unsigned)tab[0], t1 = (unsigned)tab[1];
             wtc_wgrad_piece<float, K, 1>(lc, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
-                                         (int)((t1 >> 8) & 0xffu), acc[s]);
+                                         (int)((t1 >> 8) & 0xffu), true, acc[s]);
         }
     }
 }
