@@ -390,6 +390,22 @@ def test_emulated_tiled_weight_gradients_levels_0_and_1(orc, case):
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_emulated_tiled_weight_gradients_on_64x64_tiles_of_512_threads(orc, dt):
+    """The tile shape the library tries first for the weight backward: 64 x 64
+    tiles on 512 threads (one correlation piece per thread), on a plane of
+    2 x 2 tiles, base and level 1, with the low-pass maps written too."""
+    n, c, h, w, k, L = 2, 2, 128, 128, 5, 1
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=11)
+    got, (llx, lld) = emu.wgrad_tiles(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k,
+                                      64, 64, dtype=dt, nthreads=512, planes=3, budget_floats=40960, lowpass=True)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    for gg, rr in zip(got, ref):
+        assert not np.isnan(gg).any()
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
+    assert np.abs(llx - _lowpass(inp.x)).max() <= 1e-6 and np.abs(lld - _lowpass(inp.dy)).max() <= 1e-6
+
+
 @pytest.mark.parametrize("case", [c for c in WGRAD_TILED if c[5] == 1], ids=lambda c: "x".join(map(str, c)))
 def test_emulated_tiled_weight_gradients_write_the_low_pass_maps(orc, case):
     """With L >= 2 the tiled weight-gradient pass also writes the level-1
