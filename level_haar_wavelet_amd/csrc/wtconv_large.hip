@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
             wtc_lds_barrier();
         }
         __builtin_amdgcn_s_setprio(0);
-        wtc_whole_conv<T, K, BW>(ad, cd);
+        wtc_whole_conv<T, K, BW, false>(ad, cd);
         wtc_lds_barrier();
         __builtin_amdgcn_s_setprio(2);
         wtc_whole_out<T, K, BW, false, false, 2, DL>(ad, cd);
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
             // the next image's deeper-levels input lands during the last tile
             if (t == tiles - 1 && img + 1 < cd.nimg) wtc_large_fetch_d<T>(A, cd, img + 1, raw);
             __builtin_amdgcn_s_setprio(0);
-            wtc_whole_conv<T, K, BW>(at, ct);
+            wtc_whole_conv<T, K, BW, false>(at, ct);
             wtc_lds_barrier();
             __builtin_amdgcn_s_setprio(2);
             if (t + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct);
@@ -91,6 +91,7 @@ static hipError_t launch_dl(const WtcLargeArgs<T> &a, hipStream_t stream, int *r
     const WtcWholePlan &d = a.d.p;
     const int first = d.stage_l3 ? 4 : (d.gr == 4 && d.vec >= 4 && d.levels >= 2 ? 3 : 2);
     if (DL && (d.levels != DL || first != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)))) return hipErrorInvalidValue;
+    if (d.tail || a.t.p.tail) return hipErrorInvalidValue;  // no tail loop in this kernel
     const size_t lds = (size_t)a.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_large_kernel<T, K, 4, DL>;
     if (lds > 65536) {

@@ -91,6 +91,10 @@ static inline int wtc_make_large_plan(WtcLargePlan *lp, int32_t n, int32_t c, in
     if (wtc_make_whole_plan(&d, n, c, h / 2, w / 2, k, levels - 1, rotate, nthreads, lp->planes, 4, 1 << 30, 1))
         return -1;
     if (d.gr != 4 || d.vec != 4 || d.groups != (h / 8) * (w / 8) || d.out_bw != 4) return -1;
+    // its pieces past the first round stay whole: one-row pieces there (the
+    // second workgroup on the compute unit keeps the SIMDs busy meanwhile)
+    // measured no faster at L = 3 and slower at L = 4 and 5
+    d.tail = 0;
     if (wtc_make_whole_tile_plan(&t, n, c, h, w, th, tw, k, 1, rotate, nthreads, lp->planes * tiles, elem_bytes,
                                  1 << 30, lp->nobase))
         return -1;

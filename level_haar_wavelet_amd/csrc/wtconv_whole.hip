@@ -49,7 +49,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
         // bound waves issue first when both want the SIMD (measured: stage1
         // forward 64.5 -> 60.0 us, the 256 x 256 layer's step -10 %).
         __builtin_amdgcn_s_setprio(0);
-        wtc_whole_conv<T, K, BW>(a, ctx);
+        wtc_whole_conv<T, K, BW, !TL>(a, ctx);
         wtc_lds_barrier();
         __builtin_amdgcn_s_setprio(2);
         // the convolutions above have finished reading the input and analysis
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST>
 static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
+    if (TL && a.p.tail) return hipErrorInvalidValue;  // the tiled instances carry no tail loop
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST, G4>;
     if (lds > 65536) {

@@ -56,6 +56,7 @@ struct WtcWholePlan {
     WtcMap z[WTC_MAXL + 1];   // z[0]: base output; z[m]: four conv outputs of level m; origin (0, 0)
     int32_t wf_off;
     int32_t items;       // convolution pieces per image
+    int32_t tail;        // the last `tail` pieces run as one-row pieces (see wtc_whole_layout)
     int32_t tab_off;     // piece descriptors, 4 ints each
     int32_t lds_floats;
     // Tiling, for planes too large for one workgroup: h x w above is then one
@@ -143,6 +144,14 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
     int32_t items = p->nobase ? 0 : ((p->h + P - 1) / P) * ((p->w + P - 1) / P);
     for (int32_t m = 1; m <= L; ++m) items += 4 * (((p->h >> m) + P - 1) / P) * (((p->w >> m) + P - 1) / P);
     p->items = items;
+    // Pieces past the last full round of the workgroup's threads, when their
+    // P one-row pieces fit one round, run as those (a quarter of a piece per
+    // thread): otherwise a few threads would take a whole extra piece while
+    // the rest of the workgroup waits at the barrier (the stacked 28 x 28
+    // L = 2 plan, 272 pieces on 256 threads: forward 40.1 -> 36.4 us).  Tiled
+    // plans have none (their kernel instances carry no tail loop).
+    const int32_t rem = items % p->nthreads;
+    p->tail = !p->tiled && items > p->nthreads && P * rem <= p->nthreads ? rem : 0;
     p->tab_off = off;
     off += 4 * items;
     p->lds_floats = wtc_roundup(off, 4);
@@ -884,14 +893,57 @@ WTC_HD WTC_INLINE void wtc_lds_store4(Ctx &ctx, int idx, const float (&src)[N])
 #endif
 }
 
-// The convolution phase: every thread computes pieces tid, tid + nth, ...
-template <typename T, int K, int BW>
+// One output row of P columns of piece `it` (row r0 of the piece).
+template <typename T, int K>
+WTC_HD WTC_INLINE void wtc_whole_row_piece(const WtcWholePlan &p, WtcWholeCtx<T> &ctx, int it, int r0)
+{
+    constexpr int P = WTC_WP, KK = K * K, WS = (KK + 3) / 4 * 4;
+    constexpr int NW = P + K - 1, NR = (NW + 3) / 4 * 4;  // window width, as read
+    int dsc[4];
+    {
+        float tmp[4];
+        wtc_lds_row<T, 4>(ctx, p.tab_off + 4 * it, tmp);
+        for (int e = 0; e < 4; ++e) {
+#ifdef WTC_EMULATE
+            __builtin_memcpy(&dsc[e], &tmp[e], 4);
+#else
+            dsc[e] = __float_as_int(tmp[e]);
+#endif
+        }
+    }
+    const int ip = dsc[2] & 0xffff, op = dsc[2] >> 16;
+    const int src = dsc[0] + r0 * ip, dst = dsc[1] + r0 * op;
+    const int wk = dsc[3] & 0xffff;
+    const float init = (dsc[3] >> 16) ? ctx.bias : 0.0f;
+    float wv[WS];
+    wtc_lds_row<T, WS>(ctx, wk, wv);
+    float acc[P];
+#pragma unroll
+    for (int dc = 0; dc < P; ++dc) acc[dc] = init;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+        float row[NR];
+        wtc_lds_row<T, NR>(ctx, src + u * ip, row);
+#pragma unroll
+        for (int v = 0; v < K; ++v)
+#pragma unroll
+            for (int dc = 0; dc < P; ++dc) acc[dc] = wtc_fma(wv[u * K + v], row[dc + v], acc[dc]);
+    }
+    wtc_lds_store4<T, P>(ctx, dst, acc);
+}
+
+// The convolution phase: every thread computes pieces tid, tid + nth, ...,
+// then one-row pieces of the plan's tail (four lanes to a piece).  TAIL =
+// false: an instance whose plans have no tail (tiles, the large-plane
+// kernel), compiled without that loop.
+template <typename T, int K, int BW, bool TAIL = true>
 WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int P = WTC_WP, KK = K * K, WS = (KK + 3) / 4 * 4;
     constexpr int NW = P + K - 1, NR = (NW + 3) / 4 * 4;  // window width, as read
     const WtcWholePlan &p = a.p;
-    for (int it = ctx.tid; it < p.items; it += ctx.nth) {
+    const int full = p.items - p.tail;
+    for (int it = ctx.tid; it < full; it += ctx.nth) {
         int dsc[4];
         {
             float tmp[4];
@@ -937,6 +989,10 @@ WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &
         }
 #pragma unroll
         for (int dr = 0; dr < P; ++dr) wtc_lds_store4<T, P>(ctx, dst + dr * op, acc[dr]);
+    }
+    if constexpr (TAIL) {
+        for (int it = ctx.tid; it < P * p.tail; it += ctx.nth)
+            wtc_whole_row_piece<T, K>(p, ctx, full + it / P, it % P);
     }
 }
 

@@ -100,10 +100,11 @@ def fused(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, rotate=0, dtype="f32
 
 
 def whole_plan(n, c, h, w, k, levels, rotate=0, nthreads=256, planes=1, dtype="f32", budget_floats=40960, stack=1):
-    out = (ctypes.c_int * 11)()
+    out = (ctypes.c_int * 12)()
     rc = _load().emu_whole_plan(n, c, h, w, k, levels, rotate, nthreads, planes, 4 if dtype == "f32" else 2,
                                 budget_floats, stack, out)
-    keys = ("planes", "vec", "out_bw", "lds_floats", "blocks", "nthreads", "ok", "stage_l3", "rows", "gap", "units")
+    keys = ("planes", "vec", "out_bw", "lds_floats", "items", "nthreads", "ok", "stage_l3", "rows", "gap", "units",
+            "tail")
     d = dict(zip(keys, list(out)))
     d["ok"] = rc == 0
     return d
@@ -225,7 +226,8 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
     """Run the fused large-plane kernel (deeper levels staged from x and kept
     on chip, base and level 1 on th x tw tiles; nobase: without the base path)
     on the CPU emulation.  Returns (output, info) with info = images per
-    workgroup, LDS floats, deeper-levels map floats, tiles per image."""
+    workgroup, LDS floats, deeper-levels map floats, tiles per image, and the
+    pieces and one-row tail pieces of the deeper-levels and tile plans."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -233,7 +235,7 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
     out = np.full_like(xin, np.nan)
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
-    info = (ctypes.c_int * 4)()
+    info = (ctypes.c_int * 8)()
     rc = lib.emu_large(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, th, tw, k, levels,
                        rotate, *[ptr(a) for a in keep], planes, budget_floats, int(bool(nobase)), info)
     if rc != 0:
@@ -242,7 +244,7 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
 
 
 def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floats=40960, nobase=False):
-    info = (ctypes.c_int * 4)()
+    info = (ctypes.c_int * 8)()
     rc = _load().emu_large(0 if dtype == "f32" else 1, None, None, n, c, h, w, th, tw, k, levels, 0, None, None, None,
                            None, None, planes, budget_floats, int(bool(nobase)), info)
     return None if rc != 0 else list(info)

@@ -102,6 +102,10 @@ static void run_whole(const WtcWholeArgs<T> &a)
     const int nblocks = groups * p.c;
     std::vector<float> lds((size_t)p.lds_floats);
     const int nth = p.nthreads;
+    if (TL && p.tail) {  // as the launch: the tiled instances carry no tail loop
+        fprintf(stderr, "wtconv emulation: a tiled plan with a piece tail\n");
+        abort();
+    }
     for (int bid = 0; bid < nblocks; ++bid) {
         // poison LDS: the kernel must zero it before use
         for (auto &v : lds) v = __builtin_nanf("");
@@ -129,7 +133,7 @@ static void run_whole(const WtcWholeArgs<T> &a)
         for (int img = 0; img < ctx[0].nimg; ++img) {
             for (int m = wtc_whole_first_deep(p); m <= p.levels; ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(a, ctx[t], m);
-            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(a, ctx[t]);
+            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW, !TL>(a, ctx[t]);
             for (int t = 0; t < nth; ++t) {
                 if (img + 1 < ctx[t].nimg) wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx[t]);
                 if (img + 2 < ctx[t].nimg) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx[t], img + 2);
@@ -194,6 +198,10 @@ static void run_large(const WtcLargeArgs<T> &A)
         fprintf(stderr, "wtconv emulation: deeper-levels plan does not match its instance\n");
         abort();
     }
+    if (A.d.p.tail || A.t.p.tail) {  // the kernel carries no tail loop
+        fprintf(stderr, "wtconv emulation: a large-plane plan with a piece tail\n");
+        abort();
+    }
     const WtcLargeArgs<T> &lp = A;
     const WtcWholeArgs<T> &ad = A.d, &at = A.t;
     const int groups = (lp.n + lp.planes - 1) / lp.planes;
@@ -249,14 +257,14 @@ static void run_large(const WtcLargeArgs<T> &A)
             for (int m = DL ? (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)) : wtc_whole_first_deep(ad.p);
                  m <= (DL ? DL : ad.p.levels); ++m)
                 for (int t = 0; t < nth; ++t) wtc_whole_analysis<T, K>(ad, cd[t], m);
-            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(ad, cd[t]);
+            for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW, false>(ad, cd[t]);
             for (int t = 0; t < nth; ++t) wtc_whole_out<T, K, BW, false, false, 2, DL>(ad, cd[t]);
             poison_maps();
             for (int t = 0; t < nth; ++t) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
             for (int t = 0; t < nth; ++t)
                 if (tiles > 1) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + 1);
             for (int tt = 0; tt < tiles; ++tt) {
-                for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW>(at, ct[t]);
+                for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW, false>(at, ct[t]);
                 for (int t = 0; t < nth; ++t) {
                     if (tt + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
                     if (tt + 2 < tiles) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + tt + 2);
@@ -627,8 +635,8 @@ int emu_wgrad_plan(int n, int c, int h, int w, int k, int levels, int nthreads, 
 // Images per workgroup chosen for a grid of c x ceil(n / planes) workgroups.
 int emu_choose_planes(int n, int c, int slots, double fixed) { return wtc_choose_planes(n, c, slots, fixed); }
 
-// Whole-plane plan: out[0..10] = planes, vec, out_bw, lds_floats, pieces, nthreads, ok, stage_l3, plane rows,
-// rows between stacked images, units.
+// Whole-plane plan: out[0..11] = planes, vec, out_bw, lds_floats, pieces, nthreads, ok, stage_l3, plane rows,
+// rows between stacked images, units, pieces run as one-row pieces.
 int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, int nthreads, int planes, int ebytes,
                    int budget_floats, int stack, int *out)
 {
@@ -645,6 +653,7 @@ int emu_whole_plan(int n, int c, int h, int w, int k, int levels, int rotate, in
     out[8] = p.h;
     out[9] = p.sgap;
     out[10] = p.units;
+    out[11] = p.tail;
     return rc;
 }
 
@@ -735,6 +744,10 @@ int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, 
         info[1] = p.lds_floats;
         info[2] = p.dmaps_floats;
         info[3] = p.t.tiles_x * p.t.tiles_y;
+        info[4] = p.d.items;
+        info[5] = p.d.tail;
+        info[6] = p.t.items;
+        info[7] = p.t.tail;
     }
     if (!in) return 0;
     if (dtype == 0)

@@ -564,6 +564,31 @@ def test_large_plane_plan_sizes():
     assert info is not None and info[1] * 4 <= 80 * 1024, info
 
 
+def test_convolution_piece_tails():
+    """Pieces past the last full round of a workgroup's threads run as four
+    one-row pieces each when those fit one round: the stacked 28 x 28 L = 2
+    plan has 272 pieces on 256 threads, so 16 of them.  No tail where the
+    pieces are one round (the 56 x 56 L = 3 plan: 472 pieces on 512 threads),
+    where they are fewer than the threads, or where the rest would take more
+    than a round (the 40 x 40 L = 1 plan on 128 threads: 200 pieces).  The
+    large-plane kernel keeps its deeper-levels pieces whole (64, 80 and 84 past
+    the first round at L = 3, 4, 5 of the level sweep's 128 x 128 planes); its
+    tiles have one piece per thread."""
+    for L, extra in ((2, 0), (3, 64), (4, 80), (5, 84)):
+        info = emu.large_plan(32, 128, 128, 128, 32, 64, 5, L, dtype="f32", budget_floats=160 * 256)
+        assert info[4:] == [256 + extra, 0, 256, 0], (L, info)
+    p = emu.whole_plan(64, 192, 28, 28, 5, 2, nthreads=256, dtype="f16", budget_floats=40960, stack=2)
+    assert p["ok"] and (p["items"], p["tail"]) == (272, 16)
+    p = emu.whole_plan(64, 96, 56, 56, 5, 3, nthreads=512, budget_floats=40960)
+    assert p["ok"] and (p["items"], p["tail"]) == (472, 0)
+    p = emu.whole_plan(4, 2, 16, 16, 5, 2, nthreads=256, budget_floats=40960)
+    assert p["ok"] and (p["items"], p["tail"]) == (36, 0)
+    p = emu.whole_plan(4, 2, 32, 32, 5, 2, nthreads=64, budget_floats=40960)
+    assert p["ok"] and (p["items"], p["tail"]) == (64 + 64 + 16, 16)
+    p = emu.whole_plan(4, 2, 40, 40, 5, 1, nthreads=128, budget_floats=40960)
+    assert p["ok"] and (p["items"], p["tail"]) == (100 + 100, 0)
+
+
 BWD = [
     # n, c, h, w, k, L, dtype, threads, images per workgroup
     (2, 2, 16, 16, 5, 2, "f32", 256, 2),
