@@ -597,6 +597,7 @@ BWD = [
     (2, 1, 32, 32, 3, 5, "f32", 256, 1),
     (2, 2, 24, 40, 7, 1, "f32", 512, 2),
     (2, 2, 12, 20, 1, 2, "f16", 256, 2),
+    (2, 2, 44, 44, 5, 1, "f32", 256, 1),   # 265 pieces on 256 threads: 9 run as one-row pieces
 ]
 
 
