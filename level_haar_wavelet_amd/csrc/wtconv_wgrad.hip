@@ -53,7 +53,7 @@ __global__ __launch_bounds__(512, (WtcWgradWaves<Q, (int)sizeof(T), K, TL>::v)) 
         // low wave priority for the FMA-bound correlation, high for the
         // latency-bound staging and analysis (as in the whole-plane kernel)
         __builtin_amdgcn_s_setprio(0);
-        wtc_wgrad_correlate<T, K, VEC, Q>(a, ctx, acc);
+        wtc_wgrad_correlate<T, K, VEC, Q, !TL && Q == 1>(a, ctx, acc);
         wtc_lds_barrier_wg();
         __builtin_amdgcn_s_setprio(2);
     }
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void wtconv_wgrad_finalize_kernel(int C, int k
 template <typename T, int K, int VEC, int Q, bool TL>
 static hipError_t launch_wgrad_q(const WtcWgradArgs<T> &a, hipStream_t stream, int *resident)
 {
+    if ((TL || Q != 1) && a.p.tail) return hipErrorInvalidValue;  // these instances carry no tail pieces
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_wgrad_kernel<T, K, VEC, Q, TL>;
     if (lds > 65536) {

@@ -46,6 +46,7 @@ struct WtcWgradPlan {
     int32_t groups;     // workgroups per channel
     int32_t q;          // pieces per thread
     int32_t npieces;
+    int32_t tail;       // the last `tail` pieces run as one-row pieces (see wtc_wgrad_layout)
     int32_t nmaps;      // 1 + 4L
     int32_t plen;       // floats of one partial result: k*k + 1 + 4L k*k
     int32_t vec;        // activation elements per staged row segment (at most 16 bytes)
@@ -138,6 +139,16 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     p->first[p->nmaps] = np;
     p->npieces = np;
     p->q = (np + p->nthreads - 1) / p->nthreads;
+    // One set of pieces whose last wave would hold a few: those run as P
+    // one-row pieces each on the lanes after the full waves (at most two
+    // waves of them, a quarter of a piece each), so that no wave runs a whole
+    // piece for a few lanes (the 28 x 28 L = 2 plan: 129 pieces on 256
+    // threads).  Untiled plans only; the reduction tables count threads.
+    p->tail = 0;
+    if (p->q == 1 && !p->tiled) {
+        const int32_t full = np / 64 * 64, rest = np - full;
+        if (full > 0 && rest > 0 && P * rest <= 128 && full + P * rest <= p->nthreads) p->tail = rest;
+    }
     p->plen = kk + 1 + 4 * L * kk;
     off = wtc_roundup(off, 4);
     p->tab_off = off;
@@ -154,14 +165,18 @@ static inline int32_t wtc_wgrad_layout(WtcWgradPlan *p)
     p->ctab_off = off;
     off += WTC_WG_QMAX * (WTC_WG_CHMAX + WTC_WG_NMAPS);
     p->lds_floats = wtc_roundup(off, 4);
-    // reduction tables: set s holds pieces s nth .. s nth + nth - 1
+    // reduction tables: set s holds pieces s nth .. s nth + nth - 1 (thread
+    // t: piece s nth + t), except that piece j >= F = npieces - tail of a
+    // one-set plan runs on threads F + P (j - F) .. F + P (j - F) + P - 1
+    const int32_t tf = np - p->tail;
+    auto tpos = [&](int32_t j) { return j <= tf ? j : tf + P * (j - tf); };
     for (int32_t s = 0; s < WTC_WG_QMAX; ++s) {
         int32_t nc = 0;
         for (int32_t g = 0; g < WTC_WG_NMAPS; ++g) {
             int32_t lo = 0, hi = 0;
             if (g < p->nmaps) {
-                lo = wtc_max(0, p->first[g] - s * p->nthreads);
-                hi = wtc_min(p->nthreads, p->first[g + 1] - s * p->nthreads);
+                lo = wtc_max(0, tpos(p->first[g]) - s * p->nthreads);
+                hi = wtc_min(p->nthreads, tpos(p->first[g + 1]) - s * p->nthreads);
             }
             const int32_t cnt = hi > lo ? (hi - lo + WTC_WG_CH - 1) / WTC_WG_CH : 0;
             p->mapc[s][g] = nc | (cnt << 16);
@@ -691,29 +706,75 @@ WTC_HD WTC_INLINE void wtc_wgrad_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1,
     }
 }
 
-// Q: accumulator sets the kernel holds (at least the plan's q)
-template <typename T, int K, int VEC, int Q>
+// One dy row of a piece (row r0) against its k rows of the x window.
+template <typename T, int K, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_row_piece(WtcWgradCtx<T, VEC> &ctx, int d0, int d1, int xp, int dp, bool base,
+                                          int r0, float (&acc)[K * K + 1])
+{
+    constexpr int P = WTC_WG_P;
+    constexpr int NR = (P + K - 1 + 3) / 4 * 4;  // window row, as read (16-byte reads)
+    float av[P];
+    wtc_lds_row<T, P>(ctx, d1 + r0 * dp, av);
+    if (base) {
+#pragma unroll
+        for (int c = 0; c < P; ++c) acc[K * K] += av[c];
+    }
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+        float row[NR];
+        wtc_lds_row<T, NR>(ctx, d0 + (r0 + u) * xp, row);
+#pragma unroll
+        for (int v = 0; v < K; ++v)
+#pragma unroll
+            for (int c = 0; c < P; ++c) acc[u * K + v] = wtc_fma(av[c], row[c + v], acc[u * K + v]);
+    }
+}
+
+// Piece descriptor `it`: x window, dy start, their pitches and the base flag.
+template <typename T, int VEC>
+WTC_HD WTC_INLINE void wtc_wgrad_desc(const WtcWgradPlan &p, WtcWgradCtx<T, VEC> &ctx, int it, unsigned &t0,
+                                     unsigned &t1)
+{
+    const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
+#ifdef WTC_EMULATE
+    t0 = (unsigned)tab[0];
+    t1 = (unsigned)tab[1];
+#else
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const u2 tv = *(const u2 *)tab;
+    t0 = tv.x;
+    t1 = tv.y;
+#endif
+}
+
+// Q: accumulator sets the kernel holds (at least the plan's q).  TAIL =
+// false: an instance whose plans have no tail (tiles, several sets),
+// compiled without the one-row pieces.
+template <typename T, int K, int VEC, int Q, bool TAIL = true>
 WTC_HD WTC_INLINE void wtc_wgrad_correlate(const WtcWgradArgs<T> &a, WtcWgradCtx<T, VEC> &ctx,
                                           float (&acc)[Q][K * K + 1])
 {
     const WtcWgradPlan &p = a.p;
+    const int full = p.npieces - (TAIL ? p.tail : 0);
 #pragma unroll
     for (int s = 0; s < Q; ++s) {
         const int it = s * ctx.nth + ctx.tid;
-        if (s < p.q && it < p.npieces) {
-            const int *tab = (const int *)&WTC_LDS(ctx, p.tab_off + 2 * it + 1) - 1;
+        if (s < p.q && it < full) {
             unsigned t0, t1;
-#ifdef WTC_EMULATE
-            t0 = (unsigned)tab[0];
-            t1 = (unsigned)tab[1];
-#else
-            typedef unsigned u2 __attribute__((ext_vector_type(2)));
-            const u2 tv = *(const u2 *)tab;
-            t0 = tv.x;
-            t1 = tv.y;
-#endif
+            wtc_wgrad_desc<T, VEC>(p, ctx, it, t0, t1);
             wtc_wgrad_piece<T, K, VEC>(ctx, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
                                       (int)((t1 >> 8) & 0xffu), (t1 >> 16) == 0, acc[s]);
+        }
+    }
+    if constexpr (TAIL) {
+        // the tail's one-row pieces, on the threads after the full pieces
+        // (tails exist only in one-set plans)
+        const int j = ctx.tid - full;
+        if (j >= 0 && j < WTC_WG_P * p.tail) {
+            unsigned t0, t1;
+            wtc_wgrad_desc<T, VEC>(p, ctx, full + j / WTC_WG_P, t0, t1);
+            wtc_wgrad_row_piece<T, K, VEC>(ctx, (int)(t0 & 0xffffu), (int)(t0 >> 16), (int)(t1 & 0xffu),
+                                          (int)((t1 >> 8) & 0xffu), (t1 >> 16) == 0, j % WTC_WG_P, acc[0]);
         }
     }
 }

@@ -180,10 +180,10 @@ def wgrad_tiles(x, dy, w_base, bias, s_base, w_lvl, s_lvl, k, th, tw, dtype="f32
 
 
 def wgrad_plan(n, c, h, w, k, levels, nthreads=256, planes=1, dtype="f32", budget_floats=40960):
-    out = (ctypes.c_int * 6)()
+    out = (ctypes.c_int * 7)()
     rc = _load().emu_wgrad_plan(n, c, h, w, k, levels, nthreads, planes, 4 if dtype == "f32" else 2,
                                 budget_floats, out)
-    keys = ("lds_floats", "npieces", "q", "groups", "plen", "vec")
+    keys = ("lds_floats", "npieces", "q", "groups", "plen", "vec", "tail")
     d = dict(zip(keys, list(out)))
     d["ok"] = rc == 0
     return d

@@ -629,6 +629,7 @@ int emu_wgrad_plan(int n, int c, int h, int w, int k, int levels, int nthreads, 
     out[3] = p.groups;
     out[4] = p.plen;
     out[5] = p.vec;
+    out[6] = p.tail;
     return rc;
 }
 

@@ -103,6 +103,20 @@ def test_emulated_weight_gradients_match_oracle(orc, case, tiled):
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
 
 
+def test_weight_gradient_piece_tails():
+    """A one-set weight-gradient plan whose last wave would hold a few pieces
+    runs those as four one-row pieces each on the lanes after the full waves,
+    when they take at most two waves: 129 pieces at 28 x 28, L = 2 (one tail
+    piece), 144 at 24 x 40, L = 2 (16).  None where the rest would take more
+    (28 x 28, L = 1: 113 pieces, 49 past the first wave), where no wave is
+    full (16 x 16, L = 2: 36 pieces), or where the plan has two sets (56 x 56,
+    L = 3: 472 pieces on 256 threads)."""
+    for shape, L, np_, tail in (((28, 28), 2, 129, 1), ((24, 40), 2, 144, 16), ((28, 28), 1, 113, 0),
+                                ((16, 16), 2, 36, 0), ((56, 56), 3, 472, 0)):
+        p = emu.wgrad_plan(2, 2, *shape, 5, L, nthreads=256, dtype="f16", budget_floats=1 << 16)
+        assert p["ok"] and (p["npieces"], p["tail"]) == (np_, tail), (shape, L, p)
+
+
 def _rounds_cost(n, c, slots, fixed, p):
     groups = -(-n // p)
     return -(-c * groups // slots) * (p + fixed)
