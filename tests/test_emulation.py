@@ -138,9 +138,10 @@ def test_choose_planes_fills_one_round():
     assert emu.choose_planes(64, 96, 512, 1.0) == 13
 
 
-@pytest.mark.parametrize("nthreads,planes", [(512, 2), (128, 3)])
-def test_emulated_whole_plane_thread_counts(orc, nthreads, planes):
-    n, c, h, w, k, L = 5, 2, 32, 32, 5, 3
+@pytest.mark.parametrize("nthreads,planes,L", [(512, 2, 3), (128, 3, 3), (64, 2, 2)])
+def test_emulated_whole_plane_thread_counts(orc, nthreads, planes, L):
+    # 64 threads at L = 2: 144 pieces, the last 16 as one-row pieces
+    n, c, h, w, k = 5, 2, 32, 32, 5
     inp = make_inputs(n, c, h, w, k, L, seed=nthreads + planes)
     y = emu.whole(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L, nthreads=nthreads,
                   planes=planes, budget_floats=1 << 16)

@@ -50,6 +50,10 @@ CASES = [
     (2, 3, 15, 13, 5, 2, "f32"),    # sides 2^L does not divide: the two calls
 ]
 
+# the fused pass on 256 threads, whose plans have one-row tail pieces: the
+# dx side's 265 pieces (9 of them), the gradient side's 129 (one)
+TAILS = [(2, 3, 44, 44, 5, 1, "f32"), (3, 2, 28, 28, 5, 2, "f16")]
+
 
 @pytest.fixture
 def fused(monkeypatch):
@@ -61,6 +65,15 @@ def test_backward_matches_oracle(orc, case, fused):
     n, c, h, w, k, L, dt = case
     _log("case %s" % (case,))
     inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=n + c + h + w + k + L)
+    _check(orc, inp, DevInputs(inp, dt), k, L, dt, str(case))
+
+
+@pytest.mark.parametrize("case", TAILS, ids=lambda c: "x".join(map(str, c)))
+def test_fused_pass_with_tail_pieces(orc, case, fused, monkeypatch):
+    monkeypatch.setenv("WTCONV_BWD_THREADS", "256")
+    n, c, h, w, k, L, dt = case
+    _log("case %s (256 threads)" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=3 * n + c + h + L)
     _check(orc, inp, DevInputs(inp, dt), k, L, dt, str(case))
 
 

@@ -61,13 +61,18 @@ WIDE = [
     (5, 2, 56, 56, 5, 3, "f32", 512, 3),
     (2, 3, 24, 40, 3, 3, "f16", 512, 1),
     (5, 2, 56, 56, 5, 3, "f32", 256, 2),
+    # pieces past the last full round run as one-row pieces: 144 on 64
+    # threads (16 of them), 265 on 256 threads (9)
+    (3, 2, 32, 32, 5, 2, "f32", 64, 2),
+    (2, 3, 44, 44, 5, 1, "f16", 256, 1),
 ]
 
 
 @pytest.mark.parametrize("case", WIDE, ids=lambda c: "x".join(map(str, c)))
 def test_whole_plane_thread_counts_and_image_groups(orc, case, monkeypatch):
-    """The whole-plane kernel at 256 and 512 threads and with image groups
-    that leave a ragged last group."""
+    """The whole-plane kernel at 64, 256 and 512 threads, with image groups
+    that leave a ragged last group, and with plans whose last pieces run as
+    one-row pieces."""
     n, c, h, w, k, L, dt, th, planes = case
     _log("case %s" % (case,))
     monkeypatch.setenv("WTCONV_WHOLE_THREADS", str(th))

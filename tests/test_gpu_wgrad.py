@@ -37,7 +37,9 @@ SMALL = [
     (1, 2, 32, 32, 5, 5, "f32"),
     (2, 3, 9, 13, 5, 0, "f32"),
     (2, 8, 16, 16, 5, 2, "f16"),
-    (3, 2, 28, 28, 5, 2, "f16"),
+    (3, 2, 28, 28, 5, 2, "f16"),    # 129 pieces: the last as one-row pieces
+    (2, 3, 24, 40, 3, 2, "f32"),    # 144 pieces: 16 as one-row pieces
+    (3, 2, 40, 40, 5, 1, "f16"),    # 200 pieces: 8 as one-row pieces
     (1, 2, 96, 160, 5, 4, "f32"),   # tiled path
     (2, 2, 128, 128, 3, 5, "f16"),  # tiled path
 ]
