@@ -14,8 +14,9 @@ static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitc
 // registers per lane.  DL: the deeper-levels plan's level count (L - 1) for
 // DL = 1..3, a kernel instance each, so that its staging, analysis and output
 // passes take no branch on it; DL = 0: read from the plan (L >= 5, where the
-// unrolled instances measured no faster).
-template <typename T, int K, int BW, int DL>
+// unrolled instances measured no faster).  HALF: tiles whose pieces run as
+// 2-row halves (without the base path: the nested call of a larger plane).
+template <typename T, int K, int BW, int DL, bool HALF = false>
 __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
 {
     extern __shared__ float wtc_lds[];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
             // the next image's deeper-levels input lands during the last tile
             if (t == tiles - 1 && img + 1 < cd.nimg) wtc_large_fetch_d<T>(A, cd, img + 1, raw);
             __builtin_amdgcn_s_setprio(0);
-            wtc_whole_conv<T, K, BW, false>(at, ct);
+            wtc_whole_conv<T, K, BW, false, HALF>(at, ct);
             wtc_lds_barrier();
             __builtin_amdgcn_s_setprio(2);
             if (t + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct);
@@ -84,16 +85,18 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
     }
 }
 
-template <typename T, int K, int DL>
+template <typename T, int K, int DL, bool HALF = false>
 static hipError_t launch_dl(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
 {
+    // (other instances run such plans' pieces whole)
+    if (HALF && !a.t.p.halves) return hipErrorInvalidValue;
     // the instance's analysis starts where the plan's staging stops
     const WtcWholePlan &d = a.d.p;
     const int first = d.stage_l3 ? 4 : (d.gr == 4 && d.vec >= 4 && d.levels >= 2 ? 3 : 2);
     if (DL && (d.levels != DL || first != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)))) return hipErrorInvalidValue;
     if (d.tail || a.t.p.tail) return hipErrorInvalidValue;  // no tail loop in this kernel
     const size_t lds = (size_t)a.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_large_kernel<T, K, 4, DL>;
+    const void *fn = (const void *)&wtconv_large_kernel<T, K, 4, DL, HALF>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -103,8 +106,8 @@ static hipError_t launch_dl(const WtcLargeArgs<T> &a, hipStream_t stream, int *r
         return hipSuccess;
     }
     const unsigned groups = (unsigned)((a.n + a.planes - 1) / a.planes);
-    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4, DL>), dim3(groups * (unsigned)a.c), dim3(a.t.p.nthreads), lds,
-                       stream, a);
+    hipLaunchKernelGGL((wtconv_large_kernel<T, K, 4, DL, HALF>), dim3(groups * (unsigned)a.c), dim3(a.t.p.nthreads),
+                       lds, stream, a);
     return hipGetLastError();
 }
 
@@ -112,6 +115,17 @@ template <typename T, int K>
 static hipError_t launch_k(const WtcLargeArgs<T> &a, hipStream_t stream, int *resident)
 {
     if (a.d.p.out_bw != 4 || a.t.p.out_bw != 4 || a.d.p.gr != 4) return hipErrorInvalidValue;
+    if constexpr (sizeof(T) == 4 && K == 5) {
+        // the nested call of a larger plane runs on its fp32 level-1 map
+        if (a.t.p.halves) {
+            switch (a.d.p.levels) {
+            case 1: return launch_dl<T, K, 1, true>(a, stream, resident);
+            case 2: return launch_dl<T, K, 2, true>(a, stream, resident);
+            case 3: return launch_dl<T, K, 3, true>(a, stream, resident);
+            default: return launch_dl<T, K, 0, true>(a, stream, resident);
+            }
+        }
+    }
     switch (a.d.p.levels) {
     case 1: return launch_dl<T, K, 1>(a, stream, resident);
     case 2: return launch_dl<T, K, 2>(a, stream, resident);

@@ -57,6 +57,7 @@ struct WtcWholePlan {
     int32_t wf_off;
     int32_t items;       // convolution pieces per image
     int32_t tail;        // the last `tail` pieces run as one-row pieces (see wtc_whole_layout)
+    int32_t halves;      // every piece runs as two 2-row halves, one per thread (see wtc_whole_layout)
     int32_t tab_off;     // piece descriptors, 4 ints each
     int32_t lds_floats;
     // Tiling, for planes too large for one workgroup: h x w above is then one
@@ -152,6 +153,10 @@ static inline int32_t wtc_whole_layout(WtcWholePlan *p)
     // plans have none (their kernel instances carry no tail loop).
     const int32_t rem = items % p->nthreads;
     p->tail = !p->tiled && items > p->nthreads && P * rem <= p->nthreads ? rem : 0;
+    // Tiles without the base path have level 1's pieces only, half as many as
+    // threads: as 2-row halves every wave (and so every SIMD) takes a share
+    // instead of half the waves taking all of it.
+    p->halves = p->tiled && p->nobase && 2 * items == p->nthreads;
     p->tab_off = off;
     off += 4 * items;
     p->lds_floats = wtc_roundup(off, 4);
@@ -932,16 +937,76 @@ WTC_HD WTC_INLINE void wtc_whole_row_piece(const WtcWholePlan &p, WtcWholeCtx<T>
     wtc_lds_store4<T, P>(ctx, dst, acc);
 }
 
+// R output rows of P columns of piece `it`, from its row r0 (plans with
+// halves: two threads to a piece).
+template <typename T, int K, int R>
+WTC_HD WTC_INLINE void wtc_whole_piece_rows(const WtcWholePlan &p, WtcWholeCtx<T> &ctx, int it, int r0)
+{
+    constexpr int P = WTC_WP, KK = K * K, WS = (KK + 3) / 4 * 4;
+    constexpr int NW = P + K - 1, NR = (NW + 3) / 4 * 4;  // window width, as read
+    int dsc[4];
+    {
+        float tmp[4];
+        wtc_lds_row<T, 4>(ctx, p.tab_off + 4 * it, tmp);
+        for (int e = 0; e < 4; ++e) {
+#ifdef WTC_EMULATE
+            __builtin_memcpy(&dsc[e], &tmp[e], 4);
+#else
+            dsc[e] = __float_as_int(tmp[e]);
+#endif
+        }
+    }
+    const int ip = dsc[2] & 0xffff, op = dsc[2] >> 16;
+    const int src = dsc[0] + r0 * ip, dst = dsc[1] + r0 * op;
+    const int wk = dsc[3] & 0xffff;
+    const float init = (dsc[3] >> 16) ? ctx.bias : 0.0f;
+    float wv[WS];
+    wtc_lds_row<T, WS>(ctx, wk, wv);
+    float acc[R][P];
+#pragma unroll
+    for (int dr = 0; dr < R; ++dr)
+#pragma unroll
+        for (int dc = 0; dc < P; ++dc) acc[dr][dc] = init;
+    float row[NR];
+    wtc_lds_row<T, NR>(ctx, src, row);
+#pragma unroll
+    for (int t = 0; t < R + K - 1; ++t) {
+        float nxt[NR];
+        if (t + 1 < R + K - 1) wtc_lds_row<T, NR>(ctx, src + (t + 1) * ip, nxt);
+#pragma unroll
+        for (int dr = 0; dr < R; ++dr) {
+            const int u = t - dr;
+            if (u < 0 || u >= K) continue;
+#pragma unroll
+            for (int v = 0; v < K; ++v)
+#pragma unroll
+                for (int dc = 0; dc < P; ++dc) acc[dr][dc] = wtc_fma(wv[u * K + v], row[dc + v], acc[dr][dc]);
+        }
+        if (t + 1 < R + K - 1) {
+#pragma unroll
+            for (int e = 0; e < NR; ++e) row[e] = nxt[e];
+        }
+    }
+#pragma unroll
+    for (int dr = 0; dr < R; ++dr) wtc_lds_store4<T, P>(ctx, dst + dr * op, acc[dr]);
+}
+
 // The convolution phase: every thread computes pieces tid, tid + nth, ...,
 // then one-row pieces of the plan's tail (four lanes to a piece).  TAIL =
 // false: an instance whose plans have no tail (tiles, the large-plane
-// kernel), compiled without that loop.
-template <typename T, int K, int BW, bool TAIL = true>
+// kernel), compiled without that loop.  HALF: an instance whose plans run
+// every piece as two 2-row halves (plans with halves).
+template <typename T, int K, int BW, bool TAIL = true, bool HALF = false>
 WTC_HD WTC_INLINE void wtc_whole_conv(const WtcWholeArgs<T> &a, WtcWholeCtx<T> &ctx)
 {
     constexpr int P = WTC_WP, KK = K * K, WS = (KK + 3) / 4 * 4;
     constexpr int NW = P + K - 1, NR = (NW + 3) / 4 * 4;  // window width, as read
     const WtcWholePlan &p = a.p;
+    if constexpr (HALF) {
+        for (int it = ctx.tid; it < 2 * p.items; it += ctx.nth)
+            wtc_whole_piece_rows<T, K, 2>(p, ctx, it >> 1, 2 * (it & 1));
+        return;
+    }
     const int full = p.items - p.tail;
     for (int it = ctx.tid; it < full; it += ctx.nth) {
         int dsc[4];

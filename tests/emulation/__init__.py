@@ -227,7 +227,8 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
     on chip, base and level 1 on th x tw tiles; nobase: without the base path)
     on the CPU emulation.  Returns (output, info) with info = images per
     workgroup, LDS floats, deeper-levels map floats, tiles per image, and the
-    pieces and one-row tail pieces of the deeper-levels and tile plans."""
+    pieces and one-row tail pieces of the deeper-levels and tile plans, and
+    whether the tiles run their pieces as 2-row halves."""
     lib = _load()
     n, c, h, w = x.shape
     npdt = np.float32 if dtype == "f32" else np.float16
@@ -235,7 +236,7 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
     out = np.full_like(xin, np.nan)
     keep = [_f32(w_base), _f32(bias), _f32(s_base), _f32(w_lvl), _f32(s_lvl)]
     ptr = lambda a: None if a is None else a.ctypes.data
-    info = (ctypes.c_int * 8)()
+    info = (ctypes.c_int * 9)()
     rc = lib.emu_large(0 if dtype == "f32" else 1, xin.ctypes.data, out.ctypes.data, n, c, h, w, th, tw, k, levels,
                        rotate, *[ptr(a) for a in keep], planes, budget_floats, int(bool(nobase)), info)
     if rc != 0:
@@ -244,7 +245,7 @@ def large(x, w_base, bias, s_base, w_lvl, s_lvl, k, levels, th, tw, rotate=0, dt
 
 
 def large_plan(n, c, h, w, th, tw, k, levels, dtype="f32", planes=1, budget_floats=40960, nobase=False):
-    info = (ctypes.c_int * 8)()
+    info = (ctypes.c_int * 9)()
     rc = _load().emu_large(0 if dtype == "f32" else 1, None, None, n, c, h, w, th, tw, k, levels, 0, None, None, None,
                            None, None, planes, budget_floats, int(bool(nobase)), info)
     return None if rc != 0 else list(info)

@@ -191,9 +191,10 @@ static int run_whole_t(const WtcWholeArgs<T> &a)
 // staging covers the halos), and the deeper levels must zero their own maps.
 // DL: the deeper-levels plan's level count, as the kernel instance has it
 // (0: read from the plan)
-template <typename T, int K, int BW, int DL>
+template <typename T, int K, int BW, int DL, bool HALF = false>
 static void run_large(const WtcLargeArgs<T> &A)
 {
+    if (HALF && !A.t.p.halves) abort();
     if (DL && (wtc_whole_first_deep(A.d.p) != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)) || A.d.p.levels != DL)) {
         fprintf(stderr, "wtconv emulation: deeper-levels plan does not match its instance\n");
         abort();
@@ -264,7 +265,7 @@ static void run_large(const WtcLargeArgs<T> &A)
             for (int t = 0; t < nth; ++t)
                 if (tiles > 1) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + 1);
             for (int tt = 0; tt < tiles; ++tt) {
-                for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW, false>(at, ct[t]);
+                for (int t = 0; t < nth; ++t) wtc_whole_conv<T, K, BW, false, HALF>(at, ct[t]);
                 for (int t = 0; t < nth; ++t) {
                     if (tt + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct[t]);
                     if (tt + 2 < tiles) wtc_whole_load<T, K, BW, true, false>(at, ct[t], u0 + tt + 2);
@@ -282,6 +283,16 @@ static void run_large(const WtcLargeArgs<T> &A)
 template <typename T, int K>
 static int run_large_k(const WtcLargeArgs<T> &a)
 {
+    if constexpr (sizeof(T) == 4 && K == 5) {
+        if (a.t.p.halves) {
+            switch (a.d.p.levels) {
+            case 1: run_large<T, K, 4, 1, true>(a); return 0;
+            case 2: run_large<T, K, 4, 2, true>(a); return 0;
+            case 3: run_large<T, K, 4, 3, true>(a); return 0;
+            default: run_large<T, K, 4, 0, true>(a); return 0;
+            }
+        }
+    }
     switch (a.d.p.levels) {
     case 1: run_large<T, K, 4, 1>(a); return 0;
     case 2: run_large<T, K, 4, 2>(a); return 0;
@@ -749,6 +760,7 @@ int emu_large(int dtype, const void *in, void *out, int n, int c, int h, int w, 
         info[5] = p.d.tail;
         info[6] = p.t.items;
         info[7] = p.t.tail;
+        info[8] = p.t.halves;
     }
     if (!in) return 0;
     if (dtype == 0)

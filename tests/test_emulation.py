@@ -577,6 +577,8 @@ def test_large_plane_plan_sizes():
     # map (128 x 128, L = 3) without the base path, 16 x 128 tiles
     info = emu.large_plan(16, 256, 128, 128, 16, 128, 5, 3, dtype="f32", budget_floats=160 * 256, nobase=True)
     assert info is not None and info[1] * 4 <= 80 * 1024, info
+    # its tiles have 128 level-1 pieces for 256 threads: they run as 2-row halves
+    assert info[6] == 128 and info[8] == 1, info
 
 
 def test_convolution_piece_tails():
@@ -591,7 +593,7 @@ def test_convolution_piece_tails():
     tiles have one piece per thread."""
     for L, extra in ((2, 0), (3, 64), (4, 80), (5, 84)):
         info = emu.large_plan(32, 128, 128, 128, 32, 64, 5, L, dtype="f32", budget_floats=160 * 256)
-        assert info[4:] == [256 + extra, 0, 256, 0], (L, info)
+        assert info[4:] == [256 + extra, 0, 256, 0, 0], (L, info)
     p = emu.whole_plan(64, 192, 28, 28, 5, 2, nthreads=256, dtype="f16", budget_floats=40960, stack=2)
     assert p["ok"] and (p["items"], p["tail"]) == (272, 16)
     p = emu.whole_plan(64, 96, 56, 56, 5, 3, nthreads=512, budget_floats=40960)
