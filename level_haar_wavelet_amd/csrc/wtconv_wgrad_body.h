@@ -244,8 +244,13 @@ static inline int wtc_wgrad_plan_common(WtcWgradPlan *p, int32_t n, int32_t c, i
     p->first_deep = (levels >= 2 && p->gr == 4 && vec >= 4) ? 3 : 2;
     wtc_wgrad_layout(p);
     if (p->q > WTC_WG_QMAX) return -1;
-    // descriptor fields: pitches below 256, LDS indexes below 65536
-    if (p->x.pitch > 255 || p->dy.pitch > 255 || p->lds_floats > 65535) return -1;
+    // descriptor fields: pitches below 256 and LDS indexes below 65536; the
+    // pitch of every map a piece reads counts, the level maps' too (without
+    // the base path the full-resolution maps are one zero-pitch row and the
+    // level-1 maps are the widest)
+    int32_t maxp = wtc_max(p->x.pitch, p->dy.pitch);
+    for (int32_t m = 1; m <= levels; ++m) maxp = wtc_max(maxp, wtc_max(p->u[m].pitch, p->d[m].pitch));
+    if (maxp > 255 || p->lds_floats > 65535) return -1;
     return p->lds_floats <= budget_floats ? 0 : -1;
 }
 

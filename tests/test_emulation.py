@@ -103,6 +103,25 @@ def test_emulated_weight_gradients_match_oracle(orc, case, tiled):
         assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
 
 
+def test_weight_gradient_plans_refuse_pitches_past_the_descriptor_fields(orc):
+    """Piece descriptors hold map pitches in 8 bits.  Without the base path
+    the widest maps a piece reads are level 1's, so a plane whose level-1
+    maps need a pitch above 255 (8 x 512, the nested call of a 64 x 4096
+    layer three levels down) is refused, and the one just below the limit
+    (8 x 480) computes the oracle's gradients."""
+    inp = make_inputs(1, 1, 8, 512, 3, 3, seed=5)
+    with pytest.raises(ValueError):
+        emu.wgrad(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, 3, 3, nthreads=256,
+                  budget_floats=40960, nobase=True)
+    inp = make_inputs(1, 1, 8, 480, 3, 3, seed=6)
+    got = emu.wgrad(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, 3, 3, nthreads=256,
+                    budget_floats=40960, nobase=True)
+    zero = np.zeros_like(inp.s_base)
+    ref = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, zero, inp.w_lvl, inp.s_lvl, 3, 3)
+    for gg, rr in zip(got[3:], ref[3:]):
+        assert np.linalg.norm(gg - rr) / np.linalg.norm(rr) <= 2e-6
+
+
 def test_weight_gradient_piece_tails():
     """A one-set weight-gradient plan whose last wave would hold a few pieces
     runs those as four one-row pieces each on the lanes after the full waves,

@@ -13,7 +13,8 @@ from level_haar_wavelet_amd.synthetic import WORKLOADS, make_inputs, sweep_workl
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from tests.gpu_util import DevInputs, assert_close, assert_grad_close, backward_data, backward_weight, forward
+    from tests.gpu_util import (DevInputs, assert_close, assert_grad_close, assert_grads_close, backward_data,
+                                backward_weight, forward)
 
 
 def _log(msg):
@@ -38,6 +39,34 @@ SMALL = [
     (1, 2, 28, 28, 5, 2, "f16"),
     (1, 2, 96, 160, 5, 4, "f32"),
 ]
+
+
+# the largest side the ABI takes (WTCONV_MAX_SIDE) with the most levels: the
+# tiled passes and their nested calls on the low-pass maps recurse down to
+# planes one workgroup holds
+MAXIMUM = [
+    (1, 2, 4096, 64, 5, 6, "f32"),
+    (1, 1, 64, 4096, 3, 6, "f16"),
+    (1, 1, 4096, 4096, 5, 6, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", MAXIMUM, ids=lambda c: "x".join(map(str, c)))
+def test_maximum_side_and_levels(orc, case):
+    n, c, h, w, k, L, dt = case
+    _log("case %s" % (case,))
+    inp = make_inputs(n, c, h, w, k, L, dtype=dt, seed=h + 2 * w + k + L)
+    d = DevInputs(inp, dt)
+    y = forward(d)
+    dx = backward_data(d)
+    grads = backward_weight(d)
+    torch.cuda.synchronize()
+    ref_y = orc.forward(inp.x, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(y, ref_y, dt, "y")
+    ref_dx = orc.backward_data(inp.dy, inp.w_base, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_close(dx, ref_dx, dt, "dx")
+    ref_g = orc.backward_weight(inp.x, inp.dy, inp.w_base, inp.bias, inp.s_base, inp.w_lvl, inp.s_lvl, k, L)
+    assert_grads_close(grads, ref_g, dt, str(case))
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c)))
