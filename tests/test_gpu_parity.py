@@ -48,6 +48,9 @@ MAXIMUM = [
     (1, 2, 4096, 64, 5, 6, "f32"),
     (1, 1, 64, 4096, 3, 6, "f16"),
     (1, 1, 4096, 4096, 5, 6, "f16"),
+    (1, 1, 4096, 64, 7, 6, "f32"),
+    (2, 1, 64, 4096, 1, 6, "f32"),
+    (1, 1, 4095, 65, 5, 6, "f32"),   # ragged: zero-padded to 4096 x 128
 ]
 
 
