@@ -72,6 +72,25 @@ def test_maximum_side_and_levels(orc, case):
     assert_grads_close(grads, ref_g, dt, str(case))
 
 
+# degenerate shapes: single pixels, 2-pixel sides, level maps of one pixel,
+# planes one pixel wide or high, ragged sides smaller than 2^L, many channels
+DEGENERATE = [
+    (1, 1, 1, 1, 5, 0, "f32"),
+    (1, 3, 1, 7, 5, 0, "f16"),
+    (1, 1, 4096, 1, 5, 0, "f32"),
+    (3, 2, 2, 2, 3, 1, "f32"),
+    (2, 2, 3, 3, 5, 2, "f32"),
+    (2, 3, 2, 4096, 5, 1, "f16"),
+    (1, 2, 4096, 2, 3, 1, "f32"),
+    (8, 2048, 8, 8, 5, 3, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", DEGENERATE, ids=lambda c: "x".join(map(str, c)))
+def test_degenerate_shapes(orc, case):
+    test_maximum_side_and_levels(orc, case)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c)))
 def test_small_shapes(orc, case):
     n, c, h, w, k, L, dt = case
