@@ -91,6 +91,26 @@ def test_degenerate_shapes(orc, case):
     test_maximum_side_and_levels(orc, case)
 
 
+def _random_shapes(count, seed=2024):
+    """Seeded random layers: 1-3 images, 1-4 channels, sides 1-300 (mostly
+    ragged against 2^L), every k and L = 0..6, fp32 and fp16."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    for _ in range(count):
+        n, c = rng.randint(1, 3), rng.randint(1, 4)
+        h, w = rng.randint(1, 300), rng.randint(1, 300)
+        k, L = rng.choice([1, 3, 5, 7]), rng.randint(0, 6)
+        out.append((n, c, h, w, k, L, rng.choice(["f32", "f16"])))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_shapes(40), ids=lambda c: "x".join(map(str, c)))
+def test_random_shapes(orc, case):
+    test_maximum_side_and_levels(orc, case)
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c)))
 def test_small_shapes(orc, case):
     n, c, h, w, k, L, dt = case
