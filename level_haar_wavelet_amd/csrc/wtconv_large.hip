@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256, 2) void wtconv_large_kernel(WtcLargeArgs<T> A)
             if (t + 1 < tiles) wtc_whole_stage<T, K, BW, true, false>(at, ct);
             if (t + 2 < tiles) wtc_whole_load<T, K, BW, true, false>(at, ct, u0 + t + 2);
             wtc_whole_select<T, false>(at, ct, u0 + t);
-            wtc_whole_out<T, K, BW, true, false, 1>(at, ct);
+            wtc_whole_out<T, K, BW, true, false, 1, 1>(at, ct);  // the tile plan has level 1
             wtc_lds_barrier();
         }
     }

@@ -14,8 +14,10 @@ static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitc
 // ST: stacked small planes (two images per pass); a kernel instance of its
 // own, so that the other plans carry none of its row checks.  G4: 4-row
 // staging groups, which tiled and stacked plans always have (an instance of
-// its own for whole planes whose height 4 divides measured no faster).
-template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST>
+// its own for whole planes whose height 4 divides measured no faster).  LV:
+// the plan's level count where an instance knows it (tiles of L >= 1 layers
+// carry level 1), so that the output pass reads level 1's bands untested.
+template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST, int LV = 0>
 __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
     extern __shared__ float wtc_lds[];
@@ -58,17 +60,18 @@ __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
         if (img + 1 < ctx.nimg) wtc_whole_stage<T, K, BW, TL, ST, G4>(a, ctx);
         if (img + 2 < ctx.nimg) wtc_whole_load<T, K, BW, TL, ST, G4>(a, ctx, img + 2);
         wtc_whole_select<T, ST>(a, ctx, img);
-        wtc_whole_out<T, K, BW, TL, ST>(a, ctx);
+        wtc_whole_out<T, K, BW, TL, ST, 0, LV>(a, ctx);
         wtc_lds_barrier();
     }
 }
 
-template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST>
+template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST, int LV = 0>
 static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     if (TL && a.p.tail) return hipErrorInvalidValue;  // the tiled instances carry no tail loop
+    if (LV && a.p.levels != LV) return hipErrorInvalidValue;
     const size_t lds = (size_t)a.p.lds_floats * sizeof(float);
-    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST, G4>;
+    const void *fn = (const void *)&wtconv_whole_kernel<T, K, BW, TL, ST, G4, LV>;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -79,14 +82,22 @@ static hipError_t launch_tl(const WtcWholeArgs<T> &a, hipStream_t stream, int *r
     }
     const unsigned groups = (unsigned)((a.p.units + a.p.planes - 1) / a.p.planes);
     const unsigned blocks = groups * (unsigned)a.p.c;
-    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL, ST, G4>), dim3(blocks), dim3(a.p.nthreads), lds, stream, a);
+    hipLaunchKernelGGL((wtconv_whole_kernel<T, K, BW, TL, ST, G4, LV>), dim3(blocks), dim3(a.p.nthreads), lds, stream,
+                       a);
     return hipGetLastError();
 }
 
 template <typename T, int K, int BW>
 static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
-    if (a.p.tiled) return launch_tl<T, K, BW, true, false>(a, stream, resident);
+    if (a.p.tiled) {
+        // tiles have 4-wide output blocks; L = 0 tiles (a plain depthwise
+        // convolution) take the instance that tests the level count
+        if constexpr (BW == 4) {
+            if (a.p.levels == 1) return launch_tl<T, K, BW, true, false, true, 1>(a, stream, resident);
+        }
+        return launch_tl<T, K, BW, true, false>(a, stream, resident);
+    }
     return a.p.stack > 1 ? launch_tl<T, K, BW, false, true>(a, stream, resident)
                          : launch_tl<T, K, BW, false, false>(a, stream, resident);
 }

@@ -94,7 +94,7 @@ static void emu_stage_l3(const WtcWholeArgs<T> &a, std::vector<WtcWholeCtx<T>> &
     }
 }
 
-template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST>
+template <typename T, int K, int BW, bool TL, bool ST = false, bool G4 = TL || ST, int LV = 0>
 static void run_whole(const WtcWholeArgs<T> &a)
 {
     const WtcWholePlan &p = a.p;
@@ -141,7 +141,7 @@ static void run_whole(const WtcWholeArgs<T> &a)
             if (p.stage_l3 && img + 1 < ctx[0].nimg) emu_stage_l3(a, ctx);
             for (int t = 0; t < nth; ++t) {
                 wtc_whole_select<T, ST>(a, ctx[t], img);
-                wtc_whole_out<T, K, BW, TL, ST>(a, ctx[t]);
+                wtc_whole_out<T, K, BW, TL, ST, 0, LV>(a, ctx[t]);
             }
         }
     }
@@ -153,7 +153,13 @@ static void run_whole_k(const WtcWholeArgs<T> &a)
     if (a.p.tiled) {
         switch (a.p.out_bw) {
         case 8: run_whole<T, K, 8, true>(a); break;
-        case 4: run_whole<T, K, 4, true>(a); break;
+        case 4:
+            // as the launch: L = 1 tiles take the instance that knows it
+            if (a.p.levels == 1)
+                run_whole<T, K, 4, true, false, true, 1>(a);
+            else
+                run_whole<T, K, 4, true>(a);
+            break;
         default: run_whole<T, K, 2, true>(a); break;
         }
         return;
@@ -272,7 +278,7 @@ static void run_large(const WtcLargeArgs<T> &A)
                 }
                 for (int t = 0; t < nth; ++t) {
                     wtc_whole_select<T, false>(at, ct[t], u0 + tt);
-                    wtc_whole_out<T, K, BW, true, false, 1>(at, ct[t]);
+                    wtc_whole_out<T, K, BW, true, false, 1, 1>(at, ct[t]);
                 }
             }
             poison_maps();
