@@ -95,6 +95,7 @@ static hipError_t launch_dl(const WtcLargeArgs<T> &a, hipStream_t stream, int *r
     const int first = d.stage_l3 ? 4 : (d.gr == 4 && d.vec >= 4 && d.levels >= 2 ? 3 : 2);
     if (DL && (d.levels != DL || first != (DL >= 3 ? 4 : (DL >= 2 ? 3 : 2)))) return hipErrorInvalidValue;
     if (d.tail || a.t.p.tail) return hipErrorInvalidValue;  // no tail loop in this kernel
+    if (a.t.p.levels != 1) return hipErrorInvalidValue;     // the tiles' output pass assumes level 1
     const size_t lds = (size_t)a.lds_floats * sizeof(float);
     const void *fn = (const void *)&wtconv_large_kernel<T, K, 4, DL, HALF>;
     if (lds > 65536) {

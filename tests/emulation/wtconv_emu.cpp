@@ -209,6 +209,10 @@ static void run_large(const WtcLargeArgs<T> &A)
         fprintf(stderr, "wtconv emulation: a large-plane plan with a piece tail\n");
         abort();
     }
+    if (A.t.p.levels != 1) {  // as the launch: the tiles' output pass assumes level 1
+        fprintf(stderr, "wtconv emulation: a large-plane tile plan without level 1\n");
+        abort();
+    }
     const WtcLargeArgs<T> &lp = A;
     const WtcWholeArgs<T> &ad = A.d, &at = A.t;
     const int groups = (lp.n + lp.planes - 1) / lp.planes;
