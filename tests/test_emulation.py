@@ -530,6 +530,9 @@ LARGE = [
     (1, 2, 64, 128, 7, 5, "f32", 32, 64, 1),
     (2, 1, 32, 64, 1, 2, "f16", 16, 32, 2),
     (1, 1, 128, 128, 5, 3, "f32", 32, 64, 1),  # the level sweep's plane
+    (1, 1, 128, 128, 7, 5, "f32", 32, 64, 1),  # ... with the other kernel sizes
+    (1, 1, 128, 128, 3, 5, "f16", 32, 64, 1),
+    (1, 1, 128, 128, 1, 4, "f16", 16, 128, 1),
 ]
 
 

@@ -72,6 +72,25 @@ def test_maximum_side_and_levels(orc, case):
     assert_grads_close(grads, ref_g, dt, str(case))
 
 
+# the level sweep's 128 x 128 planes with the other kernel sizes: the fused
+# large-plane kernel's k = 1, 3 and 7 instances (one per deeper-levels count
+# where L - 1 <= 3, the generic one beyond), the tiled weight pass and its
+# nested call, at their real shape
+SWEEP_K = [
+    (2, 3, 128, 128, 3, 2, "f32"),
+    (2, 3, 128, 128, 7, 5, "f32"),
+    (1, 2, 128, 128, 7, 2, "f32"),
+    (2, 3, 128, 128, 7, 3, "f16"),
+    (2, 3, 128, 128, 1, 4, "f16"),
+    (1, 2, 128, 128, 3, 5, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", SWEEP_K, ids=lambda c: "x".join(map(str, c)))
+def test_sweep_planes_other_kernel_sizes(orc, case):
+    test_maximum_side_and_levels(orc, case)
+
+
 # degenerate shapes: single pixels, 2-pixel sides, level maps of one pixel,
 # planes one pixel wide or high, ragged sides smaller than 2^L, many channels
 DEGENERATE = [
