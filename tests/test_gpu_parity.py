@@ -91,6 +91,21 @@ def test_sweep_planes_other_kernel_sizes(orc, case):
     test_maximum_side_and_levels(orc, case)
 
 
+# the 256 x 256 planes (tiles plus a nested call on the 128 x 128 level-1
+# map, itself fused without its base path) with the other kernel sizes
+LARGE_K = [
+    (1, 2, 256, 256, 7, 3, "f32"),
+    (1, 2, 256, 256, 3, 5, "f16"),
+    (1, 1, 256, 256, 1, 2, "f32"),
+    (1, 1, 256, 256, 7, 4, "f16"),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_K, ids=lambda c: "x".join(map(str, c)))
+def test_large_planes_other_kernel_sizes(orc, case):
+    test_maximum_side_and_levels(orc, case)
+
+
 # degenerate shapes: single pixels, 2-pixel sides, level maps of one pixel,
 # planes one pixel wide or high, ragged sides smaller than 2^L, many channels
 DEGENERATE = [
