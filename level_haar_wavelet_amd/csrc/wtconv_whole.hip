@@ -16,7 +16,8 @@ static __device__ __forceinline__ void wtc_lds_barrier() { asm volatile("s_waitc
 // staging groups, which tiled and stacked plans always have (an instance of
 // its own for whole planes whose height 4 divides measured no faster).  LV:
 // the plan's level count where an instance knows it (tiles of L >= 1 layers
-// carry level 1), so that the output pass reads level 1's bands untested.
+// carry level 1), so that the output pass reads level 1's bands without a
+// run-time test of the count.  LV = 0: read from the plan.
 template <typename T, int K, int BW, bool TL, bool ST, bool G4 = TL || ST, int LV = 0>
 __global__ __launch_bounds__(512) void wtconv_whole_kernel(WtcWholeArgs<T> a)
 {
@@ -91,8 +92,9 @@ template <typename T, int K, int BW>
 static hipError_t launch_bw(const WtcWholeArgs<T> &a, hipStream_t stream, int *resident)
 {
     if (a.p.tiled) {
-        // tiles have 4-wide output blocks; L = 0 tiles (a plain depthwise
-        // convolution) take the instance that tests the level count
+        // level-1 tiles with 4-wide output blocks (every tile shape the
+        // planner tries) know their level count; L = 0 tiles (a plain
+        // depthwise convolution) and wider blocks read it from the plan
         if constexpr (BW == 4) {
             if (a.p.levels == 1) return launch_tl<T, K, BW, true, false, true, 1>(a, stream, resident);
         }
