@@ -877,8 +877,21 @@ WTC_HD WTC_INLINE float wtc_wgrad_finalize_lane(int lane, int c, int g, int C, i
     const int off = g == 0 ? 0 : kk + 1 + (g - 1) * kk;
     const int nval = g == 0 ? kk + 1 : kk;
     float gsum = 0.0f;
-    if (lane < nval)
-        for (int q = 0; q < groups; ++q) gsum += partial[((int64_t)q * C + c) * plen + off + lane];
+    if (lane < nval) {
+        // eight groups' loads in flight at once, added in group order (the
+        // order of the sum stays fixed; one load at a time made every group a
+        // memory round trip)
+        const float *src = partial + (int64_t)c * plen + off + lane;
+        const int64_t stride = (int64_t)C * plen;
+        for (int q = 0; q < groups; q += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = q + u < groups ? src[(q + u) * stride] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (q + u < groups) gsum += v[u];
+        }
+    }
     float term = 0.0f;
     if (g == 0) {
         const float s0 = s_base[c];
